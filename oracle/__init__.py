@@ -1,0 +1,118 @@
+"""CPU oracle -- TEST INFRASTRUCTURE.
+
+numpy front end over ``liboracle.so`` (plain single-threaded C, see oracle.c).
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package; the product path never does.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        P = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int
+        L.oracle_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
+        L.oracle_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i64, P, P, P, P]
+        L.oracle_restripe_prob.argtypes = [P, i64, i32, i32, i64, P]
+        L.oracle_combine.argtypes = [P, i64, P, i64, i32, i32, P]
+        L.oracle_f32_to_bf16_array.argtypes = [P, i64, P]
+        L.oracle_f32_to_bf16_array.restype = None
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        for f in ("oracle_layout", "oracle_dispatch", "oracle_restripe_prob", "oracle_combine"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def layout(topk_idx, E: int, R: int, N: int) -> dict:
+    idx = _c(topk_idx, np.int64)
+    T, k = idx.shape
+    out = dict(
+        count_r=np.zeros(R, np.int32), count_n=np.zeros(N, np.int32),
+        count_e=np.zeros(E, np.int32), in_rank=np.zeros((T, R), np.uint8),
+        rank_offset=np.zeros(R + 1, np.int32), expert_offset=np.zeros(E + 1, np.int32),
+        token_slot=np.zeros((T, R), np.int32), error_flag=np.zeros(1, np.int32))
+    rc = lib().oracle_layout(_p(idx), T, k, E, R, N, _p(out["count_r"]), _p(out["count_n"]),
+                             _p(out["count_e"]), _p(out["in_rank"]), _p(out["rank_offset"]),
+                             _p(out["expert_offset"]), _p(out["token_slot"]),
+                             _p(out["error_flag"]))
+    if rc != 0:
+        raise ValueError("oracle_layout: bad arguments")
+    return out
+
+
+def dispatch(x, topk_idx, topk_w, E: int, R: int, token_slot, cap: int) -> dict:
+    x = _c(x, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    w = _c(topk_w, np.float32)
+    slot = _c(token_slot, np.int32)
+    T, H = x.shape
+    k = idx.shape[1]
+    out = dict(recv_x=np.zeros((cap, H), np.uint16), recv_idx=np.zeros((cap, k), np.int64),
+               recv_w=np.zeros((cap, k), np.float32), recv_src=np.zeros(cap, np.int32))
+    rc = lib().oracle_dispatch(_p(x), _p(idx), _p(w), T, H, k, E, R, _p(slot), cap,
+                               _p(out["recv_x"]), _p(out["recv_idx"]), _p(out["recv_w"]),
+                               _p(out["recv_src"]))
+    if rc != 0:
+        raise ValueError("oracle_dispatch: bad arguments or slot beyond capacity")
+    return out
+
+
+def restripe_prob(prob, Tmax: int, out=None) -> np.ndarray:
+    """prob: float32 [T][N][P] (copied as 32-bit words). Returns [N][Tmax][P]."""
+    pw = np.ascontiguousarray(prob).view(np.uint32)
+    T, N, P = pw.shape
+    if out is None:
+        out = np.zeros((N, Tmax, P), np.float32)
+    ow = out.view(np.uint32)
+    rc = lib().oracle_restripe_prob(_p(pw), T, N, P, Tmax, _p(ow))
+    if rc != 0:
+        raise ValueError("oracle_restripe_prob: bad arguments")
+    return out
+
+
+def combine(partial, token_slot, R: int) -> np.ndarray:
+    partial = _c(partial, np.uint16)
+    slot = _c(token_slot, np.int32)
+    rows, H = partial.shape
+    T = slot.shape[0]
+    out = np.zeros((T, H), np.uint16)
+    rc = lib().oracle_combine(_p(partial), rows, _p(slot), T, H, R, _p(out))
+    if rc != 0:
+        raise ValueError("oracle_combine: bad arguments or slot beyond the partial rows")
+    return out
+
+
+def f32_to_bf16(a) -> np.ndarray:
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    lib().oracle_f32_to_bf16_array(_p(a), a.size, _p(out))
+    return out
+
+
+def bf16_to_f32(b) -> np.ndarray:
+    """bf16 bit patterns widened to fp32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)

@@ -1,0 +1,218 @@
+/* oracle.c -- TEST INFRASTRUCTURE, not part of the product path.
+ *
+ * A plain, slow, single-threaded CPU definition of the four steps of the
+ * single-GPU core of MoE expert-parallel (EP) dispatch/combine:
+ *   layout   : per-rank / per-node / per-expert token counts, the token-in-rank
+ *              bitmap, exclusive prefix offsets and each (token, rank) receive slot;
+ *   dispatch : copy each token's bf16 row and its rank-local top-k view, in
+ *              ascending token order, into destination-major receive rows;
+ *   restripe : prob [T][N][P] -> [N][Tmax][P];
+ *   combine  : per token, sum its per-rank partial rows in fp32, round to bf16.
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * call it. It shares no code with the HIP library and uses nothing but libc.
+ *
+ * Sources (DeepEP pull-request pages):
+ *  - "[PR #347] Feature/sm free normal kernel": names get_dispatch_layout
+ *    (commit list) and fixes the workload (section 3.1).
+ *  - "[PR #634] Hybrid ep nixl restripe": sections "Baseline problem" and
+ *    "Fix" define the prob layouts and the restripe; its commit list names
+ *    the scan/permute fusion with a per-local-expert sum array.
+ *  - "[PR #453] ... Zero-Copy and TMA Offloading": a guard against too many
+ *    received tokens (commit list), here a capacity check.
+ * Where the pages leave a step open the plainest reading is taken:
+ *  - expert e lives on rank e / (E/R); rank r on node r / (R/N);
+ *  - a token counts once per rank, however many of its experts the rank holds;
+ *  - per-expert counts count every (token, slot) pair;
+ *  - expert id -1 is a masked slot (skipped); ids < -1 or >= E are skipped and
+ *    raise the error flag;
+ *  - a rank's receive rows are its tokens in ascending token order, ranks packed
+ *    one after another at the exclusive prefix of the per-rank counts;
+ *  - a receive row's top-k view keeps all k slots in order: the rank-local
+ *    expert id (e - r*E/R) and its weight where the expert is on that rank,
+ *    else -1 and +0.0f;
+ *  - combine is an unweighted sum in ascending rank order, fp32, from +0.0f,
+ *    then one round-to-nearest-even to bf16.
+ */
+#include "oracle.h"
+
+#include <stdlib.h>
+#include <string.h>
+
+/* bf16 is the top half of an IEEE-754 binary32 word. */
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a binary32 value to the nearest bf16, ties to even; a NaN stays a
+ * (quiet) NaN. Adding 0x7fff plus the lowest kept bit carries into the kept
+ * half exactly when the dropped half is above one half ulp, or equal to it
+ * with an odd kept half. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t kept_lsb = (u >> 16) & 1u;
+    u += 0x7fffu + kept_lsb;
+    return (uint16_t)(u >> 16);
+}
+
+void oracle_f32_to_bf16_array(const float *in, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_bf16(in[i]);
+}
+
+/* Layout ("get_dispatch_layout", PR #347 commit list; scan over tokens per
+ * local expert, PR #634 commit list). */
+int oracle_layout(const int64_t *topk_idx, int64_t T, int k, int E, int R, int N,
+                  int32_t *count_r, int32_t *count_n, int32_t *count_e,
+                  uint8_t *in_rank, int32_t *rank_offset, int32_t *expert_offset,
+                  int32_t *token_slot, int32_t *error_flag)
+{
+    if (T < 0 || k < 1 || E < 1 || R < 1 || N < 1 || E % R != 0 || R % N != 0 || k > E)
+        return -1;
+    const int experts_per_rank = E / R;
+    const int ranks_per_node = R / N;
+    int32_t flag = 0;
+
+    for (int r = 0; r < R; ++r) count_r[r] = 0;
+    for (int n = 0; n < N; ++n) count_n[n] = 0;
+    for (int e = 0; e < E; ++e) count_e[e] = 0;
+
+    for (int64_t t = 0; t < T; ++t) {
+        uint8_t *row = in_rank + t * R;
+        for (int r = 0; r < R; ++r) row[r] = 0;
+        for (int j = 0; j < k; ++j) {
+            int64_t e = topk_idx[t * k + j];
+            if (e == -1)
+                continue;
+            if (e < -1 || e >= E) {
+                flag = 1;
+                continue;
+            }
+            count_e[e] += 1;
+            row[e / experts_per_rank] = 1;
+        }
+        for (int r = 0; r < R; ++r)
+            if (row[r])
+                count_r[r] += 1;
+        for (int n = 0; n < N; ++n) {
+            int any = 0;
+            for (int q = 0; q < ranks_per_node; ++q)
+                if (row[n * ranks_per_node + q])
+                    any = 1;
+            if (any)
+                count_n[n] += 1;
+        }
+    }
+
+    rank_offset[0] = 0;
+    for (int r = 0; r < R; ++r)
+        rank_offset[r + 1] = rank_offset[r] + count_r[r];
+    if (expert_offset) {
+        expert_offset[0] = 0;
+        for (int e = 0; e < E; ++e)
+            expert_offset[e + 1] = expert_offset[e] + count_e[e];
+    }
+
+    /* Slot of (t, r): the rank's base row plus the number of earlier tokens
+     * that also go to r. */
+    int32_t *filled = (int32_t *)calloc((size_t)R, sizeof(int32_t));
+    if (!filled)
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int r = 0; r < R; ++r) {
+            if (in_rank[t * R + r]) {
+                token_slot[t * R + r] = rank_offset[r] + filled[r];
+                filled[r] += 1;
+            } else {
+                token_slot[t * R + r] = -1;
+            }
+        }
+    free(filled);
+    *error_flag = flag;
+    return 0;
+}
+
+/* Dispatch permute: each token's row goes, unchanged, to every rank that holds
+ * one of its experts, with that rank's view of the top-k routing. */
+int oracle_dispatch(const uint16_t *x, const int64_t *topk_idx, const float *topk_w,
+                    int64_t T, int H, int k, int E, int R, const int32_t *token_slot,
+                    int64_t cap, uint16_t *recv_x, int64_t *recv_idx, float *recv_w,
+                    int32_t *recv_src)
+{
+    if (T < 0 || H < 1 || k < 1 || E < 1 || R < 1 || E % R != 0)
+        return -1;
+    const int experts_per_rank = E / R;
+    for (int64_t t = 0; t < T; ++t)
+        for (int r = 0; r < R; ++r) {
+            int64_t s = token_slot[t * R + r];
+            if (s < 0)
+                continue;
+            if (s >= cap)
+                return -1;
+            memcpy(recv_x + s * H, x + t * H, (size_t)H * sizeof(uint16_t));
+            for (int j = 0; j < k; ++j) {
+                int64_t e = topk_idx[t * k + j];
+                int64_t local = -1;
+                if (e >= 0 && e < E && e / experts_per_rank == r)
+                    local = e - (int64_t)r * experts_per_rank;
+                recv_idx[s * k + j] = local;
+                recv_w[s * k + j] = local >= 0 ? topk_w[t * k + j] : 0.0f;
+            }
+            recv_src[s] = (int32_t)t;
+        }
+    return 0;
+}
+
+/* restripe_prob ("[PR #634] Hybrid ep nixl restripe", section "Fix"): slice
+ * (t, n) of the token-major prob moves to row t of node n's block. Rows
+ * T..Tmax-1 of each block are left untouched. Words are copied as bits. */
+int oracle_restripe_prob(const uint32_t *prob, int64_t T, int N, int P, int64_t Tmax,
+                         uint32_t *out)
+{
+    if (T < 0 || N < 1 || P < 1 || Tmax < T)
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int n = 0; n < N; ++n)
+            for (int p = 0; p < P; ++p)
+                out[((int64_t)n * Tmax + t) * P + p] = prob[(t * N + n) * P + p];
+    return 0;
+}
+
+/* Combine: out[t] = bf16( sum over ranks r = 0..R-1 holding t of partial[slot(t,r)] ),
+ * summed in fp32 in ascending r starting from +0.0f. */
+int oracle_combine(const uint16_t *partial, int64_t rows, const int32_t *token_slot,
+                   int64_t T, int H, int R, uint16_t *out)
+{
+    if (T < 0 || H < 1 || R < 1)
+        return -1;
+    float *acc = (float *)malloc((size_t)H * sizeof(float));
+    if (!acc)
+        return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h)
+            acc[h] = 0.0f;
+        for (int r = 0; r < R; ++r) {
+            int64_t s = token_slot[t * R + r];
+            if (s < 0)
+                continue;
+            if (s >= rows) {
+                free(acc);
+                return -1;
+            }
+            for (int h = 0; h < H; ++h)
+                acc[h] = acc[h] + oracle_bf16_to_f32(partial[s * H + h]);
+        }
+        for (int h = 0; h < H; ++h)
+            out[t * H + h] = oracle_f32_to_bf16(acc[h]);
+    }
+    free(acc);
+    return 0;
+}

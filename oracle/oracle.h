@@ -1,0 +1,33 @@
+/* oracle.h -- TEST INFRASTRUCTURE. Plain CPU definition of the MoE expert-parallel
+ * dispatch/combine data path, used only to check the HIP implementation.
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may call it.
+ * It shares no code, header or constant with the HIP library.
+ *
+ * All arrays are host memory, row-major, owned by the caller.
+ * Return value: 0 on success, -1 on an argument the definition does not cover.
+ */
+#ifndef EP_ORACLE_H
+#define EP_ORACLE_H
+#include <stdint.h>
+
+int oracle_layout(const int64_t *topk_idx, int64_t T, int k, int E, int R, int N,
+                  int32_t *count_r, int32_t *count_n, int32_t *count_e,
+                  uint8_t *in_rank, int32_t *rank_offset, int32_t *expert_offset,
+                  int32_t *token_slot, int32_t *error_flag);
+
+int oracle_dispatch(const uint16_t *x, const int64_t *topk_idx, const float *topk_w,
+                    int64_t T, int H, int k, int E, int R, const int32_t *token_slot,
+                    int64_t cap, uint16_t *recv_x, int64_t *recv_idx, float *recv_w,
+                    int32_t *recv_src);
+
+int oracle_restripe_prob(const uint32_t *prob, int64_t T, int N, int P, int64_t Tmax,
+                         uint32_t *out);
+
+int oracle_combine(const uint16_t *partial, int64_t rows, const int32_t *token_slot,
+                   int64_t T, int H, int R, uint16_t *out);
+
+uint16_t oracle_f32_to_bf16(float f);
+float oracle_bf16_to_f32(uint16_t b);
+void oracle_f32_to_bf16_array(const float *in, int64_t n, uint16_t *out);
+
+#endif

@@ -1,0 +1,68 @@
+"""The pages' printed (GB/s, us) pairs against the oracle's per-node counts.
+
+GB/s * us is the byte count each page's kernel moved. For uniform top-8 routing
+over 256 experts it equals sum_t (destination nodes of t) * hidden * 2, which
+pins (1) the oracle's per-node count and (2) the "algorithm bytes" definition the
+benchmark uses.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from combine_ep_get_03_amd import workloads as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+T, H, E, K, RANKS_PER_NODE = 4096, 7168, 256, 8, 8
+
+
+def _rows():
+    rows = []
+    with open(os.path.join(HERE, "golden", "pages_algorithm_bandwidth.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                src, table, nodes, eb, gbps, us, dig = [c.strip() for c in line.split("|")]
+                rows.append((src, table, int(nodes), int(eb), float(gbps), float(us), int(dig)))
+    return rows
+
+
+def expected_nodes_per_token(N):
+    """E[# distinct nodes] for k distinct experts of E, E/N per node (hypergeometric)."""
+    per = E // N
+    return N * (1 - math.comb(E - per, K) / math.comb(E, K))
+
+
+@pytest.mark.parametrize("row", _rows(), ids=lambda r: f"{r[0]}-{r[1]}-{r[2]}n")
+def test_page_bytes_match_destination_node_count(orc, row):
+    src, table, N, eb, gbps, us, digits = row
+    page_bytes = gbps * 1e9 * us * 1e-6
+    # printing precision of the pair, plus the page's own routing draw (~0.5%)
+    tol = 0.5 * 10.0**-digits / gbps + 0.05 / us + 0.01
+    model = T * H * eb * expected_nodes_per_token(N)
+    assert abs(page_bytes / model - 1) < tol, (page_bytes, model)
+    # the oracle's per-node counts on a seeded batch of the same shape
+    idx = W.routing_uniform(np.random.default_rng(N), T, E, K)
+    lay = orc.layout(idx, E, N * RANKS_PER_NODE, N)
+    oracle_bytes = int(lay["count_n"].sum()) * H * eb
+    assert abs(page_bytes / oracle_bytes - 1) < tol + 0.01
+
+
+def test_alternative_byte_definitions_do_not_fit(orc):
+    """Counting per rank, per expert slot, or remote nodes only misses the pages by far."""
+    idx = W.routing_uniform(np.random.default_rng(0), T, E, K)
+    lay = orc.layout(idx, E, 16, 2)
+    page = 163.27e9 * 716.9e-6
+    per_rank = int(lay["count_r"].sum()) * H * 2
+    per_slot = T * K * H * 2
+    remote_only = int(lay["count_n"][1:].sum()) * H * 2
+    for alt in (per_rank, per_slot, remote_only):
+        assert abs(page / alt - 1) > 0.3
+
+
+def test_physical_share_three_quarters(orc):
+    """At 4 nodes, 3/4 of a node-0 sender's (token, node) pairs leave the node."""
+    idx = W.routing_uniform(np.random.default_rng(4), T, E, K)
+    lay = orc.layout(idx, E, 32, 4)
+    cn = lay["count_n"].astype(np.float64)
+    assert abs(cn[1:].sum() / cn.sum() - 0.75) < 0.01
