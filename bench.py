@@ -1,0 +1,213 @@
+"""Benchmark of the single-GPU EP dispatch/combine path on one MI355X.
+
+One step = the whole path on one batch: ep_get_layout -> ep_dispatch -> ep_restripe_prob
+-> ep_combine, enqueued on one stream. Inputs are seeded synthetic data already resident
+in HBM when the timed region starts. Prints one JSON line.
+
+value = dispatch+combine algorithm GB/s over the whole step: (2 * M * H * 2 bytes) / step
+time, where M = number of (token, rank) pairs (each token's row counted once per
+destination rank, the pages' "algorithm bandwidth" taken at rank granularity).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine algorithm GB/s and tokens/s on 1 MI355X; % of HBM roofline"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="dsv3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bound on the oracle's CPU time for the baseline")
+    ap.add_argument("--copy-gib", type=float, default=2.0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(cfg, M: int) -> dict:
+    """Minimum bytes each kernel must move (reads + writes)."""
+    T, H, k, R, N, P, E = cfg.T, cfg.H, cfg.k, cfg.R, cfg.N, cfg.P, cfg.E
+    return {
+        "layout": T * k * 8 + T * R * (1 + 4) + (R + N + E + 1) * 4,
+        "dispatch": T * H * 2 + T * k * 12 + T * R * 4 + M * (2 * H + 12 * k + 4),
+        "restripe": 2 * T * N * P * 4,
+        "combine": T * R * 4 + M * H * 2 + T * H * 2,
+    }
+
+
+def copy_bandwidth(torch, ep, gib: float):
+    """Best of the library's 128-bit copy kernel and torch's device copy, read+write bytes."""
+    n = int(gib * (1 << 30)) // 16 * 16
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    res = {}
+    for name, fn in (("ep_hbm_copy", lambda: ep.ep_hbm_copy(a, b)),
+                     ("torch_copy", lambda: b.copy_(a))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        res[name] = 2 * n / (ms * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg, inp, seconds: float) -> dict:
+    """The CPU oracle on this host, single thread, whole step on the same batch;
+    repeated until `seconds` of CPU time (at least once)."""
+    import oracle
+
+    reps, t_total = 0, 0.0
+    M = None
+    while reps == 0 or t_total < seconds:
+        t0 = time.perf_counter()
+        lay = oracle.layout(inp.topk_idx, cfg.E, cfg.R, cfg.N)
+        d = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, cfg.E, cfg.R,
+                            lay["token_slot"], cfg.cap)
+        oracle.restripe_prob(inp.prob, cfg.Tmax)
+        partial = d["recv_x"] if inp.partials is None else inp.partials
+        oracle.combine(partial, lay["token_slot"], cfg.R)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        M = int(lay["rank_offset"][-1])
+        del d
+    s = t_total / reps
+    return {"value": round(2 * M * cfg.H * 2 / s / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} whole steps (layout+dispatch+restripe+combine) of the "
+                      f"{cfg.name} batch, {s * 1e3:.1f} ms each, single-threaded C oracle "
+                      f"incl. its output allocation; host {platform.processor() or platform.machine()}, "
+                      f"nproc {os.cpu_count()}",
+            "ms_per_step": round(s * 1e3, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is "
+              "single-GPU and uses no collectives.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import __graft_entry__
+
+    __graft_entry__._ensure_built()
+    import combine_ep_get_03_amd as ep
+    from combine_ep_get_03_amd import workloads as W
+    from combine_ep_get_03_amd.pipeline import DeviceBatch, Path
+
+    cfg = W.CONFIGS[args.config]
+    print(f"bench: generating {cfg}", file=sys.stderr, flush=True)
+    inp = W.make_inputs(cfg)
+    torch.cuda.set_device(0)
+    b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials)
+    path = Path(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax)
+    stream = torch.cuda.current_stream()
+
+    copy_bw = copy_bandwidth(torch, ep, args.copy_gib)
+    print(f"bench: copy bandwidth {copy_bw}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        path.step(b)
+    torch.cuda.synchronize()
+    if int(path.error_flag.item()) != 0:
+        raise RuntimeError(f"device error flag {int(path.error_flag.item())}")
+    M = int(path.layout_buf.rank_offset[-1].item())
+
+    names = ["layout", "dispatch", "restripe", "combine"]
+    calls = [path.layout, path.dispatch, path.restripe, path.combine]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, fn in enumerate(calls):
+            fn(b)
+            ev[s][i + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    per = {n: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
+           for i, n in enumerate(names)}
+    avg = {n: statistics.mean(v) for n, v in per.items()}
+    med = {n: statistics.median(v) for n, v in per.items()}
+
+    alg = algorithmic_bytes(cfg, M)
+    payload = 2 * M * cfg.H * 2
+    value = payload / (ms_step * 1e-3) / 1e9
+    dom = max(("dispatch", "combine"), key=lambda n: avg[n])
+    achieved = alg[dom] / (avg[dom] * 1e-3) / 1e9
+    best_copy = max(copy_bw.values())
+    kernels = {n: {"avg_us": round(avg[n] * 1e3, 2), "median_us": round(med[n] * 1e3, 2),
+                   "alg_bytes": alg[n],
+                   "hbm_gbps": round(alg[n] / (avg[n] * 1e-3) / 1e9, 1),
+                   "frac_of_copy": round(alg[n] / (avg[n] * 1e-3) / 1e9 / best_copy, 4)}
+               for n in names}
+    dc_ms = avg["dispatch"] + avg["combine"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} top-{cfg.k} "
+                               f"{cfg.routing} R={cfg.R} simulated ranks N={cfg.N} nodes "
+                               f"P={cfg.P} Tmax={cfg.Tmax}, seed {cfg.seed}",
+                   "M_token_rank_pairs": M, "global_batch": cfg.T, "parallelism": "none"},
+        "tokens_per_s": round(cfg.T / (ms_step * 1e-3), 1),
+        "dispatch_combine": {"ms": round(dc_ms, 4),
+                             "algorithm_gbps": round(payload / (dc_ms * 1e-3) / 1e9, 1),
+                             "hbm_gbps": round((alg["dispatch"] + alg["combine"]) /
+                                               (dc_ms * 1e-3) / 1e9, 1),
+                             "frac_of_copy": round((alg["dispatch"] + alg["combine"]) /
+                                                   (dc_ms * 1e-3) / 1e9 / best_copy, 4),
+                             "tokens_per_s": round(cfg.T / (dc_ms * 1e-3), 1)},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "copy_bandwidth_gbps": {k: round(v, 1) for k, v in copy_bw.items()},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

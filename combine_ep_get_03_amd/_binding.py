@@ -1,0 +1,191 @@
+"""ctypes binding over libep.so: one Python function per C entry point of include/ep.h,
+with the same names. Argument marshalling only: shapes, dtypes and devices of the torch
+tensors are checked, their device pointers and the current HIP stream are passed on,
+and a non-zero status becomes an ``EPError``. Every step of the path runs in the HIP
+kernels behind the C ABI; there is no fallback when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libep.so")
+
+EP_OK, EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_CAPACITY, EP_ERR_HIP = 0, -1, -2, -3, -4
+EP_DEVERR_TOPK_RANGE, EP_DEVERR_RECV_OVERFLOW, EP_DEVERR_SLOT_RANGE = 1, 2, 4
+EP_MAX_RANKS, EP_MAX_EXPERTS = 1024, 8192
+
+_lib = None
+
+
+class EPError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {ep_status_string(status)}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libep.so (built in-tree by __graft_entry__.build()); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.ep_status_string.argtypes = [i32]
+    L.ep_status_string.restype = ctypes.c_char_p
+    L.ep_layout_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    L.ep_layout_workspace_bytes.restype = sz
+    L.ep_get_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, sz, P]
+    L.ep_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, i64, P, P]
+    L.ep_restripe_prob.argtypes = [P, i64, i32, i32, i64, P, P]
+    L.ep_combine.argtypes = [P, i64, P, i64, i32, i32, P, P, P]
+    L.ep_hbm_copy.argtypes = [P, P, sz, P]
+    for f in ("ep_get_layout", "ep_dispatch", "ep_restripe_prob", "ep_combine", "ep_hbm_copy"):
+        getattr(L, f).restype = i32
+    _lib = L
+    return L
+
+
+def ep_status_string(status: int) -> str:
+    return load().ep_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, name: str, nullable: bool = False):
+    if t is None:
+        if nullable:
+            return None
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _shape(t: Optional[torch.Tensor], shape, name: str) -> None:
+    """Exact shape check; a leading entry of None in `shape` is not compared."""
+    if t is None:
+        return
+    if t.dim() != len(shape) or any(w is not None and int(g) != int(w)
+                                    for g, w in zip(t.shape, shape)):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _at_least(t: Optional[torch.Tensor], n: int, name: str) -> None:
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name}: needs at least {n} elements, has {t.numel()}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(status: int, where: str) -> None:
+    if status != EP_OK:
+        raise EPError(status, where)
+
+
+def ep_layout_workspace_bytes(num_tokens: int, num_experts: int, num_ranks: int,
+                              num_nodes: int) -> int:
+    return int(load().ep_layout_workspace_bytes(num_tokens, num_experts, num_ranks, num_nodes))
+
+
+def ep_get_layout(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
+                  num_tokens_per_rank, num_tokens_per_node, num_tokens_per_expert,
+                  is_token_in_rank, rank_offset, expert_offset, token_slot, error_flag,
+                  workspace, stream=None) -> None:
+    T, k = topk_idx.shape
+    E, R, N = num_experts, num_ranks, num_nodes
+    _at_least(num_tokens_per_rank, R, "num_tokens_per_rank")
+    _at_least(num_tokens_per_node, N, "num_tokens_per_node")
+    _at_least(num_tokens_per_expert, E, "num_tokens_per_expert")
+    _shape(is_token_in_rank, (T, R), "is_token_in_rank")
+    _at_least(rank_offset, R + 1, "rank_offset")
+    _at_least(expert_offset, E + 1, "expert_offset")
+    _shape(token_slot, (T, R), "token_slot")
+    _at_least(error_flag, 1, "error_flag")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().ep_get_layout(
+        _ptr(topk_idx, torch.int64, "topk_idx"), T, k, num_experts, num_ranks, num_nodes,
+        _ptr(num_tokens_per_rank, torch.int32, "num_tokens_per_rank"),
+        _ptr(num_tokens_per_node, torch.int32, "num_tokens_per_node", True),
+        _ptr(num_tokens_per_expert, torch.int32, "num_tokens_per_expert", True),
+        _ptr(is_token_in_rank, torch.uint8, "is_token_in_rank", True),
+        _ptr(rank_offset, torch.int32, "rank_offset"),
+        _ptr(expert_offset, torch.int32, "expert_offset", True),
+        _ptr(token_slot, torch.int32, "token_slot"),
+        _ptr(error_flag, torch.int32, "error_flag"),
+        _ptr(workspace, torch.uint8, "workspace", True), ws_bytes, _stream(stream)),
+        "ep_get_layout")
+
+
+def ep_dispatch(x, topk_idx, topk_weights, num_experts: int, num_ranks: int, token_slot, *,
+                recv_x, recv_topk_idx=None, recv_topk_weights=None, recv_src_idx=None,
+                error_flag=None, stream=None) -> None:
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    cap = recv_x.shape[0]
+    _shape(topk_idx, (T, k), "topk_idx")
+    _shape(topk_weights, (T, k), "topk_weights")
+    _shape(token_slot, (T, num_ranks), "token_slot")
+    _shape(recv_x, (cap, H), "recv_x")
+    _shape(recv_topk_idx, (cap, k), "recv_topk_idx")
+    _shape(recv_topk_weights, (cap, k), "recv_topk_weights")
+    _shape(recv_src_idx, (cap,), "recv_src_idx")
+    _at_least(error_flag, 1, "error_flag")
+    _check(load().ep_dispatch(
+        _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int64, "topk_idx"),
+        _ptr(topk_weights, torch.float32, "topk_weights", True), T, H, k, num_experts,
+        num_ranks, _ptr(token_slot, torch.int32, "token_slot"),
+        _ptr(recv_x, torch.bfloat16, "recv_x"),
+        _ptr(recv_topk_idx, torch.int64, "recv_topk_idx", True),
+        _ptr(recv_topk_weights, torch.float32, "recv_topk_weights", True),
+        _ptr(recv_src_idx, torch.int32, "recv_src_idx", True), cap,
+        _ptr(error_flag, torch.int32, "error_flag", True), _stream(stream)), "ep_dispatch")
+
+
+def ep_restripe_prob(prob, prob_dest_major, stream=None) -> None:
+    """prob: fp32 [T][N][P]; prob_dest_major: fp32 [N][Tmax][P]."""
+    T, N, P = prob.shape
+    if prob_dest_major.dim() != 3 or prob_dest_major.shape[0] != N or \
+            prob_dest_major.shape[2] != P:
+        raise ValueError("prob_dest_major must be [N][Tmax][P]")
+    _check(load().ep_restripe_prob(
+        _ptr(prob, torch.float32, "prob"), T, N, P, prob_dest_major.shape[1],
+        _ptr(prob_dest_major, torch.float32, "prob_dest_major"), _stream(stream)),
+        "ep_restripe_prob")
+
+
+def ep_combine(partial, token_slot, *, out, error_flag=None, stream=None) -> None:
+    """partial: bf16 [rows][H]; token_slot: int32 [T][R]; out: bf16 [T][H]."""
+    rows, H = partial.shape
+    T, R = token_slot.shape
+    _shape(out, (T, H), "out")
+    _at_least(error_flag, 1, "error_flag")
+    _check(load().ep_combine(
+        _ptr(partial, torch.bfloat16, "partial"), rows, _ptr(token_slot, torch.int32, "token_slot"),
+        T, H, R, _ptr(out, torch.bfloat16, "out"),
+        _ptr(error_flag, torch.int32, "error_flag", True), _stream(stream)), "ep_combine")
+
+
+def ep_hbm_copy(src, dst, nbytes: Optional[int] = None, stream=None) -> None:
+    if not (src.is_cuda and dst.is_cuda):
+        raise ValueError("src and dst must be device tensors")
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    if nbytes > src.numel() * src.element_size() or nbytes > dst.numel() * dst.element_size():
+        raise ValueError("nbytes exceeds a buffer")
+    _check(load().ep_hbm_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                              nbytes, _stream(stream)), "ep_hbm_copy")

@@ -1,0 +1,58 @@
+"""Device buffers for one batch, allocated with torch (memory plumbing only).
+
+Receive buffers are sized by the bound M <= T * min(k, R), so no count has to be read
+back to the host before dispatch.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import _binding as B
+
+
+@dataclasses.dataclass
+class LayoutBuffers:
+    num_tokens_per_rank: torch.Tensor    # int32 [R]
+    num_tokens_per_node: torch.Tensor    # int32 [N]
+    num_tokens_per_expert: torch.Tensor  # int32 [E]
+    is_token_in_rank: torch.Tensor       # uint8 [T][R]
+    rank_offset: torch.Tensor            # int32 [R+1]
+    expert_offset: torch.Tensor          # int32 [E+1]
+    token_slot: torch.Tensor             # int32 [T][R]
+    error_flag: torch.Tensor             # int32 [1]
+    workspace: torch.Tensor              # uint8 [ep_layout_workspace_bytes]
+
+    @classmethod
+    def alloc(cls, T: int, E: int, R: int, N: int, device="cuda") -> "LayoutBuffers":
+        i32 = dict(dtype=torch.int32, device=device)
+        ws = max(16, B.ep_layout_workspace_bytes(T, E, R, N))
+        return cls(torch.empty(R, **i32), torch.empty(N, **i32), torch.empty(E, **i32),
+                   torch.empty((T, R), dtype=torch.uint8, device=device),
+                   torch.empty(R + 1, **i32), torch.empty(E + 1, **i32),
+                   torch.empty((T, R), **i32), torch.zeros(1, **i32),
+                   torch.empty(ws, dtype=torch.uint8, device=device))
+
+    def compute(self, topk_idx: torch.Tensor, E: int, R: int, N: int, stream=None) -> None:
+        B.ep_get_layout(topk_idx, E, R, N, num_tokens_per_rank=self.num_tokens_per_rank,
+                        num_tokens_per_node=self.num_tokens_per_node,
+                        num_tokens_per_expert=self.num_tokens_per_expert,
+                        is_token_in_rank=self.is_token_in_rank, rank_offset=self.rank_offset,
+                        expert_offset=self.expert_offset, token_slot=self.token_slot,
+                        error_flag=self.error_flag, workspace=self.workspace, stream=stream)
+
+
+@dataclasses.dataclass
+class DispatchBuffers:
+    recv_x: torch.Tensor              # bf16 [cap][H]
+    recv_topk_idx: torch.Tensor       # int64 [cap][k]
+    recv_topk_weights: torch.Tensor   # fp32 [cap][k]
+    recv_src_idx: torch.Tensor        # int32 [cap]
+
+    @classmethod
+    def alloc(cls, cap: int, H: int, k: int, device="cuda") -> "DispatchBuffers":
+        return cls(torch.empty((cap, H), dtype=torch.bfloat16, device=device),
+                   torch.empty((cap, k), dtype=torch.int64, device=device),
+                   torch.empty((cap, k), dtype=torch.float32, device=device),
+                   torch.empty(cap, dtype=torch.int32, device=device))

@@ -1,0 +1,139 @@
+// ep_abi.cpp -- the extern "C" boundary declared in include/ep.h: host-side argument
+// checks, then the kernel launches on the caller's stream. Nothing is enqueued when a
+// check fails, and no C++ exception leaves this file.
+#include "ep.h"
+
+#include <limits.h>
+
+#include "ep_internal.hpp"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+// Topology sizes shared by layout and dispatch.
+bool topology_ok(int k, int E, int R, int N) {
+    if (E < 1 || E > EP_MAX_EXPERTS || R < 1 || R > EP_MAX_RANKS || N < 1) return false;
+    if (E % R != 0 || R % N != 0) return false;
+    if (k < 1 || k > E) return false;
+    return true;
+}
+
+bool slots_fit_int32(int64_t T, int k, int R) {
+    const int64_t per = k < R ? k : R;
+    return T >= 0 && (T == 0 || T <= static_cast<int64_t>(INT32_MAX) / per);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ep_status_string(int status) {
+    switch (status) {
+        case EP_OK: return "EP_OK";
+        case EP_ERR_ARG: return "EP_ERR_ARG: a count or size is out of range or a required pointer is NULL";
+        case EP_ERR_ALIGN: return "EP_ERR_ALIGN: a pointer or row length breaks the alignment rule";
+        case EP_ERR_CAPACITY: return "EP_ERR_CAPACITY: a destination or the workspace is too small";
+        case EP_ERR_HIP: return "EP_ERR_HIP: the HIP runtime reported an error at launch";
+        default: return "unknown ep status";
+    }
+}
+
+size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_experts, int num_ranks,
+                                 int num_nodes) {
+    if (num_tokens < 0 || num_experts < 1 || num_experts > EP_MAX_EXPERTS || num_ranks < 1 ||
+        num_ranks > EP_MAX_RANKS || num_nodes < 1 || num_experts % num_ranks != 0 ||
+        num_ranks % num_nodes != 0)
+        return 0;
+    return ep::layout_workspace_bytes(num_tokens, num_experts, num_ranks, num_nodes);
+}
+
+int ep_get_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                  int num_ranks, int num_nodes, int32_t* num_tokens_per_rank,
+                  int32_t* num_tokens_per_node, int32_t* num_tokens_per_expert,
+                  uint8_t* is_token_in_rank, int32_t* rank_offset, int32_t* expert_offset,
+                  int32_t* token_slot, int32_t* error_flag, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    const int64_t T = num_tokens;
+    const int k = num_topk, E = num_experts, R = num_ranks, N = num_nodes;
+    if (!topology_ok(k, E, R, N) || !slots_fit_int32(T, k, R)) return EP_ERR_ARG;
+    if (!num_tokens_per_rank || !rank_offset || !error_flag) return EP_ERR_ARG;
+    if (T > 0 && (!topk_idx || !token_slot)) return EP_ERR_ARG;
+    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) ||
+        !aligned(num_tokens_per_node, 4) || !aligned(num_tokens_per_expert, 4) ||
+        !aligned(rank_offset, 4) || !aligned(expert_offset, 4) || !aligned(token_slot, 4) ||
+        !aligned(error_flag, 4) || !aligned(workspace, 16))
+        return EP_ERR_ALIGN;
+    const size_t need = ep::layout_workspace_bytes(T, E, R, N);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return EP_ERR_CAPACITY;
+    const ep::LayoutWorkspace ws = ep::carve_layout_workspace(workspace, T, E, R, N);
+    return hip_status(ep::launch_layout(topk_idx, T, k, E, R, N, num_tokens_per_rank,
+                                        num_tokens_per_node, num_tokens_per_expert,
+                                        is_token_in_rank, rank_offset, expert_offset, token_slot,
+                                        error_flag, ws, static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                int64_t num_tokens, int hidden, int num_topk, int num_experts, int num_ranks,
+                const int32_t* token_slot, void* recv_x, int64_t* recv_topk_idx,
+                float* recv_topk_weights, int32_t* recv_src_idx, int64_t recv_capacity,
+                int32_t* error_flag, void* stream) {
+    const int64_t T = num_tokens;
+    const int H = hidden, k = num_topk, E = num_experts, R = num_ranks;
+    if (!topology_ok(k, E, R, 1) || !slots_fit_int32(T, k, R) || H < 1 || recv_capacity < 0)
+        return EP_ERR_ARG;
+    if (H % 8 != 0) return EP_ERR_ALIGN;
+    if (static_cast<int64_t>(H) / 8 * 64 > INT32_MAX) return EP_ERR_ARG;
+    if (T > 0) {
+        if (!x || !token_slot || !recv_x) return EP_ERR_ARG;
+        if ((recv_topk_idx || recv_topk_weights) && !topk_idx) return EP_ERR_ARG;
+        if (recv_topk_weights && !topk_weights) return EP_ERR_ARG;
+    }
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 8) ||
+        !aligned(topk_weights, 4) || !aligned(token_slot, 4) || !aligned(recv_topk_idx, 8) ||
+        !aligned(recv_topk_weights, 4) || !aligned(recv_src_idx, 4) || !aligned(error_flag, 4))
+        return EP_ERR_ALIGN;
+    return hip_status(ep::launch_dispatch(x, topk_idx, topk_weights, T, H, k, E, R, token_slot,
+                                          recv_x, recv_topk_idx, recv_topk_weights, recv_src_idx,
+                                          recv_capacity, error_flag,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int ep_restripe_prob(const float* prob, int64_t num_tokens, int num_nodes, int prob_per_token,
+                     int64_t max_tokens_per_rank, float* prob_dest_major, void* stream) {
+    const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
+    const int N = num_nodes, P = prob_per_token;
+    if (T < 0 || N < 1 || P < 1 || static_cast<int64_t>(N) * P > (1 << 26)) return EP_ERR_ARG;
+    if (Tmax < T) return EP_ERR_CAPACITY;
+    if (T > 0 && (!prob || !prob_dest_major)) return EP_ERR_ARG;
+    if (!aligned(prob, 4) || !aligned(prob_dest_major, 4)) return EP_ERR_ALIGN;
+    return hip_status(ep::launch_restripe(prob, T, N, P, Tmax, prob_dest_major,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine(const void* partial, int64_t num_partial_rows, const int32_t* token_slot,
+               int64_t num_tokens, int hidden, int num_ranks, void* out, int32_t* error_flag,
+               void* stream) {
+    const int64_t T = num_tokens;
+    const int H = hidden, R = num_ranks;
+    if (T < 0 || H < 1 || R < 1 || R > EP_MAX_RANKS || num_partial_rows < 0) return EP_ERR_ARG;
+    if (H % 8 != 0) return EP_ERR_ALIGN;
+    if (static_cast<int64_t>(H) / 8 * 64 > INT32_MAX) return EP_ERR_ARG;
+    if (T > 0 && (!token_slot || !out)) return EP_ERR_ARG;
+    if (T > 0 && num_partial_rows > 0 && !partial) return EP_ERR_ARG;
+    if (!aligned(partial, 16) || !aligned(out, 16) || !aligned(token_slot, 4) ||
+        !aligned(error_flag, 4))
+        return EP_ERR_ALIGN;
+    return hip_status(ep::launch_combine(partial, num_partial_rows, token_slot, T, H, R, out,
+                                         error_flag, static_cast<hipStream_t>(stream)));
+}
+
+int ep_hbm_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    if (bytes > 0 && (!src || !dst)) return EP_ERR_ARG;
+    if (bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16)) return EP_ERR_ALIGN;
+    return hip_status(ep::launch_hbm_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

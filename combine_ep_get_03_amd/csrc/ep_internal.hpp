@@ -1,0 +1,81 @@
+// ep_internal.hpp -- device helpers and kernel launchers shared by the HIP sources of
+// the EP dispatch/combine library (gfx950, wave64). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+constexpr int kWave = 64;
+
+// 32-bit lane id and the number of set bits of `mask` on lanes below this one
+// (v_mbcnt_lo / v_mbcnt_hi).
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
+
+// 128-bit word used for every row move.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
+// Sticky device error word: bits are only ever added.
+__device__ __forceinline__ void raise_error(int32_t* flag, int32_t bits) {
+    if (flag) atomicOr(flag, bits);
+}
+
+// An HSA dispatch packet counts work-items in 32 bits.
+inline bool grid_fits(int64_t blocks, int threads) {
+    return blocks >= 0 && blocks * static_cast<int64_t>(threads) <= static_cast<int64_t>(UINT32_MAX);
+}
+
+constexpr int32_t kErrTopkRange = 1;
+constexpr int32_t kErrRecvOverflow = 2;
+constexpr int32_t kErrSlotRange = 4;
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the error reported at launch. Arguments have been
+// validated by the C ABI layer.
+
+struct LayoutWorkspace {
+    int32_t* blk_rank;   // [nb][R]  per-block rank counts, then per-block exclusive prefix
+    int32_t* blk_node;   // [nb][N]
+    int32_t* blk_exp;    // [nb][E]
+    int32_t* blk_err;    // [nb]
+};
+
+constexpr int kLayoutBlockTokens = 256;  // one token per thread
+
+size_t layout_workspace_bytes(int64_t T, int E, int R, int N);
+LayoutWorkspace carve_layout_workspace(void* base, int64_t T, int E, int R, int N);
+
+hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
+                         int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
+                         int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
+                         int32_t* error_flag, const LayoutWorkspace& ws, hipStream_t stream);
+
+hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* topk_w,
+                           int64_t T, int H, int k, int E, int R, const int32_t* token_slot,
+                           void* recv_x, int64_t* recv_idx, float* recv_w, int32_t* recv_src,
+                           int64_t cap, int32_t* error_flag, hipStream_t stream);
+
+hipError_t launch_restripe(const float* prob, int64_t T, int N, int P, int64_t Tmax, float* out,
+                           hipStream_t stream);
+
+hipError_t launch_combine(const void* partial, int64_t rows, const int32_t* token_slot,
+                          int64_t T, int H, int R, void* out, int32_t* error_flag,
+                          hipStream_t stream);
+
+hipError_t launch_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+}  // namespace ep

@@ -1,0 +1,43 @@
+// hbm_copy.hip -- plain 128-bit device copy: the HBM copy-bandwidth yardstick and the
+// known-size reference for hardware byte counters. Not a step of the dispatch path.
+#include "ep_internal.hpp"
+
+namespace ep {
+namespace {
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyU = 4;
+
+__global__ __launch_bounds__(kCopyThreads) void hbm_copy_kernel(const u32x4* __restrict__ in,
+                                                                u32x4* __restrict__ out,
+                                                                int64_t n) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kCopyThreads * kCopyU;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyThreads * kCopyU + threadIdx.x;
+         base < n; base += stride) {
+        u32x4 v[kCopyU];
+#pragma unroll
+        for (int u = 0; u < kCopyU; ++u) {
+            const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
+            if (i < n) v[u] = load_stream(in + i);
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyU; ++u) {
+            const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
+            if (i < n) store_stream(out + i, v[u]);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+    const int64_t n = static_cast<int64_t>(bytes / 16);
+    if (n == 0) return hipSuccess;
+    const int64_t per_block = kCopyThreads * kCopyU;
+    const int64_t grid = std::min<int64_t>((n + per_block - 1) / per_block, 256 * 16);
+    hipLaunchKernelGGL(hbm_copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(kCopyThreads), 0,
+                       stream, static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
+    return hipGetLastError();
+}
+
+}  // namespace ep

@@ -1,0 +1,81 @@
+"""One batch through the whole path on the GPU: layout -> dispatch -> restripe_prob ->
+combine, each step one call of the C ABI on the same stream.
+
+Device buffers are allocated once per shape (torch, memory plumbing only); `step()`
+enqueues the four calls and returns without synchronising.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+from .buffers import DispatchBuffers, LayoutBuffers
+
+
+@dataclasses.dataclass
+class DeviceBatch:
+    topk_idx: torch.Tensor                 # int64 [T][k]
+    topk_weights: torch.Tensor             # fp32 [T][k]
+    x: torch.Tensor                        # bf16 [T][H]
+    prob: torch.Tensor                     # fp32 [T][N][P]
+    partials: Optional[torch.Tensor]       # bf16 [rows][H]; None = combine the dispatched rows
+
+    @classmethod
+    def from_host(cls, topk_idx, topk_weights, x_bits, prob, partial_bits=None,
+                  device="cuda") -> "DeviceBatch":
+        """numpy inputs (bf16 as uint16 bit patterns) copied to the device."""
+        import numpy as np
+
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(device)
+
+        return cls(torch.from_numpy(np.ascontiguousarray(topk_idx)).to(device),
+                   torch.from_numpy(np.ascontiguousarray(topk_weights)).to(device),
+                   bf16(x_bits), torch.from_numpy(np.ascontiguousarray(prob)).to(device),
+                   None if partial_bits is None else bf16(partial_bits))
+
+
+class Path:
+    """Buffers and calls for one shape: T tokens, hidden H, E experts, top-k, R ranks,
+    N nodes, P prob floats per (token, node), Tmax rows per node block."""
+
+    def __init__(self, T: int, H: int, E: int, k: int, R: int, N: int, P: int, Tmax: int,
+                 device="cuda", recv_capacity: Optional[int] = None):
+        self.T, self.H, self.E, self.k, self.R, self.N, self.P, self.Tmax = T, H, E, k, R, N, P, Tmax
+        self.cap = T * min(k, R) if recv_capacity is None else recv_capacity
+        self.layout_buf = LayoutBuffers.alloc(T, E, R, N, device)
+        self.recv = DispatchBuffers.alloc(self.cap, H, k, device)
+        self.prob_dest_major = torch.empty((N, Tmax, P), dtype=torch.float32, device=device)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+
+    @property
+    def error_flag(self) -> torch.Tensor:
+        return self.layout_buf.error_flag
+
+    def layout(self, b: DeviceBatch, stream=None) -> None:
+        self.layout_buf.compute(b.topk_idx, self.E, self.R, self.N, stream=stream)
+
+    def dispatch(self, b: DeviceBatch, stream=None) -> None:
+        r = self.recv
+        B.ep_dispatch(b.x, b.topk_idx, b.topk_weights, self.E, self.R,
+                      self.layout_buf.token_slot, recv_x=r.recv_x, recv_topk_idx=r.recv_topk_idx,
+                      recv_topk_weights=r.recv_topk_weights, recv_src_idx=r.recv_src_idx,
+                      error_flag=self.error_flag, stream=stream)
+
+    def restripe(self, b: DeviceBatch, stream=None) -> None:
+        B.ep_restripe_prob(b.prob, self.prob_dest_major, stream=stream)
+
+    def combine(self, b: DeviceBatch, stream=None) -> None:
+        partial = self.recv.recv_x if b.partials is None else b.partials
+        B.ep_combine(partial, self.layout_buf.token_slot, out=self.out,
+                     error_flag=self.error_flag, stream=stream)
+
+    def step(self, b: DeviceBatch, stream=None) -> None:
+        self.layout(b, stream)
+        self.dispatch(b, stream)
+        self.restripe(b, stream)
+        self.combine(b, stream)

@@ -1,0 +1,164 @@
+/* ep.h -- C ABI of the single-GPU core of MoE expert-parallel (EP) dispatch/combine,
+ * implemented by hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The path has four steps, after the DeepEP pull-request pages:
+ *   ep_get_layout     per-rank / per-node / per-expert token counts, the token-in-rank
+ *                     bitmap, exclusive prefix offsets and every (token, rank) receive slot
+ *                     ("[PR #347] Feature/sm free normal kernel" names get_dispatch_layout in
+ *                     its commit list; "[PR #634] Hybrid ep nixl restripe" names the scan
+ *                     over tokens per local expert in its commit list);
+ *   ep_dispatch       each token's bf16 row and its rank-local top-k view copied, in
+ *                     ascending token order, into destination-major receive rows, one block
+ *                     of rows per simulated EP rank (the intra-node copy hop of
+ *                     "[PR #347]", section 3.3.2; "[PR #453] Higher Performance with Lower
+ *                     SM Occupancy through Zero-Copy and TMA Offloading": data written
+ *                     straight to its final buffer);
+ *   ep_restripe_prob  prob [T][N][P] -> [N][Tmax][P] ("[PR #634]", sections "Baseline
+ *                     problem" and "Fix");
+ *   ep_combine        per token, the sum of its per-rank partial rows in fp32, rounded once
+ *                     to bf16.
+ *
+ * Conventions for every entry point:
+ *  - Every array argument is a DEVICE pointer owned by the caller; the library allocates
+ *    nothing and keeps no state between calls. All arrays are dense and row-major.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued on it and the
+ *    call returns without waiting; nothing inside synchronises with the host.
+ *  - Arguments are checked on the host before anything is enqueued. On any error return
+ *    nothing has been enqueued. No C++ exception crosses this boundary.
+ *  - Simulated topology: expert e lives on rank e / (E/R); rank r lives on node r / (R/N).
+ *  - `error_flag` is one int32 in device memory. ep_get_layout overwrites it (0 or
+ *    EP_DEVERR_TOPK_RANGE); ep_dispatch and ep_combine OR further EP_DEVERR_* bits into it.
+ *    After an error bit is set the affected outputs are as documented per call.
+ *  - Calls that share output or workspace memory must not overlap in time.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    EP_OK = 0,
+    EP_ERR_ARG = -1,       /* a count or size out of range, or a required pointer is NULL */
+    EP_ERR_ALIGN = -2,     /* a pointer or row length breaks the alignment rule of the call */
+    EP_ERR_CAPACITY = -3,  /* a destination or workspace smaller than the call requires */
+    EP_ERR_HIP = -4        /* the HIP runtime reported an error when the work was enqueued */
+};
+
+/* Bits the kernels OR into *error_flag. */
+#define EP_DEVERR_TOPK_RANGE    1  /* a topk_idx entry < -1 or >= num_experts (entry skipped) */
+#define EP_DEVERR_RECV_OVERFLOW 2  /* ep_dispatch met a slot >= recv_capacity (row skipped) */
+#define EP_DEVERR_SLOT_RANGE    4  /* ep_combine met a slot >= num_partial_rows, or a token_slot
+                                      row holds more valid slots than a token can have (skipped) */
+
+/* Limits of this implementation. */
+#define EP_MAX_RANKS   1024
+#define EP_MAX_EXPERTS 8192
+
+/* Static string for a status code; never NULL. */
+const char *ep_status_string(int status);
+
+/* Bytes of device workspace ep_get_layout needs for these sizes (0 if the sizes are invalid
+ * as ep_get_layout would reject them; a size of 0 is valid only for num_tokens == 0 ... and
+ * then still returns the few bytes the count reduction uses). */
+size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_experts, int num_ranks,
+                                 int num_nodes);
+
+/* ep_get_layout -- the dispatch layout of one batch.
+ *
+ * In:  topk_idx      int64 [T][k]; expert id per (token, slot); -1 marks an unused slot.
+ * Out (all int32 unless noted; NULL allowed where marked):
+ *   num_tokens_per_rank    [R]    tokens with at least one expert on rank r (a token counts
+ *                                 once per rank however many of its experts the rank holds)
+ *   num_tokens_per_node    [N]    tokens with at least one expert on node n       (nullable)
+ *   num_tokens_per_expert  [E]    (token, slot) pairs naming expert e             (nullable)
+ *   is_token_in_rank uint8 [T][R] 1 if token t has an expert on rank r, else 0    (nullable)
+ *   rank_offset            [R+1]  exclusive prefix sum of num_tokens_per_rank; rank_offset[R]
+ *                                 = M, the number of (token, rank) pairs
+ *   expert_offset          [E+1]  exclusive prefix sum of num_tokens_per_expert   (nullable)
+ *   token_slot             [T][R] receive row of (t, r) = rank_offset[r] + number of tokens
+ *                                 t' < t on rank r; -1 where t is not on r. The rows of rank
+ *                                 r are rank_offset[r] .. rank_offset[r+1]-1, in token order.
+ *   error_flag             [1]    overwritten: 0, or EP_DEVERR_TOPK_RANGE when an entry is
+ *                                 < -1 or >= E (such entries are skipped like -1).
+ * Workspace: `workspace` of `workspace_bytes` >= ep_layout_workspace_bytes(T, E, R, N) bytes,
+ *   16-byte aligned, contents on entry irrelevant, clobbered.
+ * Sizes: T >= 0, 1 <= k <= E, 1 <= R <= EP_MAX_RANKS, E <= EP_MAX_EXPERTS, E % R == 0,
+ *   1 <= N, R % N == 0, T * min(k, R) <= INT32_MAX.
+ * Errors: EP_ERR_ARG (sizes, NULL), EP_ERR_ALIGN (int32/int64 arrays not naturally aligned,
+ *   workspace not 16-byte aligned), EP_ERR_CAPACITY (workspace too small), EP_ERR_HIP.
+ * T == 0 is valid: counts and offsets are written as zeros. */
+int ep_get_layout(const int64_t *topk_idx, int64_t num_tokens, int num_topk,
+                  int num_experts, int num_ranks, int num_nodes,
+                  int32_t *num_tokens_per_rank, int32_t *num_tokens_per_node,
+                  int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                  int32_t *rank_offset, int32_t *expert_offset, int32_t *token_slot,
+                  int32_t *error_flag, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ep_dispatch -- pack every (token, rank) pair into its receive row.
+ *
+ * In:  x            bf16 [T][H] (any 16-bit payload; copied as bits)
+ *      topk_idx     int64 [T][k], topk_weights fp32 [T][k] (may be NULL when
+ *                   recv_topk_weights is NULL)
+ *      token_slot   int32 [T][R] from ep_get_layout
+ * Out: for each t, r with s = token_slot[t][r] >= 0:
+ *      recv_x            bf16 [cap][H]  row s = row t of x
+ *      recv_topk_idx     int64 [cap][k] row s, slot j = e - r*E/R if expert e = topk_idx[t][j]
+ *                                       lives on r, else -1                       (nullable)
+ *      recv_topk_weights fp32 [cap][k]  topk_weights[t][j] where recv_topk_idx is >= 0,
+ *                                       else +0.0f                                (nullable)
+ *      recv_src_idx      int32 [cap]    t                                         (nullable)
+ *      Rows >= M are not written.
+ * Sizes: H % 8 == 0; x and recv_x 16-byte aligned (rows move as 128-bit words);
+ *   recv_capacity >= 0 rows. A slot >= recv_capacity is skipped and sets
+ *   EP_DEVERR_RECV_OVERFLOW, so a capacity of T * min(k, R) never overflows and a capacity
+ *   of exactly M (read back from rank_offset[R]) is also valid.
+ * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_HIP. */
+int ep_dispatch(const void *x, const int64_t *topk_idx, const float *topk_weights,
+                int64_t num_tokens, int hidden, int num_topk, int num_experts, int num_ranks,
+                const int32_t *token_slot, void *recv_x, int64_t *recv_topk_idx,
+                float *recv_topk_weights, int32_t *recv_src_idx, int64_t recv_capacity,
+                int32_t *error_flag, void *stream);
+
+/* ep_restripe_prob -- prob from token-major to destination-major
+ * ("[PR #634] Hybrid ep nixl restripe", section "Fix").
+ *
+ * In:  prob            fp32 [T][N][P]
+ * Out: prob_dest_major fp32 [N][Tmax][P]; element [n][t][p] = prob[t][n][p] for t < T, copied
+ *      as 32-bit words. Rows t in [T, Tmax) of every node block are not written.
+ * Sizes: T >= 0, N >= 1, P >= 1, Tmax >= T (else EP_ERR_CAPACITY). When P % 4 == 0 and both
+ *   pointers are 16-byte aligned slices move as 128-bit words, otherwise as 32-bit words.
+ * Errors: EP_ERR_ARG, EP_ERR_ALIGN (pointers not 4-byte aligned), EP_ERR_CAPACITY,
+ *   EP_ERR_HIP. */
+int ep_restripe_prob(const float *prob, int64_t num_tokens, int num_nodes, int prob_per_token,
+                     int64_t max_tokens_per_rank, float *prob_dest_major, void *stream);
+
+/* ep_combine -- gather each token's per-rank partial rows back to token order and sum them.
+ *
+ * In:  partial     bf16 [num_partial_rows][H], laid out like ep_dispatch's recv_x
+ *      token_slot  int32 [T][R] from ep_get_layout
+ * Out: out         bf16 [T][H]; out[t][h] = bf16_rne( sum over r = 0..R-1 with
+ *                  s = token_slot[t][r] >= 0 of float(partial[s][h]) ), accumulated in fp32
+ *                  in ascending r from +0.0f; a token on no rank gets +0.0.
+ * Sizes: H % 8 == 0; partial and out 16-byte aligned. A slot >= num_partial_rows is skipped
+ *   and sets EP_DEVERR_SLOT_RANGE.
+ * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_HIP. */
+int ep_combine(const void *partial, int64_t num_partial_rows, const int32_t *token_slot,
+               int64_t num_tokens, int hidden, int num_ranks, void *out, int32_t *error_flag,
+               void *stream);
+
+/* ep_hbm_copy -- measurement helper, not a step of the path: a plain 128-bit copy of
+ * `bytes` bytes (a multiple of 16; both pointers 16-byte aligned) used as the HBM
+ * copy-bandwidth yardstick and as the known-size reference for hardware byte counters.
+ * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_HIP. */
+int ep_hbm_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

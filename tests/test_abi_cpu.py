@@ -1,0 +1,149 @@
+"""CPU checks of the C-ABI library: it loads, exports every function include/ep.h
+declares, and rejects bad arguments on the host before anything is enqueued (no GPU is
+touched: every call here fails validation)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+import combine_ep_get_03_amd as ep
+from combine_ep_get_03_amd import _binding
+
+P = ctypes.c_void_p
+A16 = P(0x10000)      # a 16-byte aligned, non-NULL stand-in pointer (never dereferenced)
+MIS = P(0x10001)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_binding.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return ep.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"ep_get_layout", "ep_dispatch", "ep_restripe_prob", "ep_combine",
+                          "ep_layout_workspace_bytes", "ep_status_string", "ep_hbm_copy"}
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ep_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    for n in names:
+        getattr(lib, n)
+
+
+def test_status_strings(lib):
+    for code in (ep.EP_OK, ep.EP_ERR_ARG, ep.EP_ERR_ALIGN, ep.EP_ERR_CAPACITY, ep.EP_ERR_HIP):
+        s = ep.ep_status_string(code)
+        assert s.startswith("EP_")
+    assert "unknown" in ep.ep_status_string(12345)
+
+
+def test_workspace_query(lib):
+    for T, E, R, N in [(4096, 256, 32, 4), (16384, 256, 64, 8), (1, 16, 4, 2), (257, 8192, 1024, 8)]:
+        nb = (T + 255) // 256
+        need = ep.ep_layout_workspace_bytes(T, E, R, N)
+        assert need >= nb * (R + N + E + 1) * 4
+        assert need % 256 == 0
+    assert ep.ep_layout_workspace_bytes(0, 16, 4, 2) == 0
+    assert ep.ep_layout_workspace_bytes(10, 15, 4, 2) == 0      # E % R
+    assert ep.ep_layout_workspace_bytes(10, 16, 4, 3) == 0      # R % N
+    assert ep.ep_layout_workspace_bytes(10, 2048, 2048, 1) == 0  # R > EP_MAX_RANKS
+
+
+def _layout(lib, T=100, k=4, E=16, R=4, N=2, idx=A16, ws=A16, wsb=1 << 20, slot=A16):
+    return lib.ep_get_layout(idx, T, k, E, R, N, A16, A16, A16, A16, A16, A16, slot, A16, ws,
+                             wsb, None)
+
+
+def test_layout_validation(lib):
+    assert _layout(lib, E=15) == ep.EP_ERR_ARG
+    assert _layout(lib, N=3) == ep.EP_ERR_ARG
+    assert _layout(lib, k=17) == ep.EP_ERR_ARG
+    assert _layout(lib, k=0) == ep.EP_ERR_ARG
+    assert _layout(lib, T=-1) == ep.EP_ERR_ARG
+    assert _layout(lib, E=16384, R=16) == ep.EP_ERR_ARG
+    assert _layout(lib, E=2048, R=2048, N=1) == ep.EP_ERR_ARG
+    assert _layout(lib, T=2**30, k=4) == ep.EP_ERR_ARG         # slots would pass INT32_MAX
+    assert _layout(lib, idx=None) == ep.EP_ERR_ARG
+    assert _layout(lib, slot=None) == ep.EP_ERR_ARG
+    assert _layout(lib, idx=MIS) == ep.EP_ERR_ALIGN
+    assert _layout(lib, ws=P(0x10004)) == ep.EP_ERR_ALIGN
+    assert _layout(lib, wsb=16) == ep.EP_ERR_CAPACITY
+    assert _layout(lib, ws=None) == ep.EP_ERR_CAPACITY
+
+
+def _dispatch(lib, T=10, H=64, k=2, E=8, R=4, x=A16, cap=100, recv_x=A16, slot=A16,
+              ridx=A16, idx=A16):
+    return lib.ep_dispatch(x, idx, A16, T, H, k, E, R, slot, recv_x, ridx, A16, A16, cap, A16,
+                           None)
+
+
+def test_dispatch_validation(lib):
+    assert _dispatch(lib, H=12) == ep.EP_ERR_ALIGN
+    assert _dispatch(lib, x=MIS) == ep.EP_ERR_ALIGN
+    assert _dispatch(lib, recv_x=P(0x10008)) == ep.EP_ERR_ALIGN
+    assert _dispatch(lib, cap=-1) == ep.EP_ERR_ARG
+    assert _dispatch(lib, x=None) == ep.EP_ERR_ARG
+    assert _dispatch(lib, slot=None) == ep.EP_ERR_ARG
+    assert _dispatch(lib, idx=None) == ep.EP_ERR_ARG             # needed for recv_topk_idx
+    assert _dispatch(lib, E=6) == ep.EP_ERR_ARG
+    assert _dispatch(lib, H=0) == ep.EP_ERR_ARG
+
+
+def test_restripe_validation(lib):
+    f = lib.ep_restripe_prob
+    assert f(A16, 10, 2, 4, 9, A16, None) == ep.EP_ERR_CAPACITY
+    assert f(A16, 10, 0, 4, 10, A16, None) == ep.EP_ERR_ARG
+    assert f(A16, 10, 2, 0, 10, A16, None) == ep.EP_ERR_ARG
+    assert f(None, 10, 2, 4, 10, A16, None) == ep.EP_ERR_ARG
+    assert f(P(0x10002), 10, 2, 4, 10, A16, None) == ep.EP_ERR_ALIGN
+
+
+def test_combine_validation(lib):
+    f = lib.ep_combine
+    assert f(A16, 10, A16, 10, 64, 0, A16, None, None) == ep.EP_ERR_ARG
+    assert f(A16, 10, A16, 10, 60, 4, A16, None, None) == ep.EP_ERR_ALIGN
+    assert f(MIS, 10, A16, 10, 64, 4, A16, None, None) == ep.EP_ERR_ALIGN
+    assert f(A16, -1, A16, 10, 64, 4, A16, None, None) == ep.EP_ERR_ARG
+    assert f(A16, 10, None, 10, 64, 4, A16, None, None) == ep.EP_ERR_ARG
+
+
+def test_copy_validation(lib):
+    assert lib.ep_hbm_copy(A16, A16, 24, None) == ep.EP_ERR_ALIGN
+    assert lib.ep_hbm_copy(None, A16, 32, None) == ep.EP_ERR_ARG
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", os.path.join(ROOT, "no_such_libep.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _binding.load()
+
+
+def test_product_path_never_imports_the_oracle():
+    code = ("import sys; import combine_ep_get_03_amd, combine_ep_get_03_amd.pipeline, "
+            "combine_ep_get_03_amd.buffers; "
+            "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules)")
+    subprocess.run([sys.executable, "-c", code], cwd=ROOT, check=True)
+    for dirpath, _, files in os.walk(os.path.join(ROOT, "combine_ep_get_03_amd")):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".hpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in text and "from oracle" not in text, fn
+                assert "oracle.h" not in text, fn
