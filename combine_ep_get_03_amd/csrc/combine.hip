@@ -15,8 +15,27 @@
 namespace ep {
 namespace {
 
+#ifndef EP_COMBINE_BLOCK_WORDS
+#define EP_COMBINE_BLOCK_WORDS 1024
+#endif
+#ifndef EP_COMBINE_NT_LOAD
+#define EP_COMBINE_NT_LOAD 1
+#endif
+#ifndef EP_COMBINE_WORDS_PER_LANE
+#define EP_COMBINE_WORDS_PER_LANE 1
+#endif
+
 constexpr int kCT = 256;     // threads per block
 constexpr int kCLoads = 8;   // source rows loaded together
+constexpr int kCBlockWords = EP_COMBINE_BLOCK_WORDS;  // output words a block aims to own
+
+__device__ __forceinline__ u32x4 load_partial_word(const u32x4* p) {
+#if EP_COMBINE_NT_LOAD
+    return load_stream(p);
+#else
+    return *p;
+#endif
+}
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -62,35 +81,58 @@ __global__ __launch_bounds__(kCT) void combine_kernel(const u32x4* __restrict__ 
     }
     __syncthreads();
 
+    // Each lane owns kCW output words per pass (kCW * up to kCLoads loads in flight).
+    constexpr int kCW = EP_COMBINE_WORDS_PER_LANE;
     const int total = nt * V;
-    for (int f = tid; f < total; f += kCT) {
-        const int tt = f / V;
-        const int vv = f - tt * V;
-        const int c = s_cnt[tt];
-        const int32_t* sl = s_slot + tt * R;
-        float acc[8];
+    for (int f0 = 0; f0 < total; f0 += kCT * kCW) {
+        int tt[kCW], vv[kCW], c[kCW];
+        float acc[kCW][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        for (int d0 = 0; d0 < c; d0 += kCLoads) {
-            u32x4 p[kCLoads];
+        for (int w = 0; w < kCW; ++w) {
+            const int f = f0 + w * kCT + tid;
+            tt[w] = f / V;
+            vv[w] = f - tt[w] * V;
+            c[w] = f < total ? s_cnt[tt[w]] : 0;
 #pragma unroll
-            for (int i = 0; i < kCLoads; ++i)
-                if (d0 + i < c) p[i] = load_stream(partial + static_cast<int64_t>(sl[d0 + i]) * V + vv);
+            for (int i = 0; i < 8; ++i) acc[w][i] = 0.0f;
+        }
+        int cmax = 0;
 #pragma unroll
-            for (int i = 0; i < kCLoads; ++i) {
-                if (d0 + i < c) {
+        for (int w = 0; w < kCW; ++w) cmax = max(cmax, c[w]);
+        for (int d0 = 0; d0 < cmax; d0 += kCLoads) {
+            u32x4 p[kCW][kCLoads];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[2 * q] = acc[2 * q] + lo_bf16(p[i][q]);
-                        acc[2 * q + 1] = acc[2 * q + 1] + hi_bf16(p[i][q]);
+            for (int w = 0; w < kCW; ++w) {
+                const int32_t* sl = s_slot + tt[w] * R;
+#pragma unroll
+                for (int i = 0; i < kCLoads; ++i)
+                    if (d0 + i < c[w])
+                        p[w][i] = load_partial_word(partial + static_cast<int64_t>(sl[d0 + i]) * V + vv[w]);
+            }
+#pragma unroll
+            for (int w = 0; w < kCW; ++w) {
+#pragma unroll
+                for (int i = 0; i < kCLoads; ++i) {
+                    if (d0 + i < c[w]) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            acc[w][2 * q] = acc[w][2 * q] + lo_bf16(p[w][i][q]);
+                            acc[w][2 * q + 1] = acc[w][2 * q + 1] + hi_bf16(p[w][i][q]);
+                        }
                     }
                 }
             }
         }
-        u32x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = pack_bf16(acc[2 * q], acc[2 * q + 1]);
-        store_stream(out + (t0 + tt) * V + vv, o);
+        for (int w = 0; w < kCW; ++w) {
+            const int f = f0 + w * kCT + tid;
+            if (f < total) {
+                u32x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = pack_bf16(acc[w][2 * q], acc[w][2 * q + 1]);
+                store_stream(out + (t0 + tt[w]) * V + vv[w], o);
+            }
+        }
     }
     if (errbits) raise_error(error_flag, errbits);
 }
@@ -102,7 +144,7 @@ hipError_t launch_combine(const void* partial, int64_t rows, const int32_t* toke
                           hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    int tpb = std::max(1, std::min(64, (kCT * 4) / V));
+    int tpb = std::max(1, std::min(64, kCBlockWords / V));
     tpb = std::max(1, std::min(tpb, 8192 / R));
     const int64_t grid = (T + tpb - 1) / tpb;
     if (!grid_fits(grid, kCT)) return hipErrorInvalidConfiguration;

@@ -11,6 +11,8 @@
 namespace ep {
 
 constexpr int kWave = 64;
+constexpr int kMaxRanks = 1024;    // = EP_MAX_RANKS of the public header
+constexpr int kMaxExperts = 8192;  // = EP_MAX_EXPERTS of the public header
 
 // 32-bit lane id and the number of set bits of `mask` on lanes below this one
 // (v_mbcnt_lo / v_mbcnt_hi).
@@ -22,6 +24,22 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 }
 
 __device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
+
+// Division by a launch-constant divisor: a shift when it is a power of two (the usual
+// experts-per-rank and ranks-per-node counts), else the integer division.
+struct FastDiv {
+    int d;
+    int shift;  // log2(d) when d is a power of two, else -1
+    static FastDiv make(int d) {
+        int s = -1;
+        if (d > 0 && (d & (d - 1)) == 0) {
+            s = 0;
+            while ((1 << s) != d) ++s;
+        }
+        return FastDiv{d, s};
+    }
+    __device__ __forceinline__ int div(int n) const { return shift >= 0 ? n >> shift : n / d; }
+};
 
 // 128-bit word used for every row move.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -6,58 +6,100 @@
 // bitmap, exclusive prefix offsets, and for every (token, rank) pair its receive row
 // = rank_offset[r] + (tokens before it on rank r).
 //
-// Three launches, no inter-block communication inside a launch, integer only, so the
-// result is the same on every run:
-//   1. count: one token per lane, 256 tokens per block. Rank and node sets of a token
-//      are bit masks; a wave64 ballot per rank gives the wave's count; per-expert
-//      counts go through an LDS histogram. Per-block counts go to the workspace.
-//   2. scan: one block walks the per-block counts column by column through an LDS tile
-//      (an exclusive prefix per rank over blocks), reduces nodes and experts, and scans
-//      the per-rank and per-expert totals into offsets.
-//   3. slot: each block rebuilds its ballots and writes token_slot and the bitmap
-//      row-major with consecutive lanes on consecutive words; a slot is the block's
-//      base for the rank plus the popcount of the ballot bits below the token.
+// Integer only and no inter-block communication inside a launch, so every run gives
+// the same result. Blocks own 256 consecutive tokens, one per lane.
+//   1. count: the rank and node sets of a token are bit masks; a 64x64 bit transpose
+//      across the wave turns the lanes' masks into one ballot per rank (node), whose
+//      popcount is the wave's count; per-expert counts go through an LDS
+//      histogram, stored as the block's inclusive prefix over experts. Per-block
+//      counts go to the workspace.
+//   2. slot: each block rebuilds its ballots; a slot is rank_offset[r] + the block's
+//      prefix for r + the popcount of the ballot bits below the token. token_slot and
+//      the bitmap are written row-major, consecutive threads on consecutive words.
+//      Expert offsets are column sums of the per-block inclusive prefixes, so they need
+//      no scan: the slot blocks split the expert columns between them.
+// When the per-block rank table is small (up to 64 blocks and 4096 cells, R <= 256)
+// every slot block reduces that table itself (two launches in all); otherwise a
+// one-block scan launch between the two computes the per-block rank prefixes.
+// Small tables are read with several loads in flight per lane: the path is latency
+// bound, so each block waits on as few memory round trips as possible.
 #include "ep_internal.hpp"
 
 namespace ep {
 namespace {
 
-constexpr int kBT = kLayoutBlockTokens;      // tokens (= threads) per block
-constexpr int kWavesBT = kBT / kWave;        // 4
+constexpr int kBT = kLayoutBlockTokens;  // tokens (= threads) per block
+constexpr int kWavesBT = kBT / kWave;    // 4
 constexpr int kScanThreads = 1024;
-constexpr int kTileInts = 8192;              // 32 KiB LDS tile for the column walks
+constexpr int kTileInts = 8192;          // 32 KiB LDS tile for the one-block column walks
+constexpr int kFusedMaxBlocks = 64;
+constexpr int kFusedMaxCells = 4096;
+constexpr int kFusedMaxRanks = kBT;
+constexpr int kBatch = 8;                // loads in flight per lane for table reads
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Rank mask (and optionally node mask) of one token; expert -1 and out-of-range ids
-// are skipped, the latter reported through `bad`.
+// are skipped, the latter reported through `bad`. The k ids are loaded 8 at a time so
+// their latencies overlap.
 template <int NW, bool kCount>
-__device__ __forceinline__ void token_masks(const int64_t* __restrict__ row, int k, int E, int er,
-                                            int rpn, uint64_t (&rm)[NW], uint64_t (&nm)[NW],
-                                            int32_t* s_hist, int& bad) {
-    for (int j = 0; j < k; ++j) {
-        const int64_t e = row[j];
-        if (e < 0 || e >= E) {
-            if (e != -1) bad = 1;
-            continue;
-        }
-        const int r = static_cast<int>(e) / er;
-        if (kCount) atomicAdd(&s_hist[e], 1);
+__device__ __forceinline__ void token_masks(const int64_t* __restrict__ row, int k, int E,
+                                            FastDiv er, FastDiv rpn, uint64_t (&rm)[NW],
+                                            uint64_t (&nm)[NW], int32_t* s_hist, int& bad) {
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+        int64_t ev[kBatch];
 #pragma unroll
-        for (int w = 0; w < NW; ++w)
-            if ((r >> 6) == w) rm[w] |= 1ull << (r & 63);
-        if (kCount) {
-            const int n = r / rpn;
+        for (int u = 0; u < kBatch; ++u) ev[u] = (j0 + u < k) ? row[j0 + u] : -1;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t e = ev[u];
+            if (e < 0 || e >= E) {
+                if (e != -1) bad = 1;
+                continue;
+            }
+            const int r = er.div(static_cast<int>(e));
+            if (kCount) atomicAdd(&s_hist[e], 1);
 #pragma unroll
             for (int w = 0; w < NW; ++w)
-                if ((n >> 6) == w) nm[w] |= 1ull << (n & 63);
+                if ((r >> 6) == w) rm[w] |= 1ull << (r & 63);
+            if (kCount) {
+                const int n = rpn.div(r);
+#pragma unroll
+                for (int w = 0; w < NW; ++w)
+                    if ((n >> 6) == w) nm[w] |= 1ull << (n & 63);
+            }
         }
     }
 }
 
-// Per wave: for each of `count` bit positions, ballot the bit across the wave and leave
-// popcount(ballot) (kPop) or the ballot itself in lane b of word w. Result stored to
-// dst[64*w + lane] for the lanes that own a position.
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int lane_mask) {
+    const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), lane_mask, kWave));
+    const uint32_t hi =
+        static_cast<uint32_t>(__shfl_xor(static_cast<int>(v >> 32), lane_mask, kWave));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Transpose of a 64x64 bit matrix held one row per lane: afterwards bit i of lane j is
+// bit j of lane i's input. Six rounds; round s swaps the off-diagonal s x s sub-blocks
+// between lanes i and i ^ s.
+__device__ __forceinline__ uint64_t wave_transpose64(uint64_t row) {
+    const int lane = lane_id();
+    constexpr uint64_t kKeep[6] = {0x00000000FFFFFFFFull, 0x0000FFFF0000FFFFull,
+                                   0x00FF00FF00FF00FFull, 0x0F0F0F0F0F0F0F0Full,
+                                   0x3333333333333333ull, 0x5555555555555555ull};
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        const int s = 32 >> i;
+        const uint64_t other = shfl_xor64(row, s);
+        row = (lane & s) ? ((row & ~kKeep[i]) | ((other & ~kKeep[i]) >> s))
+                         : ((row & kKeep[i]) | ((other & kKeep[i]) << s));
+    }
+    return row;
+}
+
+// Per wave: the ballot of each of `count` bit positions of the lanes' masks, i.e. the
+// columns of the wave's (lanes x positions) bit matrix, taken 64 positions at a time
+// by a transpose. dst[p] gets the ballot of position p (or its popcount with kPop).
 template <int NW, bool kPop, typename Out>
 __device__ __forceinline__ void wave_ballots(const uint64_t (&mask)[NW], int count, Out* dst) {
     const int lane = lane_id();
@@ -65,25 +107,170 @@ __device__ __forceinline__ void wave_ballots(const uint64_t (&mask)[NW], int cou
     for (int w = 0; w < NW; ++w) {
         const int base = w * kWave;
         if (base < count) {
-            const int lim = min(kWave, count - base);
-            Out mine = 0;
-            for (int b = 0; b < lim; ++b) {
-                const uint64_t m = wave_ballot((mask[w] >> b) & 1ull);
-                if (lane == b) mine = kPop ? static_cast<Out>(__popcll(m)) : static_cast<Out>(m);
-            }
-            if (lane < lim) dst[base + lane] = mine;
+            const uint64_t col = wave_transpose64(mask[w]);
+            if (base + lane < count)
+                dst[base + lane] = kPop ? static_cast<Out>(__popcll(col)) : static_cast<Out>(col);
         }
+    }
+}
+
+// Exclusive prefix of one value per thread over the block; `total` gets the sum.
+__device__ int block_exclusive_scan(int v, int32_t* s_tmp /*[17]*/, int& total) {
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    int x = v;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    if (lane == kWave - 1) s_tmp[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        const int ws = lane < nwaves ? s_tmp[lane] : 0;
+        int xs = ws;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int y = __shfl_up(xs, d, kWave);
+            if (lane >= d) xs += y;
+        }
+        if (lane < nwaves) s_tmp[lane] = xs - ws;
+        if (lane == nwaves - 1) s_tmp[16] = xs;
+    }
+    __syncthreads();
+    const int res = x - v + s_tmp[wave];
+    total = s_tmp[16];
+    __syncthreads();
+    return res;
+}
+
+// For i in [0, n), strided over the block: acc[col(i)] += src(i) (LDS atomics), with
+// kBatch loads in flight per lane. Used for small [rows][cols] tables.
+template <typename Src, typename Col>
+__device__ __forceinline__ void accumulate_columns(int n, Src src, Col col, int32_t* acc) {
+    for (int i0 = threadIdx.x; i0 < n; i0 += blockDim.x * kBatch) {
+        int v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = i0 + u * blockDim.x;
+            v[u] = i < n ? src(i) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = i0 + u * blockDim.x;
+            if (i < n && v[u] != 0) atomicAdd(&acc[col(i)], v[u]);
+        }
+    }
+}
+
+// token_slot and the bitmap of one block's tokens, row-major, from the block's ballots
+// (s_ball[w][r]: which of wave w's tokens are on rank r) and slot bases (s_base[w][r]).
+// With R <= 256 each thread keeps one rank column and its four ballots in registers,
+// so consecutive threads write consecutive words of a row and the loop needs no
+// division or LDS access.
+__device__ __forceinline__ void write_block_slots(const uint64_t* s_ball, const int32_t* s_base,
+                                                  int64_t T, int64_t t0, int R,
+                                                  int32_t* __restrict__ token_slot,
+                                                  uint8_t* __restrict__ in_rank) {
+    const int tid = threadIdx.x;
+    const int nt = static_cast<int>(min<int64_t>(kBT, T - t0));
+    int32_t* slot_out = token_slot + t0 * R;
+    uint8_t* bit_out = in_rank ? in_rank + t0 * R : nullptr;
+    if (R <= kBT) {
+        const int rows_per_pass = kBT / R;
+        const int r = tid % R;
+        const int q0 = tid / R;
+        if (q0 >= rows_per_pass) return;
+#pragma unroll
+        for (int w = 0; w < kWavesBT; ++w) {
+            const uint64_t m = s_ball[w * R + r];
+            const int base = s_base[w * R + r];
+            for (int l = q0; l < kWave; l += rows_per_pass) {
+                const int tt = w * kWave + l;
+                if (tt >= nt) break;
+                const bool on = (m >> l) & 1ull;
+                const int below = __popcll(m & ((1ull << l) - 1ull));
+                slot_out[tt * R + r] = on ? base + below : -1;
+                if (bit_out) bit_out[tt * R + r] = on ? 1 : 0;
+            }
+        }
+        return;
+    }
+    const int total = nt * R;
+    for (int f = tid; f < total; f += kBT) {
+        const int tt = f / R;
+        const int r = f - tt * R;
+        const int w = tt / kWave;
+        const int l = tt % kWave;
+        const uint64_t m = s_ball[w * R + r];
+        const bool on = (m >> l) & 1ull;
+        const int below = __popcll(m & ((1ull << l) - 1ull));
+        slot_out[f] = on ? s_base[w * R + r] + below : -1;
+        if (bit_out) bit_out[f] = on ? 1 : 0;
+    }
+}
+
+// token_slot and the bitmap of one wave's 64 tokens starting at tq0, from that wave's
+// ballots (ball[r]) and slot bases (base[r]). With `vec` (R % 4 == 0 and aligned
+// outputs) a thread writes four ranks of a token: one 128-bit and one 32-bit store.
+__device__ __forceinline__ void write_wave_slots(const uint64_t* ball, const int32_t* base,
+                                                 int64_t T, int64_t tq0, int R, bool vec,
+                                                 int32_t* __restrict__ token_slot,
+                                                 uint8_t* __restrict__ in_rank) {
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x;
+    const int nt = static_cast<int>(min<int64_t>(kWave, T - tq0));
+    if (nt <= 0) return;
+    int32_t* slot_out = token_slot + tq0 * R;
+    uint8_t* bit_out = in_rank ? in_rank + tq0 * R : nullptr;
+    if (vec) {
+        const int cols = R / 4;
+        const int rows_per_pass = kBT / cols;
+        const int c = tid % cols;
+        const int l0 = tid / cols;
+        if (l0 >= rows_per_pass) return;
+        uint64_t m[4];
+        int bs[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            m[u] = ball[4 * c + u];
+            bs[u] = base[4 * c + u];
+        }
+        for (int l = l0; l < nt; l += rows_per_pass) {
+            const uint64_t below = (1ull << l) - 1ull;
+            i32x4 o;
+            uint32_t bits = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t on = static_cast<uint32_t>((m[u] >> l) & 1ull);
+                o[u] = on ? bs[u] + __popcll(m[u] & below) : -1;
+                bits |= on << (8 * u);
+            }
+            *reinterpret_cast<i32x4*>(slot_out + l * R + 4 * c) = o;
+            if (bit_out) *reinterpret_cast<uint32_t*>(bit_out + l * R + 4 * c) = bits;
+        }
+        return;
+    }
+    const int total = nt * R;
+    for (int f = tid; f < total; f += kBT) {
+        const int l = f / R;
+        const int r = f - l * R;
+        const uint64_t m = ball[r];
+        const bool on = (m >> l) & 1ull;
+        slot_out[f] = on ? base[r] + __popcll(m & ((1ull << l) - 1ull)) : -1;
+        if (bit_out) bit_out[f] = on ? 1 : 0;
     }
 }
 
 template <int NW>
 __global__ __launch_bounds__(kBT) void layout_count_kernel(const int64_t* __restrict__ topk_idx,
                                                             int64_t T, int k, int E, int R, int N,
-                                                            int er, int rpn, LayoutWorkspace ws) {
+                                                            FastDiv er, FastDiv rpn,
+                                                            LayoutWorkspace ws) {
     extern __shared__ int32_t smem[];
-    int32_t* s_hist = smem;               // [E]
-    int32_t* s_wr = s_hist + E;           // [4][R]
-    int32_t* s_wn = s_wr + kWavesBT * R;  // [4][N]
+    int32_t* s_hist = smem;                                      // [E]
+    uint16_t* s_wr = reinterpret_cast<uint16_t*>(s_hist + E);    // [4][R] per-wave counts
+    uint16_t* s_wn = s_wr + kWavesBT * R;                        // [4][N]
+    __shared__ int32_t s_scan[17];
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kBT + tid;
@@ -114,38 +301,132 @@ __global__ __launch_bounds__(kBT) void layout_count_kernel(const int64_t* __rest
         for (int w = 0; w < kWavesBT; ++w) c += s_wn[w * N + n];
         ws.blk_node[b * N + n] = c;
     }
-    for (int e = tid; e < E; e += kBT) ws.blk_exp[b * E + e] = s_hist[e];
+    // inclusive prefix of this block's expert histogram
+    int carry = 0;
+    for (int c0 = 0; c0 < E; c0 += kBT) {
+        const int e = c0 + tid;
+        const int h = e < E ? s_hist[e] : 0;
+        int chunk = 0;
+        const int ex = block_exclusive_scan(h, s_scan, chunk);
+        if (e < E) ws.blk_exp[b * E + e] = carry + ex + h;
+        carry += chunk;
+    }
     const int any_bad = __syncthreads_or(bad);
     if (tid == 0) ws.blk_err[b] = any_bad;
 }
 
-// Exclusive prefix of one value per thread over the block; `total` gets the sum.
-__device__ int block_exclusive_scan(int v, int32_t* s_tmp /*[17]*/, int& total) {
-    const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
-    const int nwaves = blockDim.x / kWave;
-    int x = v;
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(x, d, kWave);
-        if (lane >= d) x += y;
-    }
-    if (lane == kWave - 1) s_tmp[wave] = x;
+// Slot kernel with the rank scan folded in (small per-block rank tables only). Four
+// launch blocks share each 256-token group: each rebuilds the group's ballots (one wave
+// per 64 tokens) and reduces the per-block rank table, and each writes the rows of its
+// own 64 tokens, so the writes are spread over four times as many CUs.
+constexpr int kQuarters = kWavesBT;
+
+template <int NW>
+__global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int N, FastDiv er, int nb,
+    LayoutWorkspace ws, int32_t* __restrict__ count_r, int32_t* __restrict__ count_n,
+    int32_t* __restrict__ count_e, int32_t* __restrict__ rank_offset,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ error_flag,
+    int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank, int vec_out) {
+    __shared__ int32_t s_cnt[kFusedMaxCells];               // [nb][R] per-group rank counts
+    __shared__ uint64_t s_ball[kWavesBT * kFusedMaxRanks];  // [4][R] the group's ballots
+    __shared__ int32_t s_base[kFusedMaxRanks];              // slot base of this quarter, per rank
+    __shared__ int32_t s_col[kMaxExperts + 1];              // this block's expert columns
+    __shared__ int32_t s_node[kFusedMaxRanks];              // N <= R
+    __shared__ int32_t s_scan[17];
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int g = blockIdx.x;
+    const int grp = g / kQuarters;
+    const int q = g % kQuarters;
+    const int nblk = gridDim.x;
+    const int64_t t0 = static_cast<int64_t>(grp) * kBT;
+    const int64_t t = t0 + tid;
+    // expert columns [c0, c1) belong to this block; s_col[c] sums column c0 - 1 + c
+    const int cw = (E + nblk - 1) / nblk;
+    const int c0 = min(E, g * cw);
+    const int c1 = min(E, c0 + cw);
+    const int ncol = c1 - c0 + 1;
+
+    for (int i = tid; i < ncol; i += kBT) s_col[i] = 0;
+    if (g == 0)
+        for (int i = tid; i < N; i += kBT) s_node[i] = 0;
     __syncthreads();
-    if (wave == 0) {
-        const int ws = lane < nwaves ? s_tmp[lane] : 0;
-        int xs = ws;
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int y = __shfl_up(xs, d, kWave);
-            if (lane >= d) xs += y;
+
+    // Issue the rank-table loads, then the token's ids, then park the table in LDS.
+    const int ncell = nb * R;
+    constexpr int kCellsPerLane = kFusedMaxCells / kBT;
+    int cell[kCellsPerLane];
+#pragma unroll
+    for (int u = 0; u < kCellsPerLane; ++u) {
+        const int i = tid + u * kBT;
+        cell[u] = i < ncell ? ws.blk_rank[i] : 0;
+    }
+    uint64_t rm[NW], nm[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) rm[w] = nm[w] = 0;
+    int bad = 0;
+    if (t < T) token_masks<NW, false>(topk_idx + t * k, k, E, er, FastDiv{1, 0}, rm, nm, nullptr, bad);
+#pragma unroll
+    for (int u = 0; u < kCellsPerLane; ++u) {
+        const int i = tid + u * kBT;
+        if (i < ncell) s_cnt[i] = cell[u];
+    }
+    accumulate_columns(
+        nb * ncol,
+        [&](int i) {
+            const int e = c0 - 1 + i % ncol;
+            return e >= 0 ? ws.blk_exp[static_cast<int64_t>(i / ncol) * E + e] : 0;
+        },
+        [&](int i) { return i % ncol; }, s_col);
+    int any_bad = 0;
+    if (g == 0) {
+        accumulate_columns(
+            nb * N, [&](int i) { return ws.blk_node[i]; }, [&](int i) { return i % N; }, s_node);
+        for (int i = tid; i < nb; i += kBT) any_bad |= ws.blk_err[i];
+    }
+    wave_ballots<NW, false>(rm, R, s_ball + wave * R);
+    __syncthreads();
+
+    // rank totals, this group's prefix, exclusive rank offsets (R <= blockDim)
+    int tot = 0, pre = 0;
+    if (tid < R) {
+        for (int bb = 0; bb < nb; ++bb) {
+            const int v = s_cnt[bb * R + tid];
+            pre += bb < grp ? v : 0;
+            tot += v;
         }
-        if (lane < nwaves) s_tmp[lane] = xs - ws;
-        if (lane == nwaves - 1) s_tmp[16] = xs;
+    }
+    int M = 0;
+    const int ro = block_exclusive_scan(tid < R ? tot : 0, s_scan, M);
+    if (tid < R) {
+        int base = ro + pre;
+        for (int w = 0; w < q; ++w) base += __popcll(s_ball[w * R + tid]);
+        s_base[tid] = base;
+        if (g == 0) {
+            count_r[tid] = tot;
+            rank_offset[tid] = ro;
+        }
+    }
+    if (g == 0 && tid == 0) rank_offset[R] = M;
+    for (int c = tid + 1; c < ncol; c += kBT) {
+        const int e = c0 - 1 + c;
+        if (count_e) count_e[e] = s_col[c] - s_col[c - 1];
+        if (expert_offset) expert_offset[e + 1] = s_col[c];
+    }
+    if (g == 0) {
+        if (expert_offset && tid == 0) expert_offset[0] = 0;
+        if (count_n)
+            for (int n = tid; n < N; n += kBT) count_n[n] = s_node[n];
     }
     __syncthreads();
-    const int res = x - v + s_tmp[wave];
-    total = s_tmp[16];
-    __syncthreads();
-    return res;
+
+    write_wave_slots(s_ball + q * R, s_base, T, t0 + q * kWave, R, vec_out != 0, token_slot,
+                     in_rank);
+    if (g == 0) {
+        any_bad = __syncthreads_or(any_bad);
+        if (tid == 0) *error_flag = any_bad ? kErrTopkRange : 0;
+    }
 }
 
 // Columns [c0, c0+width) of a [rows][cols] int32 matrix, one column per thread
@@ -184,16 +465,19 @@ __device__ int column_walk(int32_t* __restrict__ m, int rows, int cols, int c0, 
     return carry;
 }
 
+// One block: per-block exclusive rank prefixes (in place), totals, offsets, node and
+// expert counts, error flag. Used when the per-block rank table is too large to be
+// reduced by every slot block.
 __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
     int nb, int E, int R, int N, LayoutWorkspace ws, int32_t* __restrict__ count_r,
     int32_t* __restrict__ count_n, int32_t* __restrict__ count_e,
     int32_t* __restrict__ rank_offset, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ error_flag) {
     __shared__ int32_t s_tile[kTileInts];
+    __shared__ int32_t s_last[kScanThreads];
     __shared__ int32_t s_scan[17];
     const int tid = threadIdx.x;
 
-    // ranks: per-block exclusive prefix in place, totals, offsets (R <= blockDim)
     const int tot = column_walk<true>(ws.blk_rank, nb, R, 0, R, s_tile);
     int M = 0;
     const int ex = block_exclusive_scan(tid < R ? tot : 0, s_scan, M);
@@ -208,19 +492,22 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
         if (tid < N) count_n[tid] = tn;
     }
 
-    int carry = 0;
+    // the column sums of the per-block inclusive expert prefixes are expert_offset[e+1]
+    int before = 0;
     for (int c0 = 0; c0 < E; c0 += kScanThreads) {
         const int width = min(kScanThreads, E - c0);
         const int te = column_walk<false>(ws.blk_exp, nb, E, c0, width, s_tile);
-        int chunk = 0;
-        const int exe = block_exclusive_scan(tid < width ? te : 0, s_scan, chunk);
+        if (tid < width) s_last[tid] = te;
+        __syncthreads();
         if (tid < width) {
-            if (count_e) count_e[c0 + tid] = te;
-            if (expert_offset) expert_offset[c0 + tid] = carry + exe;
+            const int prev = tid == 0 ? before : s_last[tid - 1];
+            if (count_e) count_e[c0 + tid] = te - prev;
+            if (expert_offset) expert_offset[c0 + tid + 1] = te;
         }
-        carry += chunk;
+        before = s_last[width - 1];
+        __syncthreads();
     }
-    if (expert_offset && tid == 0) expert_offset[E] = carry;
+    if (expert_offset && tid == 0) expert_offset[0] = 0;
 
     int bad = 0;
     for (int i = tid; i < nb; i += blockDim.x) bad |= ws.blk_err[i];
@@ -230,11 +517,11 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
 
 template <int NW>
 __global__ __launch_bounds__(kBT) void layout_slot_kernel(
-    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int er,
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, FastDiv er,
     const int32_t* __restrict__ blk_prefix, const int32_t* __restrict__ rank_offset,
     int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank) {
     extern __shared__ uint64_t smem64[];
-    uint64_t* s_ball = smem64;                                         // [4][R]
+    uint64_t* s_ball = smem64;                                            // [4][R]
     int32_t* s_base = reinterpret_cast<int32_t*>(s_ball + kWavesBT * R);  // [4][R]
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -245,7 +532,7 @@ __global__ __launch_bounds__(kBT) void layout_slot_kernel(
 #pragma unroll
     for (int w = 0; w < NW; ++w) rm[w] = nm[w] = 0;
     int bad = 0;
-    if (t < T) token_masks<NW, false>(topk_idx + t * k, k, E, er, 1, rm, nm, nullptr, bad);
+    if (t < T) token_masks<NW, false>(topk_idx + t * k, k, E, er, FastDiv{1, 0}, rm, nm, nullptr, bad);
     wave_ballots<NW, false>(rm, R, s_ball + wave * R);
     __syncthreads();
 
@@ -260,21 +547,7 @@ __global__ __launch_bounds__(kBT) void layout_slot_kernel(
     }
     __syncthreads();
 
-    const int nt = static_cast<int>(min<int64_t>(kBT, T - t0));
-    const int total = nt * R;
-    int32_t* slot_out = token_slot + t0 * R;
-    uint8_t* bit_out = in_rank ? in_rank + t0 * R : nullptr;
-    for (int f = tid; f < total; f += kBT) {
-        const int tt = f / R;
-        const int r = f - tt * R;
-        const int w = tt / kWave;
-        const int l = tt % kWave;
-        const uint64_t m = s_ball[w * R + r];
-        const bool on = (m >> l) & 1ull;
-        const int below = __popcll(m & ((1ull << l) - 1ull));
-        slot_out[f] = on ? s_base[w * R + r] + below : -1;
-        if (bit_out) bit_out[f] = on ? 1 : 0;
-    }
+    write_block_slots(s_ball, s_base, T, t0, R, token_slot, in_rank);
 }
 
 template <int NW>
@@ -283,13 +556,24 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
                        int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
                        int32_t* error_flag, const LayoutWorkspace& ws, hipStream_t stream) {
     const int64_t nb = (T + kBT - 1) / kBT;
-    const int er = E / R;
-    const int rpn = R / N;
+    const FastDiv er = FastDiv::make(E / R);
+    const FastDiv rpn = FastDiv::make(R / N);
     if (!grid_fits(nb, kBT)) return hipErrorInvalidConfiguration;
     if (nb > 0) {
-        const size_t shm = sizeof(int32_t) * (static_cast<size_t>(E) + kWavesBT * (R + N));
+        const size_t shm = sizeof(int32_t) * static_cast<size_t>(E) +
+                           sizeof(uint16_t) * kWavesBT * (R + N);
         hipLaunchKernelGGL(layout_count_kernel<NW>, dim3(static_cast<unsigned>(nb)), dim3(kBT),
                            shm, stream, topk_idx, T, k, E, R, N, er, rpn, ws);
+    }
+    if (nb > 0 && nb <= kFusedMaxBlocks && nb * R <= kFusedMaxCells && R <= kFusedMaxRanks) {
+        const bool vec = R % 4 == 0 && reinterpret_cast<uintptr_t>(token_slot) % 16 == 0 &&
+                         reinterpret_cast<uintptr_t>(in_rank) % 4 == 0;
+        hipLaunchKernelGGL(layout_slot_fused_kernel<NW>,
+                           dim3(static_cast<unsigned>(nb * kQuarters)), dim3(kBT), 0, stream,
+                           topk_idx, T, k, E, R, N, er, static_cast<int>(nb), ws, count_r,
+                           count_n, count_e, rank_offset, expert_offset, error_flag, token_slot,
+                           in_rank, vec ? 1 : 0);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
                        static_cast<int>(nb), E, R, N, ws, count_r, count_n, count_e, rank_offset,

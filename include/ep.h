@@ -52,8 +52,7 @@ enum {
 /* Bits the kernels OR into *error_flag. */
 #define EP_DEVERR_TOPK_RANGE    1  /* a topk_idx entry < -1 or >= num_experts (entry skipped) */
 #define EP_DEVERR_RECV_OVERFLOW 2  /* ep_dispatch met a slot >= recv_capacity (row skipped) */
-#define EP_DEVERR_SLOT_RANGE    4  /* ep_combine met a slot >= num_partial_rows, or a token_slot
-                                      row holds more valid slots than a token can have (skipped) */
+#define EP_DEVERR_SLOT_RANGE    4  /* ep_combine met a slot >= num_partial_rows (skipped) */
 
 /* Limits of this implementation. */
 #define EP_MAX_RANKS   1024
@@ -62,9 +61,9 @@ enum {
 /* Static string for a status code; never NULL. */
 const char *ep_status_string(int status);
 
-/* Bytes of device workspace ep_get_layout needs for these sizes (0 if the sizes are invalid
- * as ep_get_layout would reject them; a size of 0 is valid only for num_tokens == 0 ... and
- * then still returns the few bytes the count reduction uses). */
+/* Bytes of device workspace ep_get_layout needs for these sizes. Returns 0 when
+ * num_tokens == 0 (no workspace needed; NULL is then accepted) and also when the sizes are
+ * ones ep_get_layout rejects. */
 size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_experts, int num_ranks,
                                  int num_nodes);
 

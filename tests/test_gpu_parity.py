@@ -43,6 +43,11 @@ EDGE = [
     W.Config("r100", T=513, H=16, E=200, k=10, R=100, N=4, P=52, Tmax=600),
     W.Config("r1024_max", T=700, H=8, E=2048, k=16, R=1024, N=8, P=256, Tmax=700),
     W.Config("e8192_max", T=400, H=16, E=8192, k=8, R=64, N=8, P=1024, Tmax=400),
+    # per-block count tables too large for the fused slot kernel: three-launch layout
+    W.Config("k80_wide_topk", T=300, H=16, E=256, k=80, R=16, N=4, P=64, Tmax=300),
+    W.Config("h8192_two_chunks", T=130, H=8192, E=64, k=6, R=8, N=2, P=32, Tmax=130),
+    W.Config("many_blocks", T=20000, H=8, E=64, k=4, R=8, N=2, P=4, Tmax=20000),
+    W.Config("wide_table", T=8192, H=8, E=512, k=8, R=256, N=8, P=64, Tmax=8192),
     W.Config("zipf_small_tail", T=4099, H=56, E=256, k=8, R=32, N=4, P=64, Tmax=4099,
              routing="zipf"),
     W.Config("roundtrip_small", T=2000, H=7168, E=256, k=8, R=64, N=8, P=32, Tmax=2000,
@@ -202,3 +207,45 @@ def test_abi_rejects_bad_arguments_on_gpu():
         ep.ep_dispatch(x_odd, b.topk_idx, b.topk_weights, cfg.E, cfg.R, lb.token_slot,
                        recv_x=torch.empty((10, 12), dtype=torch.bfloat16, device="cuda"))
     assert e.value.status == ep.EP_ERR_ALIGN
+
+
+@pytest.mark.parametrize("name", ["tiny", "dsv3"])
+def test_graph_replay_matches_eager(name):
+    """The whole step captured in a HIP graph: every replay, with eager work and
+    synchronisation in between, reproduces the eager outputs bit for bit."""
+    cfg = W.CONFIGS[name]
+    inp = _case(cfg)
+    ref = oracle_all(cfg, inp)
+    b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials)
+    path = Path(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax)
+    fill_sentinels(path)
+    path.step(b)
+    torch.cuda.synchronize()
+    compare_all(cfg, path, ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path.step(b)
+    for _ in range(3):
+        fill_sentinels(path)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        compare_all(cfg, path, ref)
+
+
+def test_dispatch_rows_only():
+    """Metadata outputs are optional: with all three NULL only recv_x is written."""
+    cfg = W.CONFIGS["tiny"]
+    inp = _case(cfg)
+    ref = oracle_all(cfg, inp)
+    M = ref["M"]
+    b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials)
+    path = Path(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax)
+    fill_sentinels(path)
+    path.layout(b)
+    ep.ep_dispatch(b.x, b.topk_idx, None, cfg.E, cfg.R, path.layout_buf.token_slot,
+                   recv_x=path.recv.recv_x, error_flag=path.error_flag)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(path.recv.recv_x)[:M], ref["d"]["recv_x"][:M])
+    assert np.all(host(path.recv.recv_topk_idx) == -0x123456789)
+    assert np.all(host(path.recv.recv_src_idx) == -7)
