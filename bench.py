@@ -48,6 +48,33 @@ def algorithmic_bytes(cfg, M: int) -> dict:
     }
 
 
+COUNTERS = os.path.join(ROOT, "profiles", "dsv3_hbm_counters.md")
+KERNEL_SOURCES = {"dispatch": ["ep_internal.hpp", "dispatch.hip"],
+                  "combine": ["ep_internal.hpp", "combine.hip"]}
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE,
+    calibrated on a copy kernel of known size), or None when the summary does not cover
+    this workload or the kernel's sources changed since the counters were taken."""
+    import hashlib
+
+    if workload != "dsv3" or not os.path.exists(COUNTERS):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "combine_ep_get_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    with open(COUNTERS) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 4 and parts[0] == "traffic" and parts[1] == kernel:
+                fields = dict(p.split("=", 1) for p in parts[2:])
+                if fields.get("sources_sha256") == h.hexdigest()[:16]:
+                    return int(fields["bytes_per_launch"])
+    return None
+
+
 def copy_bandwidth(torch, ep, gib: float):
     """Best of the library's 128-bit copy kernel and torch's device copy, read+write bytes."""
     n = int(gib * (1 << 30)) // 16 * 16
@@ -228,7 +255,9 @@ def main():
                              "tokens_per_s": round(cfg.T / (dc_ms * 1e-3), 1)},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(dom, cfg.name),
+                     "alg_bytes_per_launch": alg[dom], "avg_launch_us": round(avg[dom] * 1e3, 2)},
         "copy_bandwidth_gbps": {k: round(v, 1) for k, v in copy_bw.items()},
         "kernels": kernels,
     }
