@@ -17,11 +17,14 @@ _lib = None
 
 
 def lib():
+    """The oracle library; EP_ORACLE_LIB names another build of oracle.c (the mutation
+    tests load deliberately broken builds this way)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("EP_ORACLE_LIB", _build.LIB)
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int
         L.oracle_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
