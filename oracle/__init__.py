@@ -35,7 +35,15 @@ def lib():
         L.oracle_f32_to_bf16_array.restype = None
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
-        for f in ("oracle_layout", "oracle_dispatch", "oracle_restripe_prob", "oracle_combine"):
+        L.oracle_quantize_fp8.argtypes = [P, i64, i32, P, P]
+        L.oracle_dispatch_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i64, P, P, P, P,
+                                          P]
+        L.oracle_f32_to_e4m3_array.argtypes = [P, i64, P]
+        L.oracle_f32_to_e4m3_array.restype = None
+        L.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_to_f32.restype = ctypes.c_float
+        for f in ("oracle_layout", "oracle_dispatch", "oracle_restripe_prob", "oracle_combine",
+                  "oracle_quantize_fp8", "oracle_dispatch_fp8"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -119,3 +127,46 @@ def f32_to_bf16(a) -> np.ndarray:
 def bf16_to_f32(b) -> np.ndarray:
     """bf16 bit patterns widened to fp32 (exact)."""
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_e4m3(a) -> np.ndarray:
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.uint8)
+    lib().oracle_f32_to_e4m3_array(_p(a), a.size, _p(out))
+    return out
+
+
+def e4m3_to_f32(codes) -> np.ndarray:
+    L = lib()
+    table = np.array([L.oracle_e4m3_to_f32(c) for c in range(256)], np.float32)
+    return table[np.asarray(codes, np.uint8)]
+
+
+def quantize_fp8(x) -> tuple:
+    """bf16 bits [T][H] -> (e4m3 codes uint8 [T][H], fp32 scales [T][H/128])."""
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    codes = np.zeros((T, H), np.uint8)
+    scales = np.zeros((T, max(H // 128, 1)), np.float32)
+    if lib().oracle_quantize_fp8(_p(x), T, H, _p(codes), _p(scales)) != 0:
+        raise ValueError("oracle_quantize_fp8: H must be a multiple of 128")
+    return codes, scales
+
+
+def dispatch_fp8(x, topk_idx, topk_w, E: int, R: int, token_slot, cap: int) -> dict:
+    x = _c(x, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    w = _c(topk_w, np.float32)
+    slot = _c(token_slot, np.int32)
+    T, H = x.shape
+    k = idx.shape[1]
+    G = max(H // 128, 1)
+    out = dict(recv_codes=np.zeros((cap, H), np.uint8), recv_scales=np.zeros((cap, G), np.float32),
+               recv_idx=np.zeros((cap, k), np.int64), recv_w=np.zeros((cap, k), np.float32),
+               recv_src=np.zeros(cap, np.int32))
+    rc = lib().oracle_dispatch_fp8(_p(x), _p(idx), _p(w), T, H, k, E, R, _p(slot), cap,
+                                   _p(out["recv_codes"]), _p(out["recv_scales"]),
+                                   _p(out["recv_idx"]), _p(out["recv_w"]), _p(out["recv_src"]))
+    if rc != 0:
+        raise ValueError("oracle_dispatch_fp8: bad arguments or slot beyond capacity")
+    return out

@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-std=c99", "-O2", "-fno-fast-math", "-ffp-contract=off", "-Wall",
-           "-Wextra", "-shared", "-fPIC", os.path.join(HERE, "oracle.c"), "-o", LIB + ".tmp"]
+           "-Wextra", "-shared", "-fPIC", os.path.join(HERE, "oracle.c"), "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

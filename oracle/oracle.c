@@ -31,10 +31,18 @@
  *    expert id (e - r*E/R) and its weight where the expert is on that rank,
  *    else -1 and +0.0f;
  *  - combine is an unweighted sum in ascending rank order, fp32, from +0.0f,
- *    then one round-to-nearest-even to bf16.
+ *    then one round-to-nearest-even to bf16;
+ *  - FP8 dispatch ("[PR #347]" section 3.2.1 and "[PR #453]" measure dispatch with an
+ *    FP8 payload; their byte counts fit one fp32 scale per 128 channels): each token
+ *    is quantised once, per group of 128 channels, to OCP e4m3 (4 exponent bits,
+ *    bias 7, 3 mantissa bits, largest finite 448, no infinities): amax = largest
+ *    |x| in the group, scale = amax / 448, code = e4m3(x * (448 / amax)) rounded to
+ *    nearest even with the magnitude saturated at 448; an all-zero group gets scale 1
+ *    and zero codes. Every destination row receives the same codes and scales.
  */
 #include "oracle.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -66,6 +74,77 @@ void oracle_f32_to_bf16_array(const float *in, int64_t n, uint16_t *out)
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = oracle_f32_to_bf16(in[i]);
+}
+
+/* OCP e4m3 code of a finite fp32 value: round to nearest even on the e4m3 grid
+ * (spacing 2^(e-3) in binade [2^e, 2^(e+1)) for e >= -6, 2^-9 below 2^-6), with the
+ * magnitude saturated at 448. A NaN gives the NaN code 0x7f with the input's sign. */
+uint8_t oracle_f32_to_e4m3(float v)
+{
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v))
+        return sign | 0x7f;
+    const float a = fabsf(v);
+    if (a >= 464.0f) /* at or beyond the midpoint between 448 and the next step */
+        return sign | 0x7e;
+    if (a == 0.0f)
+        return sign;
+    int e2;
+    frexpf(a, &e2);        /* a = m * 2^e2, m in [0.5, 1) */
+    int ex = e2 - 1;       /* a in [2^ex, 2^(ex+1)) */
+    if (ex < -6)
+        ex = -6;           /* subnormal range: quantum 2^-9 */
+    float q = rintf(ldexpf(a, 3 - ex)); /* a in units of the quantum, nearest even */
+    if (q >= 16.0f) {      /* rounded up into the next binade */
+        ex += 1;
+        q = 8.0f;
+    }
+    if (q < 8.0f)          /* subnormal */
+        return sign | (uint8_t)q;
+    return sign | (uint8_t)(((ex + 7) << 3) | ((int)q - 8));
+}
+
+float oracle_e4m3_to_f32(uint8_t c)
+{
+    const int s = c >> 7, ef = (c >> 3) & 0xf, m = c & 7;
+    float v;
+    if (ef == 0xf && m == 7)
+        v = NAN;
+    else if (ef == 0)
+        v = ldexpf((float)m, -9);
+    else
+        v = ldexpf((float)(8 + m), ef - 7 - 3);
+    return s ? -v : v;
+}
+
+void oracle_f32_to_e4m3_array(const float *in, int64_t n, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_e4m3(in[i]);
+}
+
+/* Per token and per group of 128 channels: scale = amax / 448, codes of x * (448/amax). */
+int oracle_quantize_fp8(const uint16_t *x, int64_t T, int H, uint8_t *codes, float *scales)
+{
+    if (T < 0 || H < 128 || H % 128 != 0)
+        return -1;
+    const int G = H / 128;
+    for (int64_t t = 0; t < T; ++t)
+        for (int g = 0; g < G; ++g) {
+            const uint16_t *xg = x + t * H + g * 128;
+            float amax = 0.0f;
+            for (int c = 0; c < 128; ++c) {
+                const float a = fabsf(oracle_bf16_to_f32(xg[c]));
+                if (a > amax)
+                    amax = a;
+            }
+            const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+            const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
+            scales[t * G + g] = scale;
+            for (int c = 0; c < 128; ++c)
+                codes[t * H + g * 128 + c] = oracle_f32_to_e4m3(oracle_bf16_to_f32(xg[c]) * inv);
+        }
+    return 0;
 }
 
 /* Layout ("get_dispatch_layout", PR #347 commit list; scan over tokens per
@@ -140,6 +219,24 @@ int oracle_layout(const int64_t *topk_idx, int64_t T, int k, int E, int R, int N
     return 0;
 }
 
+/* Rank r's view of token t's routing, written to receive row s: every slot j keeps
+ * its place; an expert on r becomes its rank-local id with its weight, any other
+ * slot becomes -1 with weight +0.0f. The row also records its source token. */
+static void route_view(const int64_t *topk_idx, const float *topk_w, int64_t t, int k, int E,
+                       int experts_per_rank, int r, int64_t s, int64_t *recv_idx, float *recv_w,
+                       int32_t *recv_src)
+{
+    for (int j = 0; j < k; ++j) {
+        int64_t e = topk_idx[t * k + j];
+        int64_t local = -1;
+        if (e >= 0 && e < E && e / experts_per_rank == r)
+            local = e - (int64_t)r * experts_per_rank;
+        recv_idx[s * k + j] = local;
+        recv_w[s * k + j] = local >= 0 ? topk_w[t * k + j] : 0.0f;
+    }
+    recv_src[s] = (int32_t)t;
+}
+
 /* Dispatch permute: each token's row goes, unchanged, to every rank that holds
  * one of its experts, with that rank's view of the top-k routing. */
 int oracle_dispatch(const uint16_t *x, const int64_t *topk_idx, const float *topk_w,
@@ -158,17 +255,48 @@ int oracle_dispatch(const uint16_t *x, const int64_t *topk_idx, const float *top
             if (s >= cap)
                 return -1;
             memcpy(recv_x + s * H, x + t * H, (size_t)H * sizeof(uint16_t));
-            for (int j = 0; j < k; ++j) {
-                int64_t e = topk_idx[t * k + j];
-                int64_t local = -1;
-                if (e >= 0 && e < E && e / experts_per_rank == r)
-                    local = e - (int64_t)r * experts_per_rank;
-                recv_idx[s * k + j] = local;
-                recv_w[s * k + j] = local >= 0 ? topk_w[t * k + j] : 0.0f;
-            }
-            recv_src[s] = (int32_t)t;
+            route_view(topk_idx, topk_w, t, k, E, experts_per_rank, r, s, recv_idx, recv_w,
+                       recv_src);
         }
     return 0;
+}
+
+/* FP8 dispatch: the bf16 dispatch with each row replaced by its e4m3 codes and scales. */
+int oracle_dispatch_fp8(const uint16_t *x, const int64_t *topk_idx, const float *topk_w,
+                        int64_t T, int H, int k, int E, int R, const int32_t *token_slot,
+                        int64_t cap, uint8_t *recv_codes, float *recv_scales,
+                        int64_t *recv_idx, float *recv_w, int32_t *recv_src)
+{
+    if (T < 0 || H < 128 || H % 128 != 0 || k < 1 || E < 1 || R < 1 || E % R != 0)
+        return -1;
+    const int G = H / 128;
+    const int experts_per_rank = E / R;
+    uint8_t *codes = (uint8_t *)malloc((size_t)(T > 0 ? T : 1) * H);
+    float *scales = (float *)malloc((size_t)(T > 0 ? T : 1) * G * sizeof(float));
+    if (!codes || !scales) {
+        free(codes);
+        free(scales);
+        return -1;
+    }
+    oracle_quantize_fp8(x, T, H, codes, scales);
+    int rc = 0;
+    for (int64_t t = 0; t < T && rc == 0; ++t)
+        for (int r = 0; r < R; ++r) {
+            int64_t s = token_slot[t * R + r];
+            if (s < 0)
+                continue;
+            if (s >= cap) {
+                rc = -1;
+                break;
+            }
+            memcpy(recv_codes + s * H, codes + t * H, (size_t)H);
+            memcpy(recv_scales + s * G, scales + t * G, (size_t)G * sizeof(float));
+            route_view(topk_idx, topk_w, t, k, E, experts_per_rank, r, s, recv_idx, recv_w,
+                       recv_src);
+        }
+    free(codes);
+    free(scales);
+    return rc;
 }
 
 /* restripe_prob ("[PR #634] Hybrid ep nixl restripe", section "Fix"): slice

@@ -26,6 +26,17 @@ int oracle_restripe_prob(const uint32_t *prob, int64_t T, int N, int P, int64_t 
 int oracle_combine(const uint16_t *partial, int64_t rows, const int32_t *token_slot,
                    int64_t T, int H, int R, uint16_t *out);
 
+int oracle_quantize_fp8(const uint16_t *x, int64_t T, int H, uint8_t *codes, float *scales);
+
+int oracle_dispatch_fp8(const uint16_t *x, const int64_t *topk_idx, const float *topk_w,
+                        int64_t T, int H, int k, int E, int R, const int32_t *token_slot,
+                        int64_t cap, uint8_t *recv_codes, float *recv_scales,
+                        int64_t *recv_idx, float *recv_w, int32_t *recv_src);
+
+uint8_t oracle_f32_to_e4m3(float v);
+float oracle_e4m3_to_f32(uint8_t c);
+void oracle_f32_to_e4m3_array(const float *in, int64_t n, uint8_t *out);
+
 uint16_t oracle_f32_to_bf16(float f);
 float oracle_bf16_to_f32(uint16_t b);
 void oracle_f32_to_bf16_array(const float *in, int64_t n, uint16_t *out);

@@ -36,6 +36,8 @@ def expected_nodes_per_token(N):
 @pytest.mark.parametrize("row", _rows(), ids=lambda r: f"{r[0]}-{r[1]}-{r[2]}n")
 def test_page_bytes_match_destination_node_count(orc, row):
     src, table, N, eb, gbps, us, digits = row
+    if eb > 100:  # FP8 rows: bytes per channel given in 1e-4 units
+        eb = eb * 1e-4
     page_bytes = gbps * 1e9 * us * 1e-6
     # printing precision of the pair, plus the page's own routing draw (~0.5%)
     tol = 0.5 * 10.0**-digits / gbps + 0.05 / us + 0.01
@@ -66,3 +68,15 @@ def test_physical_share_three_quarters(orc):
     lay = orc.layout(idx, E, 32, 4)
     cn = lay["count_n"].astype(np.float64)
     assert abs(cn[1:].sum() / cn.sum() - 0.75) < 0.01
+
+
+def test_fp8_rows_fit_one_scale_per_128_channels(orc):
+    """The FP8 rows fit 7168 + 4 * 7168 / 128 bytes per token and node; one scale per
+    64 or per 256 channels, or no scales, misses the best-printed row by more."""
+    rows = [r for r in _rows() if r[3] > 100]
+    assert rows
+    best = min(rows, key=lambda r: abs(r[4] * r[5] * 1e3 / (T * 7392 * expected_nodes_per_token(r[2])) - 1))
+    page = best[4] * 1e9 * best[5] * 1e-6
+    fit = T * expected_nodes_per_token(best[2])
+    errs = {g: abs(page / (fit * (H + (4 * H // g if g else 0))) - 1) for g in (0, 64, 128, 256)}
+    assert errs[128] == min(errs.values()) and errs[128] < 0.01

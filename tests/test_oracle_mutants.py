@@ -48,12 +48,23 @@ MUTANTS = [
      "acc[h] = oracle_bf16_to_f32(oracle_f32_to_bf16(acc[h] + oracle_bf16_to_f32(partial[s * H + h])));"),
     ("combine_subtracts", "acc[h] = acc[h] + oracle_bf16_to_f32(partial[s * H + h]);",
      "acc[h] = acc[h] - oracle_bf16_to_f32(partial[s * H + h]);"),
+    ("e4m3_truncates", "float q = rintf(ldexpf(a, 3 - ex));", "float q = truncf(ldexpf(a, 3 - ex));"),
+    ("e4m3_no_subnormal_range", "    if (ex < -6)\n        ex = -6;", "    if (ex < -9)\n        ex = -9;"),
+    ("e4m3_bias_off_by_one", "return sign | (uint8_t)(((ex + 7) << 3) | ((int)q - 8));",
+     "return sign | (uint8_t)(((ex + 8) << 3) | ((int)q - 8));"),
+    ("fp8_scale_not_divided", "const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;",
+     "const float scale = amax > 0.0f ? amax : 1.0f;"),
+    ("fp8_inverse_scale_swapped", "const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;",
+     "const float inv = amax > 0.0f ? amax / 448.0f : 1.0f;"),
+    ("fp8_dispatch_scales_shifted", "memcpy(recv_scales + s * G, scales + t * G, (size_t)G * sizeof(float));",
+     "memcpy(recv_scales + s * G, scales + (t > 0 ? t - 1 : 0) * G, (size_t)G * sizeof(float));"),
     ("combine_truncates_output", "out[t * H + h] = oracle_f32_to_bf16(acc[h]);",
      "{ uint32_t bits; memcpy(&bits, &acc[h], 4); out[t * H + h] = (uint16_t)(bits >> 16); }"),
 ]
 
 # The quick pins (no exhaustive enumeration): enough to kill every mutant above.
 PIN_ARGS = ["tests/test_oracle_layout.py", "tests/test_oracle_dispatch.py",
+            "tests/test_oracle_fp8.py",
             "tests/test_oracle_restripe.py", "tests/test_oracle_combine.py",
             "tests/test_golden_pages.py", "-x", "-q", "-p", "no:cacheprovider",
             "-k", "not exhaustive"]
