@@ -43,10 +43,13 @@ def load() -> ctypes.CDLL:
     L.ep_layout_workspace_bytes.restype = sz
     L.ep_get_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, sz, P]
     L.ep_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, i64, P, P]
+    L.ep_dispatch_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, i64, P,
+                                  P]
     L.ep_restripe_prob.argtypes = [P, i64, i32, i32, i64, P, P]
     L.ep_combine.argtypes = [P, i64, P, i64, i32, i32, P, P, P]
     L.ep_hbm_copy.argtypes = [P, P, sz, P]
-    for f in ("ep_get_layout", "ep_dispatch", "ep_restripe_prob", "ep_combine", "ep_hbm_copy"):
+    for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_restripe_prob",
+              "ep_combine", "ep_hbm_copy"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -154,6 +157,36 @@ def ep_dispatch(x, topk_idx, topk_weights, num_experts: int, num_ranks: int, tok
         _ptr(recv_topk_weights, torch.float32, "recv_topk_weights", True),
         _ptr(recv_src_idx, torch.int32, "recv_src_idx", True), cap,
         _ptr(error_flag, torch.int32, "error_flag", True), _stream(stream)), "ep_dispatch")
+
+
+def ep_dispatch_fp8(x, topk_idx, topk_weights, num_experts: int, num_ranks: int, token_slot, *,
+                    recv_x_fp8, recv_scales, recv_topk_idx=None, recv_topk_weights=None,
+                    recv_src_idx=None, error_flag=None, stream=None) -> None:
+    """recv_x_fp8: uint8 or float8_e4m3fn [cap][H]; recv_scales: fp32 [cap][H/128]."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    cap = recv_x_fp8.shape[0]
+    if recv_x_fp8.dtype == torch.float8_e4m3fn:
+        recv_x_fp8 = recv_x_fp8.view(torch.uint8)
+    _shape(topk_idx, (T, k), "topk_idx")
+    _shape(topk_weights, (T, k), "topk_weights")
+    _shape(token_slot, (T, num_ranks), "token_slot")
+    _shape(recv_x_fp8, (cap, H), "recv_x_fp8")
+    _shape(recv_scales, (cap, H // 128), "recv_scales")
+    _shape(recv_topk_idx, (cap, k), "recv_topk_idx")
+    _shape(recv_topk_weights, (cap, k), "recv_topk_weights")
+    _shape(recv_src_idx, (cap,), "recv_src_idx")
+    _at_least(error_flag, 1, "error_flag")
+    _check(load().ep_dispatch_fp8(
+        _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int64, "topk_idx"),
+        _ptr(topk_weights, torch.float32, "topk_weights", True), T, H, k, num_experts,
+        num_ranks, _ptr(token_slot, torch.int32, "token_slot"),
+        _ptr(recv_x_fp8, torch.uint8, "recv_x_fp8"),
+        _ptr(recv_scales, torch.float32, "recv_scales"),
+        _ptr(recv_topk_idx, torch.int64, "recv_topk_idx", True),
+        _ptr(recv_topk_weights, torch.float32, "recv_topk_weights", True),
+        _ptr(recv_src_idx, torch.int32, "recv_src_idx", True), cap,
+        _ptr(error_flag, torch.int32, "error_flag", True), _stream(stream)), "ep_dispatch_fp8")
 
 
 def ep_restripe_prob(prob, prob_dest_major, stream=None) -> None:

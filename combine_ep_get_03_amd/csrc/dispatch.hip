@@ -111,6 +111,120 @@ __global__ __launch_bounds__(kDT) void dispatch_kernel(
     if (errbits) raise_error(error_flag, errbits);
 }
 
+// FP8 dispatch: the same walk, but each token is first quantised once, in registers:
+// per group of 128 channels (16 words, i.e. 16 aligned lanes of one load row) the
+// largest |x| is reduced with xor shuffles inside the 16 lanes; scale = amax / 448,
+// codes = e4m3(x * (448 / amax)) through the gfx950 packed fp8 convert (round to
+// nearest even; the product is clamped to +-448, which only ever removes rounding
+// excess above 448). A lane then owns 8 code bytes per word; each destination row
+// gets the codes as one burst of 64-bit stores and its H/128 scales.
+template <int WPL>
+__global__ __launch_bounds__(kDT) void dispatch_fp8_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int64_t T, int V, int k, int E, int R, int er,
+    const int32_t* __restrict__ token_slot, u32x2* __restrict__ recv_codes,
+    float* __restrict__ recv_scales, int64_t* __restrict__ recv_idx, float* __restrict__ recv_w,
+    int32_t* __restrict__ recv_src, int64_t cap, int32_t* __restrict__ error_flag) {
+    const int lane = lane_id();
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int G = V / 16;  // scale groups per row
+    const bool meta = recv_idx || recv_w;
+    int64_t e0 = -1;
+    float w0 = 0.0f;
+    if (meta && lane < k) {
+        e0 = topk_idx[t * k + lane];
+        if (topk_w) w0 = topk_w[t * k + lane];
+    }
+    const u32x4* xr = x + t * V;
+    const int32_t* srow = token_slot + t * R;
+    int32_t errbits = 0;
+
+    for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
+        u32x2 code[WPL];
+        float scale[WPL];
+        {
+            u32x4 v[WPL];
+#pragma unroll
+            for (int i = 0; i < WPL; ++i) {
+                const int vi = v0 + i * kWave + lane;
+                if (vi < V) v[i] = load_stream(xr + vi);
+            }
+#pragma unroll
+            for (int i = 0; i < WPL; ++i) {
+                const int vi = v0 + i * kWave + lane;
+                float f[8];
+                float amax = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t wq = vi < V ? v[i][q] : 0u;
+                    f[2 * q] = __uint_as_float(wq << 16);
+                    f[2 * q + 1] = __uint_as_float(wq & 0xffff0000u);
+                    amax = fmaxf(amax, fmaxf(fabsf(f[2 * q]), fabsf(f[2 * q + 1])));
+                }
+#pragma unroll
+                for (int m = 8; m >= 1; m >>= 1)
+                    amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+                const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
+                scale[i] = amax > 0.0f ? amax / 448.0f : 1.0f;
+                int packed[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float c[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        c[u] = fminf(fmaxf(f[4 * h + u] * inv, -448.0f), 448.0f);
+                    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+                    packed[h] = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], wd, true);
+                }
+                code[i][0] = static_cast<uint32_t>(packed[0]);
+                code[i][1] = static_cast<uint32_t>(packed[1]);
+            }
+        }
+        for (int r0 = 0; r0 < R; r0 += kWave) {
+            int32_t s = r0 + lane < R ? srow[r0 + lane] : -1;
+            if (s >= cap) {
+                errbits |= kErrRecvOverflow;
+                s = -1;
+            }
+            uint64_t m = wave_ballot(s >= 0);
+            while (m) {
+                const int src_lane = __builtin_ctzll(m);
+                m &= m - 1;
+                const int64_t sd = __builtin_amdgcn_readlane(s, src_lane);
+                const int rd = r0 + src_lane;
+                u32x2* row = recv_codes + sd * V;
+                float* srow_out = recv_scales + sd * G;
+#pragma unroll
+                for (int i = 0; i < WPL; ++i) {
+                    const int vi = v0 + i * kWave + lane;
+                    if (vi < V) {
+                        __builtin_nontemporal_store(code[i], row + vi);
+                        if ((lane & 15) == 0) srow_out[vi / 16] = scale[i];
+                    }
+                }
+                if (v0 != 0) continue;
+                if (meta) {
+                    for (int j0 = 0; j0 < k; j0 += kWave) {
+                        const int j = j0 + lane;
+                        if (j >= k) continue;
+                        const int64_t e = j0 == 0 ? e0 : topk_idx[t * k + j];
+                        const int64_t lo = static_cast<int64_t>(rd) * er;
+                        const bool local = e >= lo && e < lo + er;
+                        if (recv_idx) recv_idx[sd * k + j] = local ? e - lo : -1;
+                        if (recv_w) {
+                            const float wv = j0 == 0 ? w0 : topk_w[t * k + j];
+                            recv_w[sd * k + j] = local ? wv : 0.0f;
+                        }
+                    }
+                }
+                if (recv_src && lane == 0) recv_src[sd] = static_cast<int32_t>(t);
+            }
+        }
+    }
+    if (errbits) raise_error(error_flag, errbits);
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* topk_w,
@@ -133,6 +247,33 @@ hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* 
     else if (V <= 7 * kWave || EP_DISPATCH_MAX_WPL < 14) EP_DISPATCH_LAUNCH(7);
     else EP_DISPATCH_LAUNCH(14);
 #undef EP_DISPATCH_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace ep
+
+namespace ep {
+
+hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_w,
+                               int64_t T, int H, int k, int E, int R, const int32_t* token_slot,
+                               void* recv_codes, float* recv_scales, int64_t* recv_idx,
+                               float* recv_w, int32_t* recv_src, int64_t cap, int32_t* error_flag,
+                               hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int V = H / 8;
+    const int64_t grid = (T + kDWaves - 1) / kDWaves;
+    if (!grid_fits(grid, kDT)) return hipErrorInvalidConfiguration;
+#define EP_DISPATCH_FP8_LAUNCH(WPL)                                                             \
+    hipLaunchKernelGGL(dispatch_fp8_kernel<WPL>, dim3(static_cast<unsigned>(grid)), dim3(kDT), 0, \
+                       stream, static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, E, R,      \
+                       E / R, token_slot, static_cast<u32x2*>(recv_codes), recv_scales, recv_idx,  \
+                       recv_w, recv_src, cap, error_flag)
+    if (V <= kWave) EP_DISPATCH_FP8_LAUNCH(1);
+    else if (V <= 2 * kWave) EP_DISPATCH_FP8_LAUNCH(2);
+    else if (V <= 4 * kWave) EP_DISPATCH_FP8_LAUNCH(4);
+    else if (V <= 7 * kWave) EP_DISPATCH_FP8_LAUNCH(7);
+    else EP_DISPATCH_FP8_LAUNCH(14);
+#undef EP_DISPATCH_FP8_LAUNCH
     return hipGetLastError();
 }
 

@@ -101,6 +101,34 @@ int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weight
                                           static_cast<hipStream_t>(stream)));
 }
 
+int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                    int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                    int num_ranks, const int32_t* token_slot, uint8_t* recv_x_fp8,
+                    float* recv_scales, int64_t* recv_topk_idx, float* recv_topk_weights,
+                    int32_t* recv_src_idx, int64_t recv_capacity, int32_t* error_flag,
+                    void* stream) {
+    const int64_t T = num_tokens;
+    const int H = hidden, k = num_topk, E = num_experts, R = num_ranks;
+    if (!topology_ok(k, E, R, 1) || !slots_fit_int32(T, k, R) || H < 1 || recv_capacity < 0)
+        return EP_ERR_ARG;
+    if (H % 128 != 0) return EP_ERR_ALIGN;
+    if (static_cast<int64_t>(H) / 8 * 64 > INT32_MAX) return EP_ERR_ARG;
+    if (T > 0) {
+        if (!x || !token_slot || !recv_x_fp8 || !recv_scales) return EP_ERR_ARG;
+        if ((recv_topk_idx || recv_topk_weights) && !topk_idx) return EP_ERR_ARG;
+        if (recv_topk_weights && !topk_weights) return EP_ERR_ARG;
+    }
+    if (!aligned(x, 16) || !aligned(recv_x_fp8, 16) || !aligned(recv_scales, 4) ||
+        !aligned(topk_idx, 8) || !aligned(topk_weights, 4) || !aligned(token_slot, 4) ||
+        !aligned(recv_topk_idx, 8) || !aligned(recv_topk_weights, 4) ||
+        !aligned(recv_src_idx, 4) || !aligned(error_flag, 4))
+        return EP_ERR_ALIGN;
+    return hip_status(ep::launch_dispatch_fp8(x, topk_idx, topk_weights, T, H, k, E, R,
+                                              token_slot, recv_x_fp8, recv_scales, recv_topk_idx,
+                                              recv_topk_weights, recv_src_idx, recv_capacity,
+                                              error_flag, static_cast<hipStream_t>(stream)));
+}
+
 int ep_restripe_prob(const float* prob, int64_t num_tokens, int num_nodes, int prob_per_token,
                      int64_t max_tokens_per_rank, float* prob_dest_major, void* stream) {
     const int64_t T = num_tokens, Tmax = max_tokens_per_rank;

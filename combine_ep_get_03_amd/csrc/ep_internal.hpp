@@ -43,6 +43,7 @@ struct FastDiv {
 
 // 128-bit word used for every row move.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
@@ -86,6 +87,12 @@ hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* 
                            int64_t T, int H, int k, int E, int R, const int32_t* token_slot,
                            void* recv_x, int64_t* recv_idx, float* recv_w, int32_t* recv_src,
                            int64_t cap, int32_t* error_flag, hipStream_t stream);
+
+hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_w,
+                               int64_t T, int H, int k, int E, int R, const int32_t* token_slot,
+                               void* recv_codes, float* recv_scales, int64_t* recv_idx,
+                               float* recv_w, int32_t* recv_src, int64_t cap, int32_t* error_flag,
+                               hipStream_t stream);
 
 hipError_t launch_restripe(const float* prob, int64_t T, int N, int P, int64_t Tmax, float* out,
                            hipStream_t stream);

@@ -123,6 +123,30 @@ int ep_dispatch(const void *x, const int64_t *topk_idx, const float *topk_weight
                 float *recv_topk_weights, int32_t *recv_src_idx, int64_t recv_capacity,
                 int32_t *error_flag, void *stream);
 
+/* ep_dispatch_fp8 -- ep_dispatch with an FP8 payload: each token is quantised once and
+ * every destination row receives its e4m3 codes and per-128-channel scales ("[PR #347]",
+ * section 3.2.1, and "[PR #453]" measure dispatch with an FP8 payload; their byte counts
+ * fit one fp32 scale per 128 channels, 7168 + 224 bytes per 7168-wide row).
+ *
+ * In:  x            bf16 [T][H], finite values
+ *      topk_idx, topk_weights, token_slot as for ep_dispatch
+ * Out: for each t, r with s = token_slot[t][r] >= 0, and each group g of 128 channels:
+ *      recv_scales     fp32 [cap][H/128]  scale = amax / 448, amax = max |x[t][128g .. 128g+127]|
+ *                                         (1.0 for an all-zero group)
+ *      recv_x_fp8      uint8 [cap][H]     OCP e4m3 (E4M3FN) code of x[t][c] * (448 / amax),
+ *                                         rounded to nearest even, magnitude at most 448
+ *      recv_topk_idx, recv_topk_weights, recv_src_idx as for ep_dispatch (nullable)
+ *      Rows >= M are not written.
+ * Sizes: H % 128 == 0; x and recv_x_fp8 16-byte aligned, recv_scales 4-byte aligned.
+ *   Slots >= recv_capacity are skipped and set EP_DEVERR_RECV_OVERFLOW.
+ * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_HIP. */
+int ep_dispatch_fp8(const void *x, const int64_t *topk_idx, const float *topk_weights,
+                    int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                    int num_ranks, const int32_t *token_slot, uint8_t *recv_x_fp8,
+                    float *recv_scales, int64_t *recv_topk_idx, float *recv_topk_weights,
+                    int32_t *recv_src_idx, int64_t recv_capacity, int32_t *error_flag,
+                    void *stream);
+
 /* ep_restripe_prob -- prob from token-major to destination-major
  * ("[PR #634] Hybrid ep nixl restripe", section "Fix").
  *

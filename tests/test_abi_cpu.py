@@ -106,6 +106,17 @@ def test_dispatch_validation(lib):
     assert _dispatch(lib, H=0) == ep.EP_ERR_ARG
 
 
+def test_dispatch_fp8_validation(lib):
+    f = lib.ep_dispatch_fp8
+    args = lambda H=1024, x=A16, codes=A16, scales=A16: (x, A16, A16, 10, H, 2, 8, 4, A16, codes,
+                                                           scales, A16, A16, A16, 100, A16, None)
+    assert f(*args(H=1000)) == ep.EP_ERR_ALIGN
+    assert f(*args(H=1032)) == ep.EP_ERR_ALIGN
+    assert f(*args(codes=P(0x10008))) == ep.EP_ERR_ALIGN
+    assert f(*args(scales=None)) == ep.EP_ERR_ARG
+    assert f(*args(x=None)) == ep.EP_ERR_ARG
+
+
 def test_restripe_validation(lib):
     f = lib.ep_restripe_prob
     assert f(A16, 10, 2, 4, 9, A16, None) == ep.EP_ERR_CAPACITY
