@@ -213,6 +213,32 @@ def main():
         g.replay()
         avg[n] = timed(g.replay, 1) / args.steps
         del g
+    # FP8 dispatch (same routing, e4m3 payload + per-128-channel scales), when H allows it
+    fp8 = None
+    if cfg.H % 128 == 0:
+        codes = torch.empty((path.cap, cfg.H), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((path.cap, cfg.H // 128), dtype=torch.float32, device="cuda")
+        r = path.recv
+
+        def fp8_call():
+            ep.ep_dispatch_fp8(b.x, b.topk_idx, b.topk_weights, cfg.E, cfg.R,
+                               path.layout_buf.token_slot, recv_x_fp8=codes, recv_scales=scales,
+                               recv_topk_idx=r.recv_topk_idx, recv_topk_weights=r.recv_topk_weights,
+                               recv_src_idx=r.recv_src_idx, error_flag=path.error_flag)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(args.steps):
+                fp8_call()
+        g.replay()
+        fp8_ms = timed(g.replay, 1) / args.steps
+        del g
+        fb = (cfg.T * cfg.H * 2 + cfg.T * cfg.k * 12 + cfg.T * cfg.R * 4 +
+              M * (cfg.H + 4 * (cfg.H // 128) + 12 * cfg.k + 4))
+        fp8 = {"avg_us": round(fp8_ms * 1e3, 2), "alg_bytes": fb,
+               "hbm_gbps": round(fb / (fp8_ms * 1e-3) / 1e9, 1),
+               "algorithm_gbps": round(M * (cfg.H + 4 * (cfg.H // 128)) / (fp8_ms * 1e-3) / 1e9, 1),
+               "tokens_per_s": round(cfg.T / (fp8_ms * 1e-3), 1)}
+        del codes, scales
     if int(path.error_flag.item()) != 0:
         raise RuntimeError(f"device error flag {int(path.error_flag.item())}")
 
@@ -259,6 +285,7 @@ def main():
                      "traffic": measured_traffic(dom, cfg.name),
                      "alg_bytes_per_launch": alg[dom], "avg_launch_us": round(avg[dom] * 1e3, 2)},
         "copy_bandwidth_gbps": {k: round(v, 1) for k, v in copy_bw.items()},
+        "dispatch_fp8": fp8,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

@@ -26,6 +26,9 @@ namespace {
 #ifndef EP_DISPATCH_MAX_WPL
 #define EP_DISPATCH_MAX_WPL 14
 #endif
+#ifndef EP_DISPATCH_FP8_MAX_WPL
+#define EP_DISPATCH_FP8_MAX_WPL 14
+#endif
 
 #ifndef EP_DISPATCH_THREADS
 #define EP_DISPATCH_THREADS 512
@@ -271,7 +274,7 @@ hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const flo
     if (V <= kWave) EP_DISPATCH_FP8_LAUNCH(1);
     else if (V <= 2 * kWave) EP_DISPATCH_FP8_LAUNCH(2);
     else if (V <= 4 * kWave) EP_DISPATCH_FP8_LAUNCH(4);
-    else if (V <= 7 * kWave) EP_DISPATCH_FP8_LAUNCH(7);
+    else if (V <= 7 * kWave || EP_DISPATCH_FP8_MAX_WPL < 14) EP_DISPATCH_FP8_LAUNCH(7);
     else EP_DISPATCH_FP8_LAUNCH(14);
 #undef EP_DISPATCH_FP8_LAUNCH
     return hipGetLastError();
