@@ -38,12 +38,15 @@ def lib():
         L.oracle_quantize_fp8.argtypes = [P, i64, i32, P, P]
         L.oracle_dispatch_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i64, P, P, P, P,
                                           P]
+        L.oracle_expert_slots.argtypes = [P, i64, i32, i32, P]
+        L.oracle_dispatch_permute.argtypes = [P, P, P, i64, i32, i32, P, i64, P, P, P]
         L.oracle_f32_to_e4m3_array.argtypes = [P, i64, P]
         L.oracle_f32_to_e4m3_array.restype = None
         L.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_to_f32.restype = ctypes.c_float
         for f in ("oracle_layout", "oracle_dispatch", "oracle_restripe_prob", "oracle_combine",
-                  "oracle_quantize_fp8", "oracle_dispatch_fp8"):
+                  "oracle_quantize_fp8", "oracle_dispatch_fp8", "oracle_expert_slots",
+                  "oracle_dispatch_permute"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -169,4 +172,29 @@ def dispatch_fp8(x, topk_idx, topk_w, E: int, R: int, token_slot, cap: int) -> d
                                    _p(out["recv_idx"]), _p(out["recv_w"]), _p(out["recv_src"]))
     if rc != 0:
         raise ValueError("oracle_dispatch_fp8: bad arguments or slot beyond capacity")
+    return out
+
+
+def expert_slots(topk_idx, E: int) -> np.ndarray:
+    idx = _c(topk_idx, np.int64)
+    T, k = idx.shape
+    out = np.zeros((T, k), np.int32)
+    if lib().oracle_expert_slots(_p(idx), T, k, E, _p(out)) != 0:
+        raise ValueError("oracle_expert_slots: bad arguments")
+    return out
+
+
+def dispatch_permute(x, topk_idx, topk_w, expert_slot, cap: int) -> dict:
+    x = _c(x, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    w = _c(topk_w, np.float32)
+    es = _c(expert_slot, np.int32)
+    T, H = x.shape
+    k = idx.shape[1]
+    out = dict(perm_x=np.zeros((cap, H), np.uint16), perm_w=np.zeros(cap, np.float32),
+               perm_src=np.zeros(cap, np.int32))
+    rc = lib().oracle_dispatch_permute(_p(x), _p(idx), _p(w), T, H, k, _p(es), cap,
+                                       _p(out["perm_x"]), _p(out["perm_w"]), _p(out["perm_src"]))
+    if rc != 0:
+        raise ValueError("oracle_dispatch_permute: bad arguments or row beyond capacity")
     return out

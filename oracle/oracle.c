@@ -38,7 +38,12 @@
  *    bias 7, 3 mantissa bits, largest finite 448, no infinities): amax = largest
  *    |x| in the group, scale = amax / 448, code = e4m3(x * (448 / amax)) rounded to
  *    nearest even with the magnitude saturated at 448; an all-zero group gets scale 1
- *    and zero codes. Every destination row receives the same codes and scales.
+ *    and zero codes. Every destination row receives the same codes and scales;
+ *  - dispatch + permute ("[PR #634]" measures "dispatch+permute"; its commit list
+ *    names the scan over tokens per local expert): every valid (token, slot) pair
+ *    gets its own row, rows grouped by expert id (so each rank's local experts are one
+ *    contiguous range) and ordered by (token, slot) within an expert; a row carries
+ *    the token's hidden row, the slot's weight and the source token.
  */
 #include "oracle.h"
 
@@ -297,6 +302,63 @@ int oracle_dispatch_fp8(const uint16_t *x, const int64_t *topk_idx, const float 
     free(codes);
     free(scales);
     return rc;
+}
+
+/* Expert-major row of every (token, slot): the expert's exclusive offset plus the
+ * number of earlier (token, slot) pairs, in token-then-slot order, naming the same
+ * expert; -1 for masked or out-of-range ids. */
+int oracle_expert_slots(const int64_t *topk_idx, int64_t T, int k, int E, int32_t *expert_slot)
+{
+    if (T < 0 || k < 1 || E < 1)
+        return -1;
+    int32_t *offset = (int32_t *)calloc((size_t)E + 1, sizeof(int32_t));
+    int32_t *filled = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    if (!offset || !filled) {
+        free(offset);
+        free(filled);
+        return -1;
+    }
+    for (int64_t i = 0; i < T * k; ++i)
+        if (topk_idx[i] >= 0 && topk_idx[i] < E)
+            offset[topk_idx[i] + 1] += 1;
+    for (int e = 0; e < E; ++e)
+        offset[e + 1] += offset[e];
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            const int64_t e = topk_idx[t * k + j];
+            if (e < 0 || e >= E) {
+                expert_slot[t * k + j] = -1;
+                continue;
+            }
+            expert_slot[t * k + j] = offset[e] + filled[e];
+            filled[e] += 1;
+        }
+    free(offset);
+    free(filled);
+    return 0;
+}
+
+/* Dispatch + permute: row expert_slot[t][j] = row t of x, with weight w[t][j] and
+ * source token t. */
+int oracle_dispatch_permute(const uint16_t *x, const int64_t *topk_idx, const float *topk_w,
+                            int64_t T, int H, int k, const int32_t *expert_slot, int64_t cap,
+                            uint16_t *perm_x, float *perm_w, int32_t *perm_src)
+{
+    (void)topk_idx;
+    if (T < 0 || H < 1 || k < 1)
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            const int64_t q = expert_slot[t * k + j];
+            if (q < 0)
+                continue;
+            if (q >= cap)
+                return -1;
+            memcpy(perm_x + q * H, x + t * H, (size_t)H * sizeof(uint16_t));
+            perm_w[q] = topk_w[t * k + j];
+            perm_src[q] = (int32_t)t;
+        }
+    return 0;
 }
 
 /* restripe_prob ("[PR #634] Hybrid ep nixl restripe", section "Fix"): slice

@@ -33,6 +33,12 @@ int oracle_dispatch_fp8(const uint16_t *x, const int64_t *topk_idx, const float 
                         int64_t cap, uint8_t *recv_codes, float *recv_scales,
                         int64_t *recv_idx, float *recv_w, int32_t *recv_src);
 
+int oracle_expert_slots(const int64_t *topk_idx, int64_t T, int k, int E, int32_t *expert_slot);
+
+int oracle_dispatch_permute(const uint16_t *x, const int64_t *topk_idx, const float *topk_w,
+                            int64_t T, int H, int k, const int32_t *expert_slot, int64_t cap,
+                            uint16_t *perm_x, float *perm_w, int32_t *perm_src);
+
 uint8_t oracle_f32_to_e4m3(float v);
 float oracle_e4m3_to_f32(uint8_t c);
 void oracle_f32_to_e4m3_array(const float *in, int64_t n, uint8_t *out);

@@ -58,13 +58,17 @@ MUTANTS = [
      "const float inv = amax > 0.0f ? amax / 448.0f : 1.0f;"),
     ("fp8_dispatch_scales_shifted", "memcpy(recv_scales + s * G, scales + t * G, (size_t)G * sizeof(float));",
      "memcpy(recv_scales + s * G, scales + (t > 0 ? t - 1 : 0) * G, (size_t)G * sizeof(float));"),
+    ("expert_slot_unstable", "expert_slot[t * k + j] = offset[e] + filled[e];",
+     "expert_slot[t * k + j] = offset[e] + (offset[e + 1] - offset[e] - 1 - filled[e]);"),
+    ("expert_slot_offset_inclusive", "offset[e + 1] += offset[e];", "offset[e + 1] += offset[e] + (e == 0);"),
+    ("permute_weight_first_slot", "perm_w[q] = topk_w[t * k + j];", "perm_w[q] = topk_w[t * k];"),
     ("combine_truncates_output", "out[t * H + h] = oracle_f32_to_bf16(acc[h]);",
      "{ uint32_t bits; memcpy(&bits, &acc[h], 4); out[t * H + h] = (uint16_t)(bits >> 16); }"),
 ]
 
 # The quick pins (no exhaustive enumeration): enough to kill every mutant above.
 PIN_ARGS = ["tests/test_oracle_layout.py", "tests/test_oracle_dispatch.py",
-            "tests/test_oracle_fp8.py",
+            "tests/test_oracle_fp8.py", "tests/test_oracle_permute.py",
             "tests/test_oracle_restripe.py", "tests/test_oracle_combine.py",
             "tests/test_golden_pages.py", "-x", "-q", "-p", "no:cacheprovider",
             "-k", "not exhaustive"]
