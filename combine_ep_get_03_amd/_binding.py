@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libep.so")
 
 EP_OK, EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_CAPACITY, EP_ERR_HIP = 0, -1, -2, -3, -4
 EP_DEVERR_TOPK_RANGE, EP_DEVERR_RECV_OVERFLOW, EP_DEVERR_SLOT_RANGE = 1, 2, 4
-EP_MAX_RANKS, EP_MAX_EXPERTS = 1024, 8192
+EP_MAX_RANKS, EP_MAX_EXPERTS, EP_EXPERT_SLOT_MAX_K = 1024, 8192, 16
 
 _lib = None
 
@@ -41,15 +41,16 @@ def load() -> ctypes.CDLL:
     L.ep_status_string.restype = ctypes.c_char_p
     L.ep_layout_workspace_bytes.argtypes = [i64, i32, i32, i32]
     L.ep_layout_workspace_bytes.restype = sz
-    L.ep_get_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, sz, P]
+    L.ep_get_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, sz, P]
+    L.ep_dispatch_permute.argtypes = [P, P, i64, i32, i32, P, P, P, P, i64, P, P]
     L.ep_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, i64, P, P]
     L.ep_dispatch_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, i64, P,
                                   P]
     L.ep_restripe_prob.argtypes = [P, i64, i32, i32, i64, P, P]
     L.ep_combine.argtypes = [P, i64, P, i64, i32, i32, P, P, P]
     L.ep_hbm_copy.argtypes = [P, P, sz, P]
-    for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_restripe_prob",
-              "ep_combine", "ep_hbm_copy"):
+    for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
+              "ep_restripe_prob", "ep_combine", "ep_hbm_copy"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -108,7 +109,7 @@ def ep_layout_workspace_bytes(num_tokens: int, num_experts: int, num_ranks: int,
 def ep_get_layout(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
                   num_tokens_per_rank, num_tokens_per_node, num_tokens_per_expert,
                   is_token_in_rank, rank_offset, expert_offset, token_slot, error_flag,
-                  workspace, stream=None) -> None:
+                  workspace, expert_slot=None, stream=None) -> None:
     T, k = topk_idx.shape
     E, R, N = num_experts, num_ranks, num_nodes
     _at_least(num_tokens_per_rank, R, "num_tokens_per_rank")
@@ -118,6 +119,7 @@ def ep_get_layout(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
     _at_least(rank_offset, R + 1, "rank_offset")
     _at_least(expert_offset, E + 1, "expert_offset")
     _shape(token_slot, (T, R), "token_slot")
+    _shape(expert_slot, (T, k), "expert_slot")
     _at_least(error_flag, 1, "error_flag")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().ep_get_layout(
@@ -129,6 +131,7 @@ def ep_get_layout(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
         _ptr(rank_offset, torch.int32, "rank_offset"),
         _ptr(expert_offset, torch.int32, "expert_offset", True),
         _ptr(token_slot, torch.int32, "token_slot"),
+        _ptr(expert_slot, torch.int32, "expert_slot", True),
         _ptr(error_flag, torch.int32, "error_flag"),
         _ptr(workspace, torch.uint8, "workspace", True), ws_bytes, _stream(stream)),
         "ep_get_layout")
@@ -187,6 +190,27 @@ def ep_dispatch_fp8(x, topk_idx, topk_weights, num_experts: int, num_ranks: int,
         _ptr(recv_topk_weights, torch.float32, "recv_topk_weights", True),
         _ptr(recv_src_idx, torch.int32, "recv_src_idx", True), cap,
         _ptr(error_flag, torch.int32, "error_flag", True), _stream(stream)), "ep_dispatch_fp8")
+
+
+def ep_dispatch_permute(x, topk_weights, expert_slot, *, perm_x, perm_weights=None,
+                        perm_src_idx=None, error_flag=None, stream=None) -> None:
+    """x: bf16 [T][H]; expert_slot: int32 [T][k]; perm_x: bf16 [cap][H]."""
+    T, H = x.shape
+    k = expert_slot.shape[1]
+    cap = perm_x.shape[0]
+    _shape(topk_weights, (T, k), "topk_weights")
+    _shape(expert_slot, (T, k), "expert_slot")
+    _shape(perm_x, (cap, H), "perm_x")
+    _shape(perm_weights, (cap,), "perm_weights")
+    _shape(perm_src_idx, (cap,), "perm_src_idx")
+    _at_least(error_flag, 1, "error_flag")
+    _check(load().ep_dispatch_permute(
+        _ptr(x, torch.bfloat16, "x"), _ptr(topk_weights, torch.float32, "topk_weights", True),
+        T, H, k, _ptr(expert_slot, torch.int32, "expert_slot"),
+        _ptr(perm_x, torch.bfloat16, "perm_x"),
+        _ptr(perm_weights, torch.float32, "perm_weights", True),
+        _ptr(perm_src_idx, torch.int32, "perm_src_idx", True), cap,
+        _ptr(error_flag, torch.int32, "error_flag", True), _stream(stream)), "ep_dispatch_permute")
 
 
 def ep_restripe_prob(prob, prob_dest_major, stream=None) -> None:

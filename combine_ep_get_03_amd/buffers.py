@@ -6,6 +6,7 @@ back to the host before dispatch.
 from __future__ import annotations
 
 import dataclasses
+from typing import Optional
 
 import torch
 
@@ -23,16 +24,20 @@ class LayoutBuffers:
     token_slot: torch.Tensor             # int32 [T][R]
     error_flag: torch.Tensor             # int32 [1]
     workspace: torch.Tensor              # uint8 [ep_layout_workspace_bytes]
+    expert_slot: Optional[torch.Tensor] = None  # int32 [T][k], when expert-major rows are wanted
 
     @classmethod
-    def alloc(cls, T: int, E: int, R: int, N: int, device="cuda") -> "LayoutBuffers":
+    def alloc(cls, T: int, E: int, R: int, N: int, device="cuda",
+              k_expert_slots: int = 0) -> "LayoutBuffers":
+        """k_expert_slots > 0 also allocates expert_slot [T][k] (expert-major rows)."""
         i32 = dict(dtype=torch.int32, device=device)
         ws = max(16, B.ep_layout_workspace_bytes(T, E, R, N))
         return cls(torch.empty(R, **i32), torch.empty(N, **i32), torch.empty(E, **i32),
                    torch.empty((T, R), dtype=torch.uint8, device=device),
                    torch.empty(R + 1, **i32), torch.empty(E + 1, **i32),
                    torch.empty((T, R), **i32), torch.zeros(1, **i32),
-                   torch.empty(ws, dtype=torch.uint8, device=device))
+                   torch.empty(ws, dtype=torch.uint8, device=device),
+                   torch.empty((T, k_expert_slots), **i32) if k_expert_slots else None)
 
     def compute(self, topk_idx: torch.Tensor, E: int, R: int, N: int, stream=None) -> None:
         B.ep_get_layout(topk_idx, E, R, N, num_tokens_per_rank=self.num_tokens_per_rank,
@@ -40,7 +45,8 @@ class LayoutBuffers:
                         num_tokens_per_expert=self.num_tokens_per_expert,
                         is_token_in_rank=self.is_token_in_rank, rank_offset=self.rank_offset,
                         expert_offset=self.expert_offset, token_slot=self.token_slot,
-                        error_flag=self.error_flag, workspace=self.workspace, stream=stream)
+                        error_flag=self.error_flag, workspace=self.workspace,
+                        expert_slot=self.expert_slot, stream=stream)
 
 
 @dataclasses.dataclass

@@ -228,6 +228,59 @@ __global__ __launch_bounds__(kDT) void dispatch_fp8_kernel(
     if (errbits) raise_error(error_flag, errbits);
 }
 
+// Dispatch + permute: the token row goes once to each of its (token, slot) rows in the
+// expert-major order (expert_slot from the layout), with the slot's weight and the
+// source token. Same wave-per-token walk as dispatch; the destinations are the k
+// slots, walked with ballot + readlane.
+template <int WPL>
+__global__ __launch_bounds__(kDT) void dispatch_permute_kernel(
+    const u32x4* __restrict__ x, const float* __restrict__ topk_w, int64_t T, int V, int k,
+    const int32_t* __restrict__ expert_slot, u32x4* __restrict__ perm_x,
+    float* __restrict__ perm_w, int32_t* __restrict__ perm_src, int64_t cap,
+    int32_t* __restrict__ error_flag) {
+    const int lane = lane_id();
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
+    if (t >= T) return;
+    const u32x4* xr = x + t * V;
+    int32_t errbits = 0;
+    for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
+        u32x4 v[WPL];
+#pragma unroll
+        for (int i = 0; i < WPL; ++i) {
+            const int vi = v0 + i * kWave + lane;
+            if (vi < V) v[i] = load_stream(xr + vi);
+        }
+        for (int j0 = 0; j0 < k; j0 += kWave) {
+            const int j = j0 + lane;
+            int32_t q = j < k ? expert_slot[t * k + j] : -1;
+            if (q >= cap) {
+                errbits |= kErrRecvOverflow;
+                q = -1;
+            }
+            const float wj = (j < k && topk_w) ? topk_w[t * k + j] : 0.0f;
+            uint64_t m = wave_ballot(q >= 0);
+            while (m) {
+                const int src_lane = __builtin_ctzll(m);
+                m &= m - 1;
+                const int64_t qd = __builtin_amdgcn_readlane(q, src_lane);
+                const float wd =
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), src_lane));
+                u32x4* row = perm_x + qd * V;
+#pragma unroll
+                for (int i = 0; i < WPL; ++i) {
+                    const int vi = v0 + i * kWave + lane;
+                    if (vi < V) store_row_word(row + vi, v[i]);
+                }
+                if (v0 == 0 && lane == 0) {
+                    if (perm_w) perm_w[qd] = wd;
+                    if (perm_src) perm_src[qd] = static_cast<int32_t>(t);
+                }
+            }
+        }
+    }
+    if (errbits) raise_error(error_flag, errbits);
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* topk_w,
@@ -277,6 +330,32 @@ hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const flo
     else if (V <= 7 * kWave || EP_DISPATCH_FP8_MAX_WPL < 14) EP_DISPATCH_FP8_LAUNCH(7);
     else EP_DISPATCH_FP8_LAUNCH(14);
 #undef EP_DISPATCH_FP8_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace ep
+
+namespace ep {
+
+hipError_t launch_dispatch_permute(const void* x, const float* topk_w, int64_t T, int H, int k,
+                                   const int32_t* expert_slot, void* perm_x, float* perm_w,
+                                   int32_t* perm_src, int64_t cap, int32_t* error_flag,
+                                   hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int V = H / 8;
+    const int64_t grid = (T + kDWaves - 1) / kDWaves;
+    if (!grid_fits(grid, kDT)) return hipErrorInvalidConfiguration;
+#define EP_PERMUTE_LAUNCH(WPL)                                                                 \
+    hipLaunchKernelGGL(dispatch_permute_kernel<WPL>, dim3(static_cast<unsigned>(grid)),         \
+                       dim3(kDT), 0, stream, static_cast<const u32x4*>(x), topk_w, T, V, k,     \
+                       expert_slot, static_cast<u32x4*>(perm_x), perm_w, perm_src, cap,         \
+                       error_flag)
+    if (V <= kWave) EP_PERMUTE_LAUNCH(1);
+    else if (V <= 2 * kWave) EP_PERMUTE_LAUNCH(2);
+    else if (V <= 4 * kWave) EP_PERMUTE_LAUNCH(4);
+    else if (V <= 7 * kWave) EP_PERMUTE_LAUNCH(7);
+    else EP_PERMUTE_LAUNCH(14);
+#undef EP_PERMUTE_LAUNCH
     return hipGetLastError();
 }
 

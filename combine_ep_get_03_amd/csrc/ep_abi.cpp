@@ -54,14 +54,15 @@ int ep_get_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int
                   int num_ranks, int num_nodes, int32_t* num_tokens_per_rank,
                   int32_t* num_tokens_per_node, int32_t* num_tokens_per_expert,
                   uint8_t* is_token_in_rank, int32_t* rank_offset, int32_t* expert_offset,
-                  int32_t* token_slot, int32_t* error_flag, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  int32_t* token_slot, int32_t* expert_slot, int32_t* error_flag,
+                  void* workspace, size_t workspace_bytes, void* stream) {
     const int64_t T = num_tokens;
     const int k = num_topk, E = num_experts, R = num_ranks, N = num_nodes;
     if (!topology_ok(k, E, R, N) || !slots_fit_int32(T, k, R)) return EP_ERR_ARG;
     if (!num_tokens_per_rank || !rank_offset || !error_flag) return EP_ERR_ARG;
     if (T > 0 && (!topk_idx || !token_slot)) return EP_ERR_ARG;
-    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) ||
+    if (expert_slot && k > EP_EXPERT_SLOT_MAX_K) return EP_ERR_ARG;
+    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) || !aligned(expert_slot, 4) ||
         !aligned(num_tokens_per_node, 4) || !aligned(num_tokens_per_expert, 4) ||
         !aligned(rank_offset, 4) || !aligned(expert_offset, 4) || !aligned(token_slot, 4) ||
         !aligned(error_flag, 4) || !aligned(workspace, 16))
@@ -72,7 +73,8 @@ int ep_get_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int
     return hip_status(ep::launch_layout(topk_idx, T, k, E, R, N, num_tokens_per_rank,
                                         num_tokens_per_node, num_tokens_per_expert,
                                         is_token_in_rank, rank_offset, expert_offset, token_slot,
-                                        error_flag, ws, static_cast<hipStream_t>(stream)));
+                                        expert_slot, error_flag, ws,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,
@@ -127,6 +129,27 @@ int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_we
                                               token_slot, recv_x_fp8, recv_scales, recv_topk_idx,
                                               recv_topk_weights, recv_src_idx, recv_capacity,
                                               error_flag, static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch_permute(const void* x, const float* topk_weights, int64_t num_tokens, int hidden,
+                        int num_topk, const int32_t* expert_slot, void* perm_x,
+                        float* perm_weights, int32_t* perm_src_idx, int64_t capacity,
+                        int32_t* error_flag, void* stream) {
+    const int64_t T = num_tokens;
+    const int H = hidden, k = num_topk;
+    if (T < 0 || H < 1 || k < 1 || capacity < 0) return EP_ERR_ARG;
+    if (T > 0 && T > static_cast<int64_t>(INT32_MAX) / k) return EP_ERR_ARG;
+    if (H % 8 != 0) return EP_ERR_ALIGN;
+    if (static_cast<int64_t>(H) / 8 * 64 > INT32_MAX) return EP_ERR_ARG;
+    if (T > 0 && (!x || !expert_slot || !perm_x)) return EP_ERR_ARG;
+    if (T > 0 && perm_weights && !topk_weights) return EP_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(perm_x, 16) || !aligned(topk_weights, 4) ||
+        !aligned(expert_slot, 4) || !aligned(perm_weights, 4) || !aligned(perm_src_idx, 4) ||
+        !aligned(error_flag, 4))
+        return EP_ERR_ALIGN;
+    return hip_status(ep::launch_dispatch_permute(x, topk_weights, T, H, k, expert_slot, perm_x,
+                                                  perm_weights, perm_src_idx, capacity,
+                                                  error_flag, static_cast<hipStream_t>(stream)));
 }
 
 int ep_restripe_prob(const float* prob, int64_t num_tokens, int num_nodes, int prob_per_token,

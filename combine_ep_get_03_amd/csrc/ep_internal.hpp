@@ -69,7 +69,8 @@ constexpr int32_t kErrSlotRange = 4;
 struct LayoutWorkspace {
     int32_t* blk_rank;   // [nb][R]  per-block rank counts, then per-block exclusive prefix
     int32_t* blk_node;   // [nb][N]
-    int32_t* blk_exp;    // [nb][E]
+    int32_t* blk_exp;    // [nb][E]  per-block inclusive prefix of the expert histogram
+    int32_t* blk_exp_base;  // [nb][E]  first expert-major row of each block, per expert
     int32_t* blk_err;    // [nb]
 };
 
@@ -81,7 +82,10 @@ LayoutWorkspace carve_layout_workspace(void* base, int64_t T, int E, int R, int 
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
                          int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                          int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
-                         int32_t* error_flag, const LayoutWorkspace& ws, hipStream_t stream);
+                         int32_t* expert_slot, int32_t* error_flag, const LayoutWorkspace& ws,
+                         hipStream_t stream);
+
+constexpr int kExpertSlotMaxK = 16;  // top-k limit of the expert-major slot output
 
 hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* topk_w,
                            int64_t T, int H, int k, int E, int R, const int32_t* token_slot,
@@ -93,6 +97,11 @@ hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const flo
                                void* recv_codes, float* recv_scales, int64_t* recv_idx,
                                float* recv_w, int32_t* recv_src, int64_t cap, int32_t* error_flag,
                                hipStream_t stream);
+
+hipError_t launch_dispatch_permute(const void* x, const float* topk_w, int64_t T, int H, int k,
+                                   const int32_t* expert_slot, void* perm_x, float* perm_w,
+                                   int32_t* perm_src, int64_t cap, int32_t* error_flag,
+                                   hipStream_t stream);
 
 hipError_t launch_restripe(const float* prob, int64_t T, int N, int P, int64_t Tmax, float* out,
                            hipStream_t stream);

@@ -36,6 +36,8 @@ constexpr int kFusedMaxBlocks = 64;
 constexpr int kFusedMaxCells = 4096;
 constexpr int kFusedMaxRanks = kBT;
 constexpr int kBatch = 8;                // loads in flight per lane for table reads
+// Largest [nb][ncol] expert slice of one fused slot block: ncol <= E / (4 nb) + 2.
+constexpr int kFusedMaxSlice = kMaxExperts / 4 + 2 * 64;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -327,11 +329,13 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
     LayoutWorkspace ws, int32_t* __restrict__ count_r, int32_t* __restrict__ count_n,
     int32_t* __restrict__ count_e, int32_t* __restrict__ rank_offset,
     int32_t* __restrict__ expert_offset, int32_t* __restrict__ error_flag,
-    int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank, int vec_out) {
+    int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank, int vec_out,
+    int want_expert_base) {
     __shared__ int32_t s_cnt[kFusedMaxCells];               // [nb][R] per-group rank counts
     __shared__ uint64_t s_ball[kWavesBT * kFusedMaxRanks];  // [4][R] the group's ballots
     __shared__ int32_t s_base[kFusedMaxRanks];              // slot base of this quarter, per rank
-    __shared__ int32_t s_col[kMaxExperts + 1];              // this block's expert columns
+    __shared__ int32_t s_tab[kFusedMaxSlice];               // [nb][ncol] expert slice
+    __shared__ int32_t s_col[kMaxExperts / kQuarters + 2];  // column sums of the slice
     __shared__ int32_t s_node[kFusedMaxRanks];              // N <= R
     __shared__ int32_t s_scan[17];
     const int tid = threadIdx.x;
@@ -342,13 +346,12 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
     const int nblk = gridDim.x;
     const int64_t t0 = static_cast<int64_t>(grp) * kBT;
     const int64_t t = t0 + tid;
-    // expert columns [c0, c1) belong to this block; s_col[c] sums column c0 - 1 + c
+    // expert columns [c0, c1) belong to this block; slice column c is expert c0 - 1 + c
     const int cw = (E + nblk - 1) / nblk;
     const int c0 = min(E, g * cw);
     const int c1 = min(E, c0 + cw);
     const int ncol = c1 - c0 + 1;
 
-    for (int i = tid; i < ncol; i += kBT) s_col[i] = 0;
     if (g == 0)
         for (int i = tid; i < N; i += kBT) s_node[i] = 0;
     __syncthreads();
@@ -372,13 +375,22 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
         const int i = tid + u * kBT;
         if (i < ncell) s_cnt[i] = cell[u];
     }
-    accumulate_columns(
-        nb * ncol,
-        [&](int i) {
+    // the expert slice [nb][ncol] of the per-block inclusive prefixes, kBatch loads in flight
+    const int nslice = nb * ncol;
+    for (int i0 = tid; i0 < nslice; i0 += kBT * kBatch) {
+        int v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = i0 + u * kBT;
             const int e = c0 - 1 + i % ncol;
-            return e >= 0 ? ws.blk_exp[static_cast<int64_t>(i / ncol) * E + e] : 0;
-        },
-        [&](int i) { return i % ncol; }, s_col);
+            v[u] = (i < nslice && e >= 0) ? ws.blk_exp[static_cast<int64_t>(i / ncol) * E + e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = i0 + u * kBT;
+            if (i < nslice) s_tab[i] = v[u];
+        }
+    }
     int any_bad = 0;
     if (g == 0) {
         accumulate_columns(
@@ -409,10 +421,26 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
         }
     }
     if (g == 0 && tid == 0) rank_offset[R] = M;
+    // column sums of the inclusive prefixes: expert_offset[e + 1] for e = c0 - 1 + c
+    for (int c = tid; c < ncol; c += kBT) {
+        int sum = 0;
+        for (int bb = 0; bb < nb; ++bb) sum += s_tab[bb * ncol + c];
+        s_col[c] = sum;
+    }
+    __syncthreads();
     for (int c = tid + 1; c < ncol; c += kBT) {
         const int e = c0 - 1 + c;
         if (count_e) count_e[e] = s_col[c] - s_col[c - 1];
         if (expert_offset) expert_offset[e + 1] = s_col[c];
+        if (want_expert_base) {
+            // first expert-major row of expert e in each block: offset[e] plus the
+            // pairs naming e in earlier blocks (histogram = difference of prefixes)
+            int run = s_col[c - 1];
+            for (int bb = 0; bb < nb; ++bb) {
+                ws.blk_exp_base[static_cast<int64_t>(bb) * E + e] = run;
+                run += s_tab[bb * ncol + c] - s_tab[bb * ncol + c - 1];
+            }
+        }
     }
     if (g == 0) {
         if (expert_offset && tid == 0) expert_offset[0] = 0;
@@ -472,7 +500,7 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
     int nb, int E, int R, int N, LayoutWorkspace ws, int32_t* __restrict__ count_r,
     int32_t* __restrict__ count_n, int32_t* __restrict__ count_e,
     int32_t* __restrict__ rank_offset, int32_t* __restrict__ expert_offset,
-    int32_t* __restrict__ error_flag) {
+    int32_t* __restrict__ error_flag, int want_expert_base) {
     __shared__ int32_t s_tile[kTileInts];
     __shared__ int32_t s_last[kScanThreads];
     __shared__ int32_t s_scan[17];
@@ -508,6 +536,22 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
         __syncthreads();
     }
     if (expert_offset && tid == 0) expert_offset[0] = 0;
+
+    if (want_expert_base) {
+        // first expert-major row of expert e in each block: offset[e] plus the pairs
+        // naming e in earlier blocks; one column per thread, rows in order
+        for (int e = tid; e < E; e += blockDim.x) {
+            int off = 0;
+            for (int bb = 0; bb < nb; ++bb)
+                off += e > 0 ? ws.blk_exp[static_cast<int64_t>(bb) * E + e - 1] : 0;
+            int run = off;
+            for (int bb = 0; bb < nb; ++bb) {
+                ws.blk_exp_base[static_cast<int64_t>(bb) * E + e] = run;
+                const int64_t row = static_cast<int64_t>(bb) * E;
+                run += ws.blk_exp[row + e] - (e > 0 ? ws.blk_exp[row + e - 1] : 0);
+            }
+        }
+    }
 
     int bad = 0;
     for (int i = tid; i < nb; i += blockDim.x) bad |= ws.blk_err[i];
@@ -550,11 +594,88 @@ __global__ __launch_bounds__(kBT) void layout_slot_kernel(
     write_block_slots(s_ball, s_base, T, t0, R, token_slot, in_rank);
 }
 
+// Expert-major row of every (token, slot) of one 256-token block: the block's base for
+// the expert (from the slot launch) plus the number of earlier pairs of the block naming
+// the same expert, in (token, slot) order. Equal experts are found without sorting:
+// per wave and slot, one ballot per expert-id bit (and one of validity) is parked in
+// LDS; a lane matches its expert against another lane's by combining those ballots.
+__global__ __launch_bounds__(kBT) void layout_expert_slot_kernel(
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int nbits,
+    const int32_t* __restrict__ blk_exp_base, int32_t* __restrict__ expert_slot) {
+    constexpr int kK = kExpertSlotMaxK;
+    constexpr int kBits = 14;  // 1 validity + up to 13 id bits (E <= 8192)
+    __shared__ uint64_t s_key[kWavesBT][kK][kBits];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+    const int64_t b = blockIdx.x;
+    const int64_t t = b * kBT + tid;
+
+    int key[kK];
+#pragma unroll
+    for (int j = 0; j < kK; ++j) {
+        int64_t e = -1;
+        if (j < k && t < T) e = topk_idx[t * k + j];
+        key[j] = (e >= 0 && e < E) ? static_cast<int>(e) : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kK; ++j) {
+        if (j < k) {
+            const uint64_t valid = wave_ballot(key[j] >= 0);
+            if (lane == 0) s_key[wave][j][0] = valid;
+            for (int bit = 0; bit < nbits; ++bit) {
+                const uint64_t m = wave_ballot(key[j] >= 0 && ((key[j] >> bit) & 1));
+                if (lane == 0) s_key[wave][j][1 + bit] = m;
+            }
+        }
+    }
+    __syncthreads();
+
+    const uint64_t below = (1ull << lane) - 1ull;
+    int rank[kK];
+#pragma unroll
+    for (int j = 0; j < kK; ++j) rank[j] = 0;
+    for (int w = 0; w <= wave; ++w) {
+        const uint64_t lane_mask = w < wave ? ~0ull : below;
+        for (int j2 = 0; j2 < k; ++j2) {
+            uint64_t bits[kBits];
+#pragma unroll
+            for (int i = 0; i < kBits; ++i) bits[i] = i <= nbits ? s_key[w][j2][i] : 0ull;
+            bits[0] &= lane_mask;
+#pragma unroll
+            for (int j = 0; j < kK; ++j) {
+                if (j < k && key[j] >= 0) {
+                    uint64_t peers = bits[0];
+#pragma unroll
+                    for (int bit = 0; bit < kBits - 1; ++bit)
+                        if (bit < nbits)
+                            peers &= ((key[j] >> bit) & 1) ? bits[1 + bit] : ~bits[1 + bit];
+                    rank[j] += __popcll(peers);
+                }
+            }
+        }
+    }
+    if (t >= T) return;
+#pragma unroll
+    for (int j = 0; j < kK; ++j) {
+        if (j < k) {
+            int same = 0;
+#pragma unroll
+            for (int j2 = 0; j2 < kK; ++j2)
+                if (j2 < j && key[j2] == key[j]) ++same;
+            expert_slot[t * k + j] =
+                key[j] >= 0 ? blk_exp_base[b * E + key[j]] + rank[j] + same : -1;
+        }
+    }
+}
+
 template <int NW>
 hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
                        int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                        int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
-                       int32_t* error_flag, const LayoutWorkspace& ws, hipStream_t stream) {
+                       int32_t* expert_slot, int32_t* error_flag, const LayoutWorkspace& ws,
+                       hipStream_t stream) {
+    const int want_base = expert_slot != nullptr ? 1 : 0;
     const int64_t nb = (T + kBT - 1) / kBT;
     const FastDiv er = FastDiv::make(E / R);
     const FastDiv rpn = FastDiv::make(R / N);
@@ -572,17 +693,24 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
                            dim3(static_cast<unsigned>(nb * kQuarters)), dim3(kBT), 0, stream,
                            topk_idx, T, k, E, R, N, er, static_cast<int>(nb), ws, count_r,
                            count_n, count_e, rank_offset, expert_offset, error_flag, token_slot,
-                           in_rank, vec ? 1 : 0);
-        return hipGetLastError();
+                           in_rank, vec ? 1 : 0, want_base);
+    } else {
+        hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
+                           static_cast<int>(nb), E, R, N, ws, count_r, count_n, count_e,
+                           rank_offset, expert_offset, error_flag, want_base);
+        if (nb > 0) {
+            const size_t shm =
+                static_cast<size_t>(kWavesBT) * R * (sizeof(uint64_t) + sizeof(int32_t));
+            hipLaunchKernelGGL(layout_slot_kernel<NW>, dim3(static_cast<unsigned>(nb)), dim3(kBT),
+                               shm, stream, topk_idx, T, k, E, R, er, ws.blk_rank, rank_offset,
+                               token_slot, in_rank);
+        }
     }
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
-                       static_cast<int>(nb), E, R, N, ws, count_r, count_n, count_e, rank_offset,
-                       expert_offset, error_flag);
-    if (nb > 0) {
-        const size_t shm = static_cast<size_t>(kWavesBT) * R * (sizeof(uint64_t) + sizeof(int32_t));
-        hipLaunchKernelGGL(layout_slot_kernel<NW>, dim3(static_cast<unsigned>(nb)), dim3(kBT), shm,
-                           stream, topk_idx, T, k, E, R, er, ws.blk_rank, rank_offset, token_slot,
-                           in_rank);
+    if (want_base && nb > 0) {
+        int nbits = 0;
+        while ((1 << nbits) < E) ++nbits;
+        hipLaunchKernelGGL(layout_expert_slot_kernel, dim3(static_cast<unsigned>(nb)), dim3(kBT),
+                           0, stream, topk_idx, T, k, E, nbits, ws.blk_exp_base, expert_slot);
     }
     return hipGetLastError();
 }
@@ -591,7 +719,7 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
 
 size_t layout_workspace_bytes(int64_t T, int E, int R, int N) {
     const size_t nb = static_cast<size_t>((T + kBT - 1) / kBT);
-    return align_up(nb * R * 4, 256) + align_up(nb * N * 4, 256) + align_up(nb * E * 4, 256) +
+    return align_up(nb * R * 4, 256) + align_up(nb * N * 4, 256) + 2 * align_up(nb * E * 4, 256) +
            align_up(nb * 4, 256);
 }
 
@@ -605,6 +733,8 @@ LayoutWorkspace carve_layout_workspace(void* base, int64_t T, int E, int R, int 
     p += align_up(nb * N * 4, 256);
     ws.blk_exp = reinterpret_cast<int32_t*>(p);
     p += align_up(nb * E * 4, 256);
+    ws.blk_exp_base = reinterpret_cast<int32_t*>(p);
+    p += align_up(nb * E * 4, 256);
     ws.blk_err = reinterpret_cast<int32_t*>(p);
     return ws;
 }
@@ -612,10 +742,12 @@ LayoutWorkspace carve_layout_workspace(void* base, int64_t T, int E, int R, int 
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
                          int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                          int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
-                         int32_t* error_flag, const LayoutWorkspace& ws, hipStream_t stream) {
+                         int32_t* expert_slot, int32_t* error_flag, const LayoutWorkspace& ws,
+                         hipStream_t stream) {
 #define EP_LAYOUT_CASE(NW)                                                                     \
     return layout_impl<NW>(topk_idx, T, k, E, R, N, count_r, count_n, count_e, in_rank,        \
-                           rank_offset, expert_offset, token_slot, error_flag, ws, stream)
+                           rank_offset, expert_offset, token_slot, expert_slot, error_flag, ws, \
+                           stream)
     if (R <= 64) EP_LAYOUT_CASE(1);
     if (R <= 128) EP_LAYOUT_CASE(2);
     if (R <= 256) EP_LAYOUT_CASE(4);

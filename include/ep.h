@@ -57,6 +57,7 @@ enum {
 /* Limits of this implementation. */
 #define EP_MAX_RANKS   1024
 #define EP_MAX_EXPERTS 8192
+#define EP_EXPERT_SLOT_MAX_K 16  /* largest top-k for which ep_get_layout fills expert_slot */
 
 /* Static string for a status code; never NULL. */
 const char *ep_status_string(int status);
@@ -82,6 +83,11 @@ size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_experts, int num_ra
  *   token_slot             [T][R] receive row of (t, r) = rank_offset[r] + number of tokens
  *                                 t' < t on rank r; -1 where t is not on r. The rows of rank
  *                                 r are rank_offset[r] .. rank_offset[r+1]-1, in token order.
+ *   expert_slot            [T][k] expert-major row of (t, j) for ep_dispatch_permute:
+ *                                 expert_offset[e] + the number of earlier pairs, in
+ *                                 (token, slot) order, naming the same expert e; -1 for a
+ *                                 masked or bad id. Rank r's experts are one contiguous range
+ *                                 of rows. Needs k <= EP_EXPERT_SLOT_MAX_K.       (nullable)
  *   error_flag             [1]    overwritten: 0, or EP_DEVERR_TOPK_RANGE when an entry is
  *                                 < -1 or >= E (such entries are skipped like -1).
  * Workspace: `workspace` of `workspace_bytes` >= ep_layout_workspace_bytes(T, E, R, N) bytes,
@@ -96,7 +102,8 @@ int ep_get_layout(const int64_t *topk_idx, int64_t num_tokens, int num_topk,
                   int32_t *num_tokens_per_rank, int32_t *num_tokens_per_node,
                   int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
                   int32_t *rank_offset, int32_t *expert_offset, int32_t *token_slot,
-                  int32_t *error_flag, void *workspace, size_t workspace_bytes, void *stream);
+                  int32_t *expert_slot, int32_t *error_flag, void *workspace,
+                  size_t workspace_bytes, void *stream);
 
 /* ep_dispatch -- pack every (token, rank) pair into its receive row.
  *
@@ -146,6 +153,26 @@ int ep_dispatch_fp8(const void *x, const int64_t *topk_idx, const float *topk_we
                     float *recv_scales, int64_t *recv_topk_idx, float *recv_topk_weights,
                     int32_t *recv_src_idx, int64_t recv_capacity, int32_t *error_flag,
                     void *stream);
+
+/* ep_dispatch_permute -- dispatch straight into expert-major rows ("[PR #634] Hybrid ep nixl
+ * restripe" measures "dispatch+permute"; its commit list names the scan over tokens per
+ * local expert that orders them): the rows a grouped expert GEMM consumes.
+ *
+ * In:  x            bf16 [T][H]
+ *      topk_weights fp32 [T][k] (may be NULL when perm_weights is NULL)
+ *      expert_slot  int32 [T][k] from ep_get_layout
+ * Out: for each t, j with q = expert_slot[t][j] >= 0:
+ *      perm_x       bf16 [cap][H]  row q = row t of x
+ *      perm_weights fp32 [cap]     topk_weights[t][j]                              (nullable)
+ *      perm_src_idx int32 [cap]    t                                               (nullable)
+ *      Rows of expert e are expert_offset[e] .. expert_offset[e+1]-1, tokens ascending.
+ * Sizes: H % 8 == 0; x and perm_x 16-byte aligned; a row >= capacity is skipped and sets
+ *   EP_DEVERR_RECV_OVERFLOW (capacity T * k never overflows).
+ * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_HIP. */
+int ep_dispatch_permute(const void *x, const float *topk_weights, int64_t num_tokens, int hidden,
+                        int num_topk, const int32_t *expert_slot, void *perm_x,
+                        float *perm_weights, int32_t *perm_src_idx, int64_t capacity,
+                        int32_t *error_flag, void *stream);
 
 /* ep_restripe_prob -- prob from token-major to destination-major
  * ("[PR #634] Hybrid ep nixl restripe", section "Fix").

@@ -66,9 +66,10 @@ def test_workspace_query(lib):
     assert ep.ep_layout_workspace_bytes(10, 2048, 2048, 1) == 0  # R > EP_MAX_RANKS
 
 
-def _layout(lib, T=100, k=4, E=16, R=4, N=2, idx=A16, ws=A16, wsb=1 << 20, slot=A16):
-    return lib.ep_get_layout(idx, T, k, E, R, N, A16, A16, A16, A16, A16, A16, slot, A16, ws,
-                             wsb, None)
+def _layout(lib, T=100, k=4, E=16, R=4, N=2, idx=A16, ws=A16, wsb=1 << 20, slot=A16,
+            eslot=None):
+    return lib.ep_get_layout(idx, T, k, E, R, N, A16, A16, A16, A16, A16, A16, slot, eslot, A16,
+                             ws, wsb, None)
 
 
 def test_layout_validation(lib):
@@ -86,6 +87,17 @@ def test_layout_validation(lib):
     assert _layout(lib, ws=P(0x10004)) == ep.EP_ERR_ALIGN
     assert _layout(lib, wsb=16) == ep.EP_ERR_CAPACITY
     assert _layout(lib, ws=None) == ep.EP_ERR_CAPACITY
+    assert _layout(lib, k=17, E=32, eslot=A16) == ep.EP_ERR_ARG   # expert slots need k <= 16
+    assert _layout(lib, eslot=P(0x10002)) == ep.EP_ERR_ALIGN
+
+
+def test_dispatch_permute_validation(lib):
+    f = lib.ep_dispatch_permute
+    assert f(A16, A16, 10, 60, 2, A16, A16, A16, A16, 20, A16, None) == ep.EP_ERR_ALIGN
+    assert f(MIS, A16, 10, 64, 2, A16, A16, A16, A16, 20, A16, None) == ep.EP_ERR_ALIGN
+    assert f(A16, A16, 10, 64, 2, None, A16, A16, A16, 20, A16, None) == ep.EP_ERR_ARG
+    assert f(A16, None, 10, 64, 2, A16, A16, A16, A16, 20, A16, None) == ep.EP_ERR_ARG
+    assert f(A16, A16, 10, 64, 0, A16, A16, A16, A16, 20, A16, None) == ep.EP_ERR_ARG
 
 
 def _dispatch(lib, T=10, H=64, k=2, E=8, R=4, x=A16, cap=100, recv_x=A16, slot=A16,
