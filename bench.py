@@ -239,6 +239,41 @@ def main():
                "algorithm_gbps": round(M * (cfg.H + 4 * (cfg.H // 128)) / (fp8_ms * 1e-3) / 1e9, 1),
                "tokens_per_s": round(cfg.T / (fp8_ms * 1e-3), 1)}
         del codes, scales
+    # Dispatch + permute: layout with expert-major slots, then the rows straight into
+    # expert-major order (k rows per token)
+    permute = None
+    if cfg.k <= ep.EP_EXPERT_SLOT_MAX_K:
+        from combine_ep_get_03_amd.buffers import LayoutBuffers
+
+        lbe = LayoutBuffers.alloc(cfg.T, cfg.E, cfg.R, cfg.N, k_expert_slots=cfg.k)
+        px = torch.empty((cfg.T * cfg.k, cfg.H), dtype=torch.bfloat16, device="cuda")
+        pw = torch.empty(cfg.T * cfg.k, dtype=torch.float32, device="cuda")
+        ps = torch.empty(cfg.T * cfg.k, dtype=torch.int32, device="cuda")
+
+        def layout_e():
+            lbe.compute(b.topk_idx, cfg.E, cfg.R, cfg.N)
+
+        def permute_call():
+            ep.ep_dispatch_permute(b.x, b.topk_weights, lbe.expert_slot, perm_x=px,
+                                   perm_weights=pw, perm_src_idx=ps, error_flag=lbe.error_flag)
+        res = {}
+        for n, fn in (("layout_with_expert_slots", layout_e), ("dispatch_permute", permute_call)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(args.steps):
+                    fn()
+            g.replay()
+            res[n] = timed(g.replay, 1) / args.steps
+            del g
+        if int(lbe.error_flag.item()) != 0:
+            raise RuntimeError("device error flag in dispatch+permute")
+        rows = cfg.T * cfg.k
+        pb = cfg.T * cfg.H * 2 + rows * (4 + 4) + rows * (2 * cfg.H + 8)
+        permute = {"layout_with_expert_slots_us": round(res["layout_with_expert_slots"] * 1e3, 2),
+                   "dispatch_permute_us": round(res["dispatch_permute"] * 1e3, 2),
+                   "alg_bytes": pb,
+                   "hbm_gbps": round(pb / (res["dispatch_permute"] * 1e-3) / 1e9, 1)}
+        del px, pw, ps, lbe
     if int(path.error_flag.item()) != 0:
         raise RuntimeError(f"device error flag {int(path.error_flag.item())}")
 
@@ -286,6 +321,7 @@ def main():
                      "alg_bytes_per_launch": alg[dom], "avg_launch_us": round(avg[dom] * 1e3, 2)},
         "copy_bandwidth_gbps": {k: round(v, 1) for k, v in copy_bw.items()},
         "dispatch_fp8": fp8,
+        "dispatch_permute": permute,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

@@ -39,6 +39,8 @@ def lib():
         L.oracle_dispatch_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i64, P, P, P, P,
                                           P]
         L.oracle_expert_slots.argtypes = [P, i64, i32, i32, P]
+        L.oracle_node_slots.argtypes = [P, i64, i32, i32, i32, i32, P]
+        L.oracle_restripe_prob_sparse.argtypes = [P, i64, i32, i32, P, i64, P]
         L.oracle_dispatch_permute.argtypes = [P, P, P, i64, i32, i32, P, i64, P, P, P]
         L.oracle_f32_to_e4m3_array.argtypes = [P, i64, P]
         L.oracle_f32_to_e4m3_array.restype = None
@@ -46,7 +48,8 @@ def lib():
         L.oracle_e4m3_to_f32.restype = ctypes.c_float
         for f in ("oracle_layout", "oracle_dispatch", "oracle_restripe_prob", "oracle_combine",
                   "oracle_quantize_fp8", "oracle_dispatch_fp8", "oracle_expert_slots",
-                  "oracle_dispatch_permute"):
+                  "oracle_dispatch_permute", "oracle_node_slots",
+                  "oracle_restripe_prob_sparse"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -197,4 +200,25 @@ def dispatch_permute(x, topk_idx, topk_w, expert_slot, cap: int) -> dict:
                                        _p(out["perm_x"]), _p(out["perm_w"]), _p(out["perm_src"]))
     if rc != 0:
         raise ValueError("oracle_dispatch_permute: bad arguments or row beyond capacity")
+    return out
+
+
+def node_slots(topk_idx, E: int, R: int, N: int) -> np.ndarray:
+    idx = _c(topk_idx, np.int64)
+    T, k = idx.shape
+    out = np.zeros((T, N), np.int32)
+    if lib().oracle_node_slots(_p(idx), T, k, E, R, N, _p(out)) != 0:
+        raise ValueError("oracle_node_slots: bad arguments")
+    return out
+
+
+def restripe_prob_sparse(prob, node_slot, Tmax: int, out=None) -> np.ndarray:
+    pw = np.ascontiguousarray(prob).view(np.uint32)
+    T, N, P = pw.shape
+    ns = _c(node_slot, np.int32)
+    if out is None:
+        out = np.zeros((N, Tmax, P), np.float32)
+    rc = lib().oracle_restripe_prob_sparse(_p(pw), T, N, P, _p(ns), Tmax, _p(out.view(np.uint32)))
+    if rc != 0:
+        raise ValueError("oracle_restripe_prob_sparse: bad arguments")
     return out

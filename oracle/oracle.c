@@ -43,7 +43,11 @@
  *    names the scan over tokens per local expert): every valid (token, slot) pair
  *    gets its own row, rows grouped by expert id (so each rank's local experts are one
  *    contiguous range) and ordered by (token, slot) within an expert; a row carries
- *    the token's hidden row, the slot's weight and the source token.
+ *    the token's hidden row, the slot's weight and the source token;
+ *  - sparse restripe ("[PR #634]", section "Fix": one put per run in the sparse
+ *    path): only the (token, node) slices of tokens with a destination on the node are
+ *    moved, packed at the start of the node's block in token order, so the slices of
+ *    any run of consecutive tokens routed to a node are contiguous.
  */
 #include "oracle.h"
 
@@ -302,6 +306,55 @@ int oracle_dispatch_fp8(const uint16_t *x, const int64_t *topk_idx, const float 
     free(codes);
     free(scales);
     return rc;
+}
+
+/* Packed row of (t, n) in node n's block: the number of earlier tokens with a
+ * destination rank on node n; -1 when t has none there. */
+int oracle_node_slots(const int64_t *topk_idx, int64_t T, int k, int E, int R, int N,
+                      int32_t *node_slot)
+{
+    if (T < 0 || k < 1 || E < 1 || R < 1 || N < 1 || E % R != 0 || R % N != 0)
+        return -1;
+    const int experts_per_node = E / N;
+    int32_t *filled = (int32_t *)calloc((size_t)N, sizeof(int32_t));
+    uint8_t *on = (uint8_t *)malloc((size_t)N);
+    if (!filled || !on) {
+        free(filled);
+        free(on);
+        return -1;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        memset(on, 0, (size_t)N);
+        for (int j = 0; j < k; ++j) {
+            const int64_t e = topk_idx[t * k + j];
+            if (e >= 0 && e < E)
+                on[e / experts_per_node] = 1;
+        }
+        for (int n = 0; n < N; ++n)
+            node_slot[t * N + n] = on[n] ? filled[n]++ : -1;
+    }
+    free(filled);
+    free(on);
+    return 0;
+}
+
+/* Sparse restripe: out[n][node_slot[t][n]][p] = prob[t][n][p] for routed (t, n). */
+int oracle_restripe_prob_sparse(const uint32_t *prob, int64_t T, int N, int P,
+                                const int32_t *node_slot, int64_t Tmax, uint32_t *out)
+{
+    if (T < 0 || N < 1 || P < 1 || Tmax < T)
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int n = 0; n < N; ++n) {
+            const int64_t s = node_slot[t * N + n];
+            if (s < 0)
+                continue;
+            if (s >= Tmax)
+                return -1;
+            for (int p = 0; p < P; ++p)
+                out[((int64_t)n * Tmax + s) * P + p] = prob[(t * N + n) * P + p];
+        }
+    return 0;
 }
 
 /* Expert-major row of every (token, slot): the expert's exclusive offset plus the

@@ -33,6 +33,12 @@ int oracle_dispatch_fp8(const uint16_t *x, const int64_t *topk_idx, const float 
                         int64_t cap, uint8_t *recv_codes, float *recv_scales,
                         int64_t *recv_idx, float *recv_w, int32_t *recv_src);
 
+int oracle_node_slots(const int64_t *topk_idx, int64_t T, int k, int E, int R, int N,
+                      int32_t *node_slot);
+
+int oracle_restripe_prob_sparse(const uint32_t *prob, int64_t T, int N, int P,
+                                const int32_t *node_slot, int64_t Tmax, uint32_t *out);
+
 int oracle_expert_slots(const int64_t *topk_idx, int64_t T, int k, int E, int32_t *expert_slot);
 
 int oracle_dispatch_permute(const uint16_t *x, const int64_t *topk_idx, const float *topk_w,

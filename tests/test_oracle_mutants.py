@@ -62,6 +62,9 @@ MUTANTS = [
      "expert_slot[t * k + j] = offset[e] + (offset[e + 1] - offset[e] - 1 - filled[e]);"),
     ("expert_slot_offset_inclusive", "offset[e + 1] += offset[e];", "offset[e + 1] += offset[e] + (e == 0);"),
     ("permute_weight_first_slot", "perm_w[q] = topk_w[t * k + j];", "perm_w[q] = topk_w[t * k];"),
+    ("node_slot_by_rank", "on[e / experts_per_node] = 1;", "on[(e / experts_per_node) % N] = 1; on[0] |= (N > 1 && e % 2);"),
+    ("sparse_restripe_dense_row", "out[((int64_t)n * Tmax + s) * P + p] = prob[(t * N + n) * P + p];",
+     "out[((int64_t)n * Tmax + t) * P + p] = prob[(t * N + n) * P + p];"),
     ("combine_truncates_output", "out[t * H + h] = oracle_f32_to_bf16(acc[h]);",
      "{ uint32_t bits; memcpy(&bits, &acc[h], 4); out[t * H + h] = (uint16_t)(bits >> 16); }"),
 ]
@@ -69,6 +72,7 @@ MUTANTS = [
 # The quick pins (no exhaustive enumeration): enough to kill every mutant above.
 PIN_ARGS = ["tests/test_oracle_layout.py", "tests/test_oracle_dispatch.py",
             "tests/test_oracle_fp8.py", "tests/test_oracle_permute.py",
+            "tests/test_oracle_sparse.py",
             "tests/test_oracle_restripe.py", "tests/test_oracle_combine.py",
             "tests/test_golden_pages.py", "-x", "-q", "-p", "no:cacheprovider",
             "-k", "not exhaustive"]
