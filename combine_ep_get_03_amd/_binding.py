@@ -41,7 +41,9 @@ def load() -> ctypes.CDLL:
     L.ep_status_string.restype = ctypes.c_char_p
     L.ep_layout_workspace_bytes.argtypes = [i64, i32, i32, i32]
     L.ep_layout_workspace_bytes.restype = sz
-    L.ep_get_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, sz, P]
+    L.ep_get_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, sz,
+                                P]
+    L.ep_restripe_prob_sparse.argtypes = [P, i64, i32, i32, P, i64, P, P, P]
     L.ep_dispatch_permute.argtypes = [P, P, i64, i32, i32, P, P, P, P, i64, P, P]
     L.ep_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, i64, P, P]
     L.ep_dispatch_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, i64, P,
@@ -50,7 +52,7 @@ def load() -> ctypes.CDLL:
     L.ep_combine.argtypes = [P, i64, P, i64, i32, i32, P, P, P]
     L.ep_hbm_copy.argtypes = [P, P, sz, P]
     for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
-              "ep_restripe_prob", "ep_combine", "ep_hbm_copy"):
+              "ep_restripe_prob", "ep_restripe_prob_sparse", "ep_combine", "ep_hbm_copy"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -109,7 +111,7 @@ def ep_layout_workspace_bytes(num_tokens: int, num_experts: int, num_ranks: int,
 def ep_get_layout(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
                   num_tokens_per_rank, num_tokens_per_node, num_tokens_per_expert,
                   is_token_in_rank, rank_offset, expert_offset, token_slot, error_flag,
-                  workspace, expert_slot=None, stream=None) -> None:
+                  workspace, expert_slot=None, node_slot=None, stream=None) -> None:
     T, k = topk_idx.shape
     E, R, N = num_experts, num_ranks, num_nodes
     _at_least(num_tokens_per_rank, R, "num_tokens_per_rank")
@@ -120,6 +122,7 @@ def ep_get_layout(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
     _at_least(expert_offset, E + 1, "expert_offset")
     _shape(token_slot, (T, R), "token_slot")
     _shape(expert_slot, (T, k), "expert_slot")
+    _shape(node_slot, (T, N), "node_slot")
     _at_least(error_flag, 1, "error_flag")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().ep_get_layout(
@@ -132,6 +135,7 @@ def ep_get_layout(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
         _ptr(expert_offset, torch.int32, "expert_offset", True),
         _ptr(token_slot, torch.int32, "token_slot"),
         _ptr(expert_slot, torch.int32, "expert_slot", True),
+        _ptr(node_slot, torch.int32, "node_slot", True),
         _ptr(error_flag, torch.int32, "error_flag"),
         _ptr(workspace, torch.uint8, "workspace", True), ws_bytes, _stream(stream)),
         "ep_get_layout")
@@ -223,6 +227,22 @@ def ep_restripe_prob(prob, prob_dest_major, stream=None) -> None:
         _ptr(prob, torch.float32, "prob"), T, N, P, prob_dest_major.shape[1],
         _ptr(prob_dest_major, torch.float32, "prob_dest_major"), _stream(stream)),
         "ep_restripe_prob")
+
+
+def ep_restripe_prob_sparse(prob, node_slot, prob_dest_major, error_flag=None,
+                            stream=None) -> None:
+    """prob: fp32 [T][N][P]; node_slot: int32 [T][N]; prob_dest_major: fp32 [N][Tmax][P]."""
+    T, N, P = prob.shape
+    if prob_dest_major.dim() != 3 or prob_dest_major.shape[0] != N or \
+            prob_dest_major.shape[2] != P:
+        raise ValueError("prob_dest_major must be [N][Tmax][P]")
+    _shape(node_slot, (T, N), "node_slot")
+    _at_least(error_flag, 1, "error_flag")
+    _check(load().ep_restripe_prob_sparse(
+        _ptr(prob, torch.float32, "prob"), T, N, P, _ptr(node_slot, torch.int32, "node_slot"),
+        prob_dest_major.shape[1], _ptr(prob_dest_major, torch.float32, "prob_dest_major"),
+        _ptr(error_flag, torch.int32, "error_flag", True), _stream(stream)),
+        "ep_restripe_prob_sparse")
 
 
 def ep_combine(partial, token_slot, *, out, error_flag=None, stream=None) -> None:

@@ -25,11 +25,13 @@ class LayoutBuffers:
     error_flag: torch.Tensor             # int32 [1]
     workspace: torch.Tensor              # uint8 [ep_layout_workspace_bytes]
     expert_slot: Optional[torch.Tensor] = None  # int32 [T][k], when expert-major rows are wanted
+    node_slot: Optional[torch.Tensor] = None    # int32 [T][N], for the sparse restripe
 
     @classmethod
     def alloc(cls, T: int, E: int, R: int, N: int, device="cuda",
-              k_expert_slots: int = 0) -> "LayoutBuffers":
-        """k_expert_slots > 0 also allocates expert_slot [T][k] (expert-major rows)."""
+              k_expert_slots: int = 0, node_slots: bool = False) -> "LayoutBuffers":
+        """k_expert_slots > 0 also allocates expert_slot [T][k] (expert-major rows);
+        node_slots also allocates node_slot [T][N] (sparse restripe)."""
         i32 = dict(dtype=torch.int32, device=device)
         ws = max(16, B.ep_layout_workspace_bytes(T, E, R, N))
         return cls(torch.empty(R, **i32), torch.empty(N, **i32), torch.empty(E, **i32),
@@ -37,7 +39,8 @@ class LayoutBuffers:
                    torch.empty(R + 1, **i32), torch.empty(E + 1, **i32),
                    torch.empty((T, R), **i32), torch.zeros(1, **i32),
                    torch.empty(ws, dtype=torch.uint8, device=device),
-                   torch.empty((T, k_expert_slots), **i32) if k_expert_slots else None)
+                   torch.empty((T, k_expert_slots), **i32) if k_expert_slots else None,
+                   torch.empty((T, N), **i32) if node_slots else None)
 
     def compute(self, topk_idx: torch.Tensor, E: int, R: int, N: int, stream=None) -> None:
         B.ep_get_layout(topk_idx, E, R, N, num_tokens_per_rank=self.num_tokens_per_rank,
@@ -46,7 +49,7 @@ class LayoutBuffers:
                         is_token_in_rank=self.is_token_in_rank, rank_offset=self.rank_offset,
                         expert_offset=self.expert_offset, token_slot=self.token_slot,
                         error_flag=self.error_flag, workspace=self.workspace,
-                        expert_slot=self.expert_slot, stream=stream)
+                        expert_slot=self.expert_slot, node_slot=self.node_slot, stream=stream)
 
 
 @dataclasses.dataclass

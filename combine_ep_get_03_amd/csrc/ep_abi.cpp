@@ -54,8 +54,8 @@ int ep_get_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int
                   int num_ranks, int num_nodes, int32_t* num_tokens_per_rank,
                   int32_t* num_tokens_per_node, int32_t* num_tokens_per_expert,
                   uint8_t* is_token_in_rank, int32_t* rank_offset, int32_t* expert_offset,
-                  int32_t* token_slot, int32_t* expert_slot, int32_t* error_flag,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+                  int32_t* token_slot, int32_t* expert_slot, int32_t* node_slot,
+                  int32_t* error_flag, void* workspace, size_t workspace_bytes, void* stream) {
     const int64_t T = num_tokens;
     const int k = num_topk, E = num_experts, R = num_ranks, N = num_nodes;
     if (!topology_ok(k, E, R, N) || !slots_fit_int32(T, k, R)) return EP_ERR_ARG;
@@ -63,6 +63,7 @@ int ep_get_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int
     if (T > 0 && (!topk_idx || !token_slot)) return EP_ERR_ARG;
     if (expert_slot && k > EP_EXPERT_SLOT_MAX_K) return EP_ERR_ARG;
     if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) || !aligned(expert_slot, 4) ||
+        !aligned(node_slot, 4) ||
         !aligned(num_tokens_per_node, 4) || !aligned(num_tokens_per_expert, 4) ||
         !aligned(rank_offset, 4) || !aligned(expert_offset, 4) || !aligned(token_slot, 4) ||
         !aligned(error_flag, 4) || !aligned(workspace, 16))
@@ -73,7 +74,7 @@ int ep_get_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int
     return hip_status(ep::launch_layout(topk_idx, T, k, E, R, N, num_tokens_per_rank,
                                         num_tokens_per_node, num_tokens_per_expert,
                                         is_token_in_rank, rank_offset, expert_offset, token_slot,
-                                        expert_slot, error_flag, ws,
+                                        expert_slot, node_slot, error_flag, ws,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -162,6 +163,22 @@ int ep_restripe_prob(const float* prob, int64_t num_tokens, int num_nodes, int p
     if (!aligned(prob, 4) || !aligned(prob_dest_major, 4)) return EP_ERR_ALIGN;
     return hip_status(ep::launch_restripe(prob, T, N, P, Tmax, prob_dest_major,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int ep_restripe_prob_sparse(const float* prob, int64_t num_tokens, int num_nodes,
+                            int prob_per_token, const int32_t* node_slot,
+                            int64_t max_tokens_per_rank, float* prob_dest_major,
+                            int32_t* error_flag, void* stream) {
+    const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
+    const int N = num_nodes, P = prob_per_token;
+    if (T < 0 || N < 1 || P < 1 || static_cast<int64_t>(N) * P > (1 << 26)) return EP_ERR_ARG;
+    if (Tmax < T) return EP_ERR_CAPACITY;
+    if (T > 0 && (!prob || !prob_dest_major || !node_slot)) return EP_ERR_ARG;
+    if (!aligned(prob, 4) || !aligned(prob_dest_major, 4) || !aligned(node_slot, 4) ||
+        !aligned(error_flag, 4))
+        return EP_ERR_ALIGN;
+    return hip_status(ep::launch_restripe_sparse(prob, T, N, P, node_slot, Tmax, prob_dest_major,
+                                                 error_flag, static_cast<hipStream_t>(stream)));
 }
 
 int ep_combine(const void* partial, int64_t num_partial_rows, const int32_t* token_slot,

@@ -82,8 +82,8 @@ LayoutWorkspace carve_layout_workspace(void* base, int64_t T, int E, int R, int 
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
                          int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                          int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
-                         int32_t* expert_slot, int32_t* error_flag, const LayoutWorkspace& ws,
-                         hipStream_t stream);
+                         int32_t* expert_slot, int32_t* node_slot, int32_t* error_flag,
+                         const LayoutWorkspace& ws, hipStream_t stream);
 
 constexpr int kExpertSlotMaxK = 16;  // top-k limit of the expert-major slot output
 
@@ -109,6 +109,10 @@ hipError_t launch_restripe(const float* prob, int64_t T, int N, int P, int64_t T
 hipError_t launch_combine(const void* partial, int64_t rows, const int32_t* token_slot,
                           int64_t T, int H, int R, void* out, int32_t* error_flag,
                           hipStream_t stream);
+
+hipError_t launch_restripe_sparse(const float* prob, int64_t T, int N, int P,
+                                  const int32_t* node_slot, int64_t Tmax, float* out,
+                                  int32_t* error_flag, hipStream_t stream);
 
 hipError_t launch_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 

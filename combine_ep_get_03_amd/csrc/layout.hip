@@ -44,7 +44,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Rank mask (and optionally node mask) of one token; expert -1 and out-of-range ids
 // are skipped, the latter reported through `bad`. The k ids are loaded 8 at a time so
 // their latencies overlap.
-template <int NW, bool kCount>
+template <int NW, bool kCount, bool kNodes = kCount>
 __device__ __forceinline__ void token_masks(const int64_t* __restrict__ row, int k, int E,
                                             FastDiv er, FastDiv rpn, uint64_t (&rm)[NW],
                                             uint64_t (&nm)[NW], int32_t* s_hist, int& bad) {
@@ -64,7 +64,7 @@ __device__ __forceinline__ void token_masks(const int64_t* __restrict__ row, int
 #pragma unroll
             for (int w = 0; w < NW; ++w)
                 if ((r >> 6) == w) rm[w] |= 1ull << (r & 63);
-            if (kCount) {
+            if (kNodes) {
                 const int n = rpn.div(r);
 #pragma unroll
                 for (int w = 0; w < NW; ++w)
@@ -330,13 +330,16 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
     int32_t* __restrict__ count_e, int32_t* __restrict__ rank_offset,
     int32_t* __restrict__ expert_offset, int32_t* __restrict__ error_flag,
     int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank, int vec_out,
-    int want_expert_base) {
+    int want_expert_base, FastDiv rpn, int32_t* __restrict__ node_slot, int vec_node) {
     __shared__ int32_t s_cnt[kFusedMaxCells];               // [nb][R] per-group rank counts
     __shared__ uint64_t s_ball[kWavesBT * kFusedMaxRanks];  // [4][R] the group's ballots
     __shared__ int32_t s_base[kFusedMaxRanks];              // slot base of this quarter, per rank
     __shared__ int32_t s_tab[kFusedMaxSlice];               // [nb][ncol] expert slice
     __shared__ int32_t s_col[kMaxExperts / kQuarters + 2];  // column sums of the slice
     __shared__ int32_t s_node[kFusedMaxRanks];              // N <= R
+    __shared__ uint64_t s_nball[kWavesBT * kFusedMaxRanks];  // [4][N] node ballots
+    __shared__ int32_t s_npre[kFusedMaxRanks];               // node counts of earlier groups
+    __shared__ int32_t s_nbase[kFusedMaxRanks];              // packed node row base, per node
     __shared__ int32_t s_scan[17];
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -352,8 +355,10 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
     const int c1 = min(E, c0 + cw);
     const int ncol = c1 - c0 + 1;
 
-    if (g == 0)
-        for (int i = tid; i < N; i += kBT) s_node[i] = 0;
+    for (int i = tid; i < N; i += kBT) {
+        s_node[i] = 0;
+        s_npre[i] = 0;
+    }
     __syncthreads();
 
     // Issue the rank-table loads, then the token's ids, then park the table in LDS.
@@ -369,7 +374,12 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
 #pragma unroll
     for (int w = 0; w < NW; ++w) rm[w] = nm[w] = 0;
     int bad = 0;
-    if (t < T) token_masks<NW, false>(topk_idx + t * k, k, E, er, FastDiv{1, 0}, rm, nm, nullptr, bad);
+    if (t < T) {
+        if (node_slot)
+            token_masks<NW, false, true>(topk_idx + t * k, k, E, er, rpn, rm, nm, nullptr, bad);
+        else
+            token_masks<NW, false>(topk_idx + t * k, k, E, er, FastDiv{1, 0}, rm, nm, nullptr, bad);
+    }
 #pragma unroll
     for (int u = 0; u < kCellsPerLane; ++u) {
         const int i = tid + u * kBT;
@@ -397,6 +407,11 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
             nb * N, [&](int i) { return ws.blk_node[i]; }, [&](int i) { return i % N; }, s_node);
         for (int i = tid; i < nb; i += kBT) any_bad |= ws.blk_err[i];
     }
+    if (node_slot) {
+        accumulate_columns(
+            grp * N, [&](int i) { return ws.blk_node[i]; }, [&](int i) { return i % N; }, s_npre);
+        wave_ballots<NW, false>(nm, N, s_nball + wave * N);
+    }
     wave_ballots<NW, false>(rm, R, s_ball + wave * R);
     __syncthreads();
 
@@ -421,6 +436,11 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
         }
     }
     if (g == 0 && tid == 0) rank_offset[R] = M;
+    if (node_slot && tid < N) {
+        int base = s_npre[tid];
+        for (int w = 0; w < q; ++w) base += __popcll(s_nball[w * N + tid]);
+        s_nbase[tid] = base;
+    }
     // column sums of the inclusive prefixes: expert_offset[e + 1] for e = c0 - 1 + c
     for (int c = tid; c < ncol; c += kBT) {
         int sum = 0;
@@ -451,6 +471,9 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
 
     write_wave_slots(s_ball + q * R, s_base, T, t0 + q * kWave, R, vec_out != 0, token_slot,
                      in_rank);
+    if (node_slot)
+        write_wave_slots(s_nball + q * N, s_nbase, T, t0 + q * kWave, N, vec_node != 0, node_slot,
+                         nullptr);
     if (g == 0) {
         any_bad = __syncthreads_or(any_bad);
         if (tid == 0) *error_flag = any_bad ? kErrTopkRange : 0;
@@ -500,7 +523,7 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
     int nb, int E, int R, int N, LayoutWorkspace ws, int32_t* __restrict__ count_r,
     int32_t* __restrict__ count_n, int32_t* __restrict__ count_e,
     int32_t* __restrict__ rank_offset, int32_t* __restrict__ expert_offset,
-    int32_t* __restrict__ error_flag, int want_expert_base) {
+    int32_t* __restrict__ error_flag, int want_expert_base, int want_node_prefix) {
     __shared__ int32_t s_tile[kTileInts];
     __shared__ int32_t s_last[kScanThreads];
     __shared__ int32_t s_scan[17];
@@ -515,7 +538,11 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
     }
     if (tid == 0) rank_offset[R] = M;
 
-    if (count_n) {
+    if (want_node_prefix) {
+        // per-block exclusive node prefixes in place (for node_slot), totals as counts
+        const int tn = column_walk<true>(ws.blk_node, nb, N, 0, N, s_tile);
+        if (count_n && tid < N) count_n[tid] = tn;
+    } else if (count_n) {
         const int tn = column_walk<false>(ws.blk_node, nb, N, 0, N, s_tile);
         if (tid < N) count_n[tid] = tn;
     }
@@ -563,7 +590,8 @@ template <int NW>
 __global__ __launch_bounds__(kBT) void layout_slot_kernel(
     const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, FastDiv er,
     const int32_t* __restrict__ blk_prefix, const int32_t* __restrict__ rank_offset,
-    int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank) {
+    int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank, int N, FastDiv rpn,
+    const int32_t* __restrict__ blk_node_prefix, int32_t* __restrict__ node_slot) {
     extern __shared__ uint64_t smem64[];
     uint64_t* s_ball = smem64;                                            // [4][R]
     int32_t* s_base = reinterpret_cast<int32_t*>(s_ball + kWavesBT * R);  // [4][R]
@@ -576,7 +604,7 @@ __global__ __launch_bounds__(kBT) void layout_slot_kernel(
 #pragma unroll
     for (int w = 0; w < NW; ++w) rm[w] = nm[w] = 0;
     int bad = 0;
-    if (t < T) token_masks<NW, false>(topk_idx + t * k, k, E, er, FastDiv{1, 0}, rm, nm, nullptr, bad);
+    if (t < T) token_masks<NW, false, true>(topk_idx + t * k, k, E, er, rpn, rm, nm, nullptr, bad);
     wave_ballots<NW, false>(rm, R, s_ball + wave * R);
     __syncthreads();
 
@@ -590,8 +618,24 @@ __global__ __launch_bounds__(kBT) void layout_slot_kernel(
         }
     }
     __syncthreads();
-
     write_block_slots(s_ball, s_base, T, t0, R, token_slot, in_rank);
+
+    if (node_slot) {
+        // second pass over the same LDS, N <= R: node ballots and packed-row bases
+        __syncthreads();
+        wave_ballots<NW, false>(nm, N, s_ball + wave * N);
+        __syncthreads();
+        for (int n = tid; n < N; n += kBT) {
+            int base = blk_node_prefix[b * N + n];
+#pragma unroll
+            for (int w = 0; w < kWavesBT; ++w) {
+                s_base[w * N + n] = base;
+                base += __popcll(s_ball[w * N + n]);
+            }
+        }
+        __syncthreads();
+        write_block_slots(s_ball, s_base, T, t0, N, node_slot, nullptr);
+    }
 }
 
 // Expert-major row of every (token, slot) of one 256-token block: the block's base for
@@ -673,8 +717,8 @@ template <int NW>
 hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
                        int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                        int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
-                       int32_t* expert_slot, int32_t* error_flag, const LayoutWorkspace& ws,
-                       hipStream_t stream) {
+                       int32_t* expert_slot, int32_t* node_slot, int32_t* error_flag,
+                       const LayoutWorkspace& ws, hipStream_t stream) {
     const int want_base = expert_slot != nullptr ? 1 : 0;
     const int64_t nb = (T + kBT - 1) / kBT;
     const FastDiv er = FastDiv::make(E / R);
@@ -686,24 +730,31 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
         hipLaunchKernelGGL(layout_count_kernel<NW>, dim3(static_cast<unsigned>(nb)), dim3(kBT),
                            shm, stream, topk_idx, T, k, E, R, N, er, rpn, ws);
     }
-    if (nb > 0 && nb <= kFusedMaxBlocks && nb * R <= kFusedMaxCells && R <= kFusedMaxRanks) {
+    bool fused = false;
+    if constexpr (NW * kWave <= kFusedMaxRanks)  // the fused kernel needs R <= 256
+        fused = nb > 0 && nb <= kFusedMaxBlocks && nb * R <= kFusedMaxCells;
+    if (fused) {
+        if constexpr (NW * kWave <= kFusedMaxRanks) {
         const bool vec = R % 4 == 0 && reinterpret_cast<uintptr_t>(token_slot) % 16 == 0 &&
                          reinterpret_cast<uintptr_t>(in_rank) % 4 == 0;
+        const bool vec_node = N % 4 == 0 && reinterpret_cast<uintptr_t>(node_slot) % 16 == 0;
         hipLaunchKernelGGL(layout_slot_fused_kernel<NW>,
                            dim3(static_cast<unsigned>(nb * kQuarters)), dim3(kBT), 0, stream,
                            topk_idx, T, k, E, R, N, er, static_cast<int>(nb), ws, count_r,
                            count_n, count_e, rank_offset, expert_offset, error_flag, token_slot,
-                           in_rank, vec ? 1 : 0, want_base);
+                           in_rank, vec ? 1 : 0, want_base, rpn, node_slot, vec_node ? 1 : 0);
+        }
     } else {
         hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
                            static_cast<int>(nb), E, R, N, ws, count_r, count_n, count_e,
-                           rank_offset, expert_offset, error_flag, want_base);
+                           rank_offset, expert_offset, error_flag, want_base,
+                           node_slot != nullptr ? 1 : 0);
         if (nb > 0) {
             const size_t shm =
                 static_cast<size_t>(kWavesBT) * R * (sizeof(uint64_t) + sizeof(int32_t));
             hipLaunchKernelGGL(layout_slot_kernel<NW>, dim3(static_cast<unsigned>(nb)), dim3(kBT),
                                shm, stream, topk_idx, T, k, E, R, er, ws.blk_rank, rank_offset,
-                               token_slot, in_rank);
+                               token_slot, in_rank, N, rpn, ws.blk_node, node_slot);
         }
     }
     if (want_base && nb > 0) {
@@ -742,12 +793,12 @@ LayoutWorkspace carve_layout_workspace(void* base, int64_t T, int E, int R, int 
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
                          int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                          int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
-                         int32_t* expert_slot, int32_t* error_flag, const LayoutWorkspace& ws,
-                         hipStream_t stream) {
+                         int32_t* expert_slot, int32_t* node_slot, int32_t* error_flag,
+                         const LayoutWorkspace& ws, hipStream_t stream) {
 #define EP_LAYOUT_CASE(NW)                                                                     \
     return layout_impl<NW>(topk_idx, T, k, E, R, N, count_r, count_n, count_e, in_rank,        \
-                           rank_offset, expert_offset, token_slot, expert_slot, error_flag, ws, \
-                           stream)
+                           rank_offset, expert_offset, token_slot, expert_slot, node_slot,      \
+                           error_flag, ws, stream)
     if (R <= 64) EP_LAYOUT_CASE(1);
     if (R <= 128) EP_LAYOUT_CASE(2);
     if (R <= 256) EP_LAYOUT_CASE(4);

@@ -46,6 +46,52 @@ __global__ __launch_bounds__(kRT) void restripe_kernel(const W* __restrict__ in,
     }
 }
 
+// Sparse path: only routed (token, node) slices move, to row node_slot[t][n] of the node's
+// block (packed in token order). Same source-order walk as the dense restripe; the
+// destination row comes from node_slot (one int32 per slice, cached across its words).
+template <typename W>
+__global__ __launch_bounds__(kRT) void restripe_sparse_kernel(
+    const W* __restrict__ in, int64_t T, int N, int NV, int VP, const int32_t* __restrict__ node_slot,
+    int64_t Tmax, W* __restrict__ out, int32_t* __restrict__ error_flag, int tpb) {
+    const int tid = threadIdx.x;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tpb;
+    const int nt = static_cast<int>(min<int64_t>(tpb, T - t0));
+    const int total = nt * NV;
+    const W* src = in + t0 * NV;
+    int32_t errbits = 0;
+    for (int f0 = 0; f0 < total; f0 += kRT * kRU) {
+        W v[kRU];
+        int32_t s[kRU];
+#pragma unroll
+        for (int u = 0; u < kRU; ++u) {
+            const int f = f0 + u * kRT + tid;
+            s[u] = -1;
+            if (f < total) {
+                const int tt = f / NV;
+                const int n = (f - tt * NV) / VP;
+                s[u] = node_slot[(t0 + tt) * N + n];
+                if (s[u] >= 0) v[u] = __builtin_nontemporal_load(src + f);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRU; ++u) {
+            const int f = f0 + u * kRT + tid;
+            if (f < total && s[u] >= 0) {
+                if (s[u] >= Tmax) {
+                    errbits |= kErrRecvOverflow;
+                    continue;
+                }
+                const int tt = f / NV;
+                const int rem = f - tt * NV;
+                const int n = rem / VP;
+                const int vv = rem - n * VP;
+                __builtin_nontemporal_store(v[u], out + (static_cast<int64_t>(n) * Tmax + s[u]) * VP + vv);
+            }
+        }
+    }
+    if (errbits) raise_error(error_flag, errbits);
+}
+
 }  // namespace
 
 hipError_t launch_restripe(const float* prob, int64_t T, int N, int P, int64_t Tmax, float* out,
@@ -66,6 +112,33 @@ hipError_t launch_restripe(const float* prob, int64_t T, int N, int P, int64_t T
         hipLaunchKernelGGL(restripe_kernel<uint32_t>, dim3(static_cast<unsigned>(grid)), dim3(kRT),
                            0, stream, reinterpret_cast<const uint32_t*>(prob), T, NV, VP, Tmax,
                            reinterpret_cast<uint32_t*>(out), tpb);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ep
+
+namespace ep {
+
+hipError_t launch_restripe_sparse(const float* prob, int64_t T, int N, int P,
+                                  const int32_t* node_slot, int64_t Tmax, float* out,
+                                  int32_t* error_flag, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const bool vec = (P % 4 == 0) && (reinterpret_cast<uintptr_t>(prob) % 16 == 0) &&
+                     (reinterpret_cast<uintptr_t>(out) % 16 == 0);
+    const int VP = vec ? P / 4 : P;
+    const int NV = N * VP;
+    const int tpb = std::max(1, (kRT * kRU) / NV);
+    const int64_t grid = (T + tpb - 1) / tpb;
+    if (!grid_fits(grid, kRT)) return hipErrorInvalidConfiguration;
+    if (vec) {
+        hipLaunchKernelGGL(restripe_sparse_kernel<u32x4>, dim3(static_cast<unsigned>(grid)),
+                           dim3(kRT), 0, stream, reinterpret_cast<const u32x4*>(prob), T, N, NV, VP,
+                           node_slot, Tmax, reinterpret_cast<u32x4*>(out), error_flag, tpb);
+    } else {
+        hipLaunchKernelGGL(restripe_sparse_kernel<uint32_t>, dim3(static_cast<unsigned>(grid)),
+                           dim3(kRT), 0, stream, reinterpret_cast<const uint32_t*>(prob), T, N, NV,
+                           VP, node_slot, Tmax, reinterpret_cast<uint32_t*>(out), error_flag, tpb);
     }
     return hipGetLastError();
 }

@@ -88,6 +88,9 @@ size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_experts, int num_ra
  *                                 (token, slot) order, naming the same expert e; -1 for a
  *                                 masked or bad id. Rank r's experts are one contiguous range
  *                                 of rows. Needs k <= EP_EXPERT_SLOT_MAX_K.       (nullable)
+ *   node_slot              [T][N] packed row of (t, n) for ep_restripe_prob_sparse: the
+ *                                 number of tokens t' < t with a destination on node n; -1
+ *                                 where t has none on n.                          (nullable)
  *   error_flag             [1]    overwritten: 0, or EP_DEVERR_TOPK_RANGE when an entry is
  *                                 < -1 or >= E (such entries are skipped like -1).
  * Workspace: `workspace` of `workspace_bytes` >= ep_layout_workspace_bytes(T, E, R, N) bytes,
@@ -102,8 +105,8 @@ int ep_get_layout(const int64_t *topk_idx, int64_t num_tokens, int num_topk,
                   int32_t *num_tokens_per_rank, int32_t *num_tokens_per_node,
                   int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
                   int32_t *rank_offset, int32_t *expert_offset, int32_t *token_slot,
-                  int32_t *expert_slot, int32_t *error_flag, void *workspace,
-                  size_t workspace_bytes, void *stream);
+                  int32_t *expert_slot, int32_t *node_slot, int32_t *error_flag,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* ep_dispatch -- pack every (token, rank) pair into its receive row.
  *
@@ -186,6 +189,24 @@ int ep_dispatch_permute(const void *x, const float *topk_weights, int64_t num_to
  *   EP_ERR_HIP. */
 int ep_restripe_prob(const float *prob, int64_t num_tokens, int num_nodes, int prob_per_token,
                      int64_t max_tokens_per_rank, float *prob_dest_major, void *stream);
+
+/* ep_restripe_prob_sparse -- the sparse-path restripe ("[PR #634]", section "Fix": one put
+ * per run in the sparse path): only slices of tokens routed to a node move, packed in
+ * token order at the start of the node's block, so any run of consecutive routed tokens
+ * is one contiguous range.
+ *
+ * In:  prob        fp32 [T][N][P]
+ *      node_slot   int32 [T][N] from ep_get_layout
+ * Out: prob_dest_major fp32 [N][Tmax][P]; row node_slot[t][n] of block n = prob[t][n][:] for
+ *      every (t, n) with node_slot[t][n] >= 0 (32-bit words copied as bits). Other rows are
+ *      not written. A slot >= Tmax is skipped and sets EP_DEVERR_RECV_OVERFLOW (error_flag
+ *      nullable).
+ * Sizes and alignment as for ep_restripe_prob. Errors: EP_ERR_ARG, EP_ERR_ALIGN,
+ *   EP_ERR_CAPACITY (Tmax < T), EP_ERR_HIP. */
+int ep_restripe_prob_sparse(const float *prob, int64_t num_tokens, int num_nodes,
+                            int prob_per_token, const int32_t *node_slot,
+                            int64_t max_tokens_per_rank, float *prob_dest_major,
+                            int32_t *error_flag, void *stream);
 
 /* ep_combine -- gather each token's per-rank partial rows back to token order and sum them.
  *

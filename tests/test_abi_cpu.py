@@ -68,8 +68,8 @@ def test_workspace_query(lib):
 
 def _layout(lib, T=100, k=4, E=16, R=4, N=2, idx=A16, ws=A16, wsb=1 << 20, slot=A16,
             eslot=None):
-    return lib.ep_get_layout(idx, T, k, E, R, N, A16, A16, A16, A16, A16, A16, slot, eslot, A16,
-                             ws, wsb, None)
+    return lib.ep_get_layout(idx, T, k, E, R, N, A16, A16, A16, A16, A16, A16, slot, eslot, None,
+                             A16, ws, wsb, None)
 
 
 def test_layout_validation(lib):
@@ -136,6 +136,13 @@ def test_restripe_validation(lib):
     assert f(A16, 10, 2, 0, 10, A16, None) == ep.EP_ERR_ARG
     assert f(None, 10, 2, 4, 10, A16, None) == ep.EP_ERR_ARG
     assert f(P(0x10002), 10, 2, 4, 10, A16, None) == ep.EP_ERR_ALIGN
+
+
+def test_restripe_sparse_validation(lib):
+    f = lib.ep_restripe_prob_sparse
+    assert f(A16, 10, 2, 4, A16, 9, A16, None, None) == ep.EP_ERR_CAPACITY
+    assert f(A16, 10, 2, 4, None, 10, A16, None, None) == ep.EP_ERR_ARG
+    assert f(A16, 10, 2, 4, P(0x10002), 10, A16, None, None) == ep.EP_ERR_ALIGN
 
 
 def test_combine_validation(lib):
