@@ -145,6 +145,7 @@ def main():
     __graft_entry__._ensure_built()
     import combine_ep_get_03_amd as ep
     from combine_ep_get_03_amd import workloads as W
+    from combine_ep_get_03_amd.buffers import LayoutBuffers
     from combine_ep_get_03_amd.pipeline import DeviceBatch, Path
 
     cfg = W.CONFIGS[args.config]
@@ -243,8 +244,6 @@ def main():
     # expert-major order (k rows per token)
     permute = None
     if cfg.k <= ep.EP_EXPERT_SLOT_MAX_K:
-        from combine_ep_get_03_amd.buffers import LayoutBuffers
-
         lbe = LayoutBuffers.alloc(cfg.T, cfg.E, cfg.R, cfg.N, k_expert_slots=cfg.k)
         px = torch.empty((cfg.T * cfg.k, cfg.H), dtype=torch.bfloat16, device="cuda")
         pw = torch.empty(cfg.T * cfg.k, dtype=torch.float32, device="cuda")
@@ -274,6 +273,34 @@ def main():
                    "alg_bytes": pb,
                    "hbm_gbps": round(pb / (res["dispatch_permute"] * 1e-3) / 1e9, 1)}
         del px, pw, ps, lbe
+    # Sparse restripe: layout with per-node slots, then only the routed (token, node)
+    # slices packed per node (the dense restripe copies all T*N of them)
+    lbn = LayoutBuffers.alloc(cfg.T, cfg.E, cfg.R, cfg.N, node_slots=True)
+    sp_out = torch.empty((cfg.N, cfg.Tmax, cfg.P), dtype=torch.float32, device="cuda")
+
+    def layout_n():
+        lbn.compute(b.topk_idx, cfg.E, cfg.R, cfg.N)
+
+    def sparse_call():
+        ep.ep_restripe_prob_sparse(b.prob, lbn.node_slot, sp_out, error_flag=lbn.error_flag)
+    res = {}
+    for n, fn in (("layout_with_node_slots", layout_n), ("restripe_sparse", sparse_call)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(args.steps):
+                fn()
+        g.replay()
+        res[n] = timed(g.replay, 1) / args.steps
+        del g
+    if int(lbn.error_flag.item()) != 0:
+        raise RuntimeError("device error flag in sparse restripe")
+    routed = int(lbn.num_tokens_per_node.sum().item())
+    sb = cfg.T * cfg.N * 4 + 2 * routed * cfg.P * 4
+    sparse = {"layout_with_node_slots_us": round(res["layout_with_node_slots"] * 1e3, 2),
+              "restripe_sparse_us": round(res["restripe_sparse"] * 1e3, 2),
+              "routed_token_node_pairs": routed, "alg_bytes": sb,
+              "hbm_gbps": round(sb / (res["restripe_sparse"] * 1e-3) / 1e9, 1)}
+    del sp_out, lbn
     if int(path.error_flag.item()) != 0:
         raise RuntimeError(f"device error flag {int(path.error_flag.item())}")
 
@@ -322,6 +349,7 @@ def main():
         "copy_bandwidth_gbps": {k: round(v, 1) for k, v in copy_bw.items()},
         "dispatch_fp8": fp8,
         "dispatch_permute": permute,
+        "restripe_sparse": sparse,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
