@@ -42,6 +42,11 @@ def lib():
         L.oracle_node_slots.argtypes = [P, i64, i32, i32, i32, i32, P]
         L.oracle_restripe_prob_sparse.argtypes = [P, i64, i32, i32, P, i64, P]
         L.oracle_dispatch_permute.argtypes = [P, P, P, i64, i32, i32, P, i64, P, P, P]
+        L.oracle_hook_dispatch_send.argtypes = [P, P, P, i64, i32, i32, i32, P, i64, P, P, P, P]
+        L.oracle_hook_dispatch_recv.argtypes = [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P,
+                                                i64, i64, P, P, P, P]
+        L.oracle_hook_combine_send.argtypes = [P, i64, P, i64, i32, i32, i32, P, i64, P]
+        L.oracle_hook_combine_recv.argtypes = [P, i32, i64, P, i64, i32, P]
         L.oracle_f32_to_e4m3_array.argtypes = [P, i64, P]
         L.oracle_f32_to_e4m3_array.restype = None
         L.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
@@ -49,7 +54,9 @@ def lib():
         for f in ("oracle_layout", "oracle_dispatch", "oracle_restripe_prob", "oracle_combine",
                   "oracle_quantize_fp8", "oracle_dispatch_fp8", "oracle_expert_slots",
                   "oracle_dispatch_permute", "oracle_node_slots",
-                  "oracle_restripe_prob_sparse"):
+                  "oracle_restripe_prob_sparse", "oracle_hook_dispatch_send",
+                  "oracle_hook_dispatch_recv", "oracle_hook_combine_send",
+                  "oracle_hook_combine_recv"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -221,4 +228,77 @@ def restripe_prob_sparse(prob, node_slot, Tmax: int, out=None) -> np.ndarray:
     rc = lib().oracle_restripe_prob_sparse(_p(pw), T, N, P, _p(ns), Tmax, _p(out.view(np.uint32)))
     if rc != 0:
         raise ValueError("oracle_restripe_prob_sparse: bad arguments")
+    return out
+
+
+def hook_dispatch_send(x, topk_idx, topk_w, node_slot, Tmax: int, out=None) -> dict:
+    """Send phase of the two-phase dispatch. Returns (or fills) the staging buffers
+    stage_x [N][Tmax][H] (bf16 bits), stage_idx [N][Tmax][k], stage_w, stage_src [N][Tmax]."""
+    x = _c(x, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    w = _c(topk_w, np.float32)
+    ns = _c(node_slot, np.int32)
+    T, H = x.shape
+    k = idx.shape[1]
+    N = ns.shape[1]
+    if out is None:
+        out = dict(stage_x=np.zeros((N, Tmax, H), np.uint16),
+                   stage_idx=np.zeros((N, Tmax, k), np.int64),
+                   stage_w=np.zeros((N, Tmax, k), np.float32),
+                   stage_src=np.zeros((N, Tmax), np.int32))
+    rc = lib().oracle_hook_dispatch_send(_p(x), _p(idx), _p(w), T, H, k, N, _p(ns), Tmax,
+                                         _p(out["stage_x"]), _p(out["stage_idx"]),
+                                         _p(out["stage_w"]), _p(out["stage_src"]))
+    if rc != 0:
+        raise ValueError("oracle_hook_dispatch_send: bad arguments or node slot beyond Tmax")
+    return out
+
+
+def hook_dispatch_recv(stage: dict, count_n, E: int, R: int, token_slot, cap: int,
+                       out=None) -> dict:
+    """Receive phase: forwards the staged rows to the ranks of each node."""
+    sx = stage["stage_x"]
+    N, Tmax, H = sx.shape
+    k = stage["stage_idx"].shape[2]
+    slot = _c(token_slot, np.int32)
+    cn = _c(count_n, np.int32)
+    T = slot.shape[0]
+    if out is None:
+        out = dict(recv_x=np.zeros((cap, H), np.uint16), recv_idx=np.zeros((cap, k), np.int64),
+                   recv_w=np.zeros((cap, k), np.float32), recv_src=np.zeros(cap, np.int32))
+    rc = lib().oracle_hook_dispatch_recv(
+        _p(sx), _p(stage["stage_idx"]), _p(stage["stage_w"]), _p(stage["stage_src"]), _p(cn),
+        N, Tmax, H, k, E, R, _p(slot), T, cap, _p(out["recv_x"]), _p(out["recv_idx"]),
+        _p(out["recv_w"]), _p(out["recv_src"]))
+    if rc != 0:
+        raise ValueError("oracle_hook_dispatch_recv: bad arguments, staged token or slot "
+                         "out of range")
+    return out
+
+
+def hook_combine_send(partial, token_slot, R: int, node_slot, Tmax: int, out=None) -> np.ndarray:
+    """Send phase of the two-phase combine: per (token, node) bf16 sums, [N][Tmax][H]."""
+    partial = _c(partial, np.uint16)
+    slot = _c(token_slot, np.int32)
+    ns = _c(node_slot, np.int32)
+    rows, H = partial.shape
+    T, N = ns.shape
+    if out is None:
+        out = np.zeros((N, Tmax, H), np.uint16)
+    rc = lib().oracle_hook_combine_send(_p(partial), rows, _p(slot), T, H, R, N, _p(ns), Tmax,
+                                        _p(out))
+    if rc != 0:
+        raise ValueError("oracle_hook_combine_send: bad arguments or slot out of range")
+    return out
+
+
+def hook_combine_recv(stage, node_slot) -> np.ndarray:
+    """Receive phase: out[t] = bf16 of the fp32 sum of t's staged node rows."""
+    stage = _c(stage, np.uint16)
+    ns = _c(node_slot, np.int32)
+    N, Tmax, H = stage.shape
+    T = ns.shape[0]
+    out = np.zeros((T, H), np.uint16)
+    if lib().oracle_hook_combine_recv(_p(stage), N, Tmax, _p(ns), T, H, _p(out)) != 0:
+        raise ValueError("oracle_hook_combine_recv: bad arguments or node slot beyond Tmax")
     return out

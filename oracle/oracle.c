@@ -228,22 +228,23 @@ int oracle_layout(const int64_t *topk_idx, int64_t T, int k, int E, int R, int N
     return 0;
 }
 
-/* Rank r's view of token t's routing, written to receive row s: every slot j keeps
- * its place; an expert on r becomes its rank-local id with its weight, any other
- * slot becomes -1 with weight +0.0f. The row also records its source token. */
-static void route_view(const int64_t *topk_idx, const float *topk_w, int64_t t, int k, int E,
+/* Rank r's view of one token's routing (its k expert ids and weights), written to
+ * receive row s: every slot j keeps its place; an expert on r becomes its rank-local
+ * id with its weight, any other slot becomes -1 with weight +0.0f. The row also
+ * records its source token. */
+static void route_view(const int64_t *idx_row, const float *w_row, int32_t src, int k, int E,
                        int experts_per_rank, int r, int64_t s, int64_t *recv_idx, float *recv_w,
                        int32_t *recv_src)
 {
     for (int j = 0; j < k; ++j) {
-        int64_t e = topk_idx[t * k + j];
+        int64_t e = idx_row[j];
         int64_t local = -1;
         if (e >= 0 && e < E && e / experts_per_rank == r)
             local = e - (int64_t)r * experts_per_rank;
         recv_idx[s * k + j] = local;
-        recv_w[s * k + j] = local >= 0 ? topk_w[t * k + j] : 0.0f;
+        recv_w[s * k + j] = local >= 0 ? w_row[j] : 0.0f;
     }
-    recv_src[s] = (int32_t)t;
+    recv_src[s] = src;
 }
 
 /* Dispatch permute: each token's row goes, unchanged, to every rank that holds
@@ -264,8 +265,8 @@ int oracle_dispatch(const uint16_t *x, const int64_t *topk_idx, const float *top
             if (s >= cap)
                 return -1;
             memcpy(recv_x + s * H, x + t * H, (size_t)H * sizeof(uint16_t));
-            route_view(topk_idx, topk_w, t, k, E, experts_per_rank, r, s, recv_idx, recv_w,
-                       recv_src);
+            route_view(topk_idx + t * k, topk_w + t * k, (int32_t)t, k, E, experts_per_rank, r, s,
+                       recv_idx, recv_w, recv_src);
         }
     return 0;
 }
@@ -300,8 +301,8 @@ int oracle_dispatch_fp8(const uint16_t *x, const int64_t *topk_idx, const float 
             }
             memcpy(recv_codes + s * H, codes + t * H, (size_t)H);
             memcpy(recv_scales + s * G, scales + t * G, (size_t)G * sizeof(float));
-            route_view(topk_idx, topk_w, t, k, E, experts_per_rank, r, s, recv_idx, recv_w,
-                       recv_src);
+            route_view(topk_idx + t * k, topk_w + t * k, (int32_t)t, k, E, experts_per_rank, r, s,
+                       recv_idx, recv_w, recv_src);
         }
     free(codes);
     free(scales);
@@ -457,5 +458,153 @@ int oracle_combine(const uint16_t *partial, int64_t rows, const int32_t *token_s
             out[t * H + h] = oracle_f32_to_bf16(acc[h]);
     }
     free(acc);
+    return 0;
+}
+
+/* Two-phase ("hook") dispatch, "[PR #347] Feature/sm free normal kernel", section 2.1:
+ * the send phase only moves data into a large per-node buffer that holds a whole batch
+ * (section 2.2.2); the receive phase, called later, forwards the rows to the node's
+ * ranks (the intra-node hop, section 3.3.2).
+ *
+ * Send: each token's row, its k expert ids and weights and its token id go once to
+ * every node holding one of its experts, at row node_slot[t][n] of node n's block of
+ * Tmax rows. Rows past a node's count are left untouched. */
+int oracle_hook_dispatch_send(const uint16_t *x, const int64_t *topk_idx, const float *topk_w,
+                              int64_t T, int H, int k, int N, const int32_t *node_slot,
+                              int64_t Tmax, uint16_t *stage_x, int64_t *stage_idx,
+                              float *stage_w, int32_t *stage_src)
+{
+    if (T < 0 || H < 1 || k < 1 || N < 1 || Tmax < 0)
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int n = 0; n < N; ++n) {
+            const int64_t ns = node_slot[t * N + n];
+            if (ns < 0)
+                continue;
+            if (ns >= Tmax)
+                return -1;
+            const int64_t q = (int64_t)n * Tmax + ns;
+            memcpy(stage_x + q * H, x + t * H, (size_t)H * sizeof(uint16_t));
+            for (int j = 0; j < k; ++j) {
+                stage_idx[q * k + j] = topk_idx[t * k + j];
+                stage_w[q * k + j] = topk_w[t * k + j];
+            }
+            stage_src[q] = (int32_t)t;
+        }
+    return 0;
+}
+
+/* Receive: for each node n and each of its count_n[n] staged rows, the staged token t
+ * goes to every rank r of node n with a receive slot token_slot[t][r], with rank r's
+ * view of the staged routing. Together with the send phase this is the one-call
+ * dispatch. */
+int oracle_hook_dispatch_recv(const uint16_t *stage_x, const int64_t *stage_idx,
+                              const float *stage_w, const int32_t *stage_src,
+                              const int32_t *count_n, int N, int64_t Tmax, int H, int k, int E,
+                              int R, const int32_t *token_slot, int64_t T, int64_t cap,
+                              uint16_t *recv_x, int64_t *recv_idx, float *recv_w,
+                              int32_t *recv_src)
+{
+    if (H < 1 || k < 1 || E < 1 || R < 1 || N < 1 || E % R != 0 || R % N != 0 || Tmax < 0)
+        return -1;
+    const int experts_per_rank = E / R;
+    const int ranks_per_node = R / N;
+    for (int n = 0; n < N; ++n) {
+        if (count_n[n] < 0 || count_n[n] > Tmax)
+            return -1;
+        for (int64_t ns = 0; ns < count_n[n]; ++ns) {
+            const int64_t q = (int64_t)n * Tmax + ns;
+            const int64_t t = stage_src[q];
+            if (t < 0 || t >= T)
+                return -1;
+            for (int r = n * ranks_per_node; r < (n + 1) * ranks_per_node; ++r) {
+                const int64_t s = token_slot[t * R + r];
+                if (s < 0)
+                    continue;
+                if (s >= cap)
+                    return -1;
+                memcpy(recv_x + s * H, stage_x + q * H, (size_t)H * sizeof(uint16_t));
+                route_view(stage_idx + q * k, stage_w + q * k, (int32_t)t, k, E,
+                           experts_per_rank, r, s, recv_idx, recv_w, recv_src);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Two-phase combine (same page, sections 2.1 and 3.3.2: the send phase of combine is
+ * the intra-node hop). Send: for each token t and node n with a staged row, the fp32
+ * sum, from +0.0f in ascending rank order, of the partial rows of t on node n's ranks,
+ * rounded once to bf16 (the element type the pages' combine moves) into row
+ * node_slot[t][n] of node n's block. */
+int oracle_hook_combine_send(const uint16_t *partial, int64_t rows, const int32_t *token_slot,
+                             int64_t T, int H, int R, int N, const int32_t *node_slot,
+                             int64_t Tmax, uint16_t *stage)
+{
+    if (T < 0 || H < 1 || R < 1 || N < 1 || R % N != 0 || Tmax < 0)
+        return -1;
+    const int ranks_per_node = R / N;
+    float *sum = (float *)malloc((size_t)H * sizeof(float));
+    if (!sum)
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int n = 0; n < N; ++n) {
+            const int64_t ns = node_slot[t * N + n];
+            if (ns < 0)
+                continue;
+            if (ns >= Tmax) {
+                free(sum);
+                return -1;
+            }
+            for (int h = 0; h < H; ++h)
+                sum[h] = 0.0f;
+            for (int r = n * ranks_per_node; r < (n + 1) * ranks_per_node; ++r) {
+                const int64_t s = token_slot[t * R + r];
+                if (s < 0)
+                    continue;
+                if (s >= rows) {
+                    free(sum);
+                    return -1;
+                }
+                for (int h = 0; h < H; ++h)
+                    sum[h] = sum[h] + oracle_bf16_to_f32(partial[s * H + h]);
+            }
+            const int64_t q = (int64_t)n * Tmax + ns;
+            for (int h = 0; h < H; ++h)
+                stage[q * H + h] = oracle_f32_to_bf16(sum[h]);
+        }
+    free(sum);
+    return 0;
+}
+
+/* Receive: out[t] = bf16( fp32 sum, from +0.0f in ascending node order, of the staged
+ * rows node_slot[t][n] of every node n holding t ); +0 for a token on no node. */
+int oracle_hook_combine_recv(const uint16_t *stage, int N, int64_t Tmax,
+                             const int32_t *node_slot, int64_t T, int H, uint16_t *out)
+{
+    if (T < 0 || H < 1 || N < 1 || Tmax < 0)
+        return -1;
+    float *sum = (float *)malloc((size_t)H * sizeof(float));
+    if (!sum)
+        return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h)
+            sum[h] = 0.0f;
+        for (int n = 0; n < N; ++n) {
+            const int64_t ns = node_slot[t * N + n];
+            if (ns < 0)
+                continue;
+            if (ns >= Tmax) {
+                free(sum);
+                return -1;
+            }
+            const int64_t q = (int64_t)n * Tmax + ns;
+            for (int h = 0; h < H; ++h)
+                sum[h] = sum[h] + oracle_bf16_to_f32(stage[q * H + h]);
+        }
+        for (int h = 0; h < H; ++h)
+            out[t * H + h] = oracle_f32_to_bf16(sum[h]);
+    }
+    free(sum);
     return 0;
 }

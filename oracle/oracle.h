@@ -45,6 +45,25 @@ int oracle_dispatch_permute(const uint16_t *x, const int64_t *topk_idx, const fl
                             int64_t T, int H, int k, const int32_t *expert_slot, int64_t cap,
                             uint16_t *perm_x, float *perm_w, int32_t *perm_src);
 
+int oracle_hook_dispatch_send(const uint16_t *x, const int64_t *topk_idx, const float *topk_w,
+                              int64_t T, int H, int k, int N, const int32_t *node_slot,
+                              int64_t Tmax, uint16_t *stage_x, int64_t *stage_idx,
+                              float *stage_w, int32_t *stage_src);
+
+int oracle_hook_dispatch_recv(const uint16_t *stage_x, const int64_t *stage_idx,
+                              const float *stage_w, const int32_t *stage_src,
+                              const int32_t *count_n, int N, int64_t Tmax, int H, int k, int E,
+                              int R, const int32_t *token_slot, int64_t T, int64_t cap,
+                              uint16_t *recv_x, int64_t *recv_idx, float *recv_w,
+                              int32_t *recv_src);
+
+int oracle_hook_combine_send(const uint16_t *partial, int64_t rows, const int32_t *token_slot,
+                             int64_t T, int H, int R, int N, const int32_t *node_slot,
+                             int64_t Tmax, uint16_t *stage);
+
+int oracle_hook_combine_recv(const uint16_t *stage, int N, int64_t Tmax,
+                             const int32_t *node_slot, int64_t T, int H, uint16_t *out);
+
 uint8_t oracle_f32_to_e4m3(float v);
 float oracle_e4m3_to_f32(uint8_t c);
 void oracle_f32_to_e4m3_array(const float *in, int64_t n, uint8_t *out);

@@ -33,9 +33,9 @@ MUTANTS = [
     ("expert_offset_shifted", "expert_offset[e + 1] = expert_offset[e] + count_e[e];",
      "expert_offset[e + 1] = expert_offset[e] + count_e[e > 0 ? e - 1 : 0];"),
     ("local_id_not_rebased", "local = e - (int64_t)r * experts_per_rank;", "local = e;"),
-    ("weight_kept_off_rank", "recv_w[s * k + j] = local >= 0 ? topk_w[t * k + j] : 0.0f;",
-     "recv_w[s * k + j] = topk_w[t * k + j];"),
-    ("src_is_slot", "recv_src[s] = (int32_t)t;", "recv_src[s] = (int32_t)s;"),
+    ("weight_kept_off_rank", "recv_w[s * k + j] = local >= 0 ? w_row[j] : 0.0f;",
+     "recv_w[s * k + j] = w_row[j];"),
+    ("src_is_slot", "recv_src[s] = src;", "recv_src[s] = (int32_t)s;"),
     ("row_copy_short", "memcpy(recv_x + s * H, x + t * H, (size_t)H * sizeof(uint16_t));",
      "memcpy(recv_x + s * H, x + t * H, (size_t)(H - 1) * sizeof(uint16_t));"),
     ("restripe_uses_T_stride", "out[((int64_t)n * Tmax + t) * P + p] = prob[(t * N + n) * P + p];",
@@ -67,12 +67,26 @@ MUTANTS = [
      "out[((int64_t)n * Tmax + t) * P + p] = prob[(t * N + n) * P + p];"),
     ("combine_truncates_output", "out[t * H + h] = oracle_f32_to_bf16(acc[h]);",
      "{ uint32_t bits; memcpy(&bits, &acc[h], 4); out[t * H + h] = (uint16_t)(bits >> 16); }"),
+    ("hook_send_dense_row", "const int64_t q = (int64_t)n * Tmax + ns;\n            memcpy(stage_x + q * H",
+     "const int64_t q = (int64_t)n * Tmax + t;\n            memcpy(stage_x + q * H"),
+    ("hook_send_first_weight", "stage_w[q * k + j] = topk_w[t * k + j];", "stage_w[q * k + j] = topk_w[t * k];"),
+    ("hook_recv_skips_first_row", "for (int64_t ns = 0; ns < count_n[n]; ++ns) {",
+     "for (int64_t ns = 1; ns < count_n[n]; ++ns) {"),
+    ("hook_recv_view_of_node_rank", "experts_per_rank, r, s, recv_idx, recv_w, recv_src);\n            }\n        }\n    }",
+     "experts_per_rank, n * ranks_per_node, s, recv_idx, recv_w, recv_src);\n            }\n        }\n    }"),
+    ("hook_combine_send_all_ranks",
+     "for (int r = n * ranks_per_node; r < (n + 1) * ranks_per_node; ++r) {\n                const int64_t s = token_slot[t * R + r];\n                if (s < 0)\n                    continue;\n                if (s >= rows) {",
+     "for (int r = 0; r < R; ++r) {\n                const int64_t s = token_slot[t * R + r];\n                if (s < 0)\n                    continue;\n                if (s >= rows) {"),
+    ("hook_combine_recv_skips_node0", "sum[h] = 0.0f;\n        for (int n = 0; n < N; ++n) {",
+     "sum[h] = 0.0f;\n        for (int n = 1; n < N; ++n) {"),
+    ("hook_combine_send_scaled", "stage[q * H + h] = oracle_f32_to_bf16(sum[h]);",
+     "stage[q * H + h] = oracle_f32_to_bf16(sum[h] * 1.0078125f);"),
 ]
 
 # The quick pins (no exhaustive enumeration): enough to kill every mutant above.
 PIN_ARGS = ["tests/test_oracle_layout.py", "tests/test_oracle_dispatch.py",
             "tests/test_oracle_fp8.py", "tests/test_oracle_permute.py",
-            "tests/test_oracle_sparse.py",
+            "tests/test_oracle_sparse.py", "tests/test_oracle_hook.py",
             "tests/test_oracle_restripe.py", "tests/test_oracle_combine.py",
             "tests/test_golden_pages.py", "-x", "-q", "-p", "no:cacheprovider",
             "-k", "not exhaustive"]
