@@ -130,6 +130,92 @@ def cpu_baseline(cfg, inp, seconds: float) -> dict:
             "ms_per_step": round(s * 1e3, 2)}
 
 
+def hook_section(torch, cfg, b, args, timed, M: int) -> dict:
+    """Two-phase dispatch/combine: each phase's average launch time (a graph of K launches),
+    send + receive (the pages' hook-mode kernel time), and the send phase overlapped with
+    a 4096 x 4096 x 4096 bf16 GEMM on a second stream against the two run back to back."""
+    from combine_ep_get_03_amd.pipeline import Path
+
+    hp = Path(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax, node_slots=True)
+    hp.layout(b)
+    torch.cuda.synchronize()
+    routed = int(hp.layout_buf.num_tokens_per_node.sum().item())
+    holder = {}
+
+    def d_send():
+        holder["d"] = hp.dispatch_send(b)
+
+    def c_send():
+        holder["c"] = hp.combine_send(b)
+
+    d_send()
+    c_send()
+    res = {}
+    for n, fn in (("dispatch_send", d_send), ("dispatch_recv", lambda: holder["d"]()),
+                  ("combine_send", c_send), ("combine_recv", lambda: holder["c"]())):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(args.steps):
+                fn()
+        g.replay()
+        res[n] = timed(g.replay, 1) / args.steps
+        del g
+    if int(hp.error_flag.item()) != 0:
+        raise RuntimeError("device error flag in the two-phase calls")
+    T, H, k, N, R = cfg.T, cfg.H, cfg.k, cfg.N, cfg.R
+    row = 2 * H + 12 * k + 4
+    alg = {"dispatch_send": T * H * 2 + T * k * 12 + T * N * 4 + routed * row,
+           "dispatch_recv": routed * row + routed * (R // N) * 4 + N * 4 + M * row,
+           "combine_send": T * R * 4 + T * N * 4 + M * 2 * H + routed * 2 * H,
+           "combine_recv": T * N * 4 + routed * 2 * H + T * 2 * H}
+
+    # overlap: the send phase on one stream, the GEMM on another, K times
+    a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    w = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    comm, comp = torch.cuda.Stream(), torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def gemm():
+        torch.matmul(a, w, out=c)
+
+    for _ in range(3):
+        gemm()
+    gemm_ms = timed(gemm, args.steps)
+
+    def overlapped(reps):
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record(main)
+        comm.wait_stream(main)
+        comp.wait_stream(main)
+        for _ in range(reps):
+            with torch.cuda.stream(comm):
+                hp.dispatch_send(b, stream=comm)
+            with torch.cuda.stream(comp):
+                gemm()
+        main.wait_stream(comm)
+        main.wait_stream(comp)
+        s1.record(main)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / reps
+
+    overlapped(3)
+    ov_ms = overlapped(args.steps)
+    out = {n: {"avg_us": round(res[n] * 1e3, 2), "alg_bytes": alg[n],
+               "hbm_gbps": round(alg[n] / (res[n] * 1e-3) / 1e9, 1)} for n in res}
+    out["routed_token_node_pairs"] = routed
+    out["dispatch_send_plus_recv_us"] = round((res["dispatch_send"] + res["dispatch_recv"]) * 1e3, 2)
+    out["combine_send_plus_recv_us"] = round((res["combine_send"] + res["combine_recv"]) * 1e3, 2)
+    out["overlap"] = {"gemm_4096_bf16_us": round(gemm_ms * 1e3, 2),
+                      "send_us": round(res["dispatch_send"] * 1e3, 2),
+                      "serial_us": round((gemm_ms + res["dispatch_send"]) * 1e3, 2),
+                      "send_with_gemm_on_two_streams_us": round(ov_ms * 1e3, 2)}
+    del hp, a, w, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -301,6 +387,7 @@ def main():
               "routed_token_node_pairs": routed, "alg_bytes": sb,
               "hbm_gbps": round(sb / (res["restripe_sparse"] * 1e-3) / 1e9, 1)}
     del sp_out, lbn
+    hook = hook_section(torch, cfg, b, args, timed, M)
     if int(path.error_flag.item()) != 0:
         raise RuntimeError(f"device error flag {int(path.error_flag.item())}")
 
@@ -350,6 +437,7 @@ def main():
         "dispatch_fp8": fp8,
         "dispatch_permute": permute,
         "restripe_sparse": sparse,
+        "hook": hook,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

@@ -50,9 +50,15 @@ def load() -> ctypes.CDLL:
                                   P]
     L.ep_restripe_prob.argtypes = [P, i64, i32, i32, i64, P, P]
     L.ep_combine.argtypes = [P, i64, P, i64, i32, i32, P, P, P]
+    L.ep_dispatch_send.argtypes = [P, P, P, i64, i32, i32, i32, P, i64, P, P, P, P, P, P]
+    L.ep_dispatch_recv.argtypes = [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P, P, P,
+                                   P, i64, P, P]
+    L.ep_combine_send.argtypes = [P, i64, P, i64, i32, i32, i32, P, i64, P, P, P]
+    L.ep_combine_recv.argtypes = [P, i32, i64, P, i64, i32, P, P, P]
     L.ep_hbm_copy.argtypes = [P, P, sz, P]
     for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
-              "ep_restripe_prob", "ep_restripe_prob_sparse", "ep_combine", "ep_hbm_copy"):
+              "ep_restripe_prob", "ep_restripe_prob_sparse", "ep_combine", "ep_dispatch_send",
+              "ep_dispatch_recv", "ep_combine_send", "ep_combine_recv", "ep_hbm_copy"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -255,6 +261,105 @@ def ep_combine(partial, token_slot, *, out, error_flag=None, stream=None) -> Non
         _ptr(partial, torch.bfloat16, "partial"), rows, _ptr(token_slot, torch.int32, "token_slot"),
         T, H, R, _ptr(out, torch.bfloat16, "out"),
         _ptr(error_flag, torch.int32, "error_flag", True), _stream(stream)), "ep_combine")
+
+
+def _stage_dims(stage_x, name="stage_x"):
+    if stage_x.dim() != 3:
+        raise ValueError(f"{name} must be [N][Tmax][H]")
+    return tuple(int(d) for d in stage_x.shape)
+
+
+def ep_dispatch_send(x, topk_idx, topk_weights, node_slot, *, stage_x, stage_topk_idx=None,
+                     stage_topk_weights=None, stage_src, error_flag=None, stream=None) -> None:
+    """Send phase of the two-phase dispatch. x: bf16 [T][H]; node_slot: int32 [T][N];
+    stage_x: bf16 [N][Tmax][H]; stage_topk_idx / weights: [N][Tmax][k]; stage_src: [N][Tmax]."""
+    T, H = x.shape
+    N, Tmax, Hs = _stage_dims(stage_x)
+    k = topk_idx.shape[1] if topk_idx is not None else 1
+    if Hs != H:
+        raise ValueError("stage_x: hidden size differs from x")
+    _shape(topk_idx, (T, k), "topk_idx")
+    _shape(topk_weights, (T, k), "topk_weights")
+    _shape(node_slot, (T, N), "node_slot")
+    _shape(stage_topk_idx, (N, Tmax, k), "stage_topk_idx")
+    _shape(stage_topk_weights, (N, Tmax, k), "stage_topk_weights")
+    _shape(stage_src, (N, Tmax), "stage_src")
+    _at_least(error_flag, 1, "error_flag")
+    _check(load().ep_dispatch_send(
+        _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int64, "topk_idx", True),
+        _ptr(topk_weights, torch.float32, "topk_weights", True), T, H, k, N,
+        _ptr(node_slot, torch.int32, "node_slot"), Tmax, _ptr(stage_x, torch.bfloat16, "stage_x"),
+        _ptr(stage_topk_idx, torch.int64, "stage_topk_idx", True),
+        _ptr(stage_topk_weights, torch.float32, "stage_topk_weights", True),
+        _ptr(stage_src, torch.int32, "stage_src"),
+        _ptr(error_flag, torch.int32, "error_flag", True), _stream(stream)), "ep_dispatch_send")
+
+
+def ep_dispatch_recv(stage_x, stage_topk_idx, stage_topk_weights, stage_src, count_n,
+                     num_experts: int, num_ranks: int, token_slot, *, recv_x, recv_topk_idx=None,
+                     recv_topk_weights=None, recv_src_idx=None, num_topk: Optional[int] = None,
+                     error_flag=None, stream=None) -> None:
+    """Receive phase: forwards the staged rows to the ranks of each node, writing exactly
+    what ep_dispatch writes. count_n: int32 [N] (num_tokens_per_node)."""
+    N, Tmax, H = _stage_dims(stage_x)
+    T, R = token_slot.shape
+    if num_topk is None:
+        if stage_topk_idx is None:
+            raise ValueError("num_topk is needed when stage_topk_idx is None")
+        num_topk = stage_topk_idx.shape[2]
+    k = num_topk
+    cap = recv_x.shape[0]
+    _shape(stage_topk_idx, (N, Tmax, k), "stage_topk_idx")
+    _shape(stage_topk_weights, (N, Tmax, k), "stage_topk_weights")
+    _shape(stage_src, (N, Tmax), "stage_src")
+    _at_least(count_n, N, "count_n")
+    _shape(recv_x, (cap, H), "recv_x")
+    _shape(recv_topk_idx, (cap, k), "recv_topk_idx")
+    _shape(recv_topk_weights, (cap, k), "recv_topk_weights")
+    _shape(recv_src_idx, (cap,), "recv_src_idx")
+    _at_least(error_flag, 1, "error_flag")
+    _check(load().ep_dispatch_recv(
+        _ptr(stage_x, torch.bfloat16, "stage_x"),
+        _ptr(stage_topk_idx, torch.int64, "stage_topk_idx", True),
+        _ptr(stage_topk_weights, torch.float32, "stage_topk_weights", True),
+        _ptr(stage_src, torch.int32, "stage_src"), _ptr(count_n, torch.int32, "count_n"), N, Tmax,
+        H, k, num_experts, num_ranks, _ptr(token_slot, torch.int32, "token_slot"), T,
+        _ptr(recv_x, torch.bfloat16, "recv_x"),
+        _ptr(recv_topk_idx, torch.int64, "recv_topk_idx", True),
+        _ptr(recv_topk_weights, torch.float32, "recv_topk_weights", True),
+        _ptr(recv_src_idx, torch.int32, "recv_src_idx", True), cap,
+        _ptr(error_flag, torch.int32, "error_flag", True), _stream(stream)), "ep_dispatch_recv")
+
+
+def ep_combine_send(partial, token_slot, node_slot, *, stage, error_flag=None,
+                    stream=None) -> None:
+    """Send phase of the two-phase combine: per (token, node) bf16 sums of the node's
+    partial rows. partial: bf16 [rows][H]; stage: bf16 [N][Tmax][H]."""
+    rows, H = partial.shape
+    T, R = token_slot.shape
+    N, Tmax, Hs = _stage_dims(stage, "stage")
+    if Hs != H:
+        raise ValueError("stage: hidden size differs from partial")
+    _shape(node_slot, (T, N), "node_slot")
+    _at_least(error_flag, 1, "error_flag")
+    _check(load().ep_combine_send(
+        _ptr(partial, torch.bfloat16, "partial"), rows, _ptr(token_slot, torch.int32, "token_slot"),
+        T, H, R, N, _ptr(node_slot, torch.int32, "node_slot"), Tmax,
+        _ptr(stage, torch.bfloat16, "stage"), _ptr(error_flag, torch.int32, "error_flag", True),
+        _stream(stream)), "ep_combine_send")
+
+
+def ep_combine_recv(stage, node_slot, *, out, error_flag=None, stream=None) -> None:
+    """Receive phase: out[t] = bf16 of the fp32 sum of t's staged node rows."""
+    N, Tmax, H = _stage_dims(stage, "stage")
+    T = node_slot.shape[0]
+    _shape(node_slot, (T, N), "node_slot")
+    _shape(out, (T, H), "out")
+    _at_least(error_flag, 1, "error_flag")
+    _check(load().ep_combine_recv(
+        _ptr(stage, torch.bfloat16, "stage"), N, Tmax, _ptr(node_slot, torch.int32, "node_slot"),
+        T, H, _ptr(out, torch.bfloat16, "out"), _ptr(error_flag, torch.int32, "error_flag", True),
+        _stream(stream)), "ep_combine_recv")
 
 
 def ep_hbm_copy(src, dst, nbytes: Optional[int] = None, stream=None) -> None:

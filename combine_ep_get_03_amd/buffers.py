@@ -65,3 +65,20 @@ class DispatchBuffers:
                    torch.empty((cap, k), dtype=torch.int64, device=device),
                    torch.empty((cap, k), dtype=torch.float32, device=device),
                    torch.empty(cap, dtype=torch.int32, device=device))
+
+
+@dataclasses.dataclass
+class StageBuffers:
+    """Per-node staging of the two-phase dispatch/combine: Tmax rows per node, the whole
+    batch (staged row (n, s) is row n * Tmax + s)."""
+    stage_x: torch.Tensor             # bf16 [N][Tmax][H]: dispatch rows, then combine sums
+    stage_topk_idx: torch.Tensor      # int64 [N][Tmax][k]
+    stage_topk_weights: torch.Tensor  # fp32 [N][Tmax][k]
+    stage_src: torch.Tensor           # int32 [N][Tmax]
+
+    @classmethod
+    def alloc(cls, N: int, Tmax: int, H: int, k: int, device="cuda") -> "StageBuffers":
+        return cls(torch.empty((N, Tmax, H), dtype=torch.bfloat16, device=device),
+                   torch.empty((N, Tmax, k), dtype=torch.int64, device=device),
+                   torch.empty((N, Tmax, k), dtype=torch.float32, device=device),
+                   torch.empty((N, Tmax), dtype=torch.int32, device=device))

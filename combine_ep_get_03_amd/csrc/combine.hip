@@ -13,6 +13,11 @@
 // A 1024-thread block per 7168-wide token puts the loads of every source row of the
 // token in flight together; on MI355X that measured about 8% faster than 256 threads
 // looping over the row.
+//
+// The same kernel serves the two-phase combine ("[PR #347] Feature/sm free normal
+// kernel", sections 2.1 and 3.3.2): its send phase sums, per token and node, the rows of
+// the node's ranks into the node's staged row (grouped mode); its receive phase sums each
+// token's staged node rows, addressed by node-local slots, into the output.
 #include "ep_internal.hpp"
 
 namespace ep {
@@ -42,18 +47,58 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
 }
 
-__global__ __launch_bounds__(kCT) void combine_kernel(const u32x4* __restrict__ partial,
-                                                      int64_t rows,
-                                                      const int32_t* __restrict__ token_slot,
-                                                      int64_t T, int V, int R,
-                                                      u32x4* __restrict__ out,
-                                                      int32_t* __restrict__ error_flag, int tpb) {
+// Sum of the c source rows listed at sl (ascending), word vv, fp32 from +0.0f, rounded
+// once to bf16. Up to kCLoads rows are loaded together.
+__device__ __forceinline__ u32x4 sum_rows(const u32x4* __restrict__ partial,
+                                          const int32_t* sl, int c, int V, int vv) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int d0 = 0; d0 < c; d0 += kCLoads) {
+        u32x4 p[kCLoads];
+#pragma unroll
+        for (int i = 0; i < kCLoads; ++i)
+            if (d0 + i < c) p[i] = load_stream(partial + static_cast<int64_t>(sl[d0 + i]) * V + vv);
+#pragma unroll
+        for (int i = 0; i < kCLoads; ++i) {
+            if (d0 + i < c) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = acc[2 * q] + lo_bf16(p[i][q]);
+                    acc[2 * q + 1] = acc[2 * q + 1] + hi_bf16(p[i][q]);
+                }
+            }
+        }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16(acc[2 * q], acc[2 * q + 1]);
+    return o;
+}
+
+// Source slots: row t of slot_tab holds C columns; column c with slot s >= 0 names source
+// row s + c * cbase (with cbase > 0 a slot must also be below cbase). Without kGrouped
+// every token's sources are summed into out[t]. With kGrouped the C columns form G
+// consecutive groups of C / G; group g of token t is summed into row
+// g * obase + out_slot[t][g] of out when out_slot[t][g] >= 0 (the two-phase combine's
+// send phase: one sum per node of the token).
+template <bool kGrouped>
+__global__ __launch_bounds__(kCT) void combine_kernel(
+    const u32x4* __restrict__ partial, int64_t rows, const int32_t* __restrict__ slot_tab,
+    int C, int64_t cbase, int64_t T, int V, u32x4* __restrict__ out,
+    const int32_t* __restrict__ out_slot, int G, int64_t obase,
+    int32_t* __restrict__ error_flag, int tpb) {
     extern __shared__ int32_t smem[];
-    int32_t* s_cnt = smem;          // [tpb]
-    int32_t* s_slot = s_cnt + tpb;  // [tpb][R]
+    // flat: s_cnt [tpb]; grouped: group starts [tpb][G + 1] and output rows [tpb][G]
+    const int head = kGrouped ? tpb * (2 * G + 1) : tpb;
+    int32_t* s_cnt = smem;
+    int32_t* s_gs = smem;
+    int32_t* s_os = smem + tpb * (G + 1);
+    int32_t* s_slot = smem + head;  // [tpb][C]
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
+    const int gsize = C / G;
     const int64_t ngroups = (T + tpb - 1) / tpb;
     int32_t errbits = 0;
 
@@ -61,55 +106,60 @@ __global__ __launch_bounds__(kCT) void combine_kernel(const u32x4* __restrict__ 
         const int64_t t0 = grp * tpb;
         const int nt = static_cast<int>(min<int64_t>(tpb, T - t0));
 
-        // source slots of each token, ascending rank, compacted by wave ballots
+        // source slots of each token, ascending column, compacted by wave ballots
         for (int tt = wave; tt < nt; tt += kCT / kWave) {
-            const int32_t* srow = token_slot + (t0 + tt) * R;
+            const int32_t* srow = slot_tab + (t0 + tt) * C;
             int found = 0;
-            for (int r0 = 0; r0 < R; r0 += kWave) {
-                const int r = r0 + lane;
-                int32_t s = r < R ? srow[r] : -1;
-                if (s >= rows) {
+            for (int c0 = 0; c0 < C; c0 += kWave) {
+                const int c = c0 + lane;
+                int32_t s = c < C ? srow[c] : -1;
+                int64_t a = static_cast<int64_t>(s) + c * cbase;
+                if (s >= 0 && (a >= rows || (cbase > 0 && s >= cbase))) {
                     errbits |= kErrSlotRange;
                     s = -1;
                 }
                 const uint64_t m = wave_ballot(s >= 0);
                 const int pos = found + lanes_below(m);
-                if (s >= 0) s_slot[tt * R + pos] = s;
+                if (s >= 0) s_slot[tt * C + pos] = static_cast<int32_t>(a);
+                if (kGrouped && c < C && c % gsize == 0) s_gs[tt * (G + 1) + c / gsize] = pos;
                 found += __popcll(m);
             }
-            if (lane == 0) s_cnt[tt] = found;
+            if (lane == 0) {
+                if (kGrouped) s_gs[tt * (G + 1) + G] = found;
+                else s_cnt[tt] = found;
+            }
+            if (kGrouped) {
+                for (int g = lane; g < G; g += kWave) s_os[tt * G + g] = out_slot[(t0 + tt) * G + g];
+            }
         }
         __syncthreads();
 
-        const int total = nt * V;
-        for (int f = tid; f < total; f += kCT) {
-            const int tt = f / V;
-            const int vv = f - tt * V;
-            const int c = s_cnt[tt];
-            const int32_t* sl = s_slot + tt * R;
-            float acc[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-            for (int d0 = 0; d0 < c; d0 += kCLoads) {
-                u32x4 p[kCLoads];
-#pragma unroll
-                for (int i = 0; i < kCLoads; ++i)
-                    if (d0 + i < c) p[i] = load_stream(partial + static_cast<int64_t>(sl[d0 + i]) * V + vv);
-#pragma unroll
-                for (int i = 0; i < kCLoads; ++i) {
-                    if (d0 + i < c) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            acc[2 * q] = acc[2 * q] + lo_bf16(p[i][q]);
-                            acc[2 * q + 1] = acc[2 * q + 1] + hi_bf16(p[i][q]);
-                        }
-                    }
-                }
+        if (!kGrouped) {
+            const int total = nt * V;
+            for (int f = tid; f < total; f += kCT) {
+                const int tt = f / V;
+                const int vv = f - tt * V;
+                store_stream(out + (t0 + tt) * V + vv,
+                             sum_rows(partial, s_slot + tt * C, s_cnt[tt], V, vv));
             }
-            u32x4 o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = pack_bf16(acc[2 * q], acc[2 * q + 1]);
-            store_stream(out + (t0 + tt) * V + vv, o);
+        } else {
+            const int total = nt * G * V;
+            for (int f = tid; f < total; f += kCT) {
+                const int tg = f / V;
+                const int vv = f - tg * V;
+                const int tt = tg / G;
+                const int g = tg - tt * G;
+                const int32_t os = s_os[tg];
+                if (os < 0) continue;
+                if (os >= obase) {
+                    errbits |= kErrRecvOverflow;
+                    continue;
+                }
+                const int b = s_gs[tt * (G + 1) + g];
+                const int e = s_gs[tt * (G + 1) + g + 1];
+                store_stream(out + (g * obase + os) * V + vv,
+                             sum_rows(partial, s_slot + tt * C + b, e - b, V, vv));
+            }
         }
         if (kCGridCap > 0) __syncthreads();  // the next group reuses the LDS lists
     }
@@ -118,21 +168,52 @@ __global__ __launch_bounds__(kCT) void combine_kernel(const u32x4* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const void* partial, int64_t rows, const int32_t* token_slot,
-                          int64_t T, int H, int R, void* out, int32_t* error_flag,
-                          hipStream_t stream) {
+// Tokens per block: enough words for about kCBlockWords outputs, and LDS lists within
+// 32 KB.
+static int combine_tokens_per_block(int V, int lds_ints_per_token) {
+    int tpb = std::max(1, std::min(64, kCBlockWords / V));
+    return std::max(1, std::min(tpb, 8192 / lds_ints_per_token));
+}
+
+template <bool kGrouped>
+static hipError_t launch_combine_impl(const void* partial, int64_t rows, const int32_t* slot_tab, int C,
+                               int64_t cbase, int64_t T, int H, void* out,
+                               const int32_t* out_slot, int G, int64_t obase,
+                               int32_t* error_flag, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    int tpb = std::max(1, std::min(64, kCBlockWords / V));
-    tpb = std::max(1, std::min(tpb, 8192 / R));
+    const int per_token = C + (kGrouped ? 2 * G + 1 : 1);
+    const int tpb = combine_tokens_per_block(kGrouped ? V * G : V, per_token);
     const int64_t groups = (T + tpb - 1) / tpb;
     const int64_t grid = kCGridCap > 0 ? std::min<int64_t>(groups, kCGridCap) : groups;
     if (!grid_fits(grid, kCT)) return hipErrorInvalidConfiguration;
-    const size_t shm = sizeof(int32_t) * (static_cast<size_t>(tpb) + static_cast<size_t>(tpb) * R);
-    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(grid)), dim3(kCT), shm, stream,
-                       static_cast<const u32x4*>(partial), rows, token_slot, T, V, R,
-                       static_cast<u32x4*>(out), error_flag, tpb);
+    const size_t shm = sizeof(int32_t) * static_cast<size_t>(tpb) * per_token;
+    hipLaunchKernelGGL(combine_kernel<kGrouped>, dim3(static_cast<unsigned>(grid)), dim3(kCT),
+                       shm, stream, static_cast<const u32x4*>(partial), rows, slot_tab, C, cbase,
+                       T, V, static_cast<u32x4*>(out), out_slot, G, obase, error_flag, tpb);
     return hipGetLastError();
+}
+
+hipError_t launch_combine(const void* partial, int64_t rows, const int32_t* token_slot,
+                          int64_t T, int H, int R, void* out, int32_t* error_flag,
+                          hipStream_t stream) {
+    return launch_combine_impl<false>(partial, rows, token_slot, R, 0, T, H, out, nullptr, 1, 0,
+                                      error_flag, stream);
+}
+
+hipError_t launch_combine_send(const void* partial, int64_t rows, const int32_t* token_slot,
+                               int64_t T, int H, int R, int N, const int32_t* node_slot,
+                               int64_t Tmax, void* stage, int32_t* error_flag,
+                               hipStream_t stream) {
+    return launch_combine_impl<true>(partial, rows, token_slot, R, 0, T, H, stage, node_slot, N,
+                                     Tmax, error_flag, stream);
+}
+
+hipError_t launch_combine_recv(const void* stage, int N, int64_t Tmax, const int32_t* node_slot,
+                               int64_t T, int H, void* out, int32_t* error_flag,
+                               hipStream_t stream) {
+    return launch_combine_impl<false>(stage, static_cast<int64_t>(N) * Tmax, node_slot, N, Tmax,
+                                      T, H, out, nullptr, 1, 0, error_flag, stream);
 }
 
 }  // namespace ep

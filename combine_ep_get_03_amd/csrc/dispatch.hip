@@ -45,28 +45,29 @@ __device__ __forceinline__ void store_row_word(u32x4* p, u32x4 v) {
 #endif
 }
 
-template <int WPL>
-__global__ __launch_bounds__(kDT) void dispatch_kernel(
-    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_w, int64_t T, int V, int k, int E, int R, int er,
-    const int32_t* __restrict__ token_slot, u32x4* __restrict__ recv_x,
-    int64_t* __restrict__ recv_idx, float* __restrict__ recv_w, int32_t* __restrict__ recv_src,
-    int64_t cap, int32_t* __restrict__ error_flag) {
+// The walk shared by the bf16 dispatch kernels: the calling wave moves one source row,
+// and its k-slot routing, to every destination named by a row of C slots. Slot c, when
+// >= 0, names row slot + c * cbase of the destination (a slot >= cap is an overflow and
+// is skipped); destinations are walked in ascending c. With kRankView the routing is
+// written as rank (rank0 + c)'s view: the local expert id and the weight where the
+// expert is on that rank, else -1 and +0.0f. Without it the ids and weights are copied
+// unchanged. idx_row must be non-null when dst_idx or dst_w is.
+template <int WPL, bool kRankView>
+__device__ __forceinline__ void scatter_row(
+    const u32x4* __restrict__ xr, int V, const int64_t* __restrict__ idx_row,
+    const float* __restrict__ w_row, int k, int er, int32_t src,
+    const int32_t* __restrict__ srow, int C, int64_t cbase, int rank0, int64_t cap,
+    u32x4* __restrict__ dst_x, int64_t* __restrict__ dst_idx, float* __restrict__ dst_w,
+    int32_t* __restrict__ dst_src, int32_t& errbits) {
     const int lane = lane_id();
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
-    if (t >= T) return;
-    const bool meta = recv_idx || recv_w;
+    const bool meta = dst_idx || dst_w;
     // this lane's top-k slot (k <= 64 in one go; larger k reloads per destination)
     int64_t e0 = -1;
     float w0 = 0.0f;
     if (meta && lane < k) {
-        e0 = topk_idx[t * k + lane];
-        if (topk_w) w0 = topk_w[t * k + lane];
+        e0 = idx_row[lane];
+        if (w_row) w0 = w_row[lane];
     }
-    const u32x4* xr = x + t * V;
-    const int32_t* srow = token_slot + t * R;
-    int32_t errbits = 0;
-
     for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
         u32x4 v[WPL];
 #pragma unroll
@@ -74,8 +75,8 @@ __global__ __launch_bounds__(kDT) void dispatch_kernel(
             const int vi = v0 + i * kWave + lane;
             if (vi < V) v[i] = load_stream(xr + vi);
         }
-        for (int r0 = 0; r0 < R; r0 += kWave) {
-            int32_t s = r0 + lane < R ? srow[r0 + lane] : -1;
+        for (int c0 = 0; c0 < C; c0 += kWave) {
+            int32_t s = c0 + lane < C ? srow[c0 + lane] : -1;
             if (s >= cap) {
                 errbits |= kErrRecvOverflow;
                 s = -1;
@@ -84,9 +85,9 @@ __global__ __launch_bounds__(kDT) void dispatch_kernel(
             while (m) {
                 const int src_lane = __builtin_ctzll(m);
                 m &= m - 1;
-                const int64_t sd = __builtin_amdgcn_readlane(s, src_lane);
-                const int rd = r0 + src_lane;
-                u32x4* row = recv_x + sd * V;
+                const int cd = c0 + src_lane;
+                const int64_t sd = __builtin_amdgcn_readlane(s, src_lane) + cd * cbase;
+                u32x4* row = dst_x + sd * V;
 #pragma unroll
                 for (int i = 0; i < WPL; ++i) {
                     const int vi = v0 + i * kWave + lane;
@@ -97,21 +98,96 @@ __global__ __launch_bounds__(kDT) void dispatch_kernel(
                     for (int j0 = 0; j0 < k; j0 += kWave) {
                         const int j = j0 + lane;
                         if (j >= k) continue;
-                        const int64_t e = j0 == 0 ? e0 : topk_idx[t * k + j];
-                        const int64_t lo = static_cast<int64_t>(rd) * er;
-                        const bool local = e >= lo && e < lo + er;
-                        if (recv_idx) recv_idx[sd * k + j] = local ? e - static_cast<int64_t>(rd) * er : -1;
-                        if (recv_w) {
-                            const float wv = j0 == 0 ? w0 : topk_w[t * k + j];
-                            recv_w[sd * k + j] = local ? wv : 0.0f;
+                        const int64_t e = j0 == 0 ? e0 : idx_row[j];
+                        const float wv = j0 == 0 ? w0 : (w_row ? w_row[j] : 0.0f);
+                        if (kRankView) {
+                            const int64_t lo = static_cast<int64_t>(rank0 + cd) * er;
+                            const bool local = e >= lo && e < lo + er;
+                            if (dst_idx) dst_idx[sd * k + j] = local ? e - lo : -1;
+                            if (dst_w) dst_w[sd * k + j] = local ? wv : 0.0f;
+                        } else {
+                            if (dst_idx) dst_idx[sd * k + j] = e;
+                            if (dst_w) dst_w[sd * k + j] = wv;
                         }
                     }
                 }
-                if (recv_src && lane == 0) recv_src[sd] = static_cast<int32_t>(t);
+                if (dst_src && lane == 0) dst_src[sd] = src;
             }
         }
     }
+}
+
+template <int WPL>
+__global__ __launch_bounds__(kDT) void dispatch_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int64_t T, int V, int k, int R, int er,
+    const int32_t* __restrict__ token_slot, u32x4* __restrict__ recv_x,
+    int64_t* __restrict__ recv_idx, float* __restrict__ recv_w, int32_t* __restrict__ recv_src,
+    int64_t cap, int32_t* __restrict__ error_flag) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
+    if (t >= T) return;
+    int32_t errbits = 0;
+    scatter_row<WPL, true>(x + t * V, V, topk_idx ? topk_idx + t * k : nullptr,
+                           topk_w ? topk_w + t * k : nullptr, k, er, static_cast<int32_t>(t),
+                           token_slot + t * R, R, 0, 0, cap, recv_x, recv_idx, recv_w, recv_src,
+                           errbits);
     if (errbits) raise_error(error_flag, errbits);
+}
+
+// Two-phase dispatch ("[PR #347] Feature/sm free normal kernel", section 2.1), send
+// phase: each token's row, its k expert ids and weights and its id go once to every
+// node holding one of its experts, at row node_slot[t][n] of node n's block of Tmax rows
+// (the large per-node buffer that holds a whole batch, section 2.2.2).
+template <int WPL>
+__global__ __launch_bounds__(kDT) void dispatch_send_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int64_t T, int V, int k, int N,
+    const int32_t* __restrict__ node_slot, int64_t Tmax, u32x4* __restrict__ stage_x,
+    int64_t* __restrict__ stage_idx, float* __restrict__ stage_w, int32_t* __restrict__ stage_src,
+    int32_t* __restrict__ error_flag) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
+    if (t >= T) return;
+    int32_t errbits = 0;
+    scatter_row<WPL, false>(x + t * V, V, topk_idx ? topk_idx + t * k : nullptr,
+                            topk_w ? topk_w + t * k : nullptr, k, 0, static_cast<int32_t>(t),
+                            node_slot + t * N, N, Tmax, 0, Tmax, stage_x, stage_idx, stage_w,
+                            stage_src, errbits);
+    if (errbits) raise_error(error_flag, errbits);
+}
+
+// Receive phase (the intra-node hop, same page, section 3.3.2): block (b, n) owns staged
+// rows [8b, 8b + 8) of node n, one wave each; rows at or past count_n[n] are idle. A
+// staged row goes to every rank of node n with a receive slot for its token, with that
+// rank's view of the staged routing, exactly as the one-call dispatch writes it.
+template <int WPL>
+__global__ __launch_bounds__(kDT) void dispatch_recv_kernel(
+    const u32x4* __restrict__ stage_x, const int64_t* __restrict__ stage_idx,
+    const float* __restrict__ stage_w, const int32_t* __restrict__ stage_src,
+    const int32_t* __restrict__ count_n, int64_t Tmax, int64_t T, int V, int k, int R, int rpn,
+    int er, const int32_t* __restrict__ token_slot, u32x4* __restrict__ recv_x,
+    int64_t* __restrict__ recv_idx, float* __restrict__ recv_w, int32_t* __restrict__ recv_src,
+    int64_t cap, int32_t* __restrict__ error_flag) {
+    const int n = blockIdx.y;
+    const int64_t s = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
+    int64_t cnt = count_n[n];
+    int32_t errbits = 0;
+    if (cnt < 0 || cnt > Tmax || cnt > T) {
+        errbits |= kErrRecvOverflow;
+        cnt = cnt < 0 ? 0 : (Tmax < T ? Tmax : T);
+    }
+    if (s < cnt) {
+        const int64_t q = static_cast<int64_t>(n) * Tmax + s;
+        const int64_t t = stage_src[q];
+        if (t < 0 || t >= T) {
+            errbits |= kErrSlotRange;
+        } else {
+            scatter_row<WPL, true>(stage_x + q * V, V, stage_idx ? stage_idx + q * k : nullptr,
+                                   stage_w ? stage_w + q * k : nullptr, k, er,
+                                   static_cast<int32_t>(t), token_slot + t * R + n * rpn, rpn, 0,
+                                   n * rpn, cap, recv_x, recv_idx, recv_w, recv_src, errbits);
+        }
+    }
+    if (errbits && (s < cnt || s == 0)) raise_error(error_flag, errbits);
 }
 
 // FP8 dispatch: the same walk, but each token is first quantised once, in registers:
@@ -293,7 +369,7 @@ hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* 
     if (!grid_fits(grid, kDT)) return hipErrorInvalidConfiguration;
 #define EP_DISPATCH_LAUNCH(WPL)                                                              \
     hipLaunchKernelGGL(dispatch_kernel<WPL>, dim3(static_cast<unsigned>(grid)), dim3(kDT), 0, \
-                       stream, static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, E, R, \
+                       stream, static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, R,    \
                        E / R, token_slot, static_cast<u32x4*>(recv_x), recv_idx, recv_w,       \
                        recv_src, cap, error_flag)
     // words per lane: the smallest that holds a row, 14 (a 7168-wide bf16 row) at most
@@ -356,6 +432,57 @@ hipError_t launch_dispatch_permute(const void* x, const float* topk_w, int64_t T
     else if (V <= 7 * kWave) EP_PERMUTE_LAUNCH(7);
     else EP_PERMUTE_LAUNCH(14);
 #undef EP_PERMUTE_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace ep
+
+namespace ep {
+
+hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const float* topk_w,
+                                int64_t T, int H, int k, int N, const int32_t* node_slot,
+                                int64_t Tmax, void* stage_x, int64_t* stage_idx, float* stage_w,
+                                int32_t* stage_src, int32_t* error_flag, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int V = H / 8;
+    const int64_t grid = (T + kDWaves - 1) / kDWaves;
+    if (!grid_fits(grid, kDT)) return hipErrorInvalidConfiguration;
+#define EP_SEND_LAUNCH(WPL)                                                                    \
+    hipLaunchKernelGGL(dispatch_send_kernel<WPL>, dim3(static_cast<unsigned>(grid)), dim3(kDT), \
+                       0, stream, static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, N,  \
+                       node_slot, Tmax, static_cast<u32x4*>(stage_x), stage_idx, stage_w,      \
+                       stage_src, error_flag)
+    if (V <= kWave) EP_SEND_LAUNCH(1);
+    else if (V <= 2 * kWave) EP_SEND_LAUNCH(2);
+    else if (V <= 4 * kWave) EP_SEND_LAUNCH(4);
+    else if (V <= 7 * kWave) EP_SEND_LAUNCH(7);
+    else EP_SEND_LAUNCH(14);
+#undef EP_SEND_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_recv(const void* stage_x, const int64_t* stage_idx,
+                                const float* stage_w, const int32_t* stage_src,
+                                const int32_t* count_n, int N, int64_t Tmax, int H, int k, int E,
+                                int R, const int32_t* token_slot, int64_t T, void* recv_x,
+                                int64_t* recv_idx, float* recv_w, int32_t* recv_src, int64_t cap,
+                                int32_t* error_flag, hipStream_t stream) {
+    const int64_t rows = std::min(T, Tmax);  // a node holds at most min(T, Tmax) rows
+    if (rows == 0) return hipSuccess;
+    const int V = H / 8;
+    const int64_t bx = (rows + kDWaves - 1) / kDWaves;
+    if (!grid_fits(bx * N, kDT) || N > 65535) return hipErrorInvalidConfiguration;
+#define EP_RECV_LAUNCH(WPL)                                                                    \
+    hipLaunchKernelGGL(dispatch_recv_kernel<WPL>, dim3(static_cast<unsigned>(bx), N),          \
+                       dim3(kDT), 0, stream, static_cast<const u32x4*>(stage_x), stage_idx,    \
+                       stage_w, stage_src, count_n, Tmax, T, V, k, R, R / N, E / R, token_slot, \
+                       static_cast<u32x4*>(recv_x), recv_idx, recv_w, recv_src, cap, error_flag)
+    if (V <= kWave) EP_RECV_LAUNCH(1);
+    else if (V <= 2 * kWave) EP_RECV_LAUNCH(2);
+    else if (V <= 4 * kWave) EP_RECV_LAUNCH(4);
+    else if (V <= 7 * kWave) EP_RECV_LAUNCH(7);
+    else EP_RECV_LAUNCH(14);
+#undef EP_RECV_LAUNCH
     return hipGetLastError();
 }
 

@@ -198,6 +198,103 @@ int ep_combine(const void* partial, int64_t num_partial_rows, const int32_t* tok
                                          error_flag, static_cast<hipStream_t>(stream)));
 }
 
+int ep_dispatch_send(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                     int64_t num_tokens, int hidden, int num_topk, int num_nodes,
+                     const int32_t* node_slot, int64_t max_tokens_per_rank, void* stage_x,
+                     int64_t* stage_topk_idx, float* stage_topk_weights, int32_t* stage_src,
+                     int32_t* error_flag, void* stream) {
+    const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
+    const int H = hidden, k = num_topk, N = num_nodes;
+    if (T < 0 || H < 1 || k < 1 || N < 1 || N > EP_MAX_RANKS || Tmax < 0 || Tmax > INT32_MAX)
+        return EP_ERR_ARG;
+    if (H % 8 != 0) return EP_ERR_ALIGN;
+    if (static_cast<int64_t>(H) / 8 * 64 > INT32_MAX) return EP_ERR_ARG;
+    if (T > INT32_MAX) return EP_ERR_ARG;
+    if (T > 0) {
+        if (!x || !node_slot || !stage_x || !stage_src) return EP_ERR_ARG;
+        if ((stage_topk_idx || stage_topk_weights) && !topk_idx) return EP_ERR_ARG;
+        if (stage_topk_weights && !topk_weights) return EP_ERR_ARG;
+    }
+    if (!aligned(x, 16) || !aligned(stage_x, 16) || !aligned(topk_idx, 8) ||
+        !aligned(topk_weights, 4) || !aligned(node_slot, 4) || !aligned(stage_topk_idx, 8) ||
+        !aligned(stage_topk_weights, 4) || !aligned(stage_src, 4) || !aligned(error_flag, 4))
+        return EP_ERR_ALIGN;
+    return hip_status(ep::launch_dispatch_send(x, topk_idx, topk_weights, T, H, k, N, node_slot,
+                                               Tmax, stage_x, stage_topk_idx, stage_topk_weights,
+                                               stage_src, error_flag,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch_recv(const void* stage_x, const int64_t* stage_topk_idx,
+                     const float* stage_topk_weights, const int32_t* stage_src,
+                     const int32_t* count_n, int num_nodes, int64_t max_tokens_per_rank,
+                     int hidden, int num_topk, int num_experts, int num_ranks,
+                     const int32_t* token_slot, int64_t num_tokens, void* recv_x,
+                     int64_t* recv_topk_idx, float* recv_topk_weights, int32_t* recv_src_idx,
+                     int64_t recv_capacity, int32_t* error_flag, void* stream) {
+    const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
+    const int H = hidden, k = num_topk, E = num_experts, R = num_ranks, N = num_nodes;
+    if (!topology_ok(k, E, R, N) || !slots_fit_int32(T, k, R) || H < 1 || recv_capacity < 0 ||
+        Tmax < 0 || Tmax > INT32_MAX)
+        return EP_ERR_ARG;
+    if (H % 8 != 0) return EP_ERR_ALIGN;
+    if (static_cast<int64_t>(H) / 8 * 64 > INT32_MAX) return EP_ERR_ARG;
+    if (T > 0 && Tmax > 0) {
+        if (!stage_x || !stage_src || !count_n || !token_slot || !recv_x) return EP_ERR_ARG;
+        if ((recv_topk_idx || recv_topk_weights) && !stage_topk_idx) return EP_ERR_ARG;
+        if (recv_topk_weights && !stage_topk_weights) return EP_ERR_ARG;
+    }
+    if (!aligned(stage_x, 16) || !aligned(recv_x, 16) || !aligned(stage_topk_idx, 8) ||
+        !aligned(stage_topk_weights, 4) || !aligned(stage_src, 4) || !aligned(count_n, 4) ||
+        !aligned(token_slot, 4) || !aligned(recv_topk_idx, 8) || !aligned(recv_topk_weights, 4) ||
+        !aligned(recv_src_idx, 4) || !aligned(error_flag, 4))
+        return EP_ERR_ALIGN;
+    return hip_status(ep::launch_dispatch_recv(stage_x, stage_topk_idx, stage_topk_weights,
+                                               stage_src, count_n, N, Tmax, H, k, E, R,
+                                               token_slot, T, recv_x, recv_topk_idx,
+                                               recv_topk_weights, recv_src_idx, recv_capacity,
+                                               error_flag, static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine_send(const void* partial, int64_t num_partial_rows, const int32_t* token_slot,
+                    int64_t num_tokens, int hidden, int num_ranks, int num_nodes,
+                    const int32_t* node_slot, int64_t max_tokens_per_rank, void* stage,
+                    int32_t* error_flag, void* stream) {
+    const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
+    const int H = hidden, R = num_ranks, N = num_nodes;
+    if (T < 0 || H < 1 || R < 1 || R > EP_MAX_RANKS || N < 1 || R % N != 0 ||
+        num_partial_rows < 0 || num_partial_rows > INT32_MAX || Tmax < 0 || Tmax > INT32_MAX)
+        return EP_ERR_ARG;
+    if (H % 8 != 0) return EP_ERR_ALIGN;
+    if (static_cast<int64_t>(H) / 8 * 64 * N > INT32_MAX) return EP_ERR_ARG;
+    if (T > 0 && (!token_slot || !node_slot || !stage)) return EP_ERR_ARG;
+    if (T > 0 && num_partial_rows > 0 && !partial) return EP_ERR_ARG;
+    if (!aligned(partial, 16) || !aligned(stage, 16) || !aligned(token_slot, 4) ||
+        !aligned(node_slot, 4) || !aligned(error_flag, 4))
+        return EP_ERR_ALIGN;
+    return hip_status(ep::launch_combine_send(partial, num_partial_rows, token_slot, T, H, R, N,
+                                              node_slot, Tmax, stage, error_flag,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine_recv(const void* stage, int num_nodes, int64_t max_tokens_per_rank,
+                    const int32_t* node_slot, int64_t num_tokens, int hidden, void* out,
+                    int32_t* error_flag, void* stream) {
+    const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
+    const int H = hidden, N = num_nodes;
+    if (T < 0 || H < 1 || N < 1 || N > EP_MAX_RANKS || Tmax < 0) return EP_ERR_ARG;
+    if (static_cast<int64_t>(N) * Tmax > INT32_MAX) return EP_ERR_ARG;
+    if (H % 8 != 0) return EP_ERR_ALIGN;
+    if (static_cast<int64_t>(H) / 8 * 64 > INT32_MAX) return EP_ERR_ARG;
+    if (T > 0 && (!node_slot || !out)) return EP_ERR_ARG;
+    if (T > 0 && Tmax > 0 && !stage) return EP_ERR_ARG;
+    if (!aligned(stage, 16) || !aligned(out, 16) || !aligned(node_slot, 4) ||
+        !aligned(error_flag, 4))
+        return EP_ERR_ALIGN;
+    return hip_status(ep::launch_combine_recv(stage, N, Tmax, node_slot, T, H, out, error_flag,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int ep_hbm_copy(const void* src, void* dst, size_t bytes, void* stream) {
     if (bytes > 0 && (!src || !dst)) return EP_ERR_ARG;
     if (bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16)) return EP_ERR_ALIGN;

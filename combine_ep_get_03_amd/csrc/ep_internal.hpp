@@ -109,6 +109,23 @@ hipError_t launch_restripe(const float* prob, int64_t T, int N, int P, int64_t T
 hipError_t launch_combine(const void* partial, int64_t rows, const int32_t* token_slot,
                           int64_t T, int H, int R, void* out, int32_t* error_flag,
                           hipStream_t stream);
+hipError_t launch_combine_send(const void* partial, int64_t rows, const int32_t* token_slot,
+                               int64_t T, int H, int R, int N, const int32_t* node_slot,
+                               int64_t Tmax, void* stage, int32_t* error_flag,
+                               hipStream_t stream);
+hipError_t launch_combine_recv(const void* stage, int N, int64_t Tmax, const int32_t* node_slot,
+                               int64_t T, int H, void* out, int32_t* error_flag,
+                               hipStream_t stream);
+hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const float* topk_w,
+                                int64_t T, int H, int k, int N, const int32_t* node_slot,
+                                int64_t Tmax, void* stage_x, int64_t* stage_idx, float* stage_w,
+                                int32_t* stage_src, int32_t* error_flag, hipStream_t stream);
+hipError_t launch_dispatch_recv(const void* stage_x, const int64_t* stage_idx,
+                                const float* stage_w, const int32_t* stage_src,
+                                const int32_t* count_n, int N, int64_t Tmax, int H, int k, int E,
+                                int R, const int32_t* token_slot, int64_t T, void* recv_x,
+                                int64_t* recv_idx, float* recv_w, int32_t* recv_src, int64_t cap,
+                                int32_t* error_flag, hipStream_t stream);
 
 hipError_t launch_restripe_sparse(const float* prob, int64_t T, int N, int P,
                                   const int32_t* node_slot, int64_t Tmax, float* out,

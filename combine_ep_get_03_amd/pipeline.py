@@ -1,5 +1,7 @@
 """One batch through the whole path on the GPU: layout -> dispatch -> restripe_prob ->
-combine, each step one call of the C ABI on the same stream.
+combine, each step one call of the C ABI on the same stream; and the two-phase
+("hook") form of dispatch and combine, whose send phase returns a callable that enqueues
+the receive phase later.
 
 Device buffers are allocated once per shape (torch, memory plumbing only); `step()`
 enqueues the four calls and returns without synchronising.
@@ -12,7 +14,7 @@ from typing import Optional
 import torch
 
 from . import _binding as B
-from .buffers import DispatchBuffers, LayoutBuffers
+from .buffers import DispatchBuffers, LayoutBuffers, StageBuffers
 
 
 @dataclasses.dataclass
@@ -44,13 +46,14 @@ class Path:
     N nodes, P prob floats per (token, node), Tmax rows per node block."""
 
     def __init__(self, T: int, H: int, E: int, k: int, R: int, N: int, P: int, Tmax: int,
-                 device="cuda", recv_capacity: Optional[int] = None):
+                 device="cuda", recv_capacity: Optional[int] = None, node_slots: bool = False):
         self.T, self.H, self.E, self.k, self.R, self.N, self.P, self.Tmax = T, H, E, k, R, N, P, Tmax
         self.cap = T * min(k, R) if recv_capacity is None else recv_capacity
-        self.layout_buf = LayoutBuffers.alloc(T, E, R, N, device)
+        self.layout_buf = LayoutBuffers.alloc(T, E, R, N, device, node_slots=node_slots)
         self.recv = DispatchBuffers.alloc(self.cap, H, k, device)
         self.prob_dest_major = torch.empty((N, Tmax, P), dtype=torch.float32, device=device)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+        self.stage: Optional[StageBuffers] = None
 
     @property
     def error_flag(self) -> torch.Tensor:
@@ -79,3 +82,45 @@ class Path:
         self.dispatch(b, stream)
         self.restripe(b, stream)
         self.combine(b, stream)
+
+    # --- two-phase ("hook") dispatch and combine -----------------------------------------
+
+    def _hook_buffers(self) -> StageBuffers:
+        if self.stage is None:
+            self.stage = StageBuffers.alloc(self.N, self.Tmax, self.H, self.k,
+                                            self.out.device)
+        if self.layout_buf.node_slot is None:
+            raise ValueError("the two-phase calls need node slots: build the Path with "
+                             "node_slots=True and run layout() first")
+        return self.stage
+
+    def dispatch_send(self, b: DeviceBatch, stream=None):
+        """Enqueue the send phase; returns the receive hook, a callable(stream=None) that
+        enqueues the receive phase (on a stream ordered after this one)."""
+        st, lb = self._hook_buffers(), self.layout_buf
+        B.ep_dispatch_send(b.x, b.topk_idx, b.topk_weights, lb.node_slot, stage_x=st.stage_x,
+                           stage_topk_idx=st.stage_topk_idx,
+                           stage_topk_weights=st.stage_topk_weights, stage_src=st.stage_src,
+                           error_flag=self.error_flag, stream=stream)
+
+        def recv_hook(stream=None) -> None:
+            r = self.recv
+            B.ep_dispatch_recv(st.stage_x, st.stage_topk_idx, st.stage_topk_weights,
+                               st.stage_src, lb.num_tokens_per_node, self.E, self.R,
+                               lb.token_slot, recv_x=r.recv_x, recv_topk_idx=r.recv_topk_idx,
+                               recv_topk_weights=r.recv_topk_weights,
+                               recv_src_idx=r.recv_src_idx, error_flag=self.error_flag,
+                               stream=stream)
+        return recv_hook
+
+    def combine_send(self, b: DeviceBatch, stream=None):
+        """Enqueue the combine's send phase (per-node sums); returns its receive hook."""
+        st, lb = self._hook_buffers(), self.layout_buf
+        partial = self.recv.recv_x if b.partials is None else b.partials
+        B.ep_combine_send(partial, lb.token_slot, lb.node_slot, stage=st.stage_x,
+                          error_flag=self.error_flag, stream=stream)
+
+        def recv_hook(stream=None) -> None:
+            B.ep_combine_recv(st.stage_x, lb.node_slot, out=self.out, error_flag=self.error_flag,
+                              stream=stream)
+        return recv_hook

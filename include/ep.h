@@ -222,6 +222,74 @@ int ep_combine(const void *partial, int64_t num_partial_rows, const int32_t *tok
                int64_t num_tokens, int hidden, int num_ranks, void *out, int32_t *error_flag,
                void *stream);
 
+/* Two-phase ("hook") dispatch and combine ("[PR #347] Feature/sm free normal kernel",
+ * section 2.1): the first call runs only the send phase and returns; the caller may run
+ * other work (the page overlaps a GEMM) and later makes the receive-phase call on a
+ * stream ordered after the send. Between the two, a per-node staging buffer of Tmax rows
+ * per node holds the whole batch (the large buffer of section 2.2.2; on one GPU it is both
+ * the send and the receive side of that buffer). The receive phase of dispatch and the
+ * send phase of combine are the intra-node hop (section 3.3.2). Staged row (n, s) is row
+ * n * Tmax + s of every staging array.
+ *
+ * ep_dispatch_send -- In: x bf16 [T][H]; topk_idx int64 [T][k]; topk_weights fp32 [T][k];
+ *      node_slot int32 [T][N] from ep_get_layout.
+ * Out: for every (t, n) with s = node_slot[t][n] >= 0, staged row (n, s):
+ *      stage_x     bf16 [N][Tmax][H]  row t of x
+ *      stage_topk_idx     int64 [N][Tmax][k]  topk_idx[t][:] unchanged          (nullable)
+ *      stage_topk_weights fp32  [N][Tmax][k]  topk_weights[t][:] unchanged      (nullable)
+ *      stage_src   int32 [N][Tmax]    t
+ *      Other rows are not written. A slot >= Tmax is skipped and sets
+ *      EP_DEVERR_RECV_OVERFLOW. topk_idx / topk_weights may be NULL when the matching
+ *      staging array is NULL.
+ * Sizes: H % 8 == 0; x and stage_x 16-byte aligned. Errors: EP_ERR_ARG, EP_ERR_ALIGN,
+ *   EP_ERR_HIP. */
+int ep_dispatch_send(const void *x, const int64_t *topk_idx, const float *topk_weights,
+                     int64_t num_tokens, int hidden, int num_topk, int num_nodes,
+                     const int32_t *node_slot, int64_t max_tokens_per_rank, void *stage_x,
+                     int64_t *stage_topk_idx, float *stage_topk_weights, int32_t *stage_src,
+                     int32_t *error_flag, void *stream);
+
+/* ep_dispatch_recv -- In: the staging arrays written by ep_dispatch_send; count_n int32 [N]
+ *      (num_tokens_per_node from ep_get_layout: the staged rows of node n are 0..count_n[n]-1);
+ *      token_slot int32 [T][R] from ep_get_layout.
+ * Out: exactly what ep_dispatch writes: for every staged row (n, s) with token
+ *      t = stage_src[n][s] and every rank r of node n with d = token_slot[t][r] >= 0, row d
+ *      of recv_x = the staged row, recv_topk_idx / recv_topk_weights [d] = rank r's view of
+ *      the staged routing (local id and weight where the expert is on r, else -1 and +0.0f),
+ *      recv_src_idx[d] = t. recv_topk_idx needs stage_topk_idx; recv_topk_weights needs
+ *      both staged arrays. A staged token outside [0, T) sets EP_DEVERR_SLOT_RANGE; a count
+ *      above min(T, Tmax) or a row >= recv_capacity sets EP_DEVERR_RECV_OVERFLOW.
+ * Sizes: as ep_dispatch, and R % N == 0. Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_HIP. */
+int ep_dispatch_recv(const void *stage_x, const int64_t *stage_topk_idx,
+                     const float *stage_topk_weights, const int32_t *stage_src,
+                     const int32_t *count_n, int num_nodes, int64_t max_tokens_per_rank,
+                     int hidden, int num_topk, int num_experts, int num_ranks,
+                     const int32_t *token_slot, int64_t num_tokens, void *recv_x,
+                     int64_t *recv_topk_idx, float *recv_topk_weights, int32_t *recv_src_idx,
+                     int64_t recv_capacity, int32_t *error_flag, void *stream);
+
+/* ep_combine_send -- In: partial bf16 [num_partial_rows][H] (ep_dispatch's receive layout);
+ *      token_slot int32 [T][R]; node_slot int32 [T][N] from ep_get_layout.
+ * Out: stage bf16 [N][Tmax][H]; for every (t, n) with s = node_slot[t][n] >= 0, staged row
+ *      (n, s) = bf16_rne( sum over the ranks r of node n, ascending, with
+ *      d = token_slot[t][r] >= 0 of float(partial[d]) ), fp32 from +0.0f. Other rows are not
+ *      written. A slot >= num_partial_rows sets EP_DEVERR_SLOT_RANGE, a node slot >= Tmax
+ *      EP_DEVERR_RECV_OVERFLOW (both skipped).
+ * ep_combine_recv -- In: stage from ep_combine_send; node_slot.
+ * Out: out bf16 [T][H]; out[t] = bf16_rne( sum over nodes n ascending with
+ *      s = node_slot[t][n] >= 0 of float(staged row (n, s)) ), fp32 from +0.0f; +0.0 for a
+ *      token on no node. A node slot >= Tmax is skipped and sets EP_DEVERR_SLOT_RANGE.
+ *      The result differs from ep_combine's by the extra rounding of each node's sum.
+ * Sizes: H % 8 == 0; partial, stage and out 16-byte aligned; R % N == 0.
+ * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_HIP. */
+int ep_combine_send(const void *partial, int64_t num_partial_rows, const int32_t *token_slot,
+                    int64_t num_tokens, int hidden, int num_ranks, int num_nodes,
+                    const int32_t *node_slot, int64_t max_tokens_per_rank, void *stage,
+                    int32_t *error_flag, void *stream);
+int ep_combine_recv(const void *stage, int num_nodes, int64_t max_tokens_per_rank,
+                    const int32_t *node_slot, int64_t num_tokens, int hidden, void *out,
+                    int32_t *error_flag, void *stream);
+
 /* ep_hbm_copy -- measurement helper, not a step of the path: a plain 128-bit copy of
  * `bytes` bytes (a multiple of 16; both pointers 16-byte aligned) used as the HBM
  * copy-bandwidth yardstick and as the known-size reference for hardware byte counters.

@@ -38,7 +38,10 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"ep_get_layout", "ep_dispatch", "ep_restripe_prob", "ep_combine",
-                          "ep_layout_workspace_bytes", "ep_status_string", "ep_hbm_copy"}
+                          "ep_layout_workspace_bytes", "ep_status_string", "ep_hbm_copy",
+                          "ep_dispatch_fp8", "ep_dispatch_permute", "ep_restripe_prob_sparse",
+                          "ep_dispatch_send", "ep_dispatch_recv", "ep_combine_send",
+                          "ep_combine_recv"}
     out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (ep_\w+)", out))
@@ -152,6 +155,43 @@ def test_combine_validation(lib):
     assert f(MIS, 10, A16, 10, 64, 4, A16, None, None) == ep.EP_ERR_ALIGN
     assert f(A16, -1, A16, 10, 64, 4, A16, None, None) == ep.EP_ERR_ARG
     assert f(A16, 10, None, 10, 64, 4, A16, None, None) == ep.EP_ERR_ARG
+
+
+def test_dispatch_send_recv_validation(lib):
+    send = lib.ep_dispatch_send
+    a = lambda H=64, N=2, x=A16, idx=A16, ns=A16, sx=A16, sidx=A16, src=A16: (
+        x, idx, A16, 10, H, 2, N, ns, 10, sx, sidx, A16, src, A16, None)
+    assert send(*a(H=60)) == ep.EP_ERR_ALIGN
+    assert send(*a(x=MIS)) == ep.EP_ERR_ALIGN
+    assert send(*a(sx=P(0x10008))) == ep.EP_ERR_ALIGN
+    assert send(*a(N=0)) == ep.EP_ERR_ARG
+    assert send(*a(ns=None)) == ep.EP_ERR_ARG
+    assert send(*a(src=None)) == ep.EP_ERR_ARG
+    assert send(*a(idx=None)) == ep.EP_ERR_ARG              # staged ids need topk_idx
+    recv = lib.ep_dispatch_recv
+    b = lambda H=64, N=2, R=4, cn=A16, sidx=A16, ridx=A16, rx=A16: (
+        A16, sidx, A16, A16, cn, N, 10, H, 2, 8, R, A16, 10, rx, ridx, A16, A16, 40, A16, None)
+    assert recv(*b(N=3)) == ep.EP_ERR_ARG                    # R % N
+    assert recv(*b(cn=None)) == ep.EP_ERR_ARG
+    assert recv(*b(sidx=None)) == ep.EP_ERR_ARG              # rank view needs staged ids
+    assert recv(*b(H=12)) == ep.EP_ERR_ALIGN
+    assert recv(*b(rx=MIS)) == ep.EP_ERR_ALIGN
+
+
+def test_combine_send_recv_validation(lib):
+    send = lib.ep_combine_send
+    a = lambda H=64, R=4, N=2, st=A16, ns=A16, part=A16: (part, 10, A16, 10, H, R, N, ns, 10, st,
+                                                          A16, None)
+    assert send(*a(N=3)) == ep.EP_ERR_ARG
+    assert send(*a(ns=None)) == ep.EP_ERR_ARG
+    assert send(*a(st=P(0x10008))) == ep.EP_ERR_ALIGN
+    assert send(*a(H=20)) == ep.EP_ERR_ALIGN
+    assert send(*a(part=MIS)) == ep.EP_ERR_ALIGN
+    recv = lib.ep_combine_recv
+    assert recv(A16, 2, 2**31, A16, 10, 64, A16, None, None) == ep.EP_ERR_ARG   # N * Tmax
+    assert recv(A16, 0, 10, A16, 10, 64, A16, None, None) == ep.EP_ERR_ARG
+    assert recv(A16, 2, 10, A16, 10, 64, MIS, None, None) == ep.EP_ERR_ALIGN
+    assert recv(None, 2, 10, A16, 10, 64, A16, None, None) == ep.EP_ERR_ARG
 
 
 def test_copy_validation(lib):

@@ -1,0 +1,184 @@
+"""GPU parity of the two-phase ("hook") dispatch and combine through the C ABI.
+
+Send phase: the per-node staging buffers equal the oracle's send phase bit for bit, rows
+past each node's count untouched. Receive phase: the receive rows equal the one-call
+dispatch oracle bit for bit (the two phases together are the dispatch). Combine: the
+staged per-node sums and the final rows equal the oracle's two-phase combine bit for bit
+(same summation order on both sides).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_get_03_amd import workloads as W
+from combine_ep_get_03_amd.pipeline import DeviceBatch, Path
+
+from gpu_util import SENT_I64, SENT_U16, SENT_U32, host
+
+pytestmark = pytest.mark.gpu
+
+I16 = int(np.uint16(SENT_U16).view(np.int16))
+I32 = int(np.uint32(SENT_U32).view(np.int32))
+
+
+def setup(cfg, seed_shift=0):
+    inp = W.make_inputs(cfg)
+    b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials)
+    path = Path(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax, node_slots=True)
+    path.layout(b)
+    path._hook_buffers()
+    fill(path)
+    return inp, b, path
+
+
+def fill(path):
+    st, r = path.stage, path.recv
+    st.stage_x.view(torch.int16).fill_(I16)
+    st.stage_topk_idx.fill_(SENT_I64)
+    st.stage_topk_weights.view(torch.int32).fill_(I32)
+    st.stage_src.fill_(-7)
+    r.recv_x.view(torch.int16).fill_(I16)
+    r.recv_topk_idx.fill_(SENT_I64)
+    r.recv_topk_weights.view(torch.int32).fill_(I32)
+    r.recv_src_idx.fill_(-7)
+    path.out.view(torch.int16).fill_(I16)
+
+
+def oracle_refs(cfg, inp):
+    lay = oracle.layout(inp.topk_idx, cfg.E, cfg.R, cfg.N)
+    ns = oracle.node_slots(inp.topk_idx, cfg.E, cfg.R, cfg.N)
+    st = oracle.hook_dispatch_send(inp.x, inp.topk_idx, inp.topk_weights, ns, cfg.Tmax, out=dict(
+        stage_x=np.full((cfg.N, cfg.Tmax, cfg.H), SENT_U16, np.uint16),
+        stage_idx=np.full((cfg.N, cfg.Tmax, cfg.k), SENT_I64, np.int64),
+        stage_w=np.full((cfg.N, cfg.Tmax, cfg.k), SENT_U32, np.uint32).view(np.float32),
+        stage_src=np.full((cfg.N, cfg.Tmax), -7, np.int32)))
+    d = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, cfg.E, cfg.R, lay["token_slot"],
+                        cfg.cap)
+    return lay, ns, st, d
+
+
+def check_dispatch(cfg, inp, path, refs):
+    lay, ns, st, d = refs
+    M = int(lay["rank_offset"][-1])
+    S = path.stage
+    np.testing.assert_array_equal(host(S.stage_x), st["stage_x"])
+    np.testing.assert_array_equal(host(S.stage_topk_idx), st["stage_idx"])
+    np.testing.assert_array_equal(host(S.stage_topk_weights).view(np.uint32),
+                                  st["stage_w"].view(np.uint32))
+    np.testing.assert_array_equal(host(S.stage_src), st["stage_src"])
+    r = path.recv
+    rx = host(r.recv_x)
+    np.testing.assert_array_equal(rx[:M], d["recv_x"][:M])
+    assert np.all(rx[M:] == SENT_U16)
+    np.testing.assert_array_equal(host(r.recv_topk_idx)[:M], d["recv_idx"][:M])
+    np.testing.assert_array_equal(host(r.recv_topk_weights)[:M].view(np.uint32),
+                                  d["recv_w"][:M].view(np.uint32))
+    np.testing.assert_array_equal(host(r.recv_src_idx)[:M], d["recv_src"][:M])
+    assert np.all(host(r.recv_src_idx)[M:] == -7)
+
+
+def check_combine(cfg, inp, path, refs):
+    lay, ns, _, d = refs
+    M = int(lay["rank_offset"][-1])
+    partial = d["recv_x"][:M] if inp.partials is None else inp.partials
+    want_stage = oracle.hook_combine_send(partial, lay["token_slot"], cfg.R, ns, cfg.Tmax,
+                                          out=np.full((cfg.N, cfg.Tmax, cfg.H), SENT_U16, np.uint16))
+    np.testing.assert_array_equal(host(path.stage.stage_x), want_stage)
+    np.testing.assert_array_equal(host(path.out), oracle.hook_combine_recv(want_stage, ns))
+
+
+CONFIGS = ["tiny", "restripe", "dsv3", "skewed", "large"]
+EDGE = [
+    W.Config("h_ragged", T=333, H=200, E=24, k=5, R=6, N=3, P=4, Tmax=400),
+    W.Config("h_n1", T=257, H=64, E=32, k=4, R=8, N=1, P=4, Tmax=300),
+    W.Config("h_r_eq_n", T=300, H=136, E=64, k=6, R=16, N=16, P=4, Tmax=300),
+    W.Config("h_wide_node", T=200, H=512, E=2048, k=16, R=1024, N=8, P=4, Tmax=256),
+    W.Config("h_h8192", T=100, H=8192, E=64, k=8, R=16, N=4, P=4, Tmax=100),
+    W.Config("h_one", T=1, H=8, E=8, k=2, R=4, N=2, P=4, Tmax=1),
+]
+
+
+@pytest.mark.parametrize("cfg", [W.CONFIGS[n] for n in CONFIGS] + EDGE, ids=lambda c: c.name)
+def test_hook_dispatch_and_combine(cfg):
+    print(f"\ncase: hook dispatch/combine {cfg}", flush=True)
+    inp, b, path = setup(cfg)
+    refs = oracle_refs(cfg, inp)
+    hook = path.dispatch_send(b)
+    torch.cuda.synchronize()
+    hook()
+    torch.cuda.synchronize()
+    check_dispatch(cfg, inp, path, refs)
+    # the combine's send phase reuses stage_x
+    chook = path.combine_send(b)
+    chook()
+    torch.cuda.synchronize()
+    assert int(host(path.error_flag)[0]) == 0
+    check_combine(cfg, inp, path, refs)
+
+
+def test_recv_hook_on_another_stream_overlapping_a_gemm():
+    cfg = W.CONFIGS["dsv3"]
+    print(f"\ncase: hook overlap {cfg}", flush=True)
+    inp, b, path = setup(cfg)
+    refs = oracle_refs(cfg, inp)
+    a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    w = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    comm, comp = torch.cuda.Stream(), torch.cuda.Stream()
+    comm.wait_stream(torch.cuda.current_stream())
+    comp.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(comm):
+        hook = path.dispatch_send(b, stream=comm)
+    with torch.cuda.stream(comp):
+        c = a @ w
+    comp.wait_stream(comm)
+    hook(stream=comp)            # receive phase on the compute stream, after the GEMM
+    torch.cuda.synchronize()
+    check_dispatch(cfg, inp, path, refs)
+    ref = (a[:64].float() @ w.float()).to(torch.bfloat16)
+    assert torch.allclose(c[:64].float(), ref.float(), rtol=2e-2, atol=2.0)
+
+
+def test_hook_graph_replays_match_eager():
+    cfg = W.CONFIGS["tiny"]
+    print(f"\ncase: hook graph {cfg}", flush=True)
+    inp, b, path = setup(cfg)
+    refs = oracle_refs(cfg, inp)
+
+    def two_phase():
+        path.layout(b)
+        path.dispatch_send(b)()
+
+    two_phase()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        two_phase()
+    for _ in range(3):
+        fill(path)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_dispatch(cfg, inp, path, refs)
+
+
+def test_bad_staged_token_and_count_are_flagged():
+    cfg = W.CONFIGS["tiny"]
+    print(f"\ncase: hook bad staged data {cfg}", flush=True)
+    inp, b, path = setup(cfg)
+    path.dispatch_send(b)
+    torch.cuda.synchronize()
+    path.error_flag.zero_()
+    path.stage.stage_src[0, 0] = cfg.T + 5      # a token id outside the batch: skipped
+    hook_cn = path.layout_buf.num_tokens_per_node.clone()
+    path.layout_buf.num_tokens_per_node[1] = cfg.T + 100   # more rows than a node can hold
+    import combine_ep_get_03_amd as ep
+    st, r, lb = path.stage, path.recv, path.layout_buf
+    ep.ep_dispatch_recv(st.stage_x, st.stage_topk_idx, st.stage_topk_weights, st.stage_src,
+                        lb.num_tokens_per_node, cfg.E, cfg.R, lb.token_slot, recv_x=r.recv_x,
+                        recv_topk_idx=r.recv_topk_idx, recv_topk_weights=r.recv_topk_weights,
+                        recv_src_idx=r.recv_src_idx, error_flag=path.error_flag)
+    torch.cuda.synchronize()
+    flag = int(host(path.error_flag)[0])
+    assert flag & ep.EP_DEVERR_SLOT_RANGE and flag & ep.EP_DEVERR_RECV_OVERFLOW
+    lb.num_tokens_per_node.copy_(hook_cn)
