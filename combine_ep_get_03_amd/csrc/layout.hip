@@ -639,76 +639,72 @@ __global__ __launch_bounds__(kBT) void layout_slot_kernel(
 }
 
 // Expert-major row of every (token, slot) of one 256-token block: the block's base for
-// the expert (from the slot launch) plus the number of earlier pairs of the block naming
-// the same expert, in (token, slot) order. Equal experts are found without sorting:
-// per wave and slot, one ballot per expert-id bit (and one of validity) is parked in
-// LDS; a lane matches its expert against another lane's by combining those ballots.
+// the expert (left in the workspace by the slot launch) plus the number of earlier pairs
+// of the block naming the same expert, in (token, slot) order. A stable ranking without
+// a sort: wave w owns the block's tokens [64w, 64w + 64), i.e. its 64k pairs in (token,
+// slot) order, and walks them in k rounds of 64 consecutive pairs, lane l holding pair
+// 64r + l, so rounds in order are the sort order. In a round, lanes naming the same
+// expert are matched with one ballot per id bit; a lane's rank is the count of its
+// matching lanes below it plus the wave's running count for the expert (LDS), which the
+// highest matching lane then advances. After a barrier the earlier waves' totals for the
+// expert are added.
 __global__ __launch_bounds__(kBT) void layout_expert_slot_kernel(
     const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int nbits,
     const int32_t* __restrict__ blk_exp_base, int32_t* __restrict__ expert_slot) {
     constexpr int kK = kExpertSlotMaxK;
-    constexpr int kBits = 14;  // 1 validity + up to 13 id bits (E <= 8192)
-    __shared__ uint64_t s_key[kWavesBT][kK][kBits];
+    extern __shared__ uint16_t s_run[];  // [kWavesBT][E], running count per wave and expert
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
     const int64_t b = blockIdx.x;
-    const int64_t t = b * kBT + tid;
+    for (int i = tid; i < kWavesBT * E; i += kBT) s_run[i] = 0;
+    __syncthreads();
 
+    const int64_t t0 = b * kBT + static_cast<int64_t>(wave) * kWave;  // the wave's first token
+    const int64_t npairs = max<int64_t>(0, min<int64_t>(kWave, T - t0)) * k;
+    const int64_t* ids = topk_idx + t0 * k;
+    uint16_t* run = s_run + wave * E;
     int key[kK];
+    int loc[kK];
+    int64_t e_in[kK];
 #pragma unroll
-    for (int j = 0; j < kK; ++j) {
-        int64_t e = -1;
-        if (j < k && t < T) e = topk_idx[t * k + j];
-        key[j] = (e >= 0 && e < E) ? static_cast<int>(e) : -1;
+    for (int r = 0; r < kK; ++r) {  // all loads first, in flight together
+        const int p = r * kWave + lane;
+        e_in[r] = (r < k && p < npairs) ? ids[p] : -1;
     }
 #pragma unroll
-    for (int j = 0; j < kK; ++j) {
-        if (j < k) {
-            const uint64_t valid = wave_ballot(key[j] >= 0);
-            if (lane == 0) s_key[wave][j][0] = valid;
+    for (int r = 0; r < kK; ++r) {
+        key[r] = -1;
+        loc[r] = 0;
+        if (r < k) {
+            const int64_t e = e_in[r];
+            const int kr = (e >= 0 && e < E) ? static_cast<int>(e) : -1;
+            uint64_t peers = wave_ballot(kr >= 0);
             for (int bit = 0; bit < nbits; ++bit) {
-                const uint64_t m = wave_ballot(key[j] >= 0 && ((key[j] >> bit) & 1));
-                if (lane == 0) s_key[wave][j][1 + bit] = m;
+                const bool on = kr >= 0 && ((kr >> bit) & 1);
+                const uint64_t m = wave_ballot(on);
+                peers &= on ? m : ~m;
             }
+            if (kr >= 0) {
+                const int before = __popcll(peers & ((1ull << lane) - 1ull));
+                const int cur = run[kr];
+                loc[r] = cur + before;
+                if ((peers >> lane) == 1ull) run[kr] = static_cast<uint16_t>(cur + __popcll(peers));
+            }
+            key[r] = kr;
         }
     }
     __syncthreads();
-
-    const uint64_t below = (1ull << lane) - 1ull;
-    int rank[kK];
 #pragma unroll
-    for (int j = 0; j < kK; ++j) rank[j] = 0;
-    for (int w = 0; w <= wave; ++w) {
-        const uint64_t lane_mask = w < wave ? ~0ull : below;
-        for (int j2 = 0; j2 < k; ++j2) {
-            uint64_t bits[kBits];
-#pragma unroll
-            for (int i = 0; i < kBits; ++i) bits[i] = i <= nbits ? s_key[w][j2][i] : 0ull;
-            bits[0] &= lane_mask;
-#pragma unroll
-            for (int j = 0; j < kK; ++j) {
-                if (j < k && key[j] >= 0) {
-                    uint64_t peers = bits[0];
-#pragma unroll
-                    for (int bit = 0; bit < kBits - 1; ++bit)
-                        if (bit < nbits)
-                            peers &= ((key[j] >> bit) & 1) ? bits[1 + bit] : ~bits[1 + bit];
-                    rank[j] += __popcll(peers);
-                }
+    for (int r = 0; r < kK; ++r) {
+        const int p = r * kWave + lane;
+        if (r < k && p < npairs) {
+            int slot = -1;
+            if (key[r] >= 0) {
+                slot = blk_exp_base[b * E + key[r]] + loc[r];
+                for (int w = 0; w < wave; ++w) slot += s_run[w * E + key[r]];
             }
-        }
-    }
-    if (t >= T) return;
-#pragma unroll
-    for (int j = 0; j < kK; ++j) {
-        if (j < k) {
-            int same = 0;
-#pragma unroll
-            for (int j2 = 0; j2 < kK; ++j2)
-                if (j2 < j && key[j2] == key[j]) ++same;
-            expert_slot[t * k + j] =
-                key[j] >= 0 ? blk_exp_base[b * E + key[j]] + rank[j] + same : -1;
+            expert_slot[t0 * k + p] = slot;
         }
     }
 }
@@ -761,7 +757,8 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
         int nbits = 0;
         while ((1 << nbits) < E) ++nbits;
         hipLaunchKernelGGL(layout_expert_slot_kernel, dim3(static_cast<unsigned>(nb)), dim3(kBT),
-                           0, stream, topk_idx, T, k, E, nbits, ws.blk_exp_base, expert_slot);
+                           sizeof(uint16_t) * kWavesBT * E, stream, topk_idx, T, k, E, nbits,
+                           ws.blk_exp_base, expert_slot);
     }
     return hipGetLastError();
 }
