@@ -83,7 +83,7 @@ __device__ __forceinline__ u32x4 sum_rows(const u32x4* __restrict__ partial,
 // g * obase + out_slot[t][g] of out when out_slot[t][g] >= 0 (the two-phase combine's
 // send phase: one sum per node of the token).
 template <bool kGrouped>
-__global__ __launch_bounds__(kCT) void combine_kernel(
+__device__ __forceinline__ void combine_body(
     const u32x4* __restrict__ partial, int64_t rows, const int32_t* __restrict__ slot_tab,
     int C, int64_t cbase, int64_t T, int V, u32x4* __restrict__ out,
     const int32_t* __restrict__ out_slot, int G, int64_t obase,
@@ -166,6 +166,21 @@ __global__ __launch_bounds__(kCT) void combine_kernel(
     if (errbits) raise_error(error_flag, errbits);
 }
 
+// One kernel name per call, so traces and counters tell them apart.
+#define EP_COMBINE_KERNEL(NAME, GROUPED)                                                       \
+    __global__ __launch_bounds__(kCT) void NAME(                                             \
+        const u32x4* __restrict__ partial, int64_t rows, const int32_t* __restrict__ slot_tab, \
+        int C, int64_t cbase, int64_t T, int V, u32x4* __restrict__ out,                     \
+        const int32_t* __restrict__ out_slot, int G, int64_t obase,                          \
+        int32_t* __restrict__ error_flag, int tpb) {                                          \
+        combine_body<GROUPED>(partial, rows, slot_tab, C, cbase, T, V, out, out_slot, G, obase, \
+                              error_flag, tpb);                                               \
+    }
+EP_COMBINE_KERNEL(combine_kernel, false)       // ep_combine
+EP_COMBINE_KERNEL(combine_send_kernel, true)   // ep_combine_send
+EP_COMBINE_KERNEL(combine_recv_kernel, false)  // ep_combine_recv
+#undef EP_COMBINE_KERNEL
+
 }  // namespace
 
 // Tokens per block: enough words for about kCBlockWords outputs, and LDS lists within
@@ -175,11 +190,11 @@ static int combine_tokens_per_block(int V, int lds_ints_per_token) {
     return std::max(1, std::min(tpb, 8192 / lds_ints_per_token));
 }
 
-template <bool kGrouped>
-static hipError_t launch_combine_impl(const void* partial, int64_t rows, const int32_t* slot_tab, int C,
-                               int64_t cbase, int64_t T, int H, void* out,
-                               const int32_t* out_slot, int G, int64_t obase,
-                               int32_t* error_flag, hipStream_t stream) {
+template <bool kGrouped, typename Kernel>
+static hipError_t launch_combine_impl(Kernel kernel, const void* partial, int64_t rows,
+                                      const int32_t* slot_tab, int C, int64_t cbase, int64_t T,
+                                      int H, void* out, const int32_t* out_slot, int G,
+                                      int64_t obase, int32_t* error_flag, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
     const int per_token = C + (kGrouped ? 2 * G + 1 : 1);
@@ -188,7 +203,7 @@ static hipError_t launch_combine_impl(const void* partial, int64_t rows, const i
     const int64_t grid = kCGridCap > 0 ? std::min<int64_t>(groups, kCGridCap) : groups;
     if (!grid_fits(grid, kCT)) return hipErrorInvalidConfiguration;
     const size_t shm = sizeof(int32_t) * static_cast<size_t>(tpb) * per_token;
-    hipLaunchKernelGGL(combine_kernel<kGrouped>, dim3(static_cast<unsigned>(grid)), dim3(kCT),
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kCT),
                        shm, stream, static_cast<const u32x4*>(partial), rows, slot_tab, C, cbase,
                        T, V, static_cast<u32x4*>(out), out_slot, G, obase, error_flag, tpb);
     return hipGetLastError();
@@ -197,23 +212,24 @@ static hipError_t launch_combine_impl(const void* partial, int64_t rows, const i
 hipError_t launch_combine(const void* partial, int64_t rows, const int32_t* token_slot,
                           int64_t T, int H, int R, void* out, int32_t* error_flag,
                           hipStream_t stream) {
-    return launch_combine_impl<false>(partial, rows, token_slot, R, 0, T, H, out, nullptr, 1, 0,
-                                      error_flag, stream);
+    return launch_combine_impl<false>(combine_kernel, partial, rows, token_slot, R, 0, T, H, out,
+                                      nullptr, 1, 0, error_flag, stream);
 }
 
 hipError_t launch_combine_send(const void* partial, int64_t rows, const int32_t* token_slot,
                                int64_t T, int H, int R, int N, const int32_t* node_slot,
                                int64_t Tmax, void* stage, int32_t* error_flag,
                                hipStream_t stream) {
-    return launch_combine_impl<true>(partial, rows, token_slot, R, 0, T, H, stage, node_slot, N,
-                                     Tmax, error_flag, stream);
+    return launch_combine_impl<true>(combine_send_kernel, partial, rows, token_slot, R, 0, T, H,
+                                     stage, node_slot, N, Tmax, error_flag, stream);
 }
 
 hipError_t launch_combine_recv(const void* stage, int N, int64_t Tmax, const int32_t* node_slot,
                                int64_t T, int H, void* out, int32_t* error_flag,
                                hipStream_t stream) {
-    return launch_combine_impl<false>(stage, static_cast<int64_t>(N) * Tmax, node_slot, N, Tmax,
-                                      T, H, out, nullptr, 1, 0, error_flag, stream);
+    return launch_combine_impl<false>(combine_recv_kernel, stage, static_cast<int64_t>(N) * Tmax,
+                                      node_slot, N, Tmax, T, H, out, nullptr, 1, 0, error_flag,
+                                      stream);
 }
 
 }  // namespace ep
