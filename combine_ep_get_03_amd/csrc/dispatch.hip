@@ -45,29 +45,85 @@ __device__ __forceinline__ void store_row_word(u32x4* p, u32x4 v) {
 #endif
 }
 
-// The walk shared by the bf16 dispatch kernels: the calling wave moves one source row,
-// and its k-slot routing, to every destination named by a row of C slots. Slot c, when
-// >= 0, names row slot + c * cbase of the destination (a slot >= cap is an overflow and
-// is skipped); destinations are walked in ascending c. With kRankView the routing is
-// written as rank (rank0 + c)'s view: the local expert id and the weight where the
-// expert is on that rank, else -1 and +0.0f. Without it the ids and weights are copied
-// unchanged. idx_row must be non-null when dst_idx or dst_w is.
+// The destination walk of every dispatch kernel. Slot c of the calling wave's row of C
+// slots, when >= 0, names destination row slot + c * cbase (a slot >= cap is an overflow:
+// skipped, and the error bit set). Destinations are found with one ballot per 64 slots
+// and visited in ascending c through readlane, so the row index handed to visit(row, c)
+// is wave-uniform.
+template <typename Visit>
+__device__ __forceinline__ void for_each_destination(const int32_t* __restrict__ srow, int C,
+                                                     int64_t cbase, int64_t cap,
+                                                     int32_t& errbits, Visit&& visit) {
+    const int lane = lane_id();
+    for (int c0 = 0; c0 < C; c0 += kWave) {
+        int32_t s = c0 + lane < C ? srow[c0 + lane] : -1;
+        if (s >= cap) {
+            errbits |= kErrRecvOverflow;
+            s = -1;
+        }
+        uint64_t m = wave_ballot(s >= 0);
+        while (m) {
+            const int src_lane = __builtin_ctzll(m);
+            m &= m - 1;
+            const int cd = c0 + src_lane;
+            visit(static_cast<int64_t>(__builtin_amdgcn_readlane(s, src_lane)) + cd * cbase, cd);
+        }
+    }
+}
+
+// A token's k-slot routing as it travels with its row. Lane j < 64 holds slot j (loaded
+// once); larger k reloads per destination. With kRankView the routing written to row sd
+// is rank `rank`'s view: the local expert id and the weight where the expert is on that
+// rank, else -1 and +0.0f; without it the ids and weights are copied unchanged.
+struct Routing {
+    const int64_t* idx_row;  // [k]; non-null whenever dst_idx or dst_w is
+    const float* w_row;      // [k] or null (weights read as 0)
+    int k;
+    int64_t e0;
+    float w0;
+
+    __device__ __forceinline__ Routing(const int64_t* idx, const float* w, int k_, bool meta)
+        : idx_row(idx), w_row(w), k(k_), e0(-1), w0(0.0f) {
+        const int lane = lane_id();
+        if (meta && lane < k) {
+            e0 = idx_row[lane];
+            if (w_row) w0 = w_row[lane];
+        }
+    }
+
+    template <bool kRankView>
+    __device__ __forceinline__ void write(int64_t sd, int rank, int er, int64_t* dst_idx,
+                                          float* dst_w) const {
+        const int lane = lane_id();
+        for (int j0 = 0; j0 < k; j0 += kWave) {
+            const int j = j0 + lane;
+            if (j >= k) continue;
+            const int64_t e = j0 == 0 ? e0 : idx_row[j];
+            const float wv = j0 == 0 ? w0 : (w_row ? w_row[j] : 0.0f);
+            if (kRankView) {
+                const int64_t lo = static_cast<int64_t>(rank) * er;
+                const bool local = e >= lo && e < lo + er;
+                if (dst_idx) dst_idx[sd * k + j] = local ? e - lo : -1;
+                if (dst_w) dst_w[sd * k + j] = local ? wv : 0.0f;
+            } else {
+                if (dst_idx) dst_idx[sd * k + j] = e;
+                if (dst_w) dst_w[sd * k + j] = wv;
+            }
+        }
+    }
+};
+
+// One source row of V 128-bit words, WPL words per lane in registers per pass, to every
+// destination of the walk, with the routing (rank rank0 + c's view with kRankView) and
+// the source id written once per destination.
 template <int WPL, bool kRankView>
 __device__ __forceinline__ void scatter_row(
-    const u32x4* __restrict__ xr, int V, const int64_t* __restrict__ idx_row,
-    const float* __restrict__ w_row, int k, int er, int32_t src,
+    const u32x4* __restrict__ xr, int V, const Routing& rt, int er, int32_t src,
     const int32_t* __restrict__ srow, int C, int64_t cbase, int rank0, int64_t cap,
     u32x4* __restrict__ dst_x, int64_t* __restrict__ dst_idx, float* __restrict__ dst_w,
     int32_t* __restrict__ dst_src, int32_t& errbits) {
     const int lane = lane_id();
     const bool meta = dst_idx || dst_w;
-    // this lane's top-k slot (k <= 64 in one go; larger k reloads per destination)
-    int64_t e0 = -1;
-    float w0 = 0.0f;
-    if (meta && lane < k) {
-        e0 = idx_row[lane];
-        if (w_row) w0 = w_row[lane];
-    }
     for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
         u32x4 v[WPL];
 #pragma unroll
@@ -75,45 +131,17 @@ __device__ __forceinline__ void scatter_row(
             const int vi = v0 + i * kWave + lane;
             if (vi < V) v[i] = load_stream(xr + vi);
         }
-        for (int c0 = 0; c0 < C; c0 += kWave) {
-            int32_t s = c0 + lane < C ? srow[c0 + lane] : -1;
-            if (s >= cap) {
-                errbits |= kErrRecvOverflow;
-                s = -1;
-            }
-            uint64_t m = wave_ballot(s >= 0);
-            while (m) {
-                const int src_lane = __builtin_ctzll(m);
-                m &= m - 1;
-                const int cd = c0 + src_lane;
-                const int64_t sd = __builtin_amdgcn_readlane(s, src_lane) + cd * cbase;
-                u32x4* row = dst_x + sd * V;
+        for_each_destination(srow, C, cbase, cap, errbits, [&](int64_t sd, int cd) {
+            u32x4* row = dst_x + sd * V;
 #pragma unroll
-                for (int i = 0; i < WPL; ++i) {
-                    const int vi = v0 + i * kWave + lane;
-                    if (vi < V) store_row_word(row + vi, v[i]);
-                }
-                if (v0 != 0) continue;
-                if (meta) {
-                    for (int j0 = 0; j0 < k; j0 += kWave) {
-                        const int j = j0 + lane;
-                        if (j >= k) continue;
-                        const int64_t e = j0 == 0 ? e0 : idx_row[j];
-                        const float wv = j0 == 0 ? w0 : (w_row ? w_row[j] : 0.0f);
-                        if (kRankView) {
-                            const int64_t lo = static_cast<int64_t>(rank0 + cd) * er;
-                            const bool local = e >= lo && e < lo + er;
-                            if (dst_idx) dst_idx[sd * k + j] = local ? e - lo : -1;
-                            if (dst_w) dst_w[sd * k + j] = local ? wv : 0.0f;
-                        } else {
-                            if (dst_idx) dst_idx[sd * k + j] = e;
-                            if (dst_w) dst_w[sd * k + j] = wv;
-                        }
-                    }
-                }
-                if (dst_src && lane == 0) dst_src[sd] = src;
+            for (int i = 0; i < WPL; ++i) {
+                const int vi = v0 + i * kWave + lane;
+                if (vi < V) store_row_word(row + vi, v[i]);
             }
-        }
+            if (v0 != 0) return;
+            if (meta) rt.write<kRankView>(sd, rank0 + cd, er, dst_idx, dst_w);
+            if (dst_src && lane == 0) dst_src[sd] = src;
+        });
     }
 }
 
@@ -127,10 +155,10 @@ __global__ __launch_bounds__(kDT) void dispatch_kernel(
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
     if (t >= T) return;
     int32_t errbits = 0;
-    scatter_row<WPL, true>(x + t * V, V, topk_idx ? topk_idx + t * k : nullptr,
-                           topk_w ? topk_w + t * k : nullptr, k, er, static_cast<int32_t>(t),
-                           token_slot + t * R, R, 0, 0, cap, recv_x, recv_idx, recv_w, recv_src,
-                           errbits);
+    const Routing rt(topk_idx ? topk_idx + t * k : nullptr, topk_w ? topk_w + t * k : nullptr, k,
+                     recv_idx || recv_w);
+    scatter_row<WPL, true>(x + t * V, V, rt, er, static_cast<int32_t>(t), token_slot + t * R, R,
+                           0, 0, cap, recv_x, recv_idx, recv_w, recv_src, errbits);
     if (errbits) raise_error(error_flag, errbits);
 }
 
@@ -148,10 +176,10 @@ __global__ __launch_bounds__(kDT) void dispatch_send_kernel(
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
     if (t >= T) return;
     int32_t errbits = 0;
-    scatter_row<WPL, false>(x + t * V, V, topk_idx ? topk_idx + t * k : nullptr,
-                            topk_w ? topk_w + t * k : nullptr, k, 0, static_cast<int32_t>(t),
-                            node_slot + t * N, N, Tmax, 0, Tmax, stage_x, stage_idx, stage_w,
-                            stage_src, errbits);
+    const Routing rt(topk_idx ? topk_idx + t * k : nullptr, topk_w ? topk_w + t * k : nullptr, k,
+                     stage_idx || stage_w);
+    scatter_row<WPL, false>(x + t * V, V, rt, 0, static_cast<int32_t>(t), node_slot + t * N, N,
+                            Tmax, 0, Tmax, stage_x, stage_idx, stage_w, stage_src, errbits);
     if (errbits) raise_error(error_flag, errbits);
 }
 
@@ -181,10 +209,11 @@ __global__ __launch_bounds__(kDT) void dispatch_recv_kernel(
         if (t < 0 || t >= T) {
             errbits |= kErrSlotRange;
         } else {
-            scatter_row<WPL, true>(stage_x + q * V, V, stage_idx ? stage_idx + q * k : nullptr,
-                                   stage_w ? stage_w + q * k : nullptr, k, er,
-                                   static_cast<int32_t>(t), token_slot + t * R + n * rpn, rpn, 0,
-                                   n * rpn, cap, recv_x, recv_idx, recv_w, recv_src, errbits);
+            const Routing rt(stage_idx ? stage_idx + q * k : nullptr,
+                             stage_w ? stage_w + q * k : nullptr, k, recv_idx || recv_w);
+            scatter_row<WPL, true>(stage_x + q * V, V, rt, er, static_cast<int32_t>(t),
+                                   token_slot + t * R + n * rpn, rpn, 0, n * rpn, cap, recv_x,
+                                   recv_idx, recv_w, recv_src, errbits);
         }
     }
     if (errbits && (s < cnt || s == 0)) raise_error(error_flag, errbits);
@@ -200,7 +229,7 @@ __global__ __launch_bounds__(kDT) void dispatch_recv_kernel(
 template <int WPL>
 __global__ __launch_bounds__(kDT) void dispatch_fp8_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_w, int64_t T, int V, int k, int E, int R, int er,
+    const float* __restrict__ topk_w, int64_t T, int V, int k, int R, int er,
     const int32_t* __restrict__ token_slot, u32x2* __restrict__ recv_codes,
     float* __restrict__ recv_scales, int64_t* __restrict__ recv_idx, float* __restrict__ recv_w,
     int32_t* __restrict__ recv_src, int64_t cap, int32_t* __restrict__ error_flag) {
@@ -209,14 +238,9 @@ __global__ __launch_bounds__(kDT) void dispatch_fp8_kernel(
     if (t >= T) return;
     const int G = V / 16;  // scale groups per row
     const bool meta = recv_idx || recv_w;
-    int64_t e0 = -1;
-    float w0 = 0.0f;
-    if (meta && lane < k) {
-        e0 = topk_idx[t * k + lane];
-        if (topk_w) w0 = topk_w[t * k + lane];
-    }
+    const Routing rt(topk_idx ? topk_idx + t * k : nullptr, topk_w ? topk_w + t * k : nullptr, k,
+                     meta);
     const u32x4* xr = x + t * V;
-    const int32_t* srow = token_slot + t * R;
     int32_t errbits = 0;
 
     for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
@@ -260,54 +284,28 @@ __global__ __launch_bounds__(kDT) void dispatch_fp8_kernel(
                 code[i][1] = static_cast<uint32_t>(packed[1]);
             }
         }
-        for (int r0 = 0; r0 < R; r0 += kWave) {
-            int32_t s = r0 + lane < R ? srow[r0 + lane] : -1;
-            if (s >= cap) {
-                errbits |= kErrRecvOverflow;
-                s = -1;
-            }
-            uint64_t m = wave_ballot(s >= 0);
-            while (m) {
-                const int src_lane = __builtin_ctzll(m);
-                m &= m - 1;
-                const int64_t sd = __builtin_amdgcn_readlane(s, src_lane);
-                const int rd = r0 + src_lane;
-                u32x2* row = recv_codes + sd * V;
-                float* srow_out = recv_scales + sd * G;
+        for_each_destination(token_slot + t * R, R, 0, cap, errbits, [&](int64_t sd, int rd) {
+            u32x2* row = recv_codes + sd * V;
+            float* srow_out = recv_scales + sd * G;
 #pragma unroll
-                for (int i = 0; i < WPL; ++i) {
-                    const int vi = v0 + i * kWave + lane;
-                    if (vi < V) {
-                        __builtin_nontemporal_store(code[i], row + vi);
-                        if ((lane & 15) == 0) srow_out[vi / 16] = scale[i];
-                    }
+            for (int i = 0; i < WPL; ++i) {
+                const int vi = v0 + i * kWave + lane;
+                if (vi < V) {
+                    __builtin_nontemporal_store(code[i], row + vi);
+                    if ((lane & 15) == 0) srow_out[vi / 16] = scale[i];
                 }
-                if (v0 != 0) continue;
-                if (meta) {
-                    for (int j0 = 0; j0 < k; j0 += kWave) {
-                        const int j = j0 + lane;
-                        if (j >= k) continue;
-                        const int64_t e = j0 == 0 ? e0 : topk_idx[t * k + j];
-                        const int64_t lo = static_cast<int64_t>(rd) * er;
-                        const bool local = e >= lo && e < lo + er;
-                        if (recv_idx) recv_idx[sd * k + j] = local ? e - lo : -1;
-                        if (recv_w) {
-                            const float wv = j0 == 0 ? w0 : topk_w[t * k + j];
-                            recv_w[sd * k + j] = local ? wv : 0.0f;
-                        }
-                    }
-                }
-                if (recv_src && lane == 0) recv_src[sd] = static_cast<int32_t>(t);
             }
-        }
+            if (v0 != 0) return;
+            if (meta) rt.write<true>(sd, rd, er, recv_idx, recv_w);
+            if (recv_src && lane == 0) recv_src[sd] = static_cast<int32_t>(t);
+        });
     }
     if (errbits) raise_error(error_flag, errbits);
 }
 
 // Dispatch + permute: the token row goes once to each of its (token, slot) rows in the
 // expert-major order (expert_slot from the layout), with the slot's weight and the
-// source token. Same wave-per-token walk as dispatch; the destinations are the k
-// slots, walked with ballot + readlane.
+// source token. Same wave-per-token walk, over the k expert_slot entries.
 template <int WPL>
 __global__ __launch_bounds__(kDT) void dispatch_permute_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ topk_w, int64_t T, int V, int k,
@@ -326,33 +324,18 @@ __global__ __launch_bounds__(kDT) void dispatch_permute_kernel(
             const int vi = v0 + i * kWave + lane;
             if (vi < V) v[i] = load_stream(xr + vi);
         }
-        for (int j0 = 0; j0 < k; j0 += kWave) {
-            const int j = j0 + lane;
-            int32_t q = j < k ? expert_slot[t * k + j] : -1;
-            if (q >= cap) {
-                errbits |= kErrRecvOverflow;
-                q = -1;
-            }
-            const float wj = (j < k && topk_w) ? topk_w[t * k + j] : 0.0f;
-            uint64_t m = wave_ballot(q >= 0);
-            while (m) {
-                const int src_lane = __builtin_ctzll(m);
-                m &= m - 1;
-                const int64_t qd = __builtin_amdgcn_readlane(q, src_lane);
-                const float wd =
-                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), src_lane));
-                u32x4* row = perm_x + qd * V;
+        for_each_destination(expert_slot + t * k, k, 0, cap, errbits, [&](int64_t qd, int j) {
+            u32x4* row = perm_x + qd * V;
 #pragma unroll
-                for (int i = 0; i < WPL; ++i) {
-                    const int vi = v0 + i * kWave + lane;
-                    if (vi < V) store_row_word(row + vi, v[i]);
-                }
-                if (v0 == 0 && lane == 0) {
-                    if (perm_w) perm_w[qd] = wd;
-                    if (perm_src) perm_src[qd] = static_cast<int32_t>(t);
-                }
+            for (int i = 0; i < WPL; ++i) {
+                const int vi = v0 + i * kWave + lane;
+                if (vi < V) store_row_word(row + vi, v[i]);
             }
-        }
+            if (v0 == 0 && lane == 0) {
+                if (perm_w) perm_w[qd] = topk_w[t * k + j];
+                if (perm_src) perm_src[qd] = static_cast<int32_t>(t);
+            }
+        });
     }
     if (errbits) raise_error(error_flag, errbits);
 }
@@ -397,7 +380,7 @@ hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const flo
     if (!grid_fits(grid, kDT)) return hipErrorInvalidConfiguration;
 #define EP_DISPATCH_FP8_LAUNCH(WPL)                                                             \
     hipLaunchKernelGGL(dispatch_fp8_kernel<WPL>, dim3(static_cast<unsigned>(grid)), dim3(kDT), 0, \
-                       stream, static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, E, R,      \
+                       stream, static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, R,         \
                        E / R, token_slot, static_cast<u32x2*>(recv_codes), recv_scales, recv_idx,  \
                        recv_w, recv_src, cap, error_flag)
     if (V <= kWave) EP_DISPATCH_FP8_LAUNCH(1);

@@ -14,7 +14,7 @@ constexpr int kWave = 64;
 constexpr int kMaxRanks = 1024;    // = EP_MAX_RANKS of the public header
 constexpr int kMaxExperts = 8192;  // = EP_MAX_EXPERTS of the public header
 
-// 32-bit lane id and the number of set bits of `mask` on lanes below this one
+// Lane id (0..63) and the number of set bits of `mask` on lanes below this one
 // (v_mbcnt_lo / v_mbcnt_hi).
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -87,35 +87,21 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R
 
 constexpr int kExpertSlotMaxK = 16;  // top-k limit of the expert-major slot output
 
+// dispatch.hip: one-call dispatch, FP8 dispatch, expert-major permute, and the two
+// phases of the two-phase dispatch
 hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* topk_w,
                            int64_t T, int H, int k, int E, int R, const int32_t* token_slot,
                            void* recv_x, int64_t* recv_idx, float* recv_w, int32_t* recv_src,
                            int64_t cap, int32_t* error_flag, hipStream_t stream);
-
 hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_w,
                                int64_t T, int H, int k, int E, int R, const int32_t* token_slot,
                                void* recv_codes, float* recv_scales, int64_t* recv_idx,
                                float* recv_w, int32_t* recv_src, int64_t cap, int32_t* error_flag,
                                hipStream_t stream);
-
 hipError_t launch_dispatch_permute(const void* x, const float* topk_w, int64_t T, int H, int k,
                                    const int32_t* expert_slot, void* perm_x, float* perm_w,
                                    int32_t* perm_src, int64_t cap, int32_t* error_flag,
                                    hipStream_t stream);
-
-hipError_t launch_restripe(const float* prob, int64_t T, int N, int P, int64_t Tmax, float* out,
-                           hipStream_t stream);
-
-hipError_t launch_combine(const void* partial, int64_t rows, const int32_t* token_slot,
-                          int64_t T, int H, int R, void* out, int32_t* error_flag,
-                          hipStream_t stream);
-hipError_t launch_combine_send(const void* partial, int64_t rows, const int32_t* token_slot,
-                               int64_t T, int H, int R, int N, const int32_t* node_slot,
-                               int64_t Tmax, void* stage, int32_t* error_flag,
-                               hipStream_t stream);
-hipError_t launch_combine_recv(const void* stage, int N, int64_t Tmax, const int32_t* node_slot,
-                               int64_t T, int H, void* out, int32_t* error_flag,
-                               hipStream_t stream);
 hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const float* topk_w,
                                 int64_t T, int H, int k, int N, const int32_t* node_slot,
                                 int64_t Tmax, void* stage_x, int64_t* stage_idx, float* stage_w,
@@ -127,10 +113,26 @@ hipError_t launch_dispatch_recv(const void* stage_x, const int64_t* stage_idx,
                                 int64_t* recv_idx, float* recv_w, int32_t* recv_src, int64_t cap,
                                 int32_t* error_flag, hipStream_t stream);
 
+// restripe.hip: dense and sparse-path restripe of prob
+hipError_t launch_restripe(const float* prob, int64_t T, int N, int P, int64_t Tmax, float* out,
+                           hipStream_t stream);
 hipError_t launch_restripe_sparse(const float* prob, int64_t T, int N, int P,
                                   const int32_t* node_slot, int64_t Tmax, float* out,
                                   int32_t* error_flag, hipStream_t stream);
 
+// combine.hip: one-call combine and the two phases of the two-phase combine
+hipError_t launch_combine(const void* partial, int64_t rows, const int32_t* token_slot,
+                          int64_t T, int H, int R, void* out, int32_t* error_flag,
+                          hipStream_t stream);
+hipError_t launch_combine_send(const void* partial, int64_t rows, const int32_t* token_slot,
+                               int64_t T, int H, int R, int N, const int32_t* node_slot,
+                               int64_t Tmax, void* stage, int32_t* error_flag,
+                               hipStream_t stream);
+hipError_t launch_combine_recv(const void* stage, int N, int64_t Tmax, const int32_t* node_slot,
+                               int64_t T, int H, void* out, int32_t* error_flag,
+                               hipStream_t stream);
+
+// hbm_copy.hip: the copy-bandwidth yardstick
 hipError_t launch_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 }  // namespace ep
