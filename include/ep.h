@@ -17,6 +17,16 @@
  *                     problem" and "Fix");
  *   ep_combine        per token, the sum of its per-rank partial rows in fp32, rounded once
  *                     to bf16.
+ * and, after the same pages, four variants of those steps:
+ *   ep_dispatch_fp8          the dispatch with an e4m3 payload and one fp32 scale per 128
+ *                            channels ("[PR #347]", section 3.2.1 FP8 columns);
+ *   ep_dispatch_permute      the dispatch straight into expert-major rows (with the
+ *                            layout's expert_slot; "[PR #634]", "dispatch+permute");
+ *   ep_restripe_prob_sparse  only routed (token, node) prob slices, packed per node (with
+ *                            the layout's node_slot; "[PR #634]", section "Fix");
+ *   ep_dispatch_send/_recv, ep_combine_send/_recv
+ *                            the two-phase ("hook") form of dispatch and combine
+ *                            ("[PR #347]", sections 2.1, 2.2.2 and 3.3.2).
  *
  * Conventions for every entry point:
  *  - Every array argument is a DEVICE pointer owned by the caller; the library allocates
@@ -27,8 +37,9 @@
  *    nothing has been enqueued. No C++ exception crosses this boundary.
  *  - Simulated topology: expert e lives on rank e / (E/R); rank r lives on node r / (R/N).
  *  - `error_flag` is one int32 in device memory. ep_get_layout overwrites it (0 or
- *    EP_DEVERR_TOPK_RANGE); ep_dispatch and ep_combine OR further EP_DEVERR_* bits into it.
- *    After an error bit is set the affected outputs are as documented per call.
+ *    EP_DEVERR_TOPK_RANGE); every other call ORs further EP_DEVERR_* bits into it (where
+ *    it is nullable, NULL drops them). After an error bit is set the affected outputs are
+ *    as documented per call.
  *  - Calls that share output or workspace memory must not overlap in time.
  */
 #ifndef EP_H
@@ -51,8 +62,12 @@ enum {
 
 /* Bits the kernels OR into *error_flag. */
 #define EP_DEVERR_TOPK_RANGE    1  /* a topk_idx entry < -1 or >= num_experts (entry skipped) */
-#define EP_DEVERR_RECV_OVERFLOW 2  /* ep_dispatch met a slot >= recv_capacity (row skipped) */
-#define EP_DEVERR_SLOT_RANGE    4  /* ep_combine met a slot >= num_partial_rows (skipped) */
+#define EP_DEVERR_RECV_OVERFLOW 2  /* a destination row past its buffer: a slot >= the receive
+                                      capacity, a node slot >= Tmax, a node count above
+                                      min(T, Tmax) (row skipped) */
+#define EP_DEVERR_SLOT_RANGE    4  /* a source row out of range: a slot >= num_partial_rows, a
+                                      staged token outside [0, T), a node slot >= Tmax in
+                                      ep_combine_recv (skipped) */
 
 /* Limits of this implementation. */
 #define EP_MAX_RANKS   1024

@@ -50,6 +50,17 @@ def test_every_declared_symbol_is_exported(lib):
         getattr(lib, n)
 
 
+def test_binding_constants_match_the_header():
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    defines = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (EP_\w+)\s+(-?\d+)", src)}
+    enum = {m.group(1): int(m.group(2)) for m in re.finditer(r"(EP_\w+) = (-?\d+)", src)}
+    for name, value in {**defines, **enum}.items():
+        assert getattr(ep, name) == value, name
+    assert set(defines) >= {"EP_DEVERR_TOPK_RANGE", "EP_DEVERR_RECV_OVERFLOW", "EP_DEVERR_SLOT_RANGE",
+                            "EP_MAX_RANKS", "EP_MAX_EXPERTS", "EP_EXPERT_SLOT_MAX_K"}
+    assert set(enum) == {"EP_OK", "EP_ERR_ARG", "EP_ERR_ALIGN", "EP_ERR_CAPACITY", "EP_ERR_HIP"}
+
+
 def test_status_strings(lib):
     for code in (ep.EP_OK, ep.EP_ERR_ARG, ep.EP_ERR_ALIGN, ep.EP_ERR_CAPACITY, ep.EP_ERR_HIP):
         s = ep.ep_status_string(code)
