@@ -1,0 +1,85 @@
+"""Graph capture of the variant calls: FP8 dispatch, the layout with expert slots and
+the expert-major permute, the layout with node slots and the sparse restripe, captured
+into one HIP graph and replayed three times, with eager work and host synchronisation
+between the replays. Every replay must reproduce the eager outputs bit for bit (no call
+records a memset into the graph)."""
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_get_03_amd as ep
+from combine_ep_get_03_amd import workloads as W
+from combine_ep_get_03_amd.buffers import LayoutBuffers
+from combine_ep_get_03_amd.pipeline import DeviceBatch
+
+pytestmark = pytest.mark.gpu
+
+
+def test_variant_calls_replay_in_a_graph():
+    cfg = W.CONFIGS["tiny"]
+    print(f"\ncase: variant graph {cfg}", flush=True)
+    inp = W.make_inputs(cfg)
+    b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob)
+    T, H, k, E, R, N = cfg.T, cfg.H, cfg.k, cfg.E, cfg.R, cfg.N
+    cap = T * min(k, R)
+    lb = LayoutBuffers.alloc(T, E, R, N, k_expert_slots=k, node_slots=True)
+    dev = dict(device="cuda")
+    outs = dict(
+        codes=torch.empty((cap, H), dtype=torch.uint8, **dev),
+        scales=torch.empty((cap, H // 128), dtype=torch.float32, **dev),
+        ridx=torch.empty((cap, k), dtype=torch.int64, **dev),
+        rw=torch.empty((cap, k), dtype=torch.float32, **dev),
+        rsrc=torch.empty(cap, dtype=torch.int32, **dev),
+        px=torch.empty((T * k, H), dtype=torch.bfloat16, **dev),
+        pw=torch.empty(T * k, dtype=torch.float32, **dev),
+        ps=torch.empty(T * k, dtype=torch.int32, **dev),
+        sp=torch.empty((N, cfg.Tmax, cfg.P), dtype=torch.float32, **dev))
+    layout_outs = [lb.token_slot, lb.expert_slot, lb.node_slot, lb.rank_offset, lb.expert_offset]
+
+    def calls():
+        lb.compute(b.topk_idx, E, R, N)
+        ep.ep_dispatch_fp8(b.x, b.topk_idx, b.topk_weights, E, R, lb.token_slot,
+                           recv_x_fp8=outs["codes"], recv_scales=outs["scales"],
+                           recv_topk_idx=outs["ridx"], recv_topk_weights=outs["rw"],
+                           recv_src_idx=outs["rsrc"], error_flag=lb.error_flag)
+        ep.ep_dispatch_permute(b.x, b.topk_weights, lb.expert_slot, perm_x=outs["px"],
+                               perm_weights=outs["pw"], perm_src_idx=outs["ps"],
+                               error_flag=lb.error_flag)
+        ep.ep_restripe_prob_sparse(b.prob, lb.node_slot, outs["sp"], error_flag=lb.error_flag)
+
+    def fill():
+        for t in list(outs.values()) + layout_outs:
+            t.view(torch.uint8).fill_(0x5A)
+
+    fill()
+    calls()
+    torch.cuda.synchronize()
+    M = int(lb.rank_offset[-1].item())
+    routed = int(lb.num_tokens_per_node.sum().item())
+    # only the elements every call writes are compared
+    written = lambda: [outs["codes"][:M], outs["scales"][:M], outs["ridx"][:M], outs["rw"][:M],
+                       outs["rsrc"][:M], outs["px"], outs["pw"], outs["ps"]] + layout_outs
+    eager = [t.clone() for t in written()]
+    ns = lb.node_slot.cpu().numpy()
+    eager_sp = outs["sp"].clone()
+    assert int(lb.error_flag.item()) == 0 and routed > 0
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        fill()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(written(), eager):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), rep
+        for n in range(N):
+            cnt = int((ns[:, n] >= 0).sum())
+            assert torch.equal(outs["sp"][n, :cnt].view(torch.int32),
+                               eager_sp[n, :cnt].view(torch.int32)), rep
+        assert int(lb.error_flag.item()) == 0
+        # eager work between replays
+        calls()
+        torch.cuda.synchronize()
+    del g
