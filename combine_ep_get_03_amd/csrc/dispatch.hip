@@ -13,8 +13,9 @@
 // each destination row is written as one sequential burst of non-temporal 128-bit
 // stores. No LDS and no block barrier. The work per token is bounded by min(k, R)
 // destinations whatever the skew of the per-rank counts. HBM-write bound.
-// Eight tokens per 512-thread block measured fastest on MI355X (about 5% ahead of four
-// or sixteen per block at the 4096 x 7168 top-8 shape).
+// Block sizes and the pass-loop form are chosen per kernel by measurement (below).
+#include <type_traits>
+
 #include "ep_internal.hpp"
 
 namespace ep {
@@ -23,19 +24,15 @@ namespace {
 #ifndef EP_DISPATCH_NT_STORE
 #define EP_DISPATCH_NT_STORE 1
 #endif
-#ifndef EP_DISPATCH_MAX_WPL
-#define EP_DISPATCH_MAX_WPL 14
-#endif
-#ifndef EP_DISPATCH_FP8_MAX_WPL
-#define EP_DISPATCH_FP8_MAX_WPL 14
-#endif
 
-#ifndef EP_DISPATCH_THREADS
-#define EP_DISPATCH_THREADS 512
-#endif
-
-constexpr int kDT = EP_DISPATCH_THREADS;   // threads per block: one token per wave
-constexpr int kDWaves = kDT / kWave;
+// Launch shapes, one token (or staged row) per wave, chosen by same-box A/B timing on
+// MI355X at the 4096 x 7168 and 16384 x 7168 top-8 shapes: the one-call dispatch, the
+// permute and the send phase run the pass-loop form in 512-thread blocks (the one-pass
+// form ran 4-5% slower for them), the receive phase and the FP8 dispatch the one-pass
+// form in 256-thread blocks (5% faster for the receive phase).
+constexpr int kRowThreads = 512;
+constexpr int kRecvThreads = 256;
+constexpr int kFp8Threads = 256;
 
 __device__ __forceinline__ void store_row_word(u32x4* p, u32x4 v) {
 #if EP_DISPATCH_NT_STORE
@@ -115,8 +112,10 @@ struct Routing {
 
 // One source row of V 128-bit words, WPL words per lane in registers per pass, to every
 // destination of the walk, with the routing (rank rank0 + c's view with kRankView) and
-// the source id written once per destination.
-template <int WPL, bool kRankView>
+// the source id written once per destination. Rows wider than one pass (V > 64 WPL) need
+// kMulti; without it the pass loop is known to run once, which keeps the register count
+// down (96 against 116 VGPRs at WPL = 14).
+template <int WPL, bool kMulti, bool kRankView>
 __device__ __forceinline__ void scatter_row(
     const u32x4* __restrict__ xr, int V, const Routing& rt, int er, int32_t src,
     const int32_t* __restrict__ srow, int C, int64_t cbase, int rank0, int64_t cap,
@@ -142,22 +141,23 @@ __device__ __forceinline__ void scatter_row(
             if (meta) rt.write<kRankView>(sd, rank0 + cd, er, dst_idx, dst_w);
             if (dst_src && lane == 0) dst_src[sd] = src;
         });
+        if constexpr (!kMulti) break;
     }
 }
 
-template <int WPL>
-__global__ __launch_bounds__(kDT) void dispatch_kernel(
+template <int WPL, bool kMulti, int kThreads>
+__global__ __launch_bounds__(kThreads) void dispatch_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, int64_t T, int V, int k, int R, int er,
     const int32_t* __restrict__ token_slot, u32x4* __restrict__ recv_x,
     int64_t* __restrict__ recv_idx, float* __restrict__ recv_w, int32_t* __restrict__ recv_src,
     int64_t cap, int32_t* __restrict__ error_flag) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
     if (t >= T) return;
     int32_t errbits = 0;
     const Routing rt(topk_idx ? topk_idx + t * k : nullptr, topk_w ? topk_w + t * k : nullptr, k,
                      recv_idx || recv_w);
-    scatter_row<WPL, true>(x + t * V, V, rt, er, static_cast<int32_t>(t), token_slot + t * R, R,
+    scatter_row<WPL, kMulti, true>(x + t * V, V, rt, er, static_cast<int32_t>(t), token_slot + t * R, R,
                            0, 0, cap, recv_x, recv_idx, recv_w, recv_src, errbits);
     if (errbits) raise_error(error_flag, errbits);
 }
@@ -166,29 +166,29 @@ __global__ __launch_bounds__(kDT) void dispatch_kernel(
 // phase: each token's row, its k expert ids and weights and its id go once to every
 // node holding one of its experts, at row node_slot[t][n] of node n's block of Tmax rows
 // (the large per-node buffer that holds a whole batch, section 2.2.2).
-template <int WPL>
-__global__ __launch_bounds__(kDT) void dispatch_send_kernel(
+template <int WPL, bool kMulti, int kThreads>
+__global__ __launch_bounds__(kThreads) void dispatch_send_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, int64_t T, int V, int k, int N,
     const int32_t* __restrict__ node_slot, int64_t Tmax, u32x4* __restrict__ stage_x,
     int64_t* __restrict__ stage_idx, float* __restrict__ stage_w, int32_t* __restrict__ stage_src,
     int32_t* __restrict__ error_flag) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
     if (t >= T) return;
     int32_t errbits = 0;
     const Routing rt(topk_idx ? topk_idx + t * k : nullptr, topk_w ? topk_w + t * k : nullptr, k,
                      stage_idx || stage_w);
-    scatter_row<WPL, false>(x + t * V, V, rt, 0, static_cast<int32_t>(t), node_slot + t * N, N,
+    scatter_row<WPL, kMulti, false>(x + t * V, V, rt, 0, static_cast<int32_t>(t), node_slot + t * N, N,
                             Tmax, 0, Tmax, stage_x, stage_idx, stage_w, stage_src, errbits);
     if (errbits) raise_error(error_flag, errbits);
 }
 
 // Receive phase (the intra-node hop, same page, section 3.3.2): block (b, n) owns staged
-// rows [8b, 8b + 8) of node n, one wave each; rows at or past count_n[n] are idle. A
+// rows [W b, W b + W) of node n (W waves per block), one wave each; rows at or past count_n[n] are idle. A
 // staged row goes to every rank of node n with a receive slot for its token, with that
 // rank's view of the staged routing, exactly as the one-call dispatch writes it.
-template <int WPL>
-__global__ __launch_bounds__(kDT) void dispatch_recv_kernel(
+template <int WPL, bool kMulti, int kThreads>
+__global__ __launch_bounds__(kThreads) void dispatch_recv_kernel(
     const u32x4* __restrict__ stage_x, const int64_t* __restrict__ stage_idx,
     const float* __restrict__ stage_w, const int32_t* __restrict__ stage_src,
     const int32_t* __restrict__ count_n, int64_t Tmax, int64_t T, int V, int k, int R, int rpn,
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kDT) void dispatch_recv_kernel(
     int64_t* __restrict__ recv_idx, float* __restrict__ recv_w, int32_t* __restrict__ recv_src,
     int64_t cap, int32_t* __restrict__ error_flag) {
     const int n = blockIdx.y;
-    const int64_t s = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
+    const int64_t s = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
     int64_t cnt = count_n[n];
     int32_t errbits = 0;
     if (cnt < 0 || cnt > Tmax || cnt > T) {
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kDT) void dispatch_recv_kernel(
         } else {
             const Routing rt(stage_idx ? stage_idx + q * k : nullptr,
                              stage_w ? stage_w + q * k : nullptr, k, recv_idx || recv_w);
-            scatter_row<WPL, true>(stage_x + q * V, V, rt, er, static_cast<int32_t>(t),
+            scatter_row<WPL, kMulti, true>(stage_x + q * V, V, rt, er, static_cast<int32_t>(t),
                                    token_slot + t * R + n * rpn, rpn, 0, n * rpn, cap, recv_x,
                                    recv_idx, recv_w, recv_src, errbits);
         }
@@ -219,23 +219,26 @@ __global__ __launch_bounds__(kDT) void dispatch_recv_kernel(
     if (errbits && (s < cnt || s == 0)) raise_error(error_flag, errbits);
 }
 
-// FP8 dispatch: the same walk, but each token is first quantised once, in registers:
-// per group of 128 channels (16 words, i.e. 16 aligned lanes of one load row) the
-// largest |x| is reduced with xor shuffles inside the 16 lanes; scale = amax / 448,
-// codes = e4m3(x * (448 / amax)) through the gfx950 packed fp8 convert (round to
+// FP8 dispatch: the same walk, but each token is first quantised once, in registers.
+// Lane l of a pass owns the word pair (2 pi, 2 pi + 1), pi = 64 * pass + l: 16 channels,
+// whose 16 codes leave as one 128-bit store. A group of 128 channels is 8 pairs, i.e. 8
+// aligned lanes, so its largest |x| is reduced with three xor shuffles; scale = amax /
+// 448, codes = e4m3(x * (448 / amax)) through the gfx950 packed fp8 convert (round to
 // nearest even; the product is clamped to +-448, which only ever removes rounding
-// excess above 448). A lane then owns 8 code bytes per word; each destination row
-// gets the codes as one burst of 64-bit stores and its H/128 scales.
-template <int WPL>
-__global__ __launch_bounds__(kDT) void dispatch_fp8_kernel(
+// excess above 448). Each destination row gets the codes as one burst of 128-bit
+// stores and its H/128 scales (one lane per group). Against one word per lane (64-bit
+// code stores, a 16-lane reduction) this measured 5% faster on MI355X at 4096 x 7168.
+template <int WPP, bool kMulti, int kThreads>
+__global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, int64_t T, int V, int k, int R, int er,
-    const int32_t* __restrict__ token_slot, u32x2* __restrict__ recv_codes,
+    const int32_t* __restrict__ token_slot, u32x4* __restrict__ recv_codes,
     float* __restrict__ recv_scales, int64_t* __restrict__ recv_idx, float* __restrict__ recv_w,
     int32_t* __restrict__ recv_src, int64_t cap, int32_t* __restrict__ error_flag) {
     const int lane = lane_id();
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
     if (t >= T) return;
+    const int P2 = V / 2;  // word pairs per row (V % 16 == 0)
     const int G = V / 16;  // scale groups per row
     const bool meta = recv_idx || recv_w;
     const Routing rt(topk_idx ? topk_idx + t * k : nullptr, topk_w ? topk_w + t * k : nullptr, k,
@@ -243,62 +246,66 @@ __global__ __launch_bounds__(kDT) void dispatch_fp8_kernel(
     const u32x4* xr = x + t * V;
     int32_t errbits = 0;
 
-    for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
-        u32x2 code[WPL];
-        float scale[WPL];
+    for (int p0 = 0; p0 < P2; p0 += kWave * WPP) {
+        u32x4 code[WPP];
+        float scale[WPP];
         {
-            u32x4 v[WPL];
+            u32x4 v[2 * WPP];
 #pragma unroll
-            for (int i = 0; i < WPL; ++i) {
-                const int vi = v0 + i * kWave + lane;
-                if (vi < V) v[i] = load_stream(xr + vi);
+            for (int i = 0; i < WPP; ++i) {
+                const int pi = p0 + i * kWave + lane;
+                if (pi < P2) {
+                    v[2 * i] = load_stream(xr + 2 * pi);
+                    v[2 * i + 1] = load_stream(xr + 2 * pi + 1);
+                }
             }
 #pragma unroll
-            for (int i = 0; i < WPL; ++i) {
-                const int vi = v0 + i * kWave + lane;
-                float f[8];
+            for (int i = 0; i < WPP; ++i) {
+                const int pi = p0 + i * kWave + lane;
+                float f[16];
                 float amax = 0.0f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t wq = vi < V ? v[i][q] : 0u;
-                    f[2 * q] = __uint_as_float(wq << 16);
-                    f[2 * q + 1] = __uint_as_float(wq & 0xffff0000u);
-                    amax = fmaxf(amax, fmaxf(fabsf(f[2 * q]), fabsf(f[2 * q + 1])));
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t wq = pi < P2 ? v[2 * i + h][q] : 0u;
+                        f[8 * h + 2 * q] = __uint_as_float(wq << 16);
+                        f[8 * h + 2 * q + 1] = __uint_as_float(wq & 0xffff0000u);
+                        amax = fmaxf(amax, fmaxf(fabsf(f[8 * h + 2 * q]), fabsf(f[8 * h + 2 * q + 1])));
+                    }
                 }
 #pragma unroll
-                for (int m = 8; m >= 1; m >>= 1)
+                for (int m = 4; m >= 1; m >>= 1)
                     amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
                 const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
                 scale[i] = amax > 0.0f ? amax / 448.0f : 1.0f;
-                int packed[2];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
+                for (int q = 0; q < 4; ++q) {
                     float c[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        c[u] = fminf(fmaxf(f[4 * h + u] * inv, -448.0f), 448.0f);
-                    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-                    packed[h] = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], wd, true);
+                        c[u] = fminf(fmaxf(f[4 * q + u] * inv, -448.0f), 448.0f);
+                    const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+                    code[i][q] = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], wd, true));
                 }
-                code[i][0] = static_cast<uint32_t>(packed[0]);
-                code[i][1] = static_cast<uint32_t>(packed[1]);
             }
         }
         for_each_destination(token_slot + t * R, R, 0, cap, errbits, [&](int64_t sd, int rd) {
-            u32x2* row = recv_codes + sd * V;
+            u32x4* row = recv_codes + sd * P2;
             float* srow_out = recv_scales + sd * G;
 #pragma unroll
-            for (int i = 0; i < WPL; ++i) {
-                const int vi = v0 + i * kWave + lane;
-                if (vi < V) {
-                    __builtin_nontemporal_store(code[i], row + vi);
-                    if ((lane & 15) == 0) srow_out[vi / 16] = scale[i];
+            for (int i = 0; i < WPP; ++i) {
+                const int pi = p0 + i * kWave + lane;
+                if (pi < P2) {
+                    store_stream(row + pi, code[i]);
+                    if ((lane & 7) == 0) srow_out[pi / 8] = scale[i];
                 }
             }
-            if (v0 != 0) return;
+            if (p0 != 0) return;
             if (meta) rt.write<true>(sd, rd, er, recv_idx, recv_w);
             if (recv_src && lane == 0) recv_src[sd] = static_cast<int32_t>(t);
         });
+        if constexpr (!kMulti) break;
     }
     if (errbits) raise_error(error_flag, errbits);
 }
@@ -306,14 +313,14 @@ __global__ __launch_bounds__(kDT) void dispatch_fp8_kernel(
 // Dispatch + permute: the token row goes once to each of its (token, slot) rows in the
 // expert-major order (expert_slot from the layout), with the slot's weight and the
 // source token. Same wave-per-token walk, over the k expert_slot entries.
-template <int WPL>
-__global__ __launch_bounds__(kDT) void dispatch_permute_kernel(
+template <int WPL, bool kMulti, int kThreads>
+__global__ __launch_bounds__(kThreads) void dispatch_permute_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ topk_w, int64_t T, int V, int k,
     const int32_t* __restrict__ expert_slot, u32x4* __restrict__ perm_x,
     float* __restrict__ perm_w, int32_t* __restrict__ perm_src, int64_t cap,
     int32_t* __restrict__ error_flag) {
     const int lane = lane_id();
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kDWaves + threadIdx.x / kWave;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
     if (t >= T) return;
     const u32x4* xr = x + t * V;
     int32_t errbits = 0;
@@ -336,8 +343,24 @@ __global__ __launch_bounds__(kDT) void dispatch_permute_kernel(
                 if (perm_src) perm_src[qd] = static_cast<int32_t>(t);
             }
         });
+        if constexpr (!kMulti) break;
     }
     if (errbits) raise_error(error_flag, errbits);
+}
+
+// Calls f(WPL, kMulti) with the smallest words-per-lane count (1, 2, 4, 7, ..., kMax)
+// whose single pass holds a row of `words`, or with kMax and several passes beyond that.
+// kLoop asks for the pass-loop form at every width.
+template <int kMax, bool kLoop, typename F>
+hipError_t with_row_width(int words, F&& f) {
+    using One = std::integral_constant<bool, kLoop>;
+    if (words <= kWave) f(std::integral_constant<int, 1>{}, One{});
+    else if (words <= 2 * kWave) f(std::integral_constant<int, 2>{}, One{});
+    else if (words <= 4 * kWave) f(std::integral_constant<int, 4>{}, One{});
+    else if (words <= 7 * kWave) f(std::integral_constant<int, 7>{}, One{});
+    else if (kMax > 7 && words <= kMax * kWave) f(std::integral_constant<int, kMax>{}, One{});
+    else f(std::integral_constant<int, kMax>{}, std::true_type{});
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -348,26 +371,17 @@ hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* 
                            int64_t cap, int32_t* error_flag, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    const int64_t grid = (T + kDWaves - 1) / kDWaves;
-    if (!grid_fits(grid, kDT)) return hipErrorInvalidConfiguration;
-#define EP_DISPATCH_LAUNCH(WPL)                                                              \
-    hipLaunchKernelGGL(dispatch_kernel<WPL>, dim3(static_cast<unsigned>(grid)), dim3(kDT), 0, \
-                       stream, static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, R,    \
-                       E / R, token_slot, static_cast<u32x4*>(recv_x), recv_idx, recv_w,       \
-                       recv_src, cap, error_flag)
-    // words per lane: the smallest that holds a row, 14 (a 7168-wide bf16 row) at most
-    if (V <= kWave) EP_DISPATCH_LAUNCH(1);
-    else if (V <= 2 * kWave) EP_DISPATCH_LAUNCH(2);
-    else if (V <= 4 * kWave) EP_DISPATCH_LAUNCH(4);
-    else if (V <= 7 * kWave || EP_DISPATCH_MAX_WPL < 14) EP_DISPATCH_LAUNCH(7);
-    else EP_DISPATCH_LAUNCH(14);
-#undef EP_DISPATCH_LAUNCH
-    return hipGetLastError();
+    constexpr int kThreads = kRowThreads;
+    const int64_t grid = (T + kThreads / kWave - 1) / (kThreads / kWave);
+    if (!grid_fits(grid, kThreads)) return hipErrorInvalidConfiguration;
+    return with_row_width<14, true>(V, [&](auto wpl, auto multi) {
+        hipLaunchKernelGGL((dispatch_kernel<decltype(wpl)::value, decltype(multi)::value, kThreads>),
+                           dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+                           static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, R, E / R,
+                           token_slot, static_cast<u32x4*>(recv_x), recv_idx, recv_w, recv_src,
+                           cap, error_flag);
+    });
 }
-
-}  // namespace ep
-
-namespace ep {
 
 hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_w,
                                int64_t T, int H, int k, int E, int R, const int32_t* token_slot,
@@ -376,25 +390,18 @@ hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const flo
                                hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    const int64_t grid = (T + kDWaves - 1) / kDWaves;
-    if (!grid_fits(grid, kDT)) return hipErrorInvalidConfiguration;
-#define EP_DISPATCH_FP8_LAUNCH(WPL)                                                             \
-    hipLaunchKernelGGL(dispatch_fp8_kernel<WPL>, dim3(static_cast<unsigned>(grid)), dim3(kDT), 0, \
-                       stream, static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, R,         \
-                       E / R, token_slot, static_cast<u32x2*>(recv_codes), recv_scales, recv_idx,  \
-                       recv_w, recv_src, cap, error_flag)
-    if (V <= kWave) EP_DISPATCH_FP8_LAUNCH(1);
-    else if (V <= 2 * kWave) EP_DISPATCH_FP8_LAUNCH(2);
-    else if (V <= 4 * kWave) EP_DISPATCH_FP8_LAUNCH(4);
-    else if (V <= 7 * kWave || EP_DISPATCH_FP8_MAX_WPL < 14) EP_DISPATCH_FP8_LAUNCH(7);
-    else EP_DISPATCH_FP8_LAUNCH(14);
-#undef EP_DISPATCH_FP8_LAUNCH
-    return hipGetLastError();
+    constexpr int kThreads = kFp8Threads;
+    const int64_t grid = (T + kThreads / kWave - 1) / (kThreads / kWave);
+    if (!grid_fits(grid, kThreads)) return hipErrorInvalidConfiguration;
+    // word pairs per lane: 7 covers a 7168-wide row in one pass
+    return with_row_width<7, false>(V / 2, [&](auto wpp, auto multi) {
+        hipLaunchKernelGGL((dispatch_fp8_kernel<decltype(wpp)::value, decltype(multi)::value, kThreads>),
+                           dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+                           static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, R, E / R,
+                           token_slot, static_cast<u32x4*>(recv_codes), recv_scales, recv_idx,
+                           recv_w, recv_src, cap, error_flag);
+    });
 }
-
-}  // namespace ep
-
-namespace ep {
 
 hipError_t launch_dispatch_permute(const void* x, const float* topk_w, int64_t T, int H, int k,
                                    const int32_t* expert_slot, void* perm_x, float* perm_w,
@@ -402,25 +409,16 @@ hipError_t launch_dispatch_permute(const void* x, const float* topk_w, int64_t T
                                    hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    const int64_t grid = (T + kDWaves - 1) / kDWaves;
-    if (!grid_fits(grid, kDT)) return hipErrorInvalidConfiguration;
-#define EP_PERMUTE_LAUNCH(WPL)                                                                 \
-    hipLaunchKernelGGL(dispatch_permute_kernel<WPL>, dim3(static_cast<unsigned>(grid)),         \
-                       dim3(kDT), 0, stream, static_cast<const u32x4*>(x), topk_w, T, V, k,     \
-                       expert_slot, static_cast<u32x4*>(perm_x), perm_w, perm_src, cap,         \
-                       error_flag)
-    if (V <= kWave) EP_PERMUTE_LAUNCH(1);
-    else if (V <= 2 * kWave) EP_PERMUTE_LAUNCH(2);
-    else if (V <= 4 * kWave) EP_PERMUTE_LAUNCH(4);
-    else if (V <= 7 * kWave) EP_PERMUTE_LAUNCH(7);
-    else EP_PERMUTE_LAUNCH(14);
-#undef EP_PERMUTE_LAUNCH
-    return hipGetLastError();
+    constexpr int kThreads = kRowThreads;
+    const int64_t grid = (T + kThreads / kWave - 1) / (kThreads / kWave);
+    if (!grid_fits(grid, kThreads)) return hipErrorInvalidConfiguration;
+    return with_row_width<14, true>(V, [&](auto wpl, auto multi) {
+        hipLaunchKernelGGL((dispatch_permute_kernel<decltype(wpl)::value, decltype(multi)::value, kThreads>),
+                           dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+                           static_cast<const u32x4*>(x), topk_w, T, V, k, expert_slot,
+                           static_cast<u32x4*>(perm_x), perm_w, perm_src, cap, error_flag);
+    });
 }
-
-}  // namespace ep
-
-namespace ep {
 
 hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const float* topk_w,
                                 int64_t T, int H, int k, int N, const int32_t* node_slot,
@@ -428,20 +426,16 @@ hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const fl
                                 int32_t* stage_src, int32_t* error_flag, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    const int64_t grid = (T + kDWaves - 1) / kDWaves;
-    if (!grid_fits(grid, kDT)) return hipErrorInvalidConfiguration;
-#define EP_SEND_LAUNCH(WPL)                                                                    \
-    hipLaunchKernelGGL(dispatch_send_kernel<WPL>, dim3(static_cast<unsigned>(grid)), dim3(kDT), \
-                       0, stream, static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, N,  \
-                       node_slot, Tmax, static_cast<u32x4*>(stage_x), stage_idx, stage_w,      \
-                       stage_src, error_flag)
-    if (V <= kWave) EP_SEND_LAUNCH(1);
-    else if (V <= 2 * kWave) EP_SEND_LAUNCH(2);
-    else if (V <= 4 * kWave) EP_SEND_LAUNCH(4);
-    else if (V <= 7 * kWave) EP_SEND_LAUNCH(7);
-    else EP_SEND_LAUNCH(14);
-#undef EP_SEND_LAUNCH
-    return hipGetLastError();
+    constexpr int kThreads = kRowThreads;
+    const int64_t grid = (T + kThreads / kWave - 1) / (kThreads / kWave);
+    if (!grid_fits(grid, kThreads)) return hipErrorInvalidConfiguration;
+    return with_row_width<14, true>(V, [&](auto wpl, auto multi) {
+        hipLaunchKernelGGL((dispatch_send_kernel<decltype(wpl)::value, decltype(multi)::value, kThreads>),
+                           dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+                           static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, N, node_slot,
+                           Tmax, static_cast<u32x4*>(stage_x), stage_idx, stage_w, stage_src,
+                           error_flag);
+    });
 }
 
 hipError_t launch_dispatch_recv(const void* stage_x, const int64_t* stage_idx,
@@ -453,20 +447,17 @@ hipError_t launch_dispatch_recv(const void* stage_x, const int64_t* stage_idx,
     const int64_t rows = std::min(T, Tmax);  // a node holds at most min(T, Tmax) rows
     if (rows == 0) return hipSuccess;
     const int V = H / 8;
-    const int64_t bx = (rows + kDWaves - 1) / kDWaves;
-    if (!grid_fits(bx * N, kDT) || N > 65535) return hipErrorInvalidConfiguration;
-#define EP_RECV_LAUNCH(WPL)                                                                    \
-    hipLaunchKernelGGL(dispatch_recv_kernel<WPL>, dim3(static_cast<unsigned>(bx), N),          \
-                       dim3(kDT), 0, stream, static_cast<const u32x4*>(stage_x), stage_idx,    \
-                       stage_w, stage_src, count_n, Tmax, T, V, k, R, R / N, E / R, token_slot, \
-                       static_cast<u32x4*>(recv_x), recv_idx, recv_w, recv_src, cap, error_flag)
-    if (V <= kWave) EP_RECV_LAUNCH(1);
-    else if (V <= 2 * kWave) EP_RECV_LAUNCH(2);
-    else if (V <= 4 * kWave) EP_RECV_LAUNCH(4);
-    else if (V <= 7 * kWave) EP_RECV_LAUNCH(7);
-    else EP_RECV_LAUNCH(14);
-#undef EP_RECV_LAUNCH
-    return hipGetLastError();
+    constexpr int kThreads = kRecvThreads;
+    const int64_t bx = (rows + kThreads / kWave - 1) / (kThreads / kWave);
+    if (!grid_fits(bx * N, kThreads) || N > 65535) return hipErrorInvalidConfiguration;
+    return with_row_width<14, false>(V, [&](auto wpl, auto multi) {
+        hipLaunchKernelGGL((dispatch_recv_kernel<decltype(wpl)::value, decltype(multi)::value, kThreads>),
+                           dim3(static_cast<unsigned>(bx), N), dim3(kThreads), 0, stream,
+                           static_cast<const u32x4*>(stage_x), stage_idx, stage_w, stage_src,
+                           count_n, Tmax, T, V, k, R, R / N, E / R, token_slot,
+                           static_cast<u32x4*>(recv_x), recv_idx, recv_w, recv_src, cap,
+                           error_flag);
+    });
 }
 
 }  // namespace ep

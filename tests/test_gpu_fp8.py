@@ -102,6 +102,19 @@ def test_fp8_group_scales_span_range():
     check(x, idx, w, 32, 8, 2)
 
 
+@pytest.mark.parametrize("H", [128, 384, 8192, 10240])
+def test_fp8_row_widths(H):
+    """Rows shorter than one pass of word pairs (128, 384) and rows wider than one pass
+    (8192, 10240 channels: several pair chunks per lane)."""
+    print(f"\ncase: fp8 row width H={H}", flush=True)
+    rng = np.random.default_rng(H)
+    T, E, R, N, k = 150, 64, 16, 4, 6
+    x = W.hidden_rows(rng, T, H)
+    idx = W.routing_uniform(rng, T, E, k)
+    w = W.gate_weights(rng, T, k)
+    check(x, idx, w, E, R, N)
+
+
 def test_fp8_rejects_ragged_hidden():
     x = torch.zeros((4, 1000), dtype=torch.bfloat16, device="cuda")
     idx = torch.zeros((4, 1), dtype=torch.int64, device="cuda")

@@ -182,3 +182,35 @@ def test_bad_staged_token_and_count_are_flagged():
     flag = int(host(path.error_flag)[0])
     assert flag & ep.EP_DEVERR_SLOT_RANGE and flag & ep.EP_DEVERR_RECV_OVERFLOW
     lb.num_tokens_per_node.copy_(hook_cn)
+
+
+def test_staging_smaller_than_the_batch_is_flagged():
+    """Tmax < T: staged rows past Tmax are skipped and flagged; the rows that fit match the
+    oracle's send phase computed with room for the whole batch."""
+    import combine_ep_get_03_amd as ep
+    cfg = W.CONFIGS["tiny"].with_(Tmax=100)
+    print(f"\ncase: hook staging overflow {cfg}", flush=True)
+    inp, b, path = setup(cfg)
+    path.error_flag.zero_()
+    path.dispatch_send(b)
+    torch.cuda.synchronize()
+    assert int(host(path.error_flag)[0]) & ep.EP_DEVERR_RECV_OVERFLOW
+    ns = oracle.node_slots(inp.topk_idx, cfg.E, cfg.R, cfg.N)
+    full = oracle.hook_dispatch_send(inp.x, inp.topk_idx, inp.topk_weights, ns, cfg.T, out=dict(
+        stage_x=np.full((cfg.N, cfg.T, cfg.H), SENT_U16, np.uint16),
+        stage_idx=np.full((cfg.N, cfg.T, cfg.k), SENT_I64, np.int64),
+        stage_w=np.full((cfg.N, cfg.T, cfg.k), SENT_U32, np.uint32).view(np.float32),
+        stage_src=np.full((cfg.N, cfg.T), -7, np.int32)))
+    got_x, got_src = host(path.stage.stage_x), host(path.stage.stage_src)
+    np.testing.assert_array_equal(got_x, full["stage_x"][:, :cfg.Tmax])
+    np.testing.assert_array_equal(got_src, full["stage_src"][:, :cfg.Tmax])
+    # the combine's send phase skips the same rows
+    path.error_flag.zero_()
+    path.stage.stage_x.view(torch.int16).fill_(I16)
+    path.combine_send(b)
+    torch.cuda.synchronize()
+    assert int(host(path.error_flag)[0]) & ep.EP_DEVERR_RECV_OVERFLOW
+    lay = oracle.layout(inp.topk_idx, cfg.E, cfg.R, cfg.N)
+    want = oracle.hook_combine_send(inp.partials, lay["token_slot"], cfg.R, ns, cfg.T,
+                                    out=np.full((cfg.N, cfg.T, cfg.H), SENT_U16, np.uint16))
+    np.testing.assert_array_equal(host(path.stage.stage_x), want[:, :cfg.Tmax])
