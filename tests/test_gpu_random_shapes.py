@@ -1,0 +1,109 @@
+"""Seeded sweep over random topologies: every entry point on each, bit for bit against the
+oracle. The shapes are drawn once from a fixed seed (ranks, nodes, experts per rank,
+top-k, ragged T, hidden sizes, prob widths, Tmax, uniform or Zipf routing), so the sweep
+is the same on every run; they complement the hand-picked configurations with rank
+counts off powers of two, odd top-k and ragged tails."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import combine_ep_get_03_amd as ep
+from combine_ep_get_03_amd import workloads as W
+from combine_ep_get_03_amd.buffers import LayoutBuffers
+from combine_ep_get_03_amd.pipeline import DeviceBatch, Path
+
+from gpu_util import compare_all, fill_sentinels, host, oracle_all
+
+pytestmark = pytest.mark.gpu
+
+
+def draw_shapes(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        N = int(rng.choice([1, 2, 3, 4, 8]))
+        rpn = int(rng.choice([1, 2, 3, 5, 8, 16]))
+        R = N * rpn
+        er = int(rng.choice([1, 2, 3, 4, 8]))
+        E = R * er
+        k = int(rng.integers(1, min(E, 12) + 1))
+        T = int(rng.integers(1, 1500))
+        H = int(rng.choice([8, 64, 128, 200, 384, 1024, 7168 // 4]))
+        P = int(rng.integers(1, 40))
+        Tmax = T + int(rng.integers(0, 50))
+        routing = "zipf" if rng.random() < 0.3 else "uniform"
+        shapes.append(W.Config(f"r{i}_T{T}_H{H}_E{E}_k{k}_R{R}_N{N}", T=T, H=H, E=E, k=k, R=R,
+                               N=N, P=P, Tmax=Tmax, routing=routing, seed=1000 + i))
+    return shapes
+
+
+@pytest.mark.parametrize("cfg", draw_shapes(), ids=lambda c: c.name)
+def test_random_shape_every_call(cfg):
+    print(f"\ncase: random shape {cfg}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = oracle_all(cfg, inp)
+
+    # the four steps
+    b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials)
+    path = Path(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax, node_slots=True)
+    fill_sentinels(path)
+    path.step(b)
+    torch.cuda.synchronize()
+    compare_all(cfg, path, ref)
+
+    # node slots, sparse restripe and the two-phase calls
+    lay = ref["lay"]
+    ns = oracle.node_slots(inp.topk_idx, cfg.E, cfg.R, cfg.N)
+    np.testing.assert_array_equal(host(path.layout_buf.node_slot), ns)
+    sp = torch.full((cfg.N, cfg.Tmax, cfg.P), -1.0, dtype=torch.float32, device="cuda")
+    ep.ep_restripe_prob_sparse(b.prob, path.layout_buf.node_slot, sp, error_flag=path.error_flag)
+    want_sp = oracle.restripe_prob_sparse(inp.prob, ns, cfg.Tmax,
+                                          out=np.full((cfg.N, cfg.Tmax, cfg.P), -1.0, np.float32))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(sp).view(np.uint32), want_sp.view(np.uint32))
+
+    M = ref["M"]
+    hook = path.dispatch_send(b)
+    hook()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(path.recv.recv_x)[:M], ref["d"]["recv_x"][:M])
+    np.testing.assert_array_equal(host(path.recv.recv_topk_idx)[:M], ref["d"]["recv_idx"][:M])
+    np.testing.assert_array_equal(host(path.recv.recv_src_idx)[:M], ref["d"]["recv_src"][:M])
+    chook = path.combine_send(b)
+    chook()
+    torch.cuda.synchronize()
+    stage = oracle.hook_combine_send(inp.partials, lay["token_slot"], cfg.R, ns, cfg.Tmax)
+    np.testing.assert_array_equal(host(path.out), oracle.hook_combine_recv(stage, ns))
+    assert int(host(path.error_flag)[0]) == 0
+
+    # expert-major slots and the permute
+    if cfg.k <= ep.EP_EXPERT_SLOT_MAX_K:
+        lbe = LayoutBuffers.alloc(cfg.T, cfg.E, cfg.R, cfg.N, k_expert_slots=cfg.k)
+        lbe.compute(b.topk_idx, cfg.E, cfg.R, cfg.N)
+        es = oracle.expert_slots(inp.topk_idx, cfg.E)
+        np.testing.assert_array_equal(host(lbe.expert_slot), es)
+        px = torch.empty((cfg.T * cfg.k, cfg.H), dtype=torch.bfloat16, device="cuda")
+        pw = torch.empty(cfg.T * cfg.k, dtype=torch.float32, device="cuda")
+        ps = torch.empty(cfg.T * cfg.k, dtype=torch.int32, device="cuda")
+        ep.ep_dispatch_permute(b.x, b.topk_weights, lbe.expert_slot, perm_x=px, perm_weights=pw,
+                               perm_src_idx=ps, error_flag=lbe.error_flag)
+        torch.cuda.synchronize()
+        want = oracle.dispatch_permute(inp.x, inp.topk_idx, inp.topk_weights, es, cfg.T * cfg.k)
+        n = int((es >= 0).sum())
+        np.testing.assert_array_equal(host(px)[:n], want["perm_x"][:n])
+        np.testing.assert_array_equal(host(pw)[:n].view(np.uint32), want["perm_w"][:n].view(np.uint32))
+        np.testing.assert_array_equal(host(ps)[:n], want["perm_src"][:n])
+
+    # FP8 dispatch where the hidden size allows it
+    if cfg.H % 128 == 0:
+        codes = torch.empty((cfg.cap, cfg.H), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((cfg.cap, cfg.H // 128), dtype=torch.float32, device="cuda")
+        ep.ep_dispatch_fp8(b.x, b.topk_idx, b.topk_weights, cfg.E, cfg.R, path.layout_buf.token_slot,
+                           recv_x_fp8=codes, recv_scales=scales, error_flag=path.error_flag)
+        torch.cuda.synchronize()
+        want = oracle.dispatch_fp8(inp.x, inp.topk_idx, inp.topk_weights, cfg.E, cfg.R,
+                                   lay["token_slot"], cfg.cap)
+        np.testing.assert_array_equal(host(codes)[:M], want["recv_codes"][:M])
+        np.testing.assert_array_equal(host(scales)[:M].view(np.uint32),
+                                      want["recv_scales"][:M].view(np.uint32))
