@@ -149,6 +149,7 @@ def hook_section(torch, cfg, b, args, timed, M: int) -> dict:
         holder["c"] = hp.combine_send(b)
 
     d_send()
+    holder["d"]()
     c_send()
     res = {}
     for n, fn in (("dispatch_send", d_send), ("dispatch_recv", lambda: holder["d"]()),

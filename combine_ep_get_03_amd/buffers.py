@@ -70,7 +70,8 @@ class DispatchBuffers:
 @dataclasses.dataclass
 class StageBuffers:
     """Per-node staging of the two-phase dispatch/combine: Tmax rows per node, the whole
-    batch (staged row (n, s) is row n * Tmax + s)."""
+    batch (staged row (n, s) is row n * Tmax + s). The combine's send phase writes its
+    per-node sums into stage_x, so the dispatch's receive phase must run before it."""
     stage_x: torch.Tensor             # bf16 [N][Tmax][H]: dispatch rows, then combine sums
     stage_topk_idx: torch.Tensor      # int64 [N][Tmax][k]
     stage_topk_weights: torch.Tensor  # fp32 [N][Tmax][k]

@@ -54,6 +54,7 @@ class Path:
         self.prob_dest_major = torch.empty((N, Tmax, P), dtype=torch.float32, device=device)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
         self.stage: Optional[StageBuffers] = None
+        self._dispatch_pending = False  # a dispatch send whose receive hook has not run
 
     @property
     def error_flag(self) -> torch.Tensor:
@@ -103,7 +104,10 @@ class Path:
                            stage_topk_weights=st.stage_topk_weights, stage_src=st.stage_src,
                            error_flag=self.error_flag, stream=stream)
 
+        self._dispatch_pending = True
+
         def recv_hook(stream=None) -> None:
+            self._dispatch_pending = False
             r = self.recv
             B.ep_dispatch_recv(st.stage_x, st.stage_topk_idx, st.stage_topk_weights,
                                st.stage_src, lb.num_tokens_per_node, self.E, self.R,
@@ -114,7 +118,12 @@ class Path:
         return recv_hook
 
     def combine_send(self, b: DeviceBatch, stream=None):
-        """Enqueue the combine's send phase (per-node sums); returns its receive hook."""
+        """Enqueue the combine's send phase (per-node sums); returns its receive hook.
+        The sums reuse the dispatch's staging rows, so a pending dispatch receive hook
+        must have been enqueued first."""
+        if self._dispatch_pending:
+            raise RuntimeError("combine_send would overwrite the staged dispatch rows: run the "
+                               "dispatch receive hook first")
         st, lb = self._hook_buffers(), self.layout_buf
         partial = self.recv.recv_x if b.partials is None else b.partials
         B.ep_combine_send(partial, lb.token_slot, lb.node_slot, stage=st.stage_x,

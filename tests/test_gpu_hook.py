@@ -192,7 +192,7 @@ def test_staging_smaller_than_the_batch_is_flagged():
     print(f"\ncase: hook staging overflow {cfg}", flush=True)
     inp, b, path = setup(cfg)
     path.error_flag.zero_()
-    path.dispatch_send(b)
+    hook = path.dispatch_send(b)
     torch.cuda.synchronize()
     assert int(host(path.error_flag)[0]) & ep.EP_DEVERR_RECV_OVERFLOW
     ns = oracle.node_slots(inp.topk_idx, cfg.E, cfg.R, cfg.N)
@@ -204,6 +204,11 @@ def test_staging_smaller_than_the_batch_is_flagged():
     got_x, got_src = host(path.stage.stage_x), host(path.stage.stage_src)
     np.testing.assert_array_equal(got_x, full["stage_x"][:, :cfg.Tmax])
     np.testing.assert_array_equal(got_src, full["stage_src"][:, :cfg.Tmax])
+    # the receive phase must run before the combine's send phase reuses the staging rows
+    with pytest.raises(RuntimeError):
+        path.combine_send(b)
+    hook()
+    torch.cuda.synchronize()
     # the combine's send phase skips the same rows
     path.error_flag.zero_()
     path.stage.stage_x.view(torch.int16).fill_(I16)
