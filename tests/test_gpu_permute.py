@@ -66,6 +66,7 @@ def test_permute_configs(name):
     (20000, 8, 64, 4, 8, 2),       # three-launch layout
     (8192, 8, 512, 8, 256, 8),     # three-launch layout, wide rank table
     (700, 24, 96, 16, 8, 2),       # largest k for expert slots
+    (300, 8192, 64, 4, 8, 2),      # a row wider than one pass of 14 words per lane
 ])
 def test_permute_shapes(T, H, E, k, R, N):
     print(f"\ncase: permute T={T} H={H} E={E} k={k} R={R} N={N}", flush=True)
