@@ -224,7 +224,6 @@ def main():
               "single-GPU and uses no collectives.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import __graft_entry__

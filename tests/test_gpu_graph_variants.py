@@ -3,7 +3,6 @@ the expert-major permute, the layout with node slots and the sparse restripe, ca
 into one HIP graph and replayed three times, with eager work and host synchronisation
 between the replays. Every replay must reproduce the eager outputs bit for bit (no call
 records a memset into the graph)."""
-import numpy as np
 import pytest
 import torch
 

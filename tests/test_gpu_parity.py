@@ -10,7 +10,7 @@ from combine_ep_get_03_amd import workloads as W
 import combine_ep_get_03_amd as ep
 from combine_ep_get_03_amd.pipeline import DeviceBatch, Path
 
-from gpu_util import (SENT_U16, SENT_U32, compare_all, fill_sentinels, host, oracle_all,
+from gpu_util import (SENT_U32, compare_all, fill_sentinels, host, oracle_all,
                       run_gpu)
 
 pytestmark = pytest.mark.gpu
