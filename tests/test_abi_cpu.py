@@ -210,6 +210,18 @@ def test_copy_validation(lib):
     assert lib.ep_hbm_copy(None, A16, 32, None) == ep.EP_ERR_ARG
 
 
+def test_public_header_is_plain_c():
+    """include/ep.h compiles as strict C11, alone and in the C consumer of the ABI."""
+    for src in ("#include \"ep.h\"\nint main(void) { return ep_status_string(0) == 0; }\n",):
+        subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), "-x", "c", "-"], input=src, text=True,
+                       check=True)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                    "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", os.path.join(ROOT, "oracle"), "-I", "/opt/rocm/include",
+                    os.path.join(ROOT, "tests", "c_abi", "ep_c_smoke.c")], check=True)
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_binding, "_lib", None)
     monkeypatch.setattr(_binding, "LIB_PATH", os.path.join(ROOT, "no_such_libep.so"))
