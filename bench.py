@@ -33,7 +33,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for the baseline")
-    ap.add_argument("--copy-gib", type=float, default=2.0)
+    ap.add_argument("--copy-gib", default="2,4",
+                    help="comma-separated copy sizes in GiB; the best rate is the yardstick")
+    ap.add_argument("--flush-gib", type=float, default=1.0,
+                    help="scratch written before each cold launch (evicts L2 and the 256 MB "
+                         "Infinity Cache)")
     return ap.parse_args()
 
 
@@ -75,15 +79,24 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
-def copy_bandwidth(torch, ep, gib: float):
-    """Best of the library's 128-bit copy kernel and torch's device copy, read+write bytes."""
+def copy_bandwidth(torch, ep, sizes_gib):
+    """The library's 128-bit copy kernel and torch's device copy at each size (all far
+    above the 256 MB Infinity Cache), read+write bytes; the caller takes the best."""
+    res = {}
+    for gib in sizes_gib:
+        res.update(_copy_at(torch, ep, gib))
+    return res
+
+
+def _copy_at(torch, ep, gib: float):
     n = int(gib * (1 << 30)) // 16 * 16
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty(n, dtype=torch.uint8, device="cuda")
     a.fill_(1)
     res = {}
-    for name, fn in (("ep_hbm_copy", lambda: ep.ep_hbm_copy(a, b)),
-                     ("torch_copy", lambda: b.copy_(a))):
+    tag = f"{gib:g}GiB"
+    for name, fn in ((f"ep_hbm_copy_{tag}", lambda: ep.ep_hbm_copy(a, b)),
+                     (f"torch_copy_{tag}", lambda: b.copy_(a))):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -101,14 +114,28 @@ def copy_bandwidth(torch, ep, gib: float):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(cfg, inp, seconds: float) -> dict:
     """The CPU oracle on this host, single thread, whole step on the same batch;
-    repeated until `seconds` of CPU time (at least once)."""
+    repeated until `seconds` of CPU time (at least three times). `value` is taken at the
+    median step time."""
+    import statistics
+
     import oracle
 
-    reps, t_total = 0, 0.0
+    times = []
     M = None
-    while reps == 0 or t_total < seconds:
+    while len(times) < 3 or sum(times) < seconds:
         t0 = time.perf_counter()
         lay = oracle.layout(inp.topk_idx, cfg.E, cfg.R, cfg.N)
         d = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, cfg.E, cfg.R,
@@ -116,18 +143,75 @@ def cpu_baseline(cfg, inp, seconds: float) -> dict:
         oracle.restripe_prob(inp.prob, cfg.Tmax)
         partial = d["recv_x"] if inp.partials is None else inp.partials
         oracle.combine(partial, lay["token_slot"], cfg.R)
-        t_total += time.perf_counter() - t0
-        reps += 1
+        times.append(time.perf_counter() - t0)
         M = int(lay["rank_offset"][-1])
         del d
-    s = t_total / reps
+    s = statistics.median(times)
     return {"value": round(2 * M * cfg.H * 2 / s / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{reps} whole steps (layout+dispatch+restripe+combine) of the "
-                      f"{cfg.name} batch, {s * 1e3:.1f} ms each, single-threaded C oracle "
-                      f"incl. its output allocation; host {platform.processor() or platform.machine()}, "
-                      f"nproc {os.cpu_count()}",
-            "ms_per_step": round(s * 1e3, 2)}
+            "sample": f"{len(times)} whole steps (layout+dispatch+restripe+combine) of the "
+                      f"{cfg.name} batch, median {s * 1e3:.1f} ms each, single-threaded C oracle "
+                      f"incl. its output allocation; host {cpu_model()}, nproc {os.cpu_count()}",
+            "ms_per_step": round(s * 1e3, 2),
+            "ms_per_step_min_max": [round(min(times) * 1e3, 2), round(max(times) * 1e3, 2)],
+            "host_cpu": cpu_model(), "nproc": os.cpu_count()}
+
+
+def launch_distribution(torch, ep, calls: dict, reps: int, flush_gib: float) -> dict:
+    """Time of single launches, `reps` of each call: an event pair around one launch, and
+    before it on the same stream a cushion long enough that the host has queued the events
+    and the launch by the time the GPU reaches them (so host launch cost stays outside the
+    pair). Warm: the cushion is a ~100 us spin that touches no memory, so what the previous
+    launch left in L2 and the Infinity Cache stays there. Cold: the cushion is a copy
+    through `flush_gib` GiB of scratch, which evicts both. Median, p10 and p90 in us; the
+    floor is the same measurement around a 16-byte copy (event and dispatch latency that
+    every single-launch figure includes)."""
+    import numpy as np
+
+    stream = torch.cuda.current_stream()
+    # spin cycles per microsecond of the sleep kernel, measured here
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cyc = 1 << 22
+    torch.cuda._sleep(cyc)
+    s0.record(stream)
+    torch.cuda._sleep(cyc)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    spin = max(1, int(cyc / max(s0.elapsed_time(s1) * 1e3, 1.0) * 100.0))
+    nflush = int(flush_gib * (1 << 30)) // 32 * 16
+    scratch = torch.empty(2 * nflush, dtype=torch.uint8, device="cuda")
+    scratch.fill_(0)
+    tiny = torch.zeros(32, dtype=torch.uint8, device="cuda")
+
+    def cushion(cold):
+        if cold:
+            ep.ep_hbm_copy(scratch[:nflush], scratch[nflush:])
+        else:
+            torch.cuda._sleep(spin)
+
+    def sample(fn, cold):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        fn()
+        torch.cuda.synchronize()
+        for a, b_ in ev:
+            cushion(cold)
+            a.record(stream)
+            fn()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b_) * 1e3 for a, b_ in ev])
+        return {"median_us": round(float(np.median(us)), 2),
+                "p10_us": round(float(np.percentile(us, 10)), 2),
+                "p90_us": round(float(np.percentile(us, 90)), 2)}
+
+    out = {"reps": reps, "flush_bytes": 2 * nflush,
+           "event_floor_us": sample(lambda: ep.ep_hbm_copy(tiny[:16], tiny[16:]), False)["median_us"]}
+    for mode, cold in (("warm", False), ("cold", True)):
+        out[mode] = {n: sample(fn, cold) for n, fn in calls.items()}
+    del scratch, tiny
+    torch.cuda.empty_cache()
+    return out
 
 
 def hook_section(torch, cfg, b, args, timed, M: int) -> dict:
@@ -238,11 +322,13 @@ def main():
     print(f"bench: generating {cfg}", file=sys.stderr, flush=True)
     inp = W.make_inputs(cfg)
     torch.cuda.set_device(0)
+    # every launch and event of the bench goes to one dedicated stream (default priority)
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
     b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials)
     path = Path(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax)
-    stream = torch.cuda.current_stream()
 
-    copy_bw = copy_bandwidth(torch, ep, args.copy_gib)
+    copy_bw = copy_bandwidth(torch, ep, [float(g) for g in args.copy_gib.split(",")])
     print(f"bench: copy bandwidth {copy_bw}", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
@@ -388,6 +474,9 @@ def main():
               "hbm_gbps": round(sb / (res["restripe_sparse"] * 1e-3) / 1e9, 1)}
     del sp_out, lbn
     hook = hook_section(torch, cfg, b, args, timed, M)
+    dist_calls = {n: (lambda fn=fn: fn(b)) for n, fn in zip(names, calls)}
+    dist_calls["step_graph"] = g_step.replay
+    dist = launch_distribution(torch, ep, dist_calls, args.steps, args.flush_gib)
     if int(path.error_flag.item()) != 0:
         raise RuntimeError(f"device error flag {int(path.error_flag.item())}")
 
@@ -439,6 +528,7 @@ def main():
         "restripe_sparse": sparse,
         "hook": hook,
         "kernels": kernels,
+        "launch_distribution": dist,
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
