@@ -77,9 +77,17 @@ def _ptr(t: Optional[torch.Tensor], dtype, name: str, nullable: bool = False):
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    _on_current_device(t, name)
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _on_current_device(t: torch.Tensor, name: str) -> None:
+    """Kernels run on the current device's stream, so every buffer must live there."""
+    cur = torch.cuda.current_device()
+    if t.device.index != cur:
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{cur}")
 
 
 def _shape(t: Optional[torch.Tensor], shape, name: str) -> None:
@@ -100,6 +108,9 @@ def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
     if isinstance(stream, torch.cuda.Stream):
+        cur = torch.cuda.current_device()
+        if stream.device.index != cur:
+            raise ValueError(f"stream is on {stream.device}, but the current device is cuda:{cur}")
         stream = stream.cuda_stream
     return ctypes.c_void_p(int(stream))
 
@@ -365,6 +376,8 @@ def ep_combine_recv(stage, node_slot, *, out, error_flag=None, stream=None) -> N
 def ep_hbm_copy(src, dst, nbytes: Optional[int] = None, stream=None) -> None:
     if not (src.is_cuda and dst.is_cuda):
         raise ValueError("src and dst must be device tensors")
+    _on_current_device(src, "src")
+    _on_current_device(dst, "dst")
     if nbytes is None:
         nbytes = src.numel() * src.element_size()
     if nbytes > src.numel() * src.element_size() or nbytes > dst.numel() * dst.element_size():

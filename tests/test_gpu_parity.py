@@ -209,6 +209,34 @@ def test_abi_rejects_bad_arguments_on_gpu():
     assert e.value.status == ep.EP_ERR_ALIGN
 
 
+def test_binding_rejects_buffers_off_the_current_device(monkeypatch):
+    # kernels run on the current device's stream; a buffer elsewhere is refused before any
+    # launch (a second device is simulated by reporting another current device)
+    cfg = W.CONFIGS["tiny"]
+    print(f"\ncase: off-device buffers {cfg.name}", flush=True)
+    prob = torch.zeros((cfg.T, cfg.N, cfg.P), dtype=torch.float32, device="cuda")
+    out = torch.full((cfg.N, cfg.Tmax, cfg.P), 7.0, dtype=torch.float32, device="cuda")
+    other = torch.cuda.current_device() + 1
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: other)
+    with pytest.raises(ValueError, match="current device"):
+        ep.ep_restripe_prob(prob, out)
+    with pytest.raises(ValueError, match="current device"):
+        ep.ep_hbm_copy(prob, out)
+    monkeypatch.undo()
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())  # nothing was launched
+    with pytest.raises(ValueError, match="current device"):
+        ep.ep_restripe_prob(prob, out, stream=_OtherDeviceStream())
+
+
+class _OtherDeviceStream(torch.cuda.Stream):
+    """A stream object that reports a device other than the current one."""
+
+    @property
+    def device(self):
+        return torch.device("cuda", torch.cuda.current_device() + 1)
+
+
 @pytest.mark.parametrize("name", ["tiny", "dsv3"])
 def test_graph_replay_matches_eager(name):
     """The whole step captured in a HIP graph: every replay, with eager work and
