@@ -304,6 +304,9 @@ def hook_section(torch, cfg, b, args, timed, M: int) -> dict:
 
 def main():
     args = parse()
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is "
               "single-GPU and uses no collectives.", file=sys.stderr)
@@ -332,6 +335,8 @@ def main():
     copy_bw = copy_bandwidth(torch, ep, [float(g) for g in args.copy_gib.split(",")])
     print(f"bench: copy bandwidth {copy_bw}", file=sys.stderr, flush=True)
 
+    # one eager step whose outputs every graph replay is checked against (also with W = 0)
+    path.step(b)
     for _ in range(args.warmup):
         path.step(b)
     torch.cuda.synchronize()

@@ -24,6 +24,12 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
+def test_zero_steps_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--steps" in r.stderr and r.stdout == ""
+
+
 def _nbytes(*arrays):
     return sum(a.nbytes for a in arrays)
 
