@@ -81,6 +81,17 @@ MUTANTS = [
      "sum[h] = 0.0f;\n        for (int n = 1; n < N; ++n) {"),
     ("hook_combine_send_scaled", "stage[q * H + h] = oracle_f32_to_bf16(sum[h]);",
      "stage[q * H + h] = oracle_f32_to_bf16(sum[h] * 1.0078125f);"),
+    ("e4m3_decode_bias_off", "v = ldexpf((float)(8 + m), ef - 7 - 3);",
+     "v = ldexpf((float)(8 + m), ef - 8 - 3);"),
+    ("e4m3_decode_subnormal_scale", "v = ldexpf((float)m, -9);", "v = ldexpf((float)m, -10);"),
+    ("e4m3_saturates_late", "if (a >= 464.0f)", "if (a >= 480.0f)"),
+    ("fp8_amax_signed", "const float a = fabsf(oracle_bf16_to_f32(xg[c]));",
+     "const float a = oracle_bf16_to_f32(xg[c]);"),
+    ("fp8_zero_group_scale", "const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;",
+     "const float scale = amax > 0.0f ? amax / 448.0f : 0.0f;"),
+    ("permute_src_is_row", "perm_src[q] = (int32_t)t;", "perm_src[q] = (int32_t)q;"),
+    ("permute_row_of_next_token", "memcpy(perm_x + q * H, x + t * H, (size_t)H * sizeof(uint16_t));",
+     "memcpy(perm_x + q * H, x + ((t + 1) % T) * H, (size_t)H * sizeof(uint16_t));"),
 ]
 
 # The quick pins (no exhaustive enumeration): enough to kill every mutant above.
