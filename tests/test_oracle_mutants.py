@@ -90,6 +90,15 @@ MUTANTS = [
     ("fp8_zero_group_scale", "const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;",
      "const float scale = amax > 0.0f ? amax / 448.0f : 0.0f;"),
     ("permute_src_is_row", "perm_src[q] = (int32_t)t;", "perm_src[q] = (int32_t)q;"),
+    ("node_slot_counts_unrouted", "node_slot[t * N + n] = on[n] ? filled[n]++ : -1;",
+     "node_slot[t * N + n] = on[n] ? filled[n]++ : (filled[n]++, -1);"),
+    ("node_slot_starts_at_one", "node_slot[t * N + n] = on[n] ? filled[n]++ : -1;",
+     "node_slot[t * N + n] = on[n] ? ++filled[n] : -1;"),
+    ("sparse_restripe_wrong_node_block",
+     "out[((int64_t)n * Tmax + s) * P + p] = prob[(t * N + n) * P + p];",
+     "out[((int64_t)((n + 1) % N) * Tmax + s) * P + p] = prob[(t * N + n) * P + p];"),
+    ("node_count_first_rank_only", "if (row[n * ranks_per_node + q])",
+     "if (row[n * ranks_per_node])"),
     ("permute_row_of_next_token", "memcpy(perm_x + q * H, x + t * H, (size_t)H * sizeof(uint16_t));",
      "memcpy(perm_x + q * H, x + ((t + 1) % T) * H, (size_t)H * sizeof(uint16_t));"),
 ]
