@@ -13,7 +13,11 @@
 // each destination row is written as one sequential burst of non-temporal 128-bit
 // stores. No LDS and no block barrier. The work per token is bounded by min(k, R)
 // destinations whatever the skew of the per-rank counts. HBM-write bound.
+// Batches small enough that the one-token grid would be resident at once take a form
+// with two tokens per wave (dispatch_pair_kernel), which overlaps the second token's
+// loads with the first token's stores.
 // Block sizes and the pass-loop form are chosen per kernel by measurement (below).
+#include <atomic>
 #include <type_traits>
 
 #include "ep_internal.hpp"
@@ -33,6 +37,26 @@ namespace {
 constexpr int kRowThreads = 512;
 constexpr int kRecvThreads = 256;
 constexpr int kFp8Threads = 256;
+constexpr int kPairThreads = 256;  // two tokens per wave (small batches): 256 beat 512
+
+// Token waves the one-token dispatch grid keeps resident at once: 16 per compute unit
+// (two 512-thread blocks at its register use). Below this the grid does not fill the
+// chip, and the two-tokens-per-wave form is faster. Queried per device and cached.
+int resident_token_waves() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];  // zero until first queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int waves = cache[dev].load(std::memory_order_relaxed);
+    if (waves == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        waves = 16 * cus;
+        cache[dev].store(waves, std::memory_order_relaxed);
+    }
+    return waves;
+}
 
 __device__ __forceinline__ void store_row_word(u32x4* p, u32x4 v) {
 #if EP_DISPATCH_NT_STORE
@@ -47,25 +71,30 @@ __device__ __forceinline__ void store_row_word(u32x4* p, u32x4 v) {
 // skipped, and the error bit set). Destinations are found with one ballot per 64 slots
 // and visited in ascending c through readlane, so the row index handed to visit(row, c)
 // is wave-uniform.
+// One chunk of the walk: lane l holds slot c0 + l (-1 where there is none).
+template <typename Visit>
+__device__ __forceinline__ void visit_chunk(int32_t s, int c0, int64_t cbase, int64_t cap,
+                                            int32_t& errbits, Visit&& visit) {
+    if (s >= cap) {
+        errbits |= kErrRecvOverflow;
+        s = -1;
+    }
+    uint64_t m = wave_ballot(s >= 0);
+    while (m) {
+        const int src_lane = __builtin_ctzll(m);
+        m &= m - 1;
+        const int cd = c0 + src_lane;
+        visit(static_cast<int64_t>(__builtin_amdgcn_readlane(s, src_lane)) + cd * cbase, cd);
+    }
+}
+
 template <typename Visit>
 __device__ __forceinline__ void for_each_destination(const int32_t* __restrict__ srow, int C,
                                                      int64_t cbase, int64_t cap,
                                                      int32_t& errbits, Visit&& visit) {
     const int lane = lane_id();
-    for (int c0 = 0; c0 < C; c0 += kWave) {
-        int32_t s = c0 + lane < C ? srow[c0 + lane] : -1;
-        if (s >= cap) {
-            errbits |= kErrRecvOverflow;
-            s = -1;
-        }
-        uint64_t m = wave_ballot(s >= 0);
-        while (m) {
-            const int src_lane = __builtin_ctzll(m);
-            m &= m - 1;
-            const int cd = c0 + src_lane;
-            visit(static_cast<int64_t>(__builtin_amdgcn_readlane(s, src_lane)) + cd * cbase, cd);
-        }
-    }
+    for (int c0 = 0; c0 < C; c0 += kWave)
+        visit_chunk(c0 + lane < C ? srow[c0 + lane] : -1, c0, cbase, cap, errbits, visit);
 }
 
 // A token's k-slot routing as it travels with its row. Lane j < 64 holds slot j (loaded
@@ -115,31 +144,48 @@ struct Routing {
 // the source id written once per destination. Rows wider than one pass (V > 64 WPL) need
 // kMulti; without it the pass loop is known to run once, which keeps the register count
 // down (96 against 116 VGPRs at WPL = 14).
+// One pass of a row (words v0 .. v0 + 64 WPL) into destination row sd; the first pass
+// also writes the rank's view of the routing and the source id.
+template <int WPL, bool kRankView>
+__device__ __forceinline__ void put_row(const u32x4 (&v)[WPL], int v0, int V, int64_t sd,
+                                        int rank, const Routing& rt, int er, int32_t src,
+                                        u32x4* __restrict__ dst_x, int64_t* __restrict__ dst_idx,
+                                        float* __restrict__ dst_w, int32_t* __restrict__ dst_src) {
+    const int lane = lane_id();
+    u32x4* row = dst_x + sd * V;
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) {
+        const int vi = v0 + i * kWave + lane;
+        if (vi < V) store_row_word(row + vi, v[i]);
+    }
+    if (v0 != 0) return;
+    if (dst_idx || dst_w) rt.write<kRankView>(sd, rank, er, dst_idx, dst_w);
+    if (dst_src && lane == 0) dst_src[sd] = src;
+}
+
+template <int WPL>
+__device__ __forceinline__ void load_row(u32x4 (&v)[WPL], const u32x4* __restrict__ xr, int v0,
+                                         int V) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) {
+        const int vi = v0 + i * kWave + lane;
+        if (vi < V) v[i] = load_stream(xr + vi);
+    }
+}
+
 template <int WPL, bool kMulti, bool kRankView>
 __device__ __forceinline__ void scatter_row(
     const u32x4* __restrict__ xr, int V, const Routing& rt, int er, int32_t src,
     const int32_t* __restrict__ srow, int C, int64_t cbase, int rank0, int64_t cap,
     u32x4* __restrict__ dst_x, int64_t* __restrict__ dst_idx, float* __restrict__ dst_w,
     int32_t* __restrict__ dst_src, int32_t& errbits) {
-    const int lane = lane_id();
-    const bool meta = dst_idx || dst_w;
     for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
         u32x4 v[WPL];
-#pragma unroll
-        for (int i = 0; i < WPL; ++i) {
-            const int vi = v0 + i * kWave + lane;
-            if (vi < V) v[i] = load_stream(xr + vi);
-        }
+        load_row(v, xr, v0, V);
         for_each_destination(srow, C, cbase, cap, errbits, [&](int64_t sd, int cd) {
-            u32x4* row = dst_x + sd * V;
-#pragma unroll
-            for (int i = 0; i < WPL; ++i) {
-                const int vi = v0 + i * kWave + lane;
-                if (vi < V) store_row_word(row + vi, v[i]);
-            }
-            if (v0 != 0) return;
-            if (meta) rt.write<kRankView>(sd, rank0 + cd, er, dst_idx, dst_w);
-            if (dst_src && lane == 0) dst_src[sd] = src;
+            put_row<WPL, kRankView>(v, v0, V, sd, rank0 + cd, rt, er, src, dst_x, dst_idx, dst_w,
+                                    dst_src);
         });
         if constexpr (!kMulti) break;
     }
@@ -159,6 +205,52 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
                      recv_idx || recv_w);
     scatter_row<WPL, kMulti, true>(x + t * V, V, rt, er, static_cast<int32_t>(t), token_slot + t * R, R,
                            0, 0, cap, recv_x, recv_idx, recv_w, recv_src, errbits);
+    if (errbits) raise_error(error_flag, errbits);
+}
+
+// The same dispatch for small batches (R <= 64, k <= 64, one pass per row): each wave
+// owns two tokens, t and t + W (W waves in the grid). Token t's row, slot row and routing
+// are loaded first and token t + W's right after, so token t's writes wait only for its
+// own loads and token t + W's loads arrive meanwhile. Used while the one-token grid would
+// be resident at once; on MI355X at 1024, 2048 and 4096 tokens of 7168 channels it ran
+// 16%, 9% and 2% faster than one token per wave, and 2-3% slower at 8192 and 16384.
+template <int WPL, int kThreads>
+__global__ __launch_bounds__(kThreads) void dispatch_pair_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int64_t T, int V, int k, int R, int er,
+    const int32_t* __restrict__ token_slot, u32x4* __restrict__ recv_x,
+    int64_t* __restrict__ recv_idx, float* __restrict__ recv_w, int32_t* __restrict__ recv_src,
+    int64_t cap, int32_t* __restrict__ error_flag) {
+    const int lane = lane_id();
+    const int64_t W = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+    if (t0 >= T) return;
+    const int64_t t1 = t0 + W;
+    const bool has1 = t1 < T;
+    const bool meta = recv_idx || recv_w;
+    u32x4 a[WPL], b[WPL];
+    load_row(a, x + t0 * V, 0, V);
+    const int32_t s0 = lane < R ? token_slot[t0 * R + lane] : -1;
+    const Routing r0(topk_idx ? topk_idx + t0 * k : nullptr, topk_w ? topk_w + t0 * k : nullptr,
+                     k, meta);
+    int32_t s1 = -1;
+    if (has1) {
+        load_row(b, x + t1 * V, 0, V);
+        s1 = lane < R ? token_slot[t1 * R + lane] : -1;
+    }
+    int32_t errbits = 0;
+    visit_chunk(s0, 0, 0, cap, errbits, [&](int64_t sd, int cd) {
+        put_row<WPL, true>(a, 0, V, sd, cd, r0, er, static_cast<int32_t>(t0), recv_x, recv_idx,
+                           recv_w, recv_src);
+    });
+    if (has1) {
+        const Routing r1(topk_idx ? topk_idx + t1 * k : nullptr,
+                         topk_w ? topk_w + t1 * k : nullptr, k, meta);
+        visit_chunk(s1, 0, 0, cap, errbits, [&](int64_t sd, int cd) {
+            put_row<WPL, true>(b, 0, V, sd, cd, r1, er, static_cast<int32_t>(t1), recv_x,
+                               recv_idx, recv_w, recv_src);
+        });
+    }
     if (errbits) raise_error(error_flag, errbits);
 }
 
@@ -371,6 +463,18 @@ hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* 
                            int64_t cap, int32_t* error_flag, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
+    if (V <= 14 * kWave && R <= kWave && k <= kWave && T <= resident_token_waves()) {
+        constexpr int kPT = kPairThreads;
+        const int64_t waves = (T + 1) / 2;
+        const int64_t pgrid = (waves + kPT / kWave - 1) / (kPT / kWave);
+        return with_row_width<14, false>(V, [&](auto wpl, auto) {
+            hipLaunchKernelGGL((dispatch_pair_kernel<decltype(wpl)::value, kPT>),
+                               dim3(static_cast<unsigned>(pgrid)), dim3(kPT), 0, stream,
+                               static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, R, E / R,
+                               token_slot, static_cast<u32x4*>(recv_x), recv_idx, recv_w, recv_src,
+                               cap, error_flag);
+        });
+    }
     constexpr int kThreads = kRowThreads;
     const int64_t grid = (T + kThreads / kWave - 1) / (kThreads / kWave);
     if (!grid_fits(grid, kThreads)) return hipErrorInvalidConfiguration;

@@ -237,6 +237,18 @@ class _OtherDeviceStream(torch.cuda.Stream):
         return torch.device("cuda", torch.cuda.current_device() + 1)
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 4095, 4096, 4097, 8193])
+def test_dispatch_around_the_small_batch_threshold(T):
+    # batches up to 16 waves per compute unit (4096 tokens on 256 CUs) take the
+    # two-tokens-per-wave dispatch, larger ones one token per wave; odd counts leave the
+    # last wave with a single token
+    cfg = W.Config(f"thr_T{T}", T=T, H=512, E=64, k=6, R=16, N=4, P=8, Tmax=T, seed=T)
+    inp = _case(cfg)
+    ref = oracle_all(cfg, inp)
+    path = run_gpu(cfg, inp)
+    compare_all(cfg, path, ref)
+
+
 @pytest.mark.parametrize("name", ["tiny", "dsv3"])
 def test_graph_replay_matches_eager(name):
     """The whole step captured in a HIP graph: every replay, with eager work and
