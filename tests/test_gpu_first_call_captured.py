@@ -1,0 +1,55 @@
+"""The first ep_dispatch of a process made inside HIP graph capture: the dispatch call
+picks its kernel by the device's compute-unit count, queried on first use, and that
+query must be legal while the stream is being captured. Runs in a fresh child process so
+that no earlier call has filled the cache."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+CHILD = r'''
+import sys
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+import oracle
+import combine_ep_get_03_amd as ep
+from combine_ep_get_03_amd import workloads as W
+from combine_ep_get_03_amd.buffers import DispatchBuffers, LayoutBuffers
+cfg = W.CONFIGS["tiny"]
+inp = W.make_inputs(cfg)
+idx = torch.from_numpy(inp.topk_idx).cuda()
+w = torch.from_numpy(inp.topk_weights).cuda()
+x = torch.from_numpy(inp.x.view(np.int16)).view(torch.bfloat16).cuda()
+lb = LayoutBuffers.alloc(cfg.T, cfg.E, cfg.R, cfg.N)
+rb = DispatchBuffers.alloc(cfg.cap, cfg.H, cfg.k)
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):
+    lb.compute(idx, cfg.E, cfg.R, cfg.N)
+    ep.ep_dispatch(x, idx, w, cfg.E, cfg.R, lb.token_slot, recv_x=rb.recv_x,
+                   recv_topk_idx=rb.recv_topk_idx, recv_topk_weights=rb.recv_topk_weights,
+                   recv_src_idx=rb.recv_src_idx, error_flag=lb.error_flag)
+g.replay()
+torch.cuda.synchronize()
+lay = oracle.layout(inp.topk_idx, cfg.E, cfg.R, cfg.N)
+M = int(lay["rank_offset"][-1])
+d = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, cfg.E, cfg.R, lay["token_slot"], M)
+got = rb.recv_x[:M].cpu().view(torch.int16).numpy().view(np.uint16)
+assert int(lb.error_flag.item()) == 0
+assert np.array_equal(got, d["recv_x"])
+assert np.array_equal(rb.recv_src_idx[:M].cpu().numpy(), d["recv_src"])
+print("first captured dispatch ok", M)
+'''
+
+
+def test_first_dispatch_inside_graph_capture():
+    print("\ncase: first dispatch of a process inside graph capture", flush=True)
+    r = subprocess.run([sys.executable, "-c", CHILD, ROOT], capture_output=True, text=True,
+                       timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "first captured dispatch ok" in r.stdout
