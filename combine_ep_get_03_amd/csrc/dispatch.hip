@@ -14,8 +14,8 @@
 // stores. No LDS and no block barrier. The work per token is bounded by min(k, R)
 // destinations whatever the skew of the per-rank counts. HBM-write bound.
 // Batches small enough that the one-token grid would be resident at once take a form
-// with two tokens per wave (dispatch_pair_kernel), which overlaps the second token's
-// loads with the first token's stores.
+// with two tokens per wave (dispatch_pair_kernel, and dispatch_send_pair_kernel for the
+// send phase), which overlaps the second token's loads with the first token's stores.
 // Block sizes and the pass-loop form are chosen per kernel by measurement (below).
 #include <atomic>
 #include <type_traits>
@@ -208,12 +208,56 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     if (errbits) raise_error(error_flag, errbits);
 }
 
-// The same dispatch for small batches (R <= 64, k <= 64, one pass per row): each wave
-// owns two tokens, t and t + W (W waves in the grid). Token t's row, slot row and routing
-// are loaded first and token t + W's right after, so token t's writes wait only for its
-// own loads and token t + W's loads arrive meanwhile. Used while the one-token grid would
-// be resident at once; on MI355X at 1024, 2048 and 4096 tokens of 7168 channels it ran
-// 16%, 9% and 2% faster than one token per wave, and 2-3% slower at 8192 and 16384.
+// Small batches (C <= 64 slots, k <= 64, one pass per row): each wave owns two tokens,
+// t and t + W (W waves in the grid). Token t's row, slot row and routing are loaded
+// first and token t + W's right after, so token t's writes wait only for its own loads
+// and token t + W's loads arrive meanwhile. Token t's row goes to destination row
+// slot + c * cbase for every slot c >= 0 of its row, with the routing (rank c's view with
+// kRankView, else unchanged) and the source id. Used while the one-token grid would be
+// resident at once. On MI355X at 1024, 2048 and 4096 tokens of 7168 channels the
+// dispatch ran 16%, 9% and 2% faster than one token per wave (2-3% slower at 8192 and
+// 16384), and the send phase 26%, 19% and 5.5% faster.
+template <int WPL, bool kRankView, int kThreads>
+__device__ __forceinline__ void pair_scatter(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int64_t T, int V, int k, int er,
+    const int32_t* __restrict__ slot_tab, int C, int64_t cbase, int64_t cap,
+    u32x4* __restrict__ dst_x, int64_t* __restrict__ dst_idx, float* __restrict__ dst_w,
+    int32_t* __restrict__ dst_src, int32_t* __restrict__ error_flag) {
+    const int lane = lane_id();
+    constexpr int kWpb = kThreads / kWave;
+    const int64_t W = static_cast<int64_t>(gridDim.x) * kWpb;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWpb + threadIdx.x / kWave;
+    if (t0 >= T) return;
+    const int64_t t1 = t0 + W;
+    const bool has1 = t1 < T;
+    const bool meta = dst_idx || dst_w;
+    u32x4 a[WPL], b[WPL];
+    load_row(a, x + t0 * V, 0, V);
+    const int32_t s0 = lane < C ? slot_tab[t0 * C + lane] : -1;
+    const Routing r0(topk_idx ? topk_idx + t0 * k : nullptr, topk_w ? topk_w + t0 * k : nullptr,
+                     k, meta);
+    int32_t s1 = -1;
+    if (has1) {
+        load_row(b, x + t1 * V, 0, V);
+        s1 = lane < C ? slot_tab[t1 * C + lane] : -1;
+    }
+    int32_t errbits = 0;
+    visit_chunk(s0, 0, cbase, cap, errbits, [&](int64_t sd, int cd) {
+        put_row<WPL, kRankView>(a, 0, V, sd, cd, r0, er, static_cast<int32_t>(t0), dst_x, dst_idx,
+                                dst_w, dst_src);
+    });
+    if (has1) {
+        const Routing r1(topk_idx ? topk_idx + t1 * k : nullptr,
+                         topk_w ? topk_w + t1 * k : nullptr, k, meta);
+        visit_chunk(s1, 0, cbase, cap, errbits, [&](int64_t sd, int cd) {
+            put_row<WPL, kRankView>(b, 0, V, sd, cd, r1, er, static_cast<int32_t>(t1), dst_x,
+                                    dst_idx, dst_w, dst_src);
+        });
+    }
+    if (errbits) raise_error(error_flag, errbits);
+}
+
 template <int WPL, int kThreads>
 __global__ __launch_bounds__(kThreads) void dispatch_pair_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
@@ -221,36 +265,65 @@ __global__ __launch_bounds__(kThreads) void dispatch_pair_kernel(
     const int32_t* __restrict__ token_slot, u32x4* __restrict__ recv_x,
     int64_t* __restrict__ recv_idx, float* __restrict__ recv_w, int32_t* __restrict__ recv_src,
     int64_t cap, int32_t* __restrict__ error_flag) {
+    pair_scatter<WPL, true, kThreads>(x, topk_idx, topk_w, T, V, k, er, token_slot, R, 0, cap, recv_x,
+                            recv_idx, recv_w, recv_src, error_flag);
+}
+
+// The send phase's small-batch form: node slots, rows n * Tmax + slot, routing unchanged.
+template <int WPL, int kThreads>
+__global__ __launch_bounds__(kThreads) void dispatch_send_pair_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int64_t T, int V, int k, int N,
+    const int32_t* __restrict__ node_slot, int64_t Tmax, u32x4* __restrict__ stage_x,
+    int64_t* __restrict__ stage_idx, float* __restrict__ stage_w, int32_t* __restrict__ stage_src,
+    int32_t* __restrict__ error_flag) {
+    pair_scatter<WPL, false, kThreads>(x, topk_idx, topk_w, T, V, k, 0, node_slot, N, Tmax, Tmax, stage_x,
+                             stage_idx, stage_w, stage_src, error_flag);
+}
+
+// The permute's small-batch form (k <= 64 slots, one pass per row): two tokens per wave as
+// above. Slot j's weight is loaded by lane j with the slot row and read back with
+// readlane, since the walk hands over a wave-uniform j.
+template <int WPL, int kThreads>
+__global__ __launch_bounds__(kThreads) void dispatch_permute_pair_kernel(
+    const u32x4* __restrict__ x, const float* __restrict__ topk_w, int64_t T, int V, int k,
+    const int32_t* __restrict__ expert_slot, u32x4* __restrict__ perm_x,
+    float* __restrict__ perm_w, int32_t* __restrict__ perm_src, int64_t cap,
+    int32_t* __restrict__ error_flag) {
     const int lane = lane_id();
-    const int64_t W = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+    constexpr int kWpb = kThreads / kWave;
+    const int64_t W = static_cast<int64_t>(gridDim.x) * kWpb;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWpb + threadIdx.x / kWave;
     if (t0 >= T) return;
     const int64_t t1 = t0 + W;
     const bool has1 = t1 < T;
-    const bool meta = recv_idx || recv_w;
     u32x4 a[WPL], b[WPL];
     load_row(a, x + t0 * V, 0, V);
-    const int32_t s0 = lane < R ? token_slot[t0 * R + lane] : -1;
-    const Routing r0(topk_idx ? topk_idx + t0 * k : nullptr, topk_w ? topk_w + t0 * k : nullptr,
-                     k, meta);
+    const int32_t s0 = lane < k ? expert_slot[t0 * k + lane] : -1;
+    const float w0 = perm_w && lane < k ? topk_w[t0 * k + lane] : 0.0f;
     int32_t s1 = -1;
+    float w1 = 0.0f;
     if (has1) {
         load_row(b, x + t1 * V, 0, V);
-        s1 = lane < R ? token_slot[t1 * R + lane] : -1;
+        s1 = lane < k ? expert_slot[t1 * k + lane] : -1;
+        w1 = perm_w && lane < k ? topk_w[t1 * k + lane] : 0.0f;
     }
     int32_t errbits = 0;
-    visit_chunk(s0, 0, 0, cap, errbits, [&](int64_t sd, int cd) {
-        put_row<WPL, true>(a, 0, V, sd, cd, r0, er, static_cast<int32_t>(t0), recv_x, recv_idx,
-                           recv_w, recv_src);
-    });
-    if (has1) {
-        const Routing r1(topk_idx ? topk_idx + t1 * k : nullptr,
-                         topk_w ? topk_w + t1 * k : nullptr, k, meta);
-        visit_chunk(s1, 0, 0, cap, errbits, [&](int64_t sd, int cd) {
-            put_row<WPL, true>(b, 0, V, sd, cd, r1, er, static_cast<int32_t>(t1), recv_x,
-                               recv_idx, recv_w, recv_src);
-        });
-    }
+    auto put = [&](const u32x4 (&v)[WPL], int64_t t, float w, int64_t qd, int j) {
+        u32x4* row = perm_x + qd * V;
+#pragma unroll
+        for (int i = 0; i < WPL; ++i) {
+            const int vi = i * kWave + lane;
+            if (vi < V) store_row_word(row + vi, v[i]);
+        }
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+        if (lane == 0) {
+            if (perm_w) perm_w[qd] = wj;
+            if (perm_src) perm_src[qd] = static_cast<int32_t>(t);
+        }
+    };
+    visit_chunk(s0, 0, 0, cap, errbits, [&](int64_t qd, int j) { put(a, t0, w0, qd, j); });
+    if (has1) visit_chunk(s1, 0, 0, cap, errbits, [&](int64_t qd, int j) { put(b, t1, w1, qd, j); });
     if (errbits) raise_error(error_flag, errbits);
 }
 
@@ -513,6 +586,17 @@ hipError_t launch_dispatch_permute(const void* x, const float* topk_w, int64_t T
                                    hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
+    if (V <= 14 * kWave && k <= kWave && T <= resident_token_waves()) {
+        constexpr int kPT = kPairThreads;
+        const int64_t waves = (T + 1) / 2;
+        const int64_t pgrid = (waves + kPT / kWave - 1) / (kPT / kWave);
+        return with_row_width<14, false>(V, [&](auto wpl, auto) {
+            hipLaunchKernelGGL((dispatch_permute_pair_kernel<decltype(wpl)::value, kPT>),
+                               dim3(static_cast<unsigned>(pgrid)), dim3(kPT), 0, stream,
+                               static_cast<const u32x4*>(x), topk_w, T, V, k, expert_slot,
+                               static_cast<u32x4*>(perm_x), perm_w, perm_src, cap, error_flag);
+        });
+    }
     constexpr int kThreads = kRowThreads;
     const int64_t grid = (T + kThreads / kWave - 1) / (kThreads / kWave);
     if (!grid_fits(grid, kThreads)) return hipErrorInvalidConfiguration;
@@ -530,6 +614,18 @@ hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const fl
                                 int32_t* stage_src, int32_t* error_flag, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
+    if (V <= 14 * kWave && N <= kWave && k <= kWave && T <= resident_token_waves()) {
+        constexpr int kPT = kPairThreads;
+        const int64_t waves = (T + 1) / 2;
+        const int64_t pgrid = (waves + kPT / kWave - 1) / (kPT / kWave);
+        return with_row_width<14, false>(V, [&](auto wpl, auto) {
+            hipLaunchKernelGGL((dispatch_send_pair_kernel<decltype(wpl)::value, kPT>),
+                               dim3(static_cast<unsigned>(pgrid)), dim3(kPT), 0, stream,
+                               static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, N,
+                               node_slot, Tmax, static_cast<u32x4*>(stage_x), stage_idx, stage_w,
+                               stage_src, error_flag);
+        });
+    }
     constexpr int kThreads = kRowThreads;
     const int64_t grid = (T + kThreads / kWave - 1) / (kThreads / kWave);
     if (!grid_fits(grid, kThreads)) return hipErrorInvalidConfiguration;

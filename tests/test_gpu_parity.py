@@ -249,6 +249,46 @@ def test_dispatch_around_the_small_batch_threshold(T):
     compare_all(cfg, path, ref)
 
 
+@pytest.mark.parametrize("T", [3, 4095, 4097])
+def test_permute_and_send_around_the_small_batch_threshold(T):
+    # the expert-major permute and the two-phase send switch to two tokens per wave at the
+    # same batch size as the dispatch
+    from combine_ep_get_03_amd.buffers import LayoutBuffers
+
+    cfg = W.Config(f"thr2_T{T}", T=T, H=512, E=64, k=6, R=16, N=4, P=8, Tmax=T + 5, seed=T + 1)
+    inp = _case(cfg)
+    b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob)
+    lbe = LayoutBuffers.alloc(T, cfg.E, cfg.R, cfg.N, k_expert_slots=cfg.k)
+    lbe.compute(b.topk_idx, cfg.E, cfg.R, cfg.N)
+    px = torch.full((T * cfg.k, cfg.H), 7.0, dtype=torch.bfloat16, device="cuda")
+    pw = torch.empty(T * cfg.k, dtype=torch.float32, device="cuda")
+    ps = torch.empty(T * cfg.k, dtype=torch.int32, device="cuda")
+    ep.ep_dispatch_permute(b.x, b.topk_weights, lbe.expert_slot, perm_x=px, perm_weights=pw,
+                           perm_src_idx=ps, error_flag=lbe.error_flag)
+    es = oracle.expert_slots(inp.topk_idx, cfg.E)
+    want = oracle.dispatch_permute(inp.x, inp.topk_idx, inp.topk_weights, es, T * cfg.k)
+    torch.cuda.synchronize()
+    assert int(lbe.error_flag.item()) == 0
+    np.testing.assert_array_equal(host(px), want["perm_x"])
+    np.testing.assert_array_equal(host(pw).view(np.uint32), want["perm_w"].view(np.uint32))
+    np.testing.assert_array_equal(host(ps), want["perm_src"])
+
+    path = Path(T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax, node_slots=True)
+    path.layout(b)
+    path.dispatch_send(b)
+    torch.cuda.synchronize()
+    ns = oracle.node_slots(inp.topk_idx, cfg.E, cfg.R, cfg.N)
+    st = oracle.hook_dispatch_send(inp.x, inp.topk_idx, inp.topk_weights, ns, cfg.Tmax)
+    assert int(path.error_flag.item()) == 0
+    for n in range(cfg.N):
+        cnt = int((ns[:, n] >= 0).sum())
+        np.testing.assert_array_equal(host(path.stage.stage_x[n, :cnt]), st["stage_x"][n, :cnt])
+        np.testing.assert_array_equal(host(path.stage.stage_topk_idx[n, :cnt]), st["stage_idx"][n, :cnt])
+        np.testing.assert_array_equal(host(path.stage.stage_topk_weights[n, :cnt]).view(np.uint32),
+                                      st["stage_w"][n, :cnt].view(np.uint32))
+        np.testing.assert_array_equal(host(path.stage.stage_src[n, :cnt]), st["stage_src"][n, :cnt])
+
+
 @pytest.mark.parametrize("name", ["tiny", "dsv3"])
 def test_graph_replay_matches_eager(name):
     """The whole step captured in a HIP graph: every replay, with eager work and
