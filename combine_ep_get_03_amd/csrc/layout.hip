@@ -480,6 +480,95 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
     }
 }
 
+// The whole layout of a batch of at most one 256-token group (up to 256 tokens, R <= 256)
+// in one block and one launch: the counts, offsets and slots need no cross-block
+// exchange, so the count and slot kernels collapse into one, with block barriers only.
+// Same outputs as the two-launch path; the expert-major slots (when asked for) still take
+// the expert-slot launch, whose per-block base is then the expert offset itself.
+template <int NW>
+__global__ __launch_bounds__(kBT) void layout_single_kernel(
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int N, FastDiv er,
+    FastDiv rpn, int32_t* __restrict__ count_r, int32_t* __restrict__ count_n,
+    int32_t* __restrict__ count_e, int32_t* __restrict__ rank_offset,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ error_flag,
+    int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank, int vec_out,
+    int32_t* __restrict__ exp_base, int32_t* __restrict__ node_slot, int vec_node) {
+    extern __shared__ int32_t s_hist[];                        // [E]
+    __shared__ uint64_t s_ball[kWavesBT * kFusedMaxRanks];     // [4][R]
+    __shared__ uint64_t s_nball[kWavesBT * kFusedMaxRanks];    // [4][N]
+    __shared__ int32_t s_base[kWavesBT * kFusedMaxRanks];      // [4][R] slot base per wave
+    __shared__ int32_t s_nbase[kWavesBT * kFusedMaxRanks];     // [4][N]
+    __shared__ int32_t s_scan[17];
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    for (int e = tid; e < E; e += kBT) s_hist[e] = 0;
+    __syncthreads();
+
+    uint64_t rm[NW], nm[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) rm[w] = nm[w] = 0;
+    int bad = 0;
+    if (tid < T) token_masks<NW, true, true>(topk_idx + tid * k, k, E, er, rpn, rm, nm, s_hist, bad);
+    wave_ballots<NW, false>(rm, R, s_ball + wave * R);
+    wave_ballots<NW, false>(nm, N, s_nball + wave * N);
+    __syncthreads();
+
+    // ranks: totals, exclusive offsets and each wave's slot base (R <= blockDim)
+    int tot = 0;
+    if (tid < R) {
+#pragma unroll
+        for (int w = 0; w < kWavesBT; ++w) tot += __popcll(s_ball[w * R + tid]);
+    }
+    int M = 0;
+    const int ro = block_exclusive_scan(tid < R ? tot : 0, s_scan, M);
+    if (tid < R) {
+        count_r[tid] = tot;
+        rank_offset[tid] = ro;
+        int base = ro;
+#pragma unroll
+        for (int w = 0; w < kWavesBT; ++w) {
+            s_base[w * R + tid] = base;
+            base += __popcll(s_ball[w * R + tid]);
+        }
+    }
+    if (tid == 0) rank_offset[R] = M;
+    if (tid < N) {
+        int base = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesBT; ++w) {
+            s_nbase[w * N + tid] = base;
+            base += __popcll(s_nball[w * N + tid]);
+        }
+        if (count_n) count_n[tid] = base;
+    }
+    // experts: counts and exclusive offsets
+    int carry = 0;
+    for (int c0 = 0; c0 < E; c0 += kBT) {
+        const int e = c0 + tid;
+        const int h = e < E ? s_hist[e] : 0;
+        int chunk = 0;
+        const int ex = block_exclusive_scan(h, s_scan, chunk);
+        if (e < E) {
+            if (count_e) count_e[e] = h;
+            if (expert_offset) expert_offset[e] = carry + ex;
+            if (exp_base) exp_base[e] = carry + ex;
+        }
+        carry += chunk;
+    }
+    if (tid == 0 && expert_offset) expert_offset[E] = carry;
+    const int any_bad = __syncthreads_or(bad);  // also orders the slot bases before the reads
+    if (tid == 0) *error_flag = any_bad ? kErrTopkRange : 0;
+
+#pragma unroll
+    for (int q = 0; q < kWavesBT; ++q) {
+        write_wave_slots(s_ball + q * R, s_base + q * R, T, q * kWave, R, vec_out != 0, token_slot,
+                         in_rank);
+        if (node_slot)
+            write_wave_slots(s_nball + q * N, s_nbase + q * N, T, q * kWave, N, vec_node != 0,
+                             node_slot, nullptr);
+    }
+}
+
 // Columns [c0, c0+width) of a [rows][cols] int32 matrix, one column per thread
 // (width <= blockDim), rows walked in order through an LDS tile. With kPrefix every
 // entry becomes the sum of the entries above it in its column. Returns the column
@@ -720,6 +809,26 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
     const FastDiv er = FastDiv::make(E / R);
     const FastDiv rpn = FastDiv::make(R / N);
     if (!grid_fits(nb, kBT)) return hipErrorInvalidConfiguration;
+    if constexpr (NW * kWave <= kFusedMaxRanks) {
+        if (nb == 1) {
+            const bool vec = R % 4 == 0 && reinterpret_cast<uintptr_t>(token_slot) % 16 == 0 &&
+                             reinterpret_cast<uintptr_t>(in_rank) % 4 == 0;
+            const bool vec_node = N % 4 == 0 && reinterpret_cast<uintptr_t>(node_slot) % 16 == 0;
+            hipLaunchKernelGGL(layout_single_kernel<NW>, dim3(1), dim3(kBT),
+                               sizeof(int32_t) * static_cast<size_t>(E), stream, topk_idx, T, k, E,
+                               R, N, er, rpn, count_r, count_n, count_e, rank_offset, expert_offset,
+                               error_flag, token_slot, in_rank, vec ? 1 : 0,
+                               want_base ? ws.blk_exp_base : nullptr, node_slot, vec_node ? 1 : 0);
+            if (want_base) {
+                int nbits = 0;
+                while ((1 << nbits) < E) ++nbits;
+                hipLaunchKernelGGL(layout_expert_slot_kernel, dim3(1), dim3(kBT),
+                                   sizeof(uint16_t) * kWavesBT * E, stream, topk_idx, T, k, E,
+                                   nbits, ws.blk_exp_base, expert_slot);
+            }
+            return hipGetLastError();
+        }
+    }
     if (nb > 0) {
         const size_t shm = sizeof(int32_t) * static_cast<size_t>(E) +
                            sizeof(uint16_t) * kWavesBT * (R + N);
