@@ -36,6 +36,8 @@ def parse():
                     help="bound on the oracle's CPU time for the baseline")
     ap.add_argument("--copy-gib", default="2,4",
                     help="comma-separated copy sizes in GiB; the best rate is the yardstick")
+    ap.add_argument("--small-batches", action="store_true",
+                    help="also time the whole step at 256 and 1024 tokens of the same shape")
     ap.add_argument("--flush-gib", type=float, default=1.0,
                     help="scratch written before each cold launch (evicts L2 and the 256 MB "
                          "Infinity Cache)")
@@ -302,6 +304,35 @@ def hook_section(torch, cfg, b, args, timed, M: int) -> dict:
     return out
 
 
+def small_batches(torch, W, DeviceBatch, Path, cfg, steps: int, timed) -> dict:
+    """The whole step at decode-sized batches of the same shape (256 and 1024 tokens), timed
+    like the headline step (one graph of K steps); seeded inputs of their own."""
+    out = {}
+    for T in (256, 1024):
+        c = cfg.with_(T=T, Tmax=T, name=f"{cfg.name}_T{T}")
+        inp = W.make_inputs(c)
+        b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials)
+        p = Path(c.T, c.H, c.E, c.k, c.R, c.N, c.P, c.Tmax)
+        p.step(b)
+        torch.cuda.synchronize()
+        M = int(p.layout_buf.rank_offset[-1].item())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                p.step(b)
+        g.replay()
+        ms = timed(g.replay, 1) / steps
+        del g
+        if int(p.error_flag.item()) != 0:
+            raise RuntimeError(f"device error flag at T={T}")
+        out[f"T{T}"] = {"step_us": round(ms * 1e3, 2), "M_token_rank_pairs": M,
+                        "algorithm_gbps": round(2 * M * c.H * 2 / (ms * 1e-3) / 1e9, 1),
+                        "tokens_per_s": round(T / (ms * 1e-3), 1)}
+        del p, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.steps < 1 or args.warmup < 0:
@@ -496,6 +527,8 @@ def main():
               "hbm_gbps": round(sb / (res["restripe_sparse"] * 1e-3) / 1e9, 1)}
     del sp_out, lbn
     hook = hook_section(torch, cfg, b, args, timed, M)
+    small = (small_batches(torch, W, DeviceBatch, Path, cfg, args.steps, timed)
+             if args.small_batches else None)
     dist_calls = {n: (lambda fn=fn: fn(b)) for n, fn in zip(names, calls)}
     dist_calls["step_graph"] = g_step.replay
     dist = launch_distribution(torch, ep, dist_calls, args.steps, args.flush_gib)
@@ -552,6 +585,7 @@ def main():
         "hook": hook,
         "kernels": kernels,
         "launch_distribution": dist,
+        "small_batches": small,
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
