@@ -1,7 +1,7 @@
-"""The first ep_dispatch of a process made inside HIP graph capture: the dispatch call
-picks its kernel by the device's compute-unit count, queried on first use, and that
-query must be legal while the stream is being captured. Runs in a fresh child process so
-that no earlier call has filled the cache."""
+"""The first ep_dispatch of a process made inside HIP graph capture: nothing the call does
+on the host before its launches (argument checks, launch-shape choice) may be illegal
+while the stream is being captured, also when no earlier call has run. Runs in a fresh
+child process so that no earlier call has set anything up."""
 import os
 import subprocess
 import sys

@@ -238,10 +238,9 @@ class _OtherDeviceStream(torch.cuda.Stream):
 
 
 @pytest.mark.parametrize("T", [1, 2, 3, 4095, 4096, 4097, 8193])
-def test_dispatch_around_the_small_batch_threshold(T):
-    # batches up to 16 waves per compute unit (4096 tokens on 256 CUs) take the
-    # two-tokens-per-wave dispatch, larger ones one token per wave; odd counts leave the
-    # last wave with a single token
+def test_dispatch_token_counts(T):
+    # one wave per (token, destination): token counts that leave the last block partly
+    # empty, with D = min(k, R) = 6 waves per token not dividing the block's 4 waves
     cfg = W.Config(f"thr_T{T}", T=T, H=512, E=64, k=6, R=16, N=4, P=8, Tmax=T, seed=T)
     inp = _case(cfg)
     ref = oracle_all(cfg, inp)
@@ -249,14 +248,11 @@ def test_dispatch_around_the_small_batch_threshold(T):
     compare_all(cfg, path, ref)
 
 
-@pytest.mark.parametrize("T", [3, 4095, 4097])
-def test_permute_and_send_around_the_small_batch_threshold(T):
-    # the expert-major permute and the two-phase send switch to two tokens per wave at the
-    # same batch size as the dispatch
+def _check_permute_and_send(cfg, inp):
+    """The expert-major permute and the two-phase send phase against the oracle."""
     from combine_ep_get_03_amd.buffers import LayoutBuffers
 
-    cfg = W.Config(f"thr2_T{T}", T=T, H=512, E=64, k=6, R=16, N=4, P=8, Tmax=T + 5, seed=T + 1)
-    inp = _case(cfg)
+    T = cfg.T
     b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob)
     lbe = LayoutBuffers.alloc(T, cfg.E, cfg.R, cfg.N, k_expert_slots=cfg.k)
     lbe.compute(b.topk_idx, cfg.E, cfg.R, cfg.N)
@@ -272,6 +268,7 @@ def test_permute_and_send_around_the_small_batch_threshold(T):
     np.testing.assert_array_equal(host(px), want["perm_x"])
     np.testing.assert_array_equal(host(pw).view(np.uint32), want["perm_w"].view(np.uint32))
     np.testing.assert_array_equal(host(ps), want["perm_src"])
+    del px, pw, ps, lbe, want
 
     path = Path(T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax, node_slots=True)
     path.layout(b)
@@ -287,6 +284,30 @@ def test_permute_and_send_around_the_small_batch_threshold(T):
         np.testing.assert_array_equal(host(path.stage.stage_topk_weights[n, :cnt]).view(np.uint32),
                                       st["stage_w"][n, :cnt].view(np.uint32))
         np.testing.assert_array_equal(host(path.stage.stage_src[n, :cnt]), st["stage_src"][n, :cnt])
+
+
+@pytest.mark.parametrize("T", [3, 4095, 4097])
+def test_permute_and_send_token_counts(T):
+    # the same (token, destination) form: k = 6 waves per token for the permute,
+    # min(k, N) = 4 for the send phase
+    cfg = W.Config(f"thr2_T{T}", T=T, H=512, E=64, k=6, R=16, N=4, P=8, Tmax=T + 5, seed=T + 1)
+    _check_permute_and_send(cfg, _case(cfg))
+
+
+def test_launches_split_over_token_ranges():
+    # a (token, destination) launch holds at most 2^22 waves: 600 000 tokens with 8 waves
+    # each take two launches of dispatch, permute and send (and the first range's last
+    # block must not run into the second range's tokens)
+    cfg = W.Config("split_600k", T=600_000, H=8, E=64, k=8, R=8, N=8, P=4, Tmax=600_000,
+                   seed=11)
+    assert cfg.T * min(cfg.k, cfg.R) > (1 << 22)
+    inp = _case(cfg)
+    ref = oracle_all(cfg, inp)
+    path = run_gpu(cfg, inp)
+    compare_all(cfg, path, ref)
+    del path, ref
+    torch.cuda.empty_cache()
+    _check_permute_and_send(cfg, inp)
 
 
 @pytest.mark.parametrize("name", ["tiny", "dsv3"])
