@@ -76,15 +76,19 @@ def test_measured_traffic_is_guarded_by_the_source_hash(tmp_path, monkeypatch):
 
 def test_committed_counters_agree_with_the_algorithmic_bytes():
     # where the committed counter summary matches today's sources, its calibrated bytes per
-    # launch are within 5% of the algorithmic bytes (a stale summary gives null traffic)
+    # launch are within 5% of the algorithmic bytes (a stale summary gives null traffic).
+    # The dispatch may read each token row once more: a token's waves span two blocks,
+    # which run on two XCDs, and each XCD's L2 fetches the row.
+    cfg = W.CONFIGS["dsv3"]
+    extra = {"dispatch": cfg.T * cfg.H * 2, "combine": 0}
     for k in ("dispatch", "combine"):
         v = bench.measured_traffic(k, "dsv3")
         if v is None:
             pytest.skip(f"{k}: the counter summary predates the current kernel sources")
-        cfg = W.CONFIGS["dsv3"]
         inp = W.make_inputs(cfg, with_x=False)
         M = int(oracle.layout(inp.topk_idx, cfg.E, cfg.R, cfg.N)["rank_offset"][-1])
-        assert abs(v / bench.algorithmic_bytes(cfg, M)[k] - 1.0) < 0.05
+        a = bench.algorithmic_bytes(cfg, M)[k]
+        assert 0.95 * a <= v <= 1.05 * (a + extra[k])
 
 
 def test_cpu_baseline_record():
