@@ -23,9 +23,10 @@
 // every wave, ran 30% slower in a probe of the same form. One wave per token (all its
 // destinations in turn) ran 13-19% slower on MI355X from 4096 to 16384 tokens of 7168
 // channels, top-8, because the whole resident grid then writes across the whole buffer
-// at once. HBM-write bound. The expert-major permute and the two-phase send phase use
-// the same form; the FP8 dispatch and the receive phase keep one wave per token or
-// staged row (each measured faster that way, see their kernels).
+// at once. HBM-write bound. The expert-major permute uses the same form; the FP8
+// dispatch and the two-phase send phase give each wave a range of a token's destinations
+// (at most one block of waves per token), and the receive phase keeps one wave per staged
+// row (each measured faster that way, see their kernels).
 #include <type_traits>
 
 #include "ep_internal.hpp"
@@ -40,14 +41,19 @@ namespace {
 // Launch shapes, chosen by same-box A/B timing on MI355X at 1024 to 16384 tokens of 7168
 // channels, top-8: 256-thread blocks for the (token, destination) kernels (4-6% faster
 // than 512 at every size but the smallest), the one-pass form in 256-thread blocks for
-// the receive phase and the FP8 dispatch.
+// the receive phase.
 constexpr int kDestThreads = 256;
 constexpr int kRecvThreads = 256;
-constexpr int kFp8Threads = 256;
 // Waves per launch of a (token, destination) kernel; larger batches are split over token
 // ranges, so a wave's index stays a 32-bit value and one launch stays far below the
 // dispatch packet's 2^32 work-item limit.
 constexpr int64_t kDestMaxWaves = int64_t{1} << 22;
+// The FP8 dispatch and the send phase give a token at most one block of waves (several
+// destinations per wave when it has more): same-box A/B on MI355X at 7168 channels, top-8,
+// FP8 over 32 ranks 45 against 68 us with one wave per destination, send over 8 nodes
+// 232 against 258 us at 16384 tokens. The one-call dispatch and the permute keep one
+// destination per wave, which measured faster for them (78.7 against 82.8 us at 4096).
+constexpr int kMaxWavesPerToken = kDestThreads / kWave;
 
 __device__ __forceinline__ void store_row_word(u32x4* p, u32x4 v) {
 #if EP_DISPATCH_NT_STORE
@@ -183,15 +189,15 @@ __device__ __forceinline__ void scatter_row(
     }
 }
 
-// One wave per (token, destination index). Wave d < D - 1 writes only the token's d-th
-// destination; wave D - 1 also takes every destination past it, so a slot table with
-// more than D valid entries in a row (possible for a caller-built one) is still written
-// in full. s_first is the calling lane's entry of the slot row's first 64 columns,
-// loaded before the routing and the row so the ballot waits only for it.
+// A wave's share of a token's destinations: the destinations with index in [lo, hi),
+// in ascending column order (hi = INT32_MAX for the token's last wave, which so also takes
+// every destination past the expected count: a caller-built slot table may have more
+// valid entries in a row). s_first is the calling lane's entry of the slot row's first 64
+// columns, loaded before the routing and the row so the ballot waits only for it.
 template <typename Visit>
-__device__ __forceinline__ void visit_nth_destination(int32_t s_first, const int32_t* __restrict__ srow,
-                                                      int C, int64_t cbase, int64_t cap, int d,
-                                                      bool tail, int32_t& errbits, Visit&& visit) {
+__device__ __forceinline__ void visit_destinations(int32_t s_first, const int32_t* __restrict__ srow,
+                                                   int C, int64_t cbase, int64_t cap, int lo, int hi,
+                                                   int32_t& errbits, Visit&& visit) {
     const int lane = lane_id();
     int seen = 0;
     for (int c0 = 0; c0 < C; c0 += kWave) {
@@ -201,18 +207,25 @@ __device__ __forceinline__ void visit_nth_destination(int32_t s_first, const int
             s = -1;
         }
         uint64_t m = wave_ballot(s >= 0);
-        while (m && seen < d) {  // destinations before the d-th belong to other waves
+        while (m && seen < lo) {  // destinations before lo belong to other waves
             m &= m - 1;
             ++seen;
         }
         while (m) {
+            if (seen >= hi) return;
             const int src_lane = __builtin_ctzll(m);
             m &= m - 1;
+            ++seen;
             const int cd = c0 + src_lane;
             visit(static_cast<int64_t>(__builtin_amdgcn_readlane(s, src_lane)) + cd * cbase, cd);
-            if (!tail) return;
         }
     }
+}
+
+// The destination range of wave d of D, P destinations each; the last wave's is open.
+__device__ __forceinline__ void dest_range(int d, int D, int P, int& lo, int& hi) {
+    lo = d * P;
+    hi = d == D - 1 ? INT32_MAX : lo + P;
 }
 
 template <int WPL>
@@ -243,7 +256,7 @@ template <int WPL, bool kMulti, bool kRankView, int kThreads>
 __device__ __forceinline__ void dest_scatter(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, int64_t t0, int64_t t_end, int V, int k, int er,
-    const int32_t* __restrict__ slot_tab, int C, int64_t cbase, int64_t cap, FastDiv D,
+    const int32_t* __restrict__ slot_tab, int C, int64_t cbase, int64_t cap, FastDiv D, int P,
     u32x4* __restrict__ dst_x, int64_t* __restrict__ dst_idx, float* __restrict__ dst_w,
     int32_t* __restrict__ dst_src, int32_t* __restrict__ error_flag) {
     int64_t t;
@@ -255,12 +268,13 @@ __device__ __forceinline__ void dest_scatter(
     const Routing rt(topk_idx ? topk_idx + t * k : nullptr, topk_w ? topk_w + t * k : nullptr, k,
                      dst_idx || dst_w);
     const u32x4* xr = x + t * V;
-    const bool tail = d == D.d - 1;
+    int lo, hi;
+    dest_range(d, D.d, P, lo, hi);
     int32_t errbits = 0;
     for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
         u32x4 v[WPL];
         load_row_cached(v, xr, v0, V);
-        visit_nth_destination(s_first, srow, C, cbase, cap, d, tail, errbits, [&](int64_t sd, int cd) {
+        visit_destinations(s_first, srow, C, cbase, cap, lo, hi, errbits, [&](int64_t sd, int cd) {
             put_row<WPL, kRankView>(v, v0, V, sd, cd, rt, er, static_cast<int32_t>(t), dst_x,
                                     dst_idx, dst_w, dst_src);
         });
@@ -273,11 +287,11 @@ template <int WPL, bool kMulti, int kThreads>
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, int64_t t0, int64_t t_end, int V, int k, int R, int er,
-    const int32_t* __restrict__ token_slot, FastDiv D, u32x4* __restrict__ recv_x,
+    const int32_t* __restrict__ token_slot, FastDiv D, int P, u32x4* __restrict__ recv_x,
     int64_t* __restrict__ recv_idx, float* __restrict__ recv_w, int32_t* __restrict__ recv_src,
     int64_t cap, int32_t* __restrict__ error_flag) {
     dest_scatter<WPL, kMulti, true, kThreads>(x, topk_idx, topk_w, t0, t_end, V, k, er, token_slot,
-                                              R, 0, cap, D, recv_x, recv_idx, recv_w, recv_src,
+                                              R, 0, cap, D, P, recv_x, recv_idx, recv_w, recv_src,
                                               error_flag);
 }
 
@@ -285,16 +299,16 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
 // phase: each token's row, its k expert ids and weights and its id go once to every
 // node holding one of its experts, at row node_slot[t][n] of node n's block of Tmax rows
 // (the large per-node buffer that holds a whole batch, section 2.2.2). Wave (t, d) takes
-// the token's d-th node; D = min(k, N).
+// the token's nodes [d P, d P + P), with P chosen so a token has at most one block of waves.
 template <int WPL, bool kMulti, int kThreads>
 __global__ __launch_bounds__(kThreads) void dispatch_send_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, int64_t t0, int64_t t_end, int V, int k, int N,
-    const int32_t* __restrict__ node_slot, int64_t Tmax, FastDiv D, u32x4* __restrict__ stage_x,
+    const int32_t* __restrict__ node_slot, int64_t Tmax, FastDiv D, int P, u32x4* __restrict__ stage_x,
     int64_t* __restrict__ stage_idx, float* __restrict__ stage_w, int32_t* __restrict__ stage_src,
     int32_t* __restrict__ error_flag) {
     dest_scatter<WPL, kMulti, false, kThreads>(x, topk_idx, topk_w, t0, t_end, V, k, 0, node_slot,
-                                               N, Tmax, Tmax, D, stage_x, stage_idx, stage_w,
+                                               N, Tmax, Tmax, D, P, stage_x, stage_idx, stage_w,
                                                stage_src, error_flag);
 }
 
@@ -375,19 +389,6 @@ __global__ __launch_bounds__(kThreads) void dispatch_recv_kernel(
     if (errbits && (s < cnt || s == 0)) raise_error(error_flag, errbits);
 }
 
-// FP8 dispatch: one wave per token, which quantises the row once, in registers, and
-// walks the token's destinations. One wave per (token, destination) re-quantised the row
-// in every wave at a higher register count and ran 30% slower on MI355X (68 against
-// 52 us at 4096 x 7168, top-8 over 32 ranks), so the FP8 dispatch keeps this form.
-// Lane l of a pass owns the word pair (2 pi, 2 pi + 1), pi = 64 * pass + l: 16 channels,
-// whose 16 codes leave as one 128-bit store. A group of 128 channels is 8 pairs, i.e. 8
-// aligned lanes, so its largest |x| is reduced with three xor shuffles; scale = amax /
-// 448, codes = e4m3(x * (448 / amax)) through the gfx950 packed fp8 convert (round to
-// nearest even; the product is clamped to +-448, which only ever removes rounding
-// excess above 448). Each destination row gets the codes as one burst of 128-bit
-// stores and its H/128 scales (one lane per group). Against one word per lane (64-bit
-// code stores, a 16-lane reduction) this measured 5% faster on MI355X at 4096 x 7168.
-
 // One pass of a row's FP8 quantisation: lane l owns the word pair pi = p0 + 64 i + l
 // (16 channels) of every i < WPP; code[i] gets its 16 e4m3 codes and scale[i] its group's
 // scale (one group of 128 channels = 8 aligned lanes).
@@ -400,8 +401,8 @@ __device__ __forceinline__ void quantize_fp8_pass(const u32x4* __restrict__ xr, 
     for (int i = 0; i < WPP; ++i) {
         const int pi = p0 + i * kWave + lane;
         if (pi < P2) {
-            v[2 * i] = load_stream(xr + 2 * pi);
-            v[2 * i + 1] = load_stream(xr + 2 * pi + 1);
+            v[2 * i] = xr[2 * pi];  // cached: the token's other waves hit in L2
+            v[2 * i + 1] = xr[2 * pi + 1];
         }
     }
 #pragma unroll
@@ -463,26 +464,46 @@ __device__ __forceinline__ void put_fp8_row(const u32x4 (&code)[WPP], const floa
     if (recv_src && lane == 0) recv_src[sd] = src;
 }
 
+// FP8 dispatch: wave (t, d) quantises token t's row in registers and writes it to the
+// token's destinations [d P, d P + P), at most kMaxWavesPerToken waves per token (P = 2 at
+// top-8). Lane l of a pass owns the word pair (2 pi, 2 pi + 1), pi = 64 * pass + l: 16
+// channels, whose 16 codes leave as one 128-bit store. A group of 128 channels is 8 pairs,
+// i.e. 8 aligned lanes, so its largest |x| is reduced with three xor shuffles; scale =
+// amax / 448, codes = e4m3(x * (448 / amax)) through the gfx950 packed fp8 convert (round
+// to nearest even; the product is clamped to +-448, which only ever removes rounding
+// excess above 448). Each destination row gets the codes as one burst of 128-bit stores
+// and its H/128 scales (one lane per group). Row loads are cached, so a token's other
+// waves read the row from L2. Measured on MI355X at 7168 channels, top-8 over 32 ranks,
+// against one wave per token (non-temporal loads): 45.3 against 52.6 us at 4096 tokens,
+// 83.7 against 109 at 8192; one wave per destination (8 quantisations per token) ran
+// 67.6. The word-pair mapping measured 5% faster than one word per lane (64-bit code
+// stores, a 16-lane reduction).
 template <int WPP, bool kMulti, int kThreads>
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_w, int64_t T, int V, int k, int R, int er,
-    const int32_t* __restrict__ token_slot, u32x4* __restrict__ recv_codes,
+    const float* __restrict__ topk_w, int64_t t0, int64_t t_end, int V, int k, int R, int er,
+    const int32_t* __restrict__ token_slot, FastDiv D, int P, u32x4* __restrict__ recv_codes,
     float* __restrict__ recv_scales, int64_t* __restrict__ recv_idx, float* __restrict__ recv_w,
     int32_t* __restrict__ recv_src, int64_t cap, int32_t* __restrict__ error_flag) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
-    if (t >= T) return;
-    const int P2 = V / 2;  // word pairs per row (V % 16 == 0)
-    const int G = V / 16;  // scale groups per row
+    int64_t t;
+    int d;
+    if (!dest_wave<kThreads>(t0, t_end, D, t, d)) return;
+    const int lane = lane_id();
+    const int P2 = V / 2;
+    const int G = V / 16;
+    const int32_t* srow = token_slot + t * R;
+    const int32_t s_first = lane < R ? srow[lane] : -1;
     const Routing rt(topk_idx ? topk_idx + t * k : nullptr, topk_w ? topk_w + t * k : nullptr, k,
                      recv_idx || recv_w);
     const u32x4* xr = x + t * V;
+    int lo, hi;
+    dest_range(d, D.d, P, lo, hi);
     int32_t errbits = 0;
     for (int p0 = 0; p0 < P2; p0 += kWave * WPP) {
         u32x4 code[WPP];
         float scale[WPP];
         quantize_fp8_pass<WPP>(xr, p0, P2, code, scale);
-        for_each_destination(token_slot + t * R, R, 0, cap, errbits, [&](int64_t sd, int rd) {
+        visit_destinations(s_first, srow, R, 0, cap, lo, hi, errbits, [&](int64_t sd, int rd) {
             put_fp8_row<WPP>(code, scale, p0, P2, G, sd, rd, rt, er, static_cast<int32_t>(t),
                              recv_codes, recv_scales, recv_idx, recv_w, recv_src);
         });
@@ -526,14 +547,15 @@ hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* 
                            int64_t cap, int32_t* error_flag, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    const int D = std::min(k, R);  // ranks a token can reach
+    const int P = 1;                // destinations per wave
+    const int D = std::min(k, R);   // waves per token: ranks a token can reach
     const FastDiv fd = FastDiv::make(D);
     return with_row_width<14, false>(V, [&](auto wpl, auto multi) {
         for_each_token_range(T, D, [&](int64_t t0, int64_t t_end, unsigned grid) {
             hipLaunchKernelGGL((dispatch_kernel<decltype(wpl)::value, decltype(multi)::value, kDestThreads>),
                                dim3(grid), dim3(kDestThreads), 0, stream,
                                static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, R,
-                               E / R, token_slot, fd, static_cast<u32x4*>(recv_x), recv_idx, recv_w,
+                               E / R, token_slot, fd, P, static_cast<u32x4*>(recv_x), recv_idx, recv_w,
                                recv_src, cap, error_flag);
         });
     });
@@ -546,16 +568,18 @@ hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const flo
                                hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    constexpr int kThreads = kFp8Threads;
-    const int64_t grid = (T + kThreads / kWave - 1) / (kThreads / kWave);
-    if (!grid_fits(grid, kThreads)) return hipErrorInvalidConfiguration;
+    const int P = (std::min(k, R) + kMaxWavesPerToken - 1) / kMaxWavesPerToken;
+    const int D = (std::min(k, R) + P - 1) / P;  // waves per token, at most one block
+    const FastDiv fd = FastDiv::make(D);
     // word pairs per lane: 7 covers a 7168-wide row in one pass
     return with_row_width<7, false>(V / 2, [&](auto wpp, auto multi) {
-        hipLaunchKernelGGL((dispatch_fp8_kernel<decltype(wpp)::value, decltype(multi)::value, kThreads>),
-                           dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
-                           static_cast<const u32x4*>(x), topk_idx, topk_w, T, V, k, R, E / R,
-                           token_slot, static_cast<u32x4*>(recv_codes), recv_scales, recv_idx,
-                           recv_w, recv_src, cap, error_flag);
+        for_each_token_range(T, D, [&](int64_t t0, int64_t t_end, unsigned grid) {
+            hipLaunchKernelGGL((dispatch_fp8_kernel<decltype(wpp)::value, decltype(multi)::value, kDestThreads>),
+                               dim3(grid), dim3(kDestThreads), 0, stream,
+                               static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, R,
+                               E / R, token_slot, fd, P, static_cast<u32x4*>(recv_codes),
+                               recv_scales, recv_idx, recv_w, recv_src, cap, error_flag);
+        });
     });
 }
 
@@ -582,14 +606,15 @@ hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const fl
                                 int32_t* stage_src, int32_t* error_flag, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    const int D = std::min(k, N);  // nodes a token can reach
+    const int P = (std::min(k, N) + kMaxWavesPerToken - 1) / kMaxWavesPerToken;
+    const int D = (std::min(k, N) + P - 1) / P;  // waves per token, at most one block
     const FastDiv fd = FastDiv::make(D);
     return with_row_width<14, false>(V, [&](auto wpl, auto multi) {
         for_each_token_range(T, D, [&](int64_t t0, int64_t t_end, unsigned grid) {
             hipLaunchKernelGGL((dispatch_send_kernel<decltype(wpl)::value, decltype(multi)::value, kDestThreads>),
                                dim3(grid), dim3(kDestThreads), 0, stream,
                                static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, N,
-                               node_slot, Tmax, fd, static_cast<u32x4*>(stage_x), stage_idx, stage_w,
+                               node_slot, Tmax, fd, P, static_cast<u32x4*>(stage_x), stage_idx, stage_w,
                                stage_src, error_flag);
         });
     });
