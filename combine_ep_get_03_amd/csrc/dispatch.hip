@@ -528,15 +528,31 @@ hipError_t with_row_width(int words, F&& f) {
 }
 
 // Launches f(t0, t_end, grid) over consecutive token ranges of at most kDestMaxWaves / D
-// tokens (D waves per token).
+// tokens (D waves per token). Each launch's error is checked before the next; the first
+// one is returned.
 template <typename F>
-void for_each_token_range(int64_t T, int D, F&& f) {
+hipError_t for_each_token_range(int64_t T, int D, F&& f) {
     constexpr int kWpb = kDestThreads / kWave;
     const int64_t per = std::max<int64_t>(1, kDestMaxWaves / D);
     for (int64_t t0 = 0; t0 < T; t0 += per) {
         const int64_t t_end = std::min(T, t0 + per);
         f(t0, t_end, static_cast<unsigned>(((t_end - t0) * D + kWpb - 1) / kWpb));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+// with_row_width over a launch split into token ranges: the first launch error, if any.
+template <int kMax, typename F>
+hipError_t launch_by_token_range(int V, int64_t T, int D, F&& f) {
+    hipError_t err = hipSuccess;
+    const hipError_t last = with_row_width<kMax, false>(V, [&](auto wpl, auto multi) {
+        err = for_each_token_range(T, D, [&](int64_t t0, int64_t t_end, unsigned grid) {
+            f(wpl, multi, t0, t_end, grid);
+        });
+    });
+    return err != hipSuccess ? err : last;
 }
 
 }  // namespace
@@ -550,14 +566,13 @@ hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* 
     const int P = 1;                // destinations per wave
     const int D = std::min(k, R);   // waves per token: ranks a token can reach
     const FastDiv fd = FastDiv::make(D);
-    return with_row_width<14, false>(V, [&](auto wpl, auto multi) {
-        for_each_token_range(T, D, [&](int64_t t0, int64_t t_end, unsigned grid) {
-            hipLaunchKernelGGL((dispatch_kernel<decltype(wpl)::value, decltype(multi)::value, kDestThreads>),
-                               dim3(grid), dim3(kDestThreads), 0, stream,
-                               static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, R,
-                               E / R, token_slot, fd, P, static_cast<u32x4*>(recv_x), recv_idx, recv_w,
-                               recv_src, cap, error_flag);
-        });
+    return launch_by_token_range<14>(V, T, D, [&](auto wpl, auto multi, int64_t t0, int64_t t_end,
+                                                  unsigned grid) {
+        hipLaunchKernelGGL((dispatch_kernel<decltype(wpl)::value, decltype(multi)::value, kDestThreads>),
+                           dim3(grid), dim3(kDestThreads), 0, stream,
+                           static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, R,
+                           E / R, token_slot, fd, P, static_cast<u32x4*>(recv_x), recv_idx, recv_w,
+                           recv_src, cap, error_flag);
     });
 }
 
@@ -572,14 +587,13 @@ hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const flo
     const int D = (std::min(k, R) + P - 1) / P;  // waves per token, at most one block
     const FastDiv fd = FastDiv::make(D);
     // word pairs per lane: 7 covers a 7168-wide row in one pass
-    return with_row_width<7, false>(V / 2, [&](auto wpp, auto multi) {
-        for_each_token_range(T, D, [&](int64_t t0, int64_t t_end, unsigned grid) {
-            hipLaunchKernelGGL((dispatch_fp8_kernel<decltype(wpp)::value, decltype(multi)::value, kDestThreads>),
-                               dim3(grid), dim3(kDestThreads), 0, stream,
-                               static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, R,
-                               E / R, token_slot, fd, P, static_cast<u32x4*>(recv_codes),
-                               recv_scales, recv_idx, recv_w, recv_src, cap, error_flag);
-        });
+    return launch_by_token_range<7>(V / 2, T, D, [&](auto wpp, auto multi, int64_t t0, int64_t t_end,
+                                                    unsigned grid) {
+        hipLaunchKernelGGL((dispatch_fp8_kernel<decltype(wpp)::value, decltype(multi)::value, kDestThreads>),
+                           dim3(grid), dim3(kDestThreads), 0, stream,
+                           static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, R,
+                           E / R, token_slot, fd, P, static_cast<u32x4*>(recv_codes),
+                           recv_scales, recv_idx, recv_w, recv_src, cap, error_flag);
     });
 }
 
@@ -590,13 +604,12 @@ hipError_t launch_dispatch_permute(const void* x, const float* topk_w, int64_t T
     if (T == 0) return hipSuccess;
     const int V = H / 8;
     const FastDiv fd = FastDiv::make(k);
-    return with_row_width<14, false>(V, [&](auto wpl, auto multi) {
-        for_each_token_range(T, k, [&](int64_t t0, int64_t t_end, unsigned grid) {
-            hipLaunchKernelGGL((dispatch_permute_kernel<decltype(wpl)::value, decltype(multi)::value, kDestThreads>),
-                               dim3(grid), dim3(kDestThreads), 0, stream,
-                               static_cast<const u32x4*>(x), topk_w, t0, t_end, V, k, expert_slot,
-                               fd, static_cast<u32x4*>(perm_x), perm_w, perm_src, cap, error_flag);
-        });
+    return launch_by_token_range<14>(V, T, k, [&](auto wpl, auto multi, int64_t t0, int64_t t_end,
+                                                  unsigned grid) {
+        hipLaunchKernelGGL((dispatch_permute_kernel<decltype(wpl)::value, decltype(multi)::value, kDestThreads>),
+                           dim3(grid), dim3(kDestThreads), 0, stream,
+                           static_cast<const u32x4*>(x), topk_w, t0, t_end, V, k, expert_slot,
+                           fd, static_cast<u32x4*>(perm_x), perm_w, perm_src, cap, error_flag);
     });
 }
 
@@ -609,14 +622,13 @@ hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const fl
     const int P = (std::min(k, N) + kMaxWavesPerToken - 1) / kMaxWavesPerToken;
     const int D = (std::min(k, N) + P - 1) / P;  // waves per token, at most one block
     const FastDiv fd = FastDiv::make(D);
-    return with_row_width<14, false>(V, [&](auto wpl, auto multi) {
-        for_each_token_range(T, D, [&](int64_t t0, int64_t t_end, unsigned grid) {
-            hipLaunchKernelGGL((dispatch_send_kernel<decltype(wpl)::value, decltype(multi)::value, kDestThreads>),
-                               dim3(grid), dim3(kDestThreads), 0, stream,
-                               static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, N,
-                               node_slot, Tmax, fd, P, static_cast<u32x4*>(stage_x), stage_idx, stage_w,
-                               stage_src, error_flag);
-        });
+    return launch_by_token_range<14>(V, T, D, [&](auto wpl, auto multi, int64_t t0, int64_t t_end,
+                                                  unsigned grid) {
+        hipLaunchKernelGGL((dispatch_send_kernel<decltype(wpl)::value, decltype(multi)::value, kDestThreads>),
+                           dim3(grid), dim3(kDestThreads), 0, stream,
+                           static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, N,
+                           node_slot, Tmax, fd, P, static_cast<u32x4*>(stage_x), stage_idx, stage_w,
+                           stage_src, error_flag);
     });
 }
 
