@@ -63,12 +63,11 @@ __device__ __forceinline__ void store_row_word(u32x4* p, u32x4 v) {
 #endif
 }
 
-// The destination walk of the one-wave-per-row kernels (FP8 dispatch, receive phase).
-// Slot c of the calling wave's row of C
-// slots, when >= 0, names destination row slot + c * cbase (a slot >= cap is an overflow:
-// skipped, and the error bit set). Destinations are found with one ballot per 64 slots
-// and visited in ascending c through readlane, so the row index handed to visit(row, c)
-// is wave-uniform.
+// The destination walk of the receive phase, whose waves take every destination of a
+// staged row. Slot c of the calling wave's row of C slots, when >= 0, names destination
+// row slot + c * cbase (a slot >= cap is an overflow: skipped, and the error bit set).
+// Destinations are found with one ballot per 64 slots and visited in ascending c through
+// readlane, so the row index handed to visit(row, c) is wave-uniform.
 // One chunk of the walk: lane l holds slot c0 + l (-1 where there is none).
 template <typename Visit>
 __device__ __forceinline__ void visit_chunk(int32_t s, int c0, int64_t cbase, int64_t cap,
