@@ -25,8 +25,8 @@
 // channels, top-8, because the whole resident grid then writes across the whole buffer
 // at once. HBM-write bound. The expert-major permute uses the same form; the FP8
 // dispatch and the two-phase send phase give each wave a range of a token's destinations
-// (at most one block of waves per token), and the receive phase keeps one wave per staged
-// row (each measured faster that way, see their kernels).
+// (at most one block of waves per token), and the receive phase two waves per staged row
+// (each measured faster that way, see their kernels).
 #include <type_traits>
 
 #include "ep_internal.hpp"
@@ -39,11 +39,11 @@ namespace {
 #endif
 
 // Launch shapes, chosen by same-box A/B timing on MI355X at 1024 to 16384 tokens of 7168
-// channels, top-8: 256-thread blocks for the (token, destination) kernels (4-6% faster
-// than 512 at every size but the smallest), the one-pass form in 256-thread blocks for
-// the receive phase.
+// channels, top-8: 256-thread blocks for every dispatch kernel (4-6% faster than 512 at
+// every size but the smallest, 20-35% faster than 128).
 constexpr int kDestThreads = 256;
 constexpr int kRecvThreads = 256;
+constexpr int kRecvWavesPerRow = 2;  // waves per staged row in the receive phase
 // Waves per launch of a (token, destination) kernel; larger batches are split over token
 // ranges, so a wave's index stays a 32-bit value and one launch stays far below the
 // dispatch packet's 2^32 work-item limit.
@@ -61,37 +61,6 @@ __device__ __forceinline__ void store_row_word(u32x4* p, u32x4 v) {
 #else
     *p = v;
 #endif
-}
-
-// The destination walk of the receive phase, whose waves take every destination of a
-// staged row. Slot c of the calling wave's row of C slots, when >= 0, names destination
-// row slot + c * cbase (a slot >= cap is an overflow: skipped, and the error bit set).
-// Destinations are found with one ballot per 64 slots and visited in ascending c through
-// readlane, so the row index handed to visit(row, c) is wave-uniform.
-// One chunk of the walk: lane l holds slot c0 + l (-1 where there is none).
-template <typename Visit>
-__device__ __forceinline__ void visit_chunk(int32_t s, int c0, int64_t cbase, int64_t cap,
-                                            int32_t& errbits, Visit&& visit) {
-    if (s >= cap) {
-        errbits |= kErrRecvOverflow;
-        s = -1;
-    }
-    uint64_t m = wave_ballot(s >= 0);
-    while (m) {
-        const int src_lane = __builtin_ctzll(m);
-        m &= m - 1;
-        const int cd = c0 + src_lane;
-        visit(static_cast<int64_t>(__builtin_amdgcn_readlane(s, src_lane)) + cd * cbase, cd);
-    }
-}
-
-template <typename Visit>
-__device__ __forceinline__ void for_each_destination(const int32_t* __restrict__ srow, int C,
-                                                     int64_t cbase, int64_t cap,
-                                                     int32_t& errbits, Visit&& visit) {
-    const int lane = lane_id();
-    for (int c0 = 0; c0 < C; c0 += kWave)
-        visit_chunk(c0 + lane < C ? srow[c0 + lane] : -1, c0, cbase, cap, errbits, visit);
 }
 
 // A token's k-slot routing as it travels with its row. Lane j < 64 holds slot j (loaded
@@ -136,13 +105,11 @@ struct Routing {
     }
 };
 
-// One source row of V 128-bit words, WPL words per lane in registers per pass, to every
-// destination of the walk, with the routing (rank rank0 + c's view with kRankView) and
-// the source id written once per destination. Rows wider than one pass (V > 64 WPL) need
-// kMulti; without it the pass loop is known to run once, which keeps the register count
-// down (96 against 116 VGPRs at WPL = 14).
-// One pass of a row (words v0 .. v0 + 64 WPL) into destination row sd; the first pass
-// also writes the rank's view of the routing and the source id.
+// One pass of a row (words v0 .. v0 + 64 WPL, WPL words per lane in registers) into
+// destination row sd; the first pass also writes the routing (rank `rank`'s view with
+// kRankView) and the source id. Rows wider than one pass (V > 64 WPL) take the kernels'
+// kMulti pass loop; without it the loop is known to run once, which keeps the register
+// count down.
 template <int WPL, bool kRankView>
 __device__ __forceinline__ void put_row(const u32x4 (&v)[WPL], int v0, int V, int64_t sd,
                                         int rank, const Routing& rt, int er, int32_t src,
@@ -158,34 +125,6 @@ __device__ __forceinline__ void put_row(const u32x4 (&v)[WPL], int v0, int V, in
     if (v0 != 0) return;
     if (dst_idx || dst_w) rt.write<kRankView>(sd, rank, er, dst_idx, dst_w);
     if (dst_src && lane == 0) dst_src[sd] = src;
-}
-
-template <int WPL>
-__device__ __forceinline__ void load_row(u32x4 (&v)[WPL], const u32x4* __restrict__ xr, int v0,
-                                         int V) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int i = 0; i < WPL; ++i) {
-        const int vi = v0 + i * kWave + lane;
-        if (vi < V) v[i] = load_stream(xr + vi);
-    }
-}
-
-template <int WPL, bool kMulti, bool kRankView>
-__device__ __forceinline__ void scatter_row(
-    const u32x4* __restrict__ xr, int V, const Routing& rt, int er, int32_t src,
-    const int32_t* __restrict__ srow, int C, int64_t cbase, int rank0, int64_t cap,
-    u32x4* __restrict__ dst_x, int64_t* __restrict__ dst_idx, float* __restrict__ dst_w,
-    int32_t* __restrict__ dst_src, int32_t& errbits) {
-    for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
-        u32x4 v[WPL];
-        load_row(v, xr, v0, V);
-        for_each_destination(srow, C, cbase, cap, errbits, [&](int64_t sd, int cd) {
-            put_row<WPL, kRankView>(v, v0, V, sd, rank0 + cd, rt, er, src, dst_x, dst_idx, dst_w,
-                                    dst_src);
-        });
-        if constexpr (!kMulti) break;
-    }
 }
 
 // A wave's share of a token's destinations: the destinations with index in [lo, hi),
@@ -349,23 +288,32 @@ __global__ __launch_bounds__(kThreads) void dispatch_permute_kernel(
     }
 }
 
-// Receive phase (the intra-node hop, same page, section 3.3.2): block (b, n) owns staged
-// rows [W b, W b + W) of node n (W waves per block), one wave each; rows at or past count_n[n] are idle. A
-// staged row goes to every rank of node n with a receive slot for its token, with that
-// rank's view of the staged routing, exactly as the one-call dispatch writes it. A
-// staged row has about two receiving ranks at the measured shapes, so one wave per
-// (staged row, destination) left most waves idle and ran 10-40% slower on MI355X; the
-// receive phase keeps one wave per staged row.
+// Receive phase (the intra-node hop, same page, section 3.3.2): a staged row goes to every
+// rank of node n with a receive slot for its token, with that rank's view of the staged
+// routing, exactly as the one-call dispatch writes it. Block (b, n) holds waves p of node
+// n; wave p takes staged row s = p / D of node n and its destinations [d P, d P + P),
+// d = p % D, with D = 2 waves per staged row (the second wave reads the row from L2).
+// The wave issues the staged row's loads before the chain that the destinations need
+// (staged token id, then its slot row), so the two overlap. Measured on MI355X at 7168
+// channels, top-8 over 32 ranks on 4 nodes (about two destinations per staged row): 94.8
+// against 119.6 us for one wave per staged row that loaded the row after the chain; with
+// the new load order, one wave per staged row ran 95.0 at 4096 tokens but 582.6 against
+// 544.9 at 16384 over 64 ranks on 8 nodes, and one wave per destination (8 per staged
+// row, most idle) 131.6.
 template <int WPL, bool kMulti, int kThreads>
 __global__ __launch_bounds__(kThreads) void dispatch_recv_kernel(
     const u32x4* __restrict__ stage_x, const int64_t* __restrict__ stage_idx,
     const float* __restrict__ stage_w, const int32_t* __restrict__ stage_src,
     const int32_t* __restrict__ count_n, int64_t Tmax, int64_t T, int V, int k, int R, int rpn,
-    int er, const int32_t* __restrict__ token_slot, u32x4* __restrict__ recv_x,
+    int er, const int32_t* __restrict__ token_slot, FastDiv D, int P, u32x4* __restrict__ recv_x,
     int64_t* __restrict__ recv_idx, float* __restrict__ recv_w, int32_t* __restrict__ recv_src,
     int64_t cap, int32_t* __restrict__ error_flag) {
     const int n = blockIdx.y;
-    const int64_t s = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+    const int lane = lane_id();
+    const int p = static_cast<int>(blockIdx.x) * (kThreads / kWave) + static_cast<int>(threadIdx.x) / kWave;
+    const int q0 = D.div(p);
+    const int64_t s = q0;
+    const int d = p - q0 * D.d;
     int64_t cnt = count_n[n];
     int32_t errbits = 0;
     if (cnt < 0 || cnt > Tmax || cnt > T) {
@@ -374,18 +322,32 @@ __global__ __launch_bounds__(kThreads) void dispatch_recv_kernel(
     }
     if (s < cnt) {
         const int64_t q = static_cast<int64_t>(n) * Tmax + s;
+        const u32x4* xr = stage_x + q * V;
+        u32x4 v[WPL];
+        load_row_cached(v, xr, 0, V);  // first pass, issued before the token-id chain
         const int64_t t = stage_src[q];
         if (t < 0 || t >= T) {
             errbits |= kErrSlotRange;
         } else {
+            const int32_t* srow = token_slot + t * R + static_cast<int64_t>(n) * rpn;
+            const int32_t s_first = lane < rpn ? srow[lane] : -1;
             const Routing rt(stage_idx ? stage_idx + q * k : nullptr,
                              stage_w ? stage_w + q * k : nullptr, k, recv_idx || recv_w);
-            scatter_row<WPL, kMulti, true>(stage_x + q * V, V, rt, er, static_cast<int32_t>(t),
-                                   token_slot + t * R + n * rpn, rpn, 0, n * rpn, cap, recv_x,
-                                   recv_idx, recv_w, recv_src, errbits);
+            int lo, hi;
+            dest_range(d, D.d, P, lo, hi);
+            for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
+                if (v0 != 0) load_row_cached(v, xr, v0, V);
+                visit_destinations(s_first, srow, rpn, 0, cap, lo, hi, errbits,
+                                   [&](int64_t sd, int cd) {
+                    put_row<WPL, true>(v, v0, V, sd, n * rpn + cd, rt, er,
+                                       static_cast<int32_t>(t), recv_x, recv_idx, recv_w,
+                                       recv_src);
+                });
+                if constexpr (!kMulti) break;
+            }
         }
     }
-    if (errbits && (s < cnt || s == 0)) raise_error(error_flag, errbits);
+    if (errbits && (s < cnt || (s == 0 && d == 0))) raise_error(error_flag, errbits);
 }
 
 // One pass of a row's FP8 quantisation: lane l owns the word pair pi = p0 + 64 i + l
@@ -641,13 +603,17 @@ hipError_t launch_dispatch_recv(const void* stage_x, const int64_t* stage_idx,
     if (rows == 0) return hipSuccess;
     const int V = H / 8;
     constexpr int kThreads = kRecvThreads;
-    const int64_t bx = (rows + kThreads / kWave - 1) / (kThreads / kWave);
-    if (!grid_fits(bx * N, kThreads) || N > 65535) return hipErrorInvalidConfiguration;
+    const int reach = std::min(k, R / N);  // ranks of a node a staged row can reach
+    const int D = std::min(kRecvWavesPerRow, reach);
+    const int P = (reach + D - 1) / D;
+    const int64_t bx = (rows * D + kThreads / kWave - 1) / (kThreads / kWave);
+    if (rows * D > INT32_MAX || !grid_fits(bx * N, kThreads) || N > 65535)
+        return hipErrorInvalidConfiguration;
     return with_row_width<14, false>(V, [&](auto wpl, auto multi) {
         hipLaunchKernelGGL((dispatch_recv_kernel<decltype(wpl)::value, decltype(multi)::value, kThreads>),
                            dim3(static_cast<unsigned>(bx), N), dim3(kThreads), 0, stream,
                            static_cast<const u32x4*>(stage_x), stage_idx, stage_w, stage_src,
-                           count_n, Tmax, T, V, k, R, R / N, E / R, token_slot,
+                           count_n, Tmax, T, V, k, R, R / N, E / R, token_slot, FastDiv::make(D), P,
                            static_cast<u32x4*>(recv_x), recv_idx, recv_w, recv_src, cap,
                            error_flag);
     });
