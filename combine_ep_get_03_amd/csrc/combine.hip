@@ -76,6 +76,59 @@ __device__ __forceinline__ u32x4 sum_rows(const u32x4* __restrict__ partial,
     return o;
 }
 
+// Grouped sums of word vv: the c = gs[G] source rows listed at sl (ascending) form G
+// consecutive groups, group g being sl[gs[g] .. gs[g+1]); group g's fp32 sum (from +0.0f,
+// in list order) is rounded once to bf16 and stored at row g * obase + os[g] of out when
+// os[g] >= 0 (os[g] >= obase is an overflow: skipped, error bit set). Up to kCLoads rows
+// of the whole list are loaded together, so a lane has the loads of every group in
+// flight at once rather than one group's at a time. Against one (group, word) per lane
+// (about two loads in flight at top-8 over 4 nodes), measured on MI355X at 7168 channels:
+// 111.2 against 114.4 us at 4096 tokens, 531.8 against 571.4 at 16384 over 8 nodes.
+__device__ __forceinline__ void sum_groups(const u32x4* __restrict__ partial, const int32_t* sl,
+                                           const int32_t* gs, const int32_t* os, int G, int V,
+                                           int vv, int64_t obase, u32x4* __restrict__ out,
+                                           int32_t& errbits) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    int g = 0;
+    auto close_group = [&]() {
+        const int32_t o = os[g];
+        if (o >= 0) {
+            if (o >= obase) {
+                errbits |= kErrRecvOverflow;
+            } else {
+                u32x4 w;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[q] = pack_bf16(acc[2 * q], acc[2 * q + 1]);
+                store_stream(out + (g * obase + o) * V + vv, w);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        ++g;
+    };
+    const int c = gs[G];
+    for (int d0 = 0; d0 < c; d0 += kCLoads) {
+        u32x4 p[kCLoads];
+#pragma unroll
+        for (int i = 0; i < kCLoads; ++i)
+            if (d0 + i < c) p[i] = load_stream(partial + static_cast<int64_t>(sl[d0 + i]) * V + vv);
+#pragma unroll
+        for (int i = 0; i < kCLoads; ++i) {
+            if (d0 + i < c) {
+                while (d0 + i >= gs[g + 1]) close_group();
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = acc[2 * q] + lo_bf16(p[i][q]);
+                    acc[2 * q + 1] = acc[2 * q + 1] + hi_bf16(p[i][q]);
+                }
+            }
+        }
+    }
+    while (g < G) close_group();
+}
+
 // Source slots: row t of slot_tab holds C columns; column c with slot s >= 0 names source
 // row s + c * cbase (with cbase > 0 a slot must also be below cbase). Without kGrouped
 // every token's sources are summed into out[t]. With kGrouped the C columns form G
@@ -143,22 +196,12 @@ __device__ __forceinline__ void combine_body(
                              sum_rows(partial, s_slot + tt * C, s_cnt[tt], V, vv));
             }
         } else {
-            const int total = nt * G * V;
+            const int total = nt * V;
             for (int f = tid; f < total; f += kCT) {
-                const int tg = f / V;
-                const int vv = f - tg * V;
-                const int tt = tg / G;
-                const int g = tg - tt * G;
-                const int32_t os = s_os[tg];
-                if (os < 0) continue;
-                if (os >= obase) {
-                    errbits |= kErrRecvOverflow;
-                    continue;
-                }
-                const int b = s_gs[tt * (G + 1) + g];
-                const int e = s_gs[tt * (G + 1) + g + 1];
-                store_stream(out + (g * obase + os) * V + vv,
-                             sum_rows(partial, s_slot + tt * C + b, e - b, V, vv));
+                const int tt = f / V;
+                const int vv = f - tt * V;
+                sum_groups(partial, s_slot + tt * C, s_gs + tt * (G + 1), s_os + tt * G, G, V, vv,
+                           obase, out, errbits);
             }
         }
         if (kCGridCap > 0) __syncthreads();  // the next group reuses the LDS lists
@@ -198,7 +241,7 @@ static hipError_t launch_combine_impl(Kernel kernel, const void* partial, int64_
     if (T == 0) return hipSuccess;
     const int V = H / 8;
     const int per_token = C + (kGrouped ? 2 * G + 1 : 1);
-    const int tpb = combine_tokens_per_block(kGrouped ? V * G : V, per_token);
+    const int tpb = combine_tokens_per_block(V, per_token);
     const int64_t groups = (T + tpb - 1) / tpb;
     const int64_t grid = kCGridCap > 0 ? std::min<int64_t>(groups, kCGridCap) : groups;
     if (!grid_fits(grid, kCT)) return hipErrorInvalidConfiguration;
