@@ -62,6 +62,11 @@ int ep_get_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int
     if (!num_tokens_per_rank || !rank_offset || !error_flag) return EP_ERR_ARG;
     if (T > 0 && (!topk_idx || !token_slot)) return EP_ERR_ARG;
     if (expert_slot && k > EP_EXPERT_SLOT_MAX_K) return EP_ERR_ARG;
+    // per-expert counts, expert offsets and expert-major rows count (token, slot) pairs
+    // in int32: up to T * k of them
+    if ((num_tokens_per_expert || expert_offset || expert_slot) &&
+        T > static_cast<int64_t>(INT32_MAX) / k)
+        return EP_ERR_ARG;
     if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) || !aligned(expert_slot, 4) ||
         !aligned(node_slot, 4) ||
         !aligned(num_tokens_per_node, 4) || !aligned(num_tokens_per_expert, 4) ||

@@ -66,6 +66,15 @@ constexpr int32_t kErrSlotRange = 4;
 // Each returns hipSuccess or the error reported at launch. Arguments have been
 // validated by the C ABI layer.
 
+// HIP records the status of every runtime call as the thread's last error, so a later
+// successful launch would hide an earlier failed one: a launcher that enqueues several
+// kernels checks after each launch and returns the first failure.
+#define EP_RETURN_IF_LAUNCH_FAILED()                             \
+    do {                                                         \
+        const hipError_t ep_launch_err_ = hipGetLastError();     \
+        if (ep_launch_err_ != hipSuccess) return ep_launch_err_; \
+    } while (0)
+
 struct LayoutWorkspace {
     int32_t* blk_rank;   // [nb][R]  per-block rank counts, then per-block exclusive prefix
     int32_t* blk_node;   // [nb][N]

@@ -819,14 +819,16 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
                                R, N, er, rpn, count_r, count_n, count_e, rank_offset, expert_offset,
                                error_flag, token_slot, in_rank, vec ? 1 : 0,
                                want_base ? ws.blk_exp_base : nullptr, node_slot, vec_node ? 1 : 0);
+            EP_RETURN_IF_LAUNCH_FAILED();
             if (want_base) {
                 int nbits = 0;
                 while ((1 << nbits) < E) ++nbits;
                 hipLaunchKernelGGL(layout_expert_slot_kernel, dim3(1), dim3(kBT),
                                    sizeof(uint16_t) * kWavesBT * E, stream, topk_idx, T, k, E,
                                    nbits, ws.blk_exp_base, expert_slot);
+                EP_RETURN_IF_LAUNCH_FAILED();
             }
-            return hipGetLastError();
+            return hipSuccess;
         }
     }
     if (nb > 0) {
@@ -834,6 +836,7 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
                            sizeof(uint16_t) * kWavesBT * (R + N);
         hipLaunchKernelGGL(layout_count_kernel<NW>, dim3(static_cast<unsigned>(nb)), dim3(kBT),
                            shm, stream, topk_idx, T, k, E, R, N, er, rpn, ws);
+        EP_RETURN_IF_LAUNCH_FAILED();
     }
     bool fused = false;
     if constexpr (NW * kWave <= kFusedMaxRanks)  // the fused kernel needs R <= 256
@@ -848,18 +851,21 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
                            topk_idx, T, k, E, R, N, er, static_cast<int>(nb), ws, count_r,
                            count_n, count_e, rank_offset, expert_offset, error_flag, token_slot,
                            in_rank, vec ? 1 : 0, want_base, rpn, node_slot, vec_node ? 1 : 0);
+        EP_RETURN_IF_LAUNCH_FAILED();
         }
     } else {
         hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
                            static_cast<int>(nb), E, R, N, ws, count_r, count_n, count_e,
                            rank_offset, expert_offset, error_flag, want_base,
                            node_slot != nullptr ? 1 : 0);
+        EP_RETURN_IF_LAUNCH_FAILED();
         if (nb > 0) {
             const size_t shm =
                 static_cast<size_t>(kWavesBT) * R * (sizeof(uint64_t) + sizeof(int32_t));
             hipLaunchKernelGGL(layout_slot_kernel<NW>, dim3(static_cast<unsigned>(nb)), dim3(kBT),
                                shm, stream, topk_idx, T, k, E, R, er, ws.blk_rank, rank_offset,
                                token_slot, in_rank, N, rpn, ws.blk_node, node_slot);
+            EP_RETURN_IF_LAUNCH_FAILED();
         }
     }
     if (want_base && nb > 0) {
@@ -868,8 +874,9 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
         hipLaunchKernelGGL(layout_expert_slot_kernel, dim3(static_cast<unsigned>(nb)), dim3(kBT),
                            sizeof(uint16_t) * kWavesBT * E, stream, topk_idx, T, k, E, nbits,
                            ws.blk_exp_base, expert_slot);
+        EP_RETURN_IF_LAUNCH_FAILED();
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace

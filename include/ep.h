@@ -56,7 +56,11 @@ enum {
     EP_OK = 0,
     EP_ERR_ARG = -1,       /* a count or size out of range, or a required pointer is NULL */
     EP_ERR_ALIGN = -2,     /* a pointer or row length breaks the alignment rule of the call */
-    EP_ERR_CAPACITY = -3,  /* a destination or workspace smaller than the call requires */
+    EP_ERR_CAPACITY = -3,  /* a destination or workspace smaller than the call requires
+                              (the host-side counterpart of the check against too large a
+                              receive token count in the commit list of "[PR #453] Higher
+                              Performance with Lower SM Occupancy through Zero-Copy and TMA
+                              Offloading") */
     EP_ERR_HIP = -4        /* the HIP runtime reported an error when the work was enqueued */
 };
 
@@ -77,9 +81,13 @@ enum {
 /* Static string for a status code; never NULL. */
 const char *ep_status_string(int status);
 
-/* Bytes of device workspace ep_get_layout needs for these sizes. Returns 0 when
- * num_tokens == 0 (no workspace needed; NULL is then accepted) and also when the sizes are
- * ones ep_get_layout rejects. */
+/* Bytes of device workspace ep_get_layout needs for these sizes: the size query a caller
+ * makes before allocating ("[PR #347] Feature/sm free normal kernel", section 2.2.2, a
+ * utility that estimates the minimum buffer size before the call). The workspace holds
+ * per-256-token-block count tables: rank counts [nb][R], node counts [nb][N], two expert
+ * tables [nb][E] and error bits [nb], nb = ceil(T / 256), each 256-byte aligned. Returns 0
+ * when num_tokens == 0 (no workspace needed; NULL is then accepted) and also when the
+ * sizes are ones ep_get_layout rejects. */
 size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_experts, int num_ranks,
                                  int num_nodes);
 
@@ -111,7 +119,9 @@ size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_experts, int num_ra
  * Workspace: `workspace` of `workspace_bytes` >= ep_layout_workspace_bytes(T, E, R, N) bytes,
  *   16-byte aligned, contents on entry irrelevant, clobbered.
  * Sizes: T >= 0, 1 <= k <= E, 1 <= R <= EP_MAX_RANKS, E <= EP_MAX_EXPERTS, E % R == 0,
- *   1 <= N, R % N == 0, T * min(k, R) <= INT32_MAX.
+ *   1 <= N, R % N == 0, T * min(k, R) <= INT32_MAX; and T * k <= INT32_MAX when any of
+ *   num_tokens_per_expert, expert_offset or expert_slot is non-NULL (they count
+ *   (token, slot) pairs in int32).
  * Errors: EP_ERR_ARG (sizes, NULL), EP_ERR_ALIGN (int32/int64 arrays not naturally aligned,
  *   workspace not 16-byte aligned), EP_ERR_CAPACITY (workspace too small), EP_ERR_HIP.
  * T == 0 is valid: counts and offsets are written as zeros. */
@@ -223,7 +233,11 @@ int ep_restripe_prob_sparse(const float *prob, int64_t num_tokens, int num_nodes
                             int64_t max_tokens_per_rank, float *prob_dest_major,
                             int32_t *error_flag, void *stream);
 
-/* ep_combine -- gather each token's per-rank partial rows back to token order and sum them.
+/* ep_combine -- gather each token's per-rank partial rows back to token order and sum them:
+ * the reverse of ep_dispatch, moving the same rows back ("[PR #347] Feature/sm free normal
+ * kernel", section 3.2.1: its combine table measures the dispatch payload travelling back;
+ * "[PR #453]" description: combine measured beside dispatch). The sum is unweighted: the
+ * top-k weights are taken to be applied inside each rank's expert output.
  *
  * In:  partial     bf16 [num_partial_rows][H], laid out like ep_dispatch's recv_x
  *      token_slot  int32 [T][R] from ep_get_layout

@@ -81,9 +81,9 @@ def test_workspace_query(lib):
 
 
 def _layout(lib, T=100, k=4, E=16, R=4, N=2, idx=A16, ws=A16, wsb=1 << 20, slot=A16,
-            eslot=None):
-    return lib.ep_get_layout(idx, T, k, E, R, N, A16, A16, A16, A16, A16, A16, slot, eslot, None,
-                             A16, ws, wsb, None)
+            eslot=None, count_e=A16, eoff=A16):
+    return lib.ep_get_layout(idx, T, k, E, R, N, A16, A16, count_e, A16, A16, eoff, slot, eslot,
+                             None, A16, ws, wsb, None)
 
 
 def test_layout_validation(lib):
@@ -103,6 +103,21 @@ def test_layout_validation(lib):
     assert _layout(lib, ws=None) == ep.EP_ERR_CAPACITY
     assert _layout(lib, k=17, E=32, eslot=A16) == ep.EP_ERR_ARG   # expert slots need k <= 16
     assert _layout(lib, eslot=P(0x10002)) == ep.EP_ERR_ALIGN
+
+
+def test_layout_rejects_pair_counts_past_int32(lib):
+    # top-8 over 4 ranks: T * min(k, R) = 4T fits in int32 but T * k = 8T does not, and the
+    # per-expert counts, expert offsets and expert-major rows count (token, slot) pairs
+    T, k, E, R = 300_000_000, 8, 16, 4
+    assert T * min(k, R) <= 2**31 - 1 < T * k
+    assert _layout(lib, T=T, k=k, E=E, R=R) == ep.EP_ERR_ARG
+    assert _layout(lib, T=T, k=k, E=E, R=R, eoff=None) == ep.EP_ERR_ARG
+    assert _layout(lib, T=T, k=k, E=E, R=R, count_e=None) == ep.EP_ERR_ARG
+    assert _layout(lib, T=T, k=k, E=E, R=R, count_e=None, eoff=None, eslot=A16) == ep.EP_ERR_ARG
+    # without those outputs the batch passes the size checks (and stops at the workspace)
+    assert _layout(lib, T=T, k=k, E=E, R=R, count_e=None, eoff=None) == ep.EP_ERR_CAPACITY
+    # at T * k <= INT32_MAX the same outputs are accepted
+    assert _layout(lib, T=(2**31 - 1) // k, k=k, E=E, R=R) == ep.EP_ERR_CAPACITY
 
 
 def test_dispatch_permute_validation(lib):
