@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libep.so")
 EP_OK, EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_CAPACITY, EP_ERR_HIP = 0, -1, -2, -3, -4
 EP_DEVERR_TOPK_RANGE, EP_DEVERR_RECV_OVERFLOW, EP_DEVERR_SLOT_RANGE = 1, 2, 4
 EP_MAX_RANKS, EP_MAX_EXPERTS, EP_EXPERT_SLOT_MAX_K = 1024, 8192, 16
+EP_LAYOUT_SCRATCH_BYTES = 4 << 20
 
 _lib = None
 
@@ -43,6 +44,8 @@ def load() -> ctypes.CDLL:
     L.ep_layout_workspace_bytes.restype = sz
     L.ep_get_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, sz,
                                 P]
+    L.ep_get_layout_no_alloc.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                                         P, P]
     L.ep_restripe_prob_sparse.argtypes = [P, i64, i32, i32, P, i64, P, P, P]
     L.ep_dispatch_permute.argtypes = [P, P, i64, i32, i32, P, P, P, P, i64, P, P]
     L.ep_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, i64, P, P]
@@ -56,7 +59,7 @@ def load() -> ctypes.CDLL:
     L.ep_combine_send.argtypes = [P, i64, P, i64, i32, i32, i32, P, i64, P, P, P]
     L.ep_combine_recv.argtypes = [P, i32, i64, P, i64, i32, P, P, P]
     L.ep_hbm_copy.argtypes = [P, P, sz, P]
-    for f in ("ep_get_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
+    for f in ("ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
               "ep_restripe_prob", "ep_restripe_prob_sparse", "ep_combine", "ep_dispatch_send",
               "ep_dispatch_recv", "ep_combine_send", "ep_combine_recv", "ep_hbm_copy"):
         getattr(L, f).restype = i32
@@ -125,12 +128,11 @@ def ep_layout_workspace_bytes(num_tokens: int, num_experts: int, num_ranks: int,
     return int(load().ep_layout_workspace_bytes(num_tokens, num_experts, num_ranks, num_nodes))
 
 
-def ep_get_layout(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
-                  num_tokens_per_rank, num_tokens_per_node, num_tokens_per_expert,
-                  is_token_in_rank, rank_offset, expert_offset, token_slot, error_flag,
-                  workspace, expert_slot=None, node_slot=None, stream=None) -> None:
+def _layout_outputs(topk_idx, E: int, R: int, N: int, num_tokens_per_rank, num_tokens_per_node,
+                    num_tokens_per_expert, is_token_in_rank, rank_offset, expert_offset,
+                    token_slot, expert_slot, node_slot, error_flag):
+    """Shape checks and pointers of ep_get_layout's outputs, in the C argument order."""
     T, k = topk_idx.shape
-    E, R, N = num_experts, num_ranks, num_nodes
     _at_least(num_tokens_per_rank, R, "num_tokens_per_rank")
     _at_least(num_tokens_per_node, N, "num_tokens_per_node")
     _at_least(num_tokens_per_expert, E, "num_tokens_per_expert")
@@ -141,21 +143,44 @@ def ep_get_layout(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
     _shape(expert_slot, (T, k), "expert_slot")
     _shape(node_slot, (T, N), "node_slot")
     _at_least(error_flag, 1, "error_flag")
+    return (_ptr(topk_idx, torch.int64, "topk_idx"), T, k, E, R, N,
+            _ptr(num_tokens_per_rank, torch.int32, "num_tokens_per_rank"),
+            _ptr(num_tokens_per_node, torch.int32, "num_tokens_per_node", True),
+            _ptr(num_tokens_per_expert, torch.int32, "num_tokens_per_expert", True),
+            _ptr(is_token_in_rank, torch.uint8, "is_token_in_rank", True),
+            _ptr(rank_offset, torch.int32, "rank_offset"),
+            _ptr(expert_offset, torch.int32, "expert_offset", True),
+            _ptr(token_slot, torch.int32, "token_slot"),
+            _ptr(expert_slot, torch.int32, "expert_slot", True),
+            _ptr(node_slot, torch.int32, "node_slot", True),
+            _ptr(error_flag, torch.int32, "error_flag"))
+
+
+def ep_get_layout(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
+                  num_tokens_per_rank, num_tokens_per_node, num_tokens_per_expert,
+                  is_token_in_rank, rank_offset, expert_offset, token_slot, error_flag,
+                  workspace, expert_slot=None, node_slot=None, stream=None) -> None:
+    args = _layout_outputs(topk_idx, num_experts, num_ranks, num_nodes, num_tokens_per_rank,
+                           num_tokens_per_node, num_tokens_per_expert, is_token_in_rank,
+                           rank_offset, expert_offset, token_slot, expert_slot, node_slot,
+                           error_flag)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(load().ep_get_layout(
-        _ptr(topk_idx, torch.int64, "topk_idx"), T, k, num_experts, num_ranks, num_nodes,
-        _ptr(num_tokens_per_rank, torch.int32, "num_tokens_per_rank"),
-        _ptr(num_tokens_per_node, torch.int32, "num_tokens_per_node", True),
-        _ptr(num_tokens_per_expert, torch.int32, "num_tokens_per_expert", True),
-        _ptr(is_token_in_rank, torch.uint8, "is_token_in_rank", True),
-        _ptr(rank_offset, torch.int32, "rank_offset"),
-        _ptr(expert_offset, torch.int32, "expert_offset", True),
-        _ptr(token_slot, torch.int32, "token_slot"),
-        _ptr(expert_slot, torch.int32, "expert_slot", True),
-        _ptr(node_slot, torch.int32, "node_slot", True),
-        _ptr(error_flag, torch.int32, "error_flag"),
-        _ptr(workspace, torch.uint8, "workspace", True), ws_bytes, _stream(stream)),
-        "ep_get_layout")
+    _check(load().ep_get_layout(*args, _ptr(workspace, torch.uint8, "workspace", True),
+                                ws_bytes, _stream(stream)), "ep_get_layout")
+
+
+def ep_get_layout_no_alloc(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
+                           num_tokens_per_rank, num_tokens_per_node, num_tokens_per_expert,
+                           is_token_in_rank, rank_offset, expert_offset, token_slot,
+                           error_flag, expert_slot=None, node_slot=None, stream=None) -> None:
+    """ep_get_layout without a workspace: the library's static device scratch holds the
+    per-block tables (sizes up to EP_LAYOUT_SCRATCH_BYTES of tables; calls overlapping in
+    time on one GPU race on it)."""
+    args = _layout_outputs(topk_idx, num_experts, num_ranks, num_nodes, num_tokens_per_rank,
+                           num_tokens_per_node, num_tokens_per_expert, is_token_in_rank,
+                           rank_offset, expert_offset, token_slot, expert_slot, node_slot,
+                           error_flag)
+    _check(load().ep_get_layout_no_alloc(*args, _stream(stream)), "ep_get_layout_no_alloc")
 
 
 def ep_dispatch(x, topk_idx, topk_weights, num_experts: int, num_ranks: int, token_slot, *,

@@ -26,6 +26,28 @@ bool slots_fit_int32(int64_t T, int k, int R) {
     return T >= 0 && (T == 0 || T <= static_cast<int64_t>(INT32_MAX) / per);
 }
 
+// Every check of ep_get_layout except those of the workspace.
+int check_layout_args(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
+                      const int32_t* count_r, const int32_t* count_n, const int32_t* count_e,
+                      const int32_t* rank_offset, const int32_t* expert_offset,
+                      const int32_t* token_slot, const int32_t* expert_slot,
+                      const int32_t* node_slot, const int32_t* error_flag) {
+    if (!topology_ok(k, E, R, N) || !slots_fit_int32(T, k, R)) return EP_ERR_ARG;
+    if (!count_r || !rank_offset || !error_flag) return EP_ERR_ARG;
+    if (T > 0 && (!topk_idx || !token_slot)) return EP_ERR_ARG;
+    if (expert_slot && k > EP_EXPERT_SLOT_MAX_K) return EP_ERR_ARG;
+    // per-expert counts, expert offsets and expert-major rows count (token, slot) pairs
+    // in int32: up to T * k of them
+    if ((count_e || expert_offset || expert_slot) && T > static_cast<int64_t>(INT32_MAX) / k)
+        return EP_ERR_ARG;
+    if (!aligned(topk_idx, 8) || !aligned(count_r, 4) || !aligned(expert_slot, 4) ||
+        !aligned(node_slot, 4) || !aligned(count_n, 4) || !aligned(count_e, 4) ||
+        !aligned(rank_offset, 4) || !aligned(expert_offset, 4) || !aligned(token_slot, 4) ||
+        !aligned(error_flag, 4))
+        return EP_ERR_ALIGN;
+    return EP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -58,24 +80,50 @@ int ep_get_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int
                   int32_t* error_flag, void* workspace, size_t workspace_bytes, void* stream) {
     const int64_t T = num_tokens;
     const int k = num_topk, E = num_experts, R = num_ranks, N = num_nodes;
-    if (!topology_ok(k, E, R, N) || !slots_fit_int32(T, k, R)) return EP_ERR_ARG;
-    if (!num_tokens_per_rank || !rank_offset || !error_flag) return EP_ERR_ARG;
-    if (T > 0 && (!topk_idx || !token_slot)) return EP_ERR_ARG;
-    if (expert_slot && k > EP_EXPERT_SLOT_MAX_K) return EP_ERR_ARG;
-    // per-expert counts, expert offsets and expert-major rows count (token, slot) pairs
-    // in int32: up to T * k of them
-    if ((num_tokens_per_expert || expert_offset || expert_slot) &&
-        T > static_cast<int64_t>(INT32_MAX) / k)
-        return EP_ERR_ARG;
-    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) || !aligned(expert_slot, 4) ||
-        !aligned(node_slot, 4) ||
-        !aligned(num_tokens_per_node, 4) || !aligned(num_tokens_per_expert, 4) ||
-        !aligned(rank_offset, 4) || !aligned(expert_offset, 4) || !aligned(token_slot, 4) ||
-        !aligned(error_flag, 4) || !aligned(workspace, 16))
-        return EP_ERR_ALIGN;
+    const int st = check_layout_args(topk_idx, T, k, E, R, N, num_tokens_per_rank,
+                                     num_tokens_per_node, num_tokens_per_expert, rank_offset,
+                                     expert_offset, token_slot, expert_slot, node_slot,
+                                     error_flag);
+    if (st != EP_OK) return st;
+    if (!aligned(workspace, 16)) return EP_ERR_ALIGN;
     const size_t need = ep::layout_workspace_bytes(T, E, R, N);
     if (workspace_bytes < need || (need > 0 && !workspace)) return EP_ERR_CAPACITY;
     const ep::LayoutWorkspace ws = ep::carve_layout_workspace(workspace, T, E, R, N);
+    return hip_status(ep::launch_layout(topk_idx, T, k, E, R, N, num_tokens_per_rank,
+                                        num_tokens_per_node, num_tokens_per_expert,
+                                        is_token_in_rank, rank_offset, expert_offset, token_slot,
+                                        expert_slot, node_slot, error_flag, ws,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int ep_get_layout_no_alloc(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                           int num_experts, int num_ranks, int num_nodes,
+                           int32_t* num_tokens_per_rank, int32_t* num_tokens_per_node,
+                           int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                           int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
+                           int32_t* expert_slot, int32_t* node_slot, int32_t* error_flag,
+                           void* stream) {
+    const int64_t T = num_tokens;
+    const int k = num_topk, E = num_experts, R = num_ranks, N = num_nodes;
+    const int st = check_layout_args(topk_idx, T, k, E, R, N, num_tokens_per_rank,
+                                     num_tokens_per_node, num_tokens_per_expert, rank_offset,
+                                     expert_offset, token_slot, expert_slot, node_slot,
+                                     error_flag);
+    if (st != EP_OK) return st;
+    if (ep::layout_workspace_bytes(T, E, R, N) > EP_LAYOUT_SCRATCH_BYTES) return EP_ERR_CAPACITY;
+    // The kernels run on the stream's device and use that device's copy of the scratch
+    // array, whose address is looked up with that device current.
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return EP_ERR_HIP;
+    if (stream != nullptr) {
+        int sdev = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+            return EP_ERR_HIP;
+        if (sdev != dev) return EP_ERR_ARG;
+    }
+    void* scratch = nullptr;
+    if (ep::layout_scratch_address(&scratch) != hipSuccess) return EP_ERR_HIP;
+    const ep::LayoutWorkspace ws = ep::carve_layout_workspace(scratch, T, E, R, N);
     return hip_status(ep::launch_layout(topk_idx, T, k, E, R, N, num_tokens_per_rank,
                                         num_tokens_per_node, num_tokens_per_expert,
                                         is_token_in_rank, rank_offset, expert_offset, token_slot,

@@ -88,6 +88,12 @@ constexpr int kLayoutBlockTokens = 256;  // one token per thread
 size_t layout_workspace_bytes(int64_t T, int E, int R, int N);
 LayoutWorkspace carve_layout_workspace(void* base, int64_t T, int E, int R, int N);
 
+// Size of the static device scratch that stands in for the workspace in the entry point
+// that allocates nothing (= EP_LAYOUT_SCRATCH_BYTES of the public header).
+constexpr size_t kLayoutScratchBytes = size_t{4} << 20;
+// The current device's address of that scratch array (looked up once per device).
+hipError_t layout_scratch_address(void** out);
+
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
                          int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                          int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,

@@ -23,9 +23,19 @@
 // one-block scan launch between the two computes the per-block rank prefixes.
 // Small tables are read with several loads in flight per lane: the path is latency
 // bound, so each block waits on as few memory round trips as possible.
+#include <atomic>
+#include <mutex>
+
 #include "ep_internal.hpp"
 
 namespace ep {
+
+// Device scratch for ep_get_layout_no_alloc, the entry point for callers that cannot
+// allocate: the per-block count tables go here instead of a caller workspace. Each GPU
+// holds its own copy at its own address until the process ends. In host code the name
+// is only a host-side stand-in: kernels get the address layout_scratch_address returns.
+static __device__ __align__(256) unsigned char scratch[kLayoutScratchBytes];
+
 namespace {
 
 constexpr int kBT = kLayoutBlockTokens;  // tokens (= threads) per block
@@ -901,6 +911,33 @@ LayoutWorkspace carve_layout_workspace(void* base, int64_t T, int E, int R, int 
     p += align_up(nb * E * 4, 256);
     ws.blk_err = reinterpret_cast<int32_t*>(p);
     return ws;
+}
+
+namespace {
+constexpr int kScratchMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kScratchMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+// Looked up with the device current, once per device; later calls read the kept address.
+hipError_t layout_scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
 }
 
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,

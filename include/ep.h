@@ -77,6 +77,7 @@ enum {
 #define EP_MAX_RANKS   1024
 #define EP_MAX_EXPERTS 8192
 #define EP_EXPERT_SLOT_MAX_K 16  /* largest top-k for which ep_get_layout fills expert_slot */
+#define EP_LAYOUT_SCRATCH_BYTES 4194304  /* device scratch of ep_get_layout_no_alloc (4 MiB) */
 
 /* Static string for a status code; never NULL. */
 const char *ep_status_string(int status);
@@ -132,6 +133,30 @@ int ep_get_layout(const int64_t *topk_idx, int64_t num_tokens, int num_topk,
                   int32_t *rank_offset, int32_t *expert_offset, int32_t *token_slot,
                   int32_t *expert_slot, int32_t *node_slot, int32_t *error_flag,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* ep_get_layout_no_alloc -- ep_get_layout for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, checks and outputs, bit for bit, but no workspace argument. The
+ * per-block count tables live in a static device array of EP_LAYOUT_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends; this call makes no
+ * allocation of any kind.
+ * Limit: ep_layout_workspace_bytes(T, E, R, N) <= EP_LAYOUT_SCRATCH_BYTES, else
+ *   EP_ERR_CAPACITY with nothing enqueued (at E = 256, R = 64, N = 8: up to 458 752
+ *   tokens).
+ * Every call on one GPU shares that GPU's array, and it keeps the last call's contents
+ * (nothing in it needs to start at zero). Calls whose work overlaps in time on one GPU --
+ * on two streams, or from two threads -- race on the array and give undefined outputs;
+ * stream-ordered calls are safe.
+ * `stream` must belong to the current device (else EP_ERR_ARG). The first call on a
+ * device looks up that device's address of the array (EP_ERR_HIP if the lookup fails).
+ * Errors: as ep_get_layout, with EP_ERR_CAPACITY for sizes past the scratch. */
+int ep_get_layout_no_alloc(const int64_t *topk_idx, int64_t num_tokens, int num_topk,
+                           int num_experts, int num_ranks, int num_nodes,
+                           int32_t *num_tokens_per_rank, int32_t *num_tokens_per_node,
+                           int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                           int32_t *rank_offset, int32_t *expert_offset, int32_t *token_slot,
+                           int32_t *expert_slot, int32_t *node_slot, int32_t *error_flag,
+                           void *stream);
 
 /* ep_dispatch -- pack every (token, rank) pair into its receive row.
  *

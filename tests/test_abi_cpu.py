@@ -37,7 +37,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) >= {"ep_get_layout", "ep_dispatch", "ep_restripe_prob", "ep_combine",
+    assert set(names) >= {"ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch",
+                          "ep_restripe_prob", "ep_combine",
                           "ep_layout_workspace_bytes", "ep_status_string", "ep_hbm_copy",
                           "ep_dispatch_fp8", "ep_dispatch_permute", "ep_restripe_prob_sparse",
                           "ep_dispatch_send", "ep_dispatch_recv", "ep_combine_send",
@@ -118,6 +119,27 @@ def test_layout_rejects_pair_counts_past_int32(lib):
     assert _layout(lib, T=T, k=k, E=E, R=R, count_e=None, eoff=None) == ep.EP_ERR_CAPACITY
     # at T * k <= INT32_MAX the same outputs are accepted
     assert _layout(lib, T=(2**31 - 1) // k, k=k, E=E, R=R) == ep.EP_ERR_CAPACITY
+
+
+def test_layout_no_alloc_validation(lib):
+    # the same argument checks as ep_get_layout, and tables past the static scratch are
+    # refused on the host, before any HIP call (so no GPU is touched here)
+    f = lambda T=100, k=4, E=16, R=4, N=2, idx=A16, slot=A16, eslot=None: \
+        lib.ep_get_layout_no_alloc(idx, T, k, E, R, N, A16, A16, A16, A16, A16, A16, slot, eslot,
+                                   None, A16, None)
+    assert f(E=15) == ep.EP_ERR_ARG
+    assert f(N=3) == ep.EP_ERR_ARG
+    assert f(idx=None) == ep.EP_ERR_ARG
+    assert f(slot=None) == ep.EP_ERR_ARG
+    assert f(k=17, E=32, eslot=A16) == ep.EP_ERR_ARG
+    assert f(T=300_000_000, k=8, E=16, R=4) == ep.EP_ERR_ARG   # T * k past int32
+    assert f(idx=MIS) == ep.EP_ERR_ALIGN
+    assert ep.EP_LAYOUT_SCRATCH_BYTES == 4 << 20
+    fits, past = 458752, 458753                                  # at E=256, R=64, N=8
+    assert ep.ep_layout_workspace_bytes(fits, 256, 64, 8) <= ep.EP_LAYOUT_SCRATCH_BYTES
+    assert ep.ep_layout_workspace_bytes(past, 256, 64, 8) > ep.EP_LAYOUT_SCRATCH_BYTES
+    assert f(T=past, k=8, E=256, R=64, N=8) == ep.EP_ERR_CAPACITY
+    assert f(T=10**6, k=8, E=8192, R=64, N=8) == ep.EP_ERR_CAPACITY
 
 
 def test_dispatch_permute_validation(lib):
