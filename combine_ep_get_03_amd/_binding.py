@@ -46,6 +46,8 @@ def load() -> ctypes.CDLL:
                                 P]
     L.ep_get_layout_no_alloc.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
                                          P, P]
+    L.ep_dispatch_preprocess.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                                         P, P, i32, i64, P, P, sz, P]
     L.ep_restripe_prob_sparse.argtypes = [P, i64, i32, i32, P, i64, P, P, P]
     L.ep_dispatch_permute.argtypes = [P, P, i64, i32, i32, P, P, P, P, i64, P, P]
     L.ep_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, i64, P, P]
@@ -53,15 +55,17 @@ def load() -> ctypes.CDLL:
                                   P]
     L.ep_restripe_prob.argtypes = [P, i64, i32, i32, i64, P, P]
     L.ep_combine.argtypes = [P, i64, P, i64, i32, i32, P, P, P]
-    L.ep_dispatch_send.argtypes = [P, P, P, i64, i32, i32, i32, P, i64, P, P, P, P, P, P]
+    L.ep_dispatch_send.argtypes = [P, P, P, i64, i32, i32, i32, P, i64, P, P, P, P, P, i32, P]
     L.ep_dispatch_recv.argtypes = [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P, P, P,
                                    P, i64, P, P]
-    L.ep_combine_send.argtypes = [P, i64, P, i64, i32, i32, i32, P, i64, P, P, P]
+    L.ep_combine_send.argtypes = [P, i64, P, i64, i32, i32, i32, P, i64, P, P, i32, P]
     L.ep_combine_recv.argtypes = [P, i32, i64, P, i64, i32, P, P, P]
     L.ep_hbm_copy.argtypes = [P, P, sz, P]
-    for f in ("ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
+    L.ep_hbm_fan.argtypes = [P, P, sz, i32, i32, P]
+    for f in ("ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch_preprocess", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
               "ep_restripe_prob", "ep_restripe_prob_sparse", "ep_combine", "ep_dispatch_send",
-              "ep_dispatch_recv", "ep_combine_send", "ep_combine_recv", "ep_hbm_copy"):
+              "ep_dispatch_recv", "ep_combine_send", "ep_combine_recv", "ep_hbm_copy",
+              "ep_hbm_fan"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -181,6 +185,33 @@ def ep_get_layout_no_alloc(topk_idx, num_experts: int, num_ranks: int, num_nodes
                            rank_offset, expert_offset, token_slot, expert_slot, node_slot,
                            error_flag)
     _check(load().ep_get_layout_no_alloc(*args, _stream(stream)), "ep_get_layout_no_alloc")
+
+
+def ep_dispatch_preprocess(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, prob,
+                           prob_dest_major, *, num_tokens_per_rank, num_tokens_per_node,
+                           num_tokens_per_expert, is_token_in_rank, rank_offset, expert_offset,
+                           token_slot, error_flag, workspace, expert_slot=None, node_slot=None,
+                           stream=None) -> None:
+    """ep_get_layout and ep_restripe_prob in one call (the restripe rides along in the
+    layout's first launch): prob fp32 [T][N][P] -> prob_dest_major fp32 [N][Tmax][P]."""
+    T = topk_idx.shape[0]
+    if prob.dim() != 3 or prob_dest_major.dim() != 3:
+        raise ValueError("prob must be [T][N][P] and prob_dest_major [N][Tmax][P]")
+    Tp, N, P = prob.shape
+    Nd, Tmax, Pd = prob_dest_major.shape
+    if Tp != T or N != num_nodes or Nd != N or Pd != P:
+        raise ValueError(f"prob {tuple(prob.shape)} / prob_dest_major "
+                         f"{tuple(prob_dest_major.shape)} do not match T={T}, N={num_nodes}")
+    args = _layout_outputs(topk_idx, num_experts, num_ranks, num_nodes, num_tokens_per_rank,
+                           num_tokens_per_node, num_tokens_per_expert, is_token_in_rank,
+                           rank_offset, expert_offset, token_slot, expert_slot, node_slot,
+                           error_flag)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().ep_dispatch_preprocess(
+        *args, _ptr(prob, torch.float32, "prob"), P, Tmax,
+        _ptr(prob_dest_major, torch.float32, "prob_dest_major"),
+        _ptr(workspace, torch.uint8, "workspace", True), ws_bytes, _stream(stream)),
+        "ep_dispatch_preprocess")
 
 
 def ep_dispatch(x, topk_idx, topk_weights, num_experts: int, num_ranks: int, token_slot, *,
@@ -306,9 +337,11 @@ def _stage_dims(stage_x, name="stage_x"):
 
 
 def ep_dispatch_send(x, topk_idx, topk_weights, node_slot, *, stage_x, stage_topk_idx=None,
-                     stage_topk_weights=None, stage_src, error_flag=None, stream=None) -> None:
+                     stage_topk_weights=None, stage_src, error_flag=None, num_workgroups: int = 0,
+                     stream=None) -> None:
     """Send phase of the two-phase dispatch. x: bf16 [T][H]; node_slot: int32 [T][N];
-    stage_x: bf16 [N][Tmax][H]; stage_topk_idx / weights: [N][Tmax][k]; stage_src: [N][Tmax]."""
+    stage_x: bf16 [N][Tmax][H]; stage_topk_idx / weights: [N][Tmax][k]; stage_src: [N][Tmax].
+    num_workgroups: 0 = full grid, else the most workgroups the send occupies."""
     T, H = x.shape
     N, Tmax, Hs = _stage_dims(stage_x)
     k = topk_idx.shape[1] if topk_idx is not None else 1
@@ -328,7 +361,8 @@ def ep_dispatch_send(x, topk_idx, topk_weights, node_slot, *, stage_x, stage_top
         _ptr(stage_topk_idx, torch.int64, "stage_topk_idx", True),
         _ptr(stage_topk_weights, torch.float32, "stage_topk_weights", True),
         _ptr(stage_src, torch.int32, "stage_src"),
-        _ptr(error_flag, torch.int32, "error_flag", True), _stream(stream)), "ep_dispatch_send")
+        _ptr(error_flag, torch.int32, "error_flag", True), int(num_workgroups), _stream(stream)),
+        "ep_dispatch_send")
 
 
 def ep_dispatch_recv(stage_x, stage_topk_idx, stage_topk_weights, stage_src, count_n,
@@ -368,9 +402,10 @@ def ep_dispatch_recv(stage_x, stage_topk_idx, stage_topk_weights, stage_src, cou
 
 
 def ep_combine_send(partial, token_slot, node_slot, *, stage, error_flag=None,
-                    stream=None) -> None:
+                    num_workgroups: int = 0, stream=None) -> None:
     """Send phase of the two-phase combine: per (token, node) bf16 sums of the node's
-    partial rows. partial: bf16 [rows][H]; stage: bf16 [N][Tmax][H]."""
+    partial rows. partial: bf16 [rows][H]; stage: bf16 [N][Tmax][H].
+    num_workgroups: 0 = full grid, else the most workgroups the send occupies."""
     rows, H = partial.shape
     T, R = token_slot.shape
     N, Tmax, Hs = _stage_dims(stage, "stage")
@@ -382,7 +417,7 @@ def ep_combine_send(partial, token_slot, node_slot, *, stage, error_flag=None,
         _ptr(partial, torch.bfloat16, "partial"), rows, _ptr(token_slot, torch.int32, "token_slot"),
         T, H, R, N, _ptr(node_slot, torch.int32, "node_slot"), Tmax,
         _ptr(stage, torch.bfloat16, "stage"), _ptr(error_flag, torch.int32, "error_flag", True),
-        _stream(stream)), "ep_combine_send")
+        int(num_workgroups), _stream(stream)), "ep_combine_send")
 
 
 def ep_combine_recv(stage, node_slot, *, out, error_flag=None, stream=None) -> None:
@@ -409,3 +444,17 @@ def ep_hbm_copy(src, dst, nbytes: Optional[int] = None, stream=None) -> None:
         raise ValueError("nbytes exceeds a buffer")
     _check(load().ep_hbm_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
                               nbytes, _stream(stream)), "ep_hbm_copy")
+
+
+def ep_hbm_fan(src, dst, slab_bytes: int, fan_in: int, fan_out: int, stream=None) -> None:
+    """Measurement helper: each of the fan_out slabs of dst becomes the XOR of the fan_in
+    slabs of src (slabs of slab_bytes, contiguous)."""
+    if not (src.is_cuda and dst.is_cuda):
+        raise ValueError("src and dst must be device tensors")
+    _on_current_device(src, "src")
+    _on_current_device(dst, "dst")
+    if (fan_in * slab_bytes > src.numel() * src.element_size() or
+            fan_out * slab_bytes > dst.numel() * dst.element_size()):
+        raise ValueError("fan_in / fan_out slabs exceed a buffer")
+    _check(load().ep_hbm_fan(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                             slab_bytes, fan_in, fan_out, _stream(stream)), "ep_hbm_fan")

@@ -42,6 +42,22 @@ class LayoutBuffers:
                    torch.empty((T, k_expert_slots), **i32) if k_expert_slots else None,
                    torch.empty((T, N), **i32) if node_slots else None)
 
+    def _outputs(self) -> dict:
+        return dict(num_tokens_per_rank=self.num_tokens_per_rank,
+                    num_tokens_per_node=self.num_tokens_per_node,
+                    num_tokens_per_expert=self.num_tokens_per_expert,
+                    is_token_in_rank=self.is_token_in_rank, rank_offset=self.rank_offset,
+                    expert_offset=self.expert_offset, token_slot=self.token_slot,
+                    error_flag=self.error_flag, workspace=self.workspace,
+                    expert_slot=self.expert_slot, node_slot=self.node_slot)
+
+    def compute_with_restripe(self, topk_idx: torch.Tensor, E: int, R: int, N: int,
+                              prob: torch.Tensor, prob_dest_major: torch.Tensor,
+                              stream=None) -> None:
+        """The layout and the dense restripe of prob in one call (ep_dispatch_preprocess)."""
+        B.ep_dispatch_preprocess(topk_idx, E, R, N, prob, prob_dest_major, stream=stream,
+                                 **self._outputs())
+
     def compute(self, topk_idx: torch.Tensor, E: int, R: int, N: int, stream=None) -> None:
         B.ep_get_layout(topk_idx, E, R, N, num_tokens_per_rank=self.num_tokens_per_rank,
                         num_tokens_per_node=self.num_tokens_per_node,

@@ -29,14 +29,10 @@ namespace {
 #ifndef EP_COMBINE_THREADS
 #define EP_COMBINE_THREADS 1024
 #endif
-#ifndef EP_COMBINE_GRID_CAP
-#define EP_COMBINE_GRID_CAP 0
-#endif
 
 constexpr int kCT = EP_COMBINE_THREADS;               // threads per block
 constexpr int kCLoads = 8;                            // source rows loaded together
 constexpr int kCBlockWords = EP_COMBINE_BLOCK_WORDS;  // output words a block aims to own
-constexpr int kCGridCap = EP_COMBINE_GRID_CAP;        // 0: one block per token group
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -204,7 +200,7 @@ __device__ __forceinline__ void combine_body(
                            obase, out, errbits);
             }
         }
-        if (kCGridCap > 0) __syncthreads();  // the next group reuses the LDS lists
+        if (gridDim.x < ngroups) __syncthreads();  // the next group reuses the LDS lists
     }
     if (errbits) raise_error(error_flag, errbits);
 }
@@ -233,17 +229,19 @@ static int combine_tokens_per_block(int V, int lds_ints_per_token) {
     return std::max(1, std::min(tpb, 8192 / lds_ints_per_token));
 }
 
+// max_blocks > 0 caps the grid: each block then takes token groups b, b + grid, ...
 template <bool kGrouped, typename Kernel>
 static hipError_t launch_combine_impl(Kernel kernel, const void* partial, int64_t rows,
                                       const int32_t* slot_tab, int C, int64_t cbase, int64_t T,
                                       int H, void* out, const int32_t* out_slot, int G,
-                                      int64_t obase, int32_t* error_flag, hipStream_t stream) {
+                                      int64_t obase, int32_t* error_flag, int max_blocks,
+                                      hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
     const int per_token = C + (kGrouped ? 2 * G + 1 : 1);
     const int tpb = combine_tokens_per_block(V, per_token);
     const int64_t groups = (T + tpb - 1) / tpb;
-    const int64_t grid = kCGridCap > 0 ? std::min<int64_t>(groups, kCGridCap) : groups;
+    const int64_t grid = max_blocks > 0 ? std::min<int64_t>(groups, max_blocks) : groups;
     if (!grid_fits(grid, kCT)) return hipErrorInvalidConfiguration;
     const size_t shm = sizeof(int32_t) * static_cast<size_t>(tpb) * per_token;
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kCT),
@@ -256,15 +254,15 @@ hipError_t launch_combine(const void* partial, int64_t rows, const int32_t* toke
                           int64_t T, int H, int R, void* out, int32_t* error_flag,
                           hipStream_t stream) {
     return launch_combine_impl<false>(combine_kernel, partial, rows, token_slot, R, 0, T, H, out,
-                                      nullptr, 1, 0, error_flag, stream);
+                                      nullptr, 1, 0, error_flag, 0, stream);
 }
 
 hipError_t launch_combine_send(const void* partial, int64_t rows, const int32_t* token_slot,
                                int64_t T, int H, int R, int N, const int32_t* node_slot,
-                               int64_t Tmax, void* stage, int32_t* error_flag,
+                               int64_t Tmax, void* stage, int32_t* error_flag, int max_blocks,
                                hipStream_t stream) {
     return launch_combine_impl<true>(combine_send_kernel, partial, rows, token_slot, R, 0, T, H,
-                                     stage, node_slot, N, Tmax, error_flag, stream);
+                                     stage, node_slot, N, Tmax, error_flag, max_blocks, stream);
 }
 
 hipError_t launch_combine_recv(const void* stage, int N, int64_t Tmax, const int32_t* node_slot,
@@ -272,7 +270,7 @@ hipError_t launch_combine_recv(const void* stage, int N, int64_t Tmax, const int
                                hipStream_t stream) {
     return launch_combine_impl<false>(combine_recv_kernel, stage, static_cast<int64_t>(N) * Tmax,
                                       node_slot, N, Tmax, T, H, out, nullptr, 1, 0, error_flag,
-                                      stream);
+                                      0, stream);
 }
 
 }  // namespace ep

@@ -177,29 +177,40 @@ __device__ __forceinline__ void load_row_cached(u32x4 (&v)[WPL], const u32x4* __
     }
 }
 
-// The wave's (token, destination index) in a launch over tokens [t0, t_end): wave p of the
-// grid is (t0 + p / D, p % D).
+// Index of the calling wave in the grid (wave-uniform).
 template <int kThreads>
-__device__ __forceinline__ bool dest_wave(int64_t t0, int64_t t_end, FastDiv D, int64_t& t, int& d) {
-    const int p = static_cast<int>(blockIdx.x) * (kThreads / kWave) + static_cast<int>(threadIdx.x) / kWave;
+__device__ __forceinline__ int grid_wave() {
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * (kThreads / kWave) +
+                                          static_cast<int>(threadIdx.x) / kWave);
+}
+
+// The (token, destination index) of wave p in a launch over tokens [t0, t_end): wave p
+// is (t0 + p / D, p % D).
+__device__ __forceinline__ bool dest_wave_at(int p, int64_t t0, int64_t t_end, FastDiv D,
+                                             int64_t& t, int& d) {
     const int q = D.div(p);
     t = t0 + q;
     d = p - q * D.d;
     return t < t_end;
 }
 
+template <int kThreads>
+__device__ __forceinline__ bool dest_wave(int64_t t0, int64_t t_end, FastDiv D, int64_t& t, int& d) {
+    return dest_wave_at(grid_wave<kThreads>(), t0, t_end, D, t, d);
+}
+
 // Token t's row to destination d of its slot row: rank c's view of the routing with
 // kRankView (c = the destination's column), else the routing unchanged.
-template <int WPL, bool kMulti, bool kRankView, int kThreads>
+template <int WPL, bool kMulti, bool kRankView>
 __device__ __forceinline__ void dest_scatter(
-    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    int p, const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, int64_t t0, int64_t t_end, int V, int k, int er,
     const int32_t* __restrict__ slot_tab, int C, int64_t cbase, int64_t cap, FastDiv D, int P,
     u32x4* __restrict__ dst_x, int64_t* __restrict__ dst_idx, float* __restrict__ dst_w,
     int32_t* __restrict__ dst_src, int32_t* __restrict__ error_flag) {
     int64_t t;
     int d;
-    if (!dest_wave<kThreads>(t0, t_end, D, t, d)) return;
+    if (!dest_wave_at(p, t0, t_end, D, t, d)) return;
     const int lane = lane_id();
     const int32_t* srow = slot_tab + t * C;
     const int32_t s_first = lane < C ? srow[lane] : -1;
@@ -228,9 +239,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     const int32_t* __restrict__ token_slot, FastDiv D, int P, u32x4* __restrict__ recv_x,
     int64_t* __restrict__ recv_idx, float* __restrict__ recv_w, int32_t* __restrict__ recv_src,
     int64_t cap, int32_t* __restrict__ error_flag) {
-    dest_scatter<WPL, kMulti, true, kThreads>(x, topk_idx, topk_w, t0, t_end, V, k, er, token_slot,
-                                              R, 0, cap, D, P, recv_x, recv_idx, recv_w, recv_src,
-                                              error_flag);
+    dest_scatter<WPL, kMulti, true>(grid_wave<kThreads>(), x, topk_idx, topk_w, t0, t_end, V, k,
+                                    er, token_slot, R, 0, cap, D, P, recv_x, recv_idx, recv_w,
+                                    recv_src, error_flag);
 }
 
 // Two-phase dispatch ("[PR #347] Feature/sm free normal kernel", section 2.1), send
@@ -238,6 +249,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
 // node holding one of its experts, at row node_slot[t][n] of node n's block of Tmax rows
 // (the large per-node buffer that holds a whole batch, section 2.2.2). Wave (t, d) takes
 // the token's nodes [d P, d P + P), with P chosen so a token has at most one block of waves.
+// The grid may be smaller than one wave per (t, d): each wave then takes (t, d) pairs
+// p, p + W, p + 2W, ... (W = the grid's waves), so the send occupies a bounded part of
+// the GPU and leaves the rest to work on other queues (the page's hook mode frees SMs for
+// compute while the data moves, section 2.2.2).
 template <int WPL, bool kMulti, int kThreads>
 __global__ __launch_bounds__(kThreads) void dispatch_send_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
@@ -245,9 +260,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_send_kernel(
     const int32_t* __restrict__ node_slot, int64_t Tmax, FastDiv D, int P, u32x4* __restrict__ stage_x,
     int64_t* __restrict__ stage_idx, float* __restrict__ stage_w, int32_t* __restrict__ stage_src,
     int32_t* __restrict__ error_flag) {
-    dest_scatter<WPL, kMulti, false, kThreads>(x, topk_idx, topk_w, t0, t_end, V, k, 0, node_slot,
-                                               N, Tmax, Tmax, D, P, stage_x, stage_idx, stage_w,
-                                               stage_src, error_flag);
+    const int nw = static_cast<int>((t_end - t0) * D.d);
+    const int stride = static_cast<int>(gridDim.x) * (kThreads / kWave);
+    for (int p = grid_wave<kThreads>(); p < nw; p += stride)
+        dest_scatter<WPL, kMulti, false>(p, x, topk_idx, topk_w, t0, t_end, V, k, 0, node_slot, N,
+                                         Tmax, Tmax, D, P, stage_x, stage_idx, stage_w, stage_src,
+                                         error_flag);
 }
 
 // Dispatch + permute: token t's row goes to each of its (token, slot) rows in the
@@ -579,7 +597,8 @@ hipError_t launch_dispatch_permute(const void* x, const float* topk_w, int64_t T
 hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const float* topk_w,
                                 int64_t T, int H, int k, int N, const int32_t* node_slot,
                                 int64_t Tmax, void* stage_x, int64_t* stage_idx, float* stage_w,
-                                int32_t* stage_src, int32_t* error_flag, hipStream_t stream) {
+                                int32_t* stage_src, int32_t* error_flag, int max_blocks,
+                                hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
     const int P = (std::min(k, N) + kMaxWavesPerToken - 1) / kMaxWavesPerToken;
@@ -587,6 +606,7 @@ hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const fl
     const FastDiv fd = FastDiv::make(D);
     return launch_by_token_range<14>(V, T, D, [&](auto wpl, auto multi, int64_t t0, int64_t t_end,
                                                   unsigned grid) {
+        if (max_blocks > 0) grid = std::min(grid, static_cast<unsigned>(max_blocks));
         hipLaunchKernelGGL((dispatch_send_kernel<decltype(wpl)::value, decltype(multi)::value, kDestThreads>),
                            dim3(grid), dim3(kDestThreads), 0, stream,
                            static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, N,

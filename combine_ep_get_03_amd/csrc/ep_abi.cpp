@@ -92,7 +92,7 @@ int ep_get_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int
     return hip_status(ep::launch_layout(topk_idx, T, k, E, R, N, num_tokens_per_rank,
                                         num_tokens_per_node, num_tokens_per_expert,
                                         is_token_in_rank, rank_offset, expert_offset, token_slot,
-                                        expert_slot, node_slot, error_flag, ws,
+                                        expert_slot, node_slot, error_flag, ws, nullptr,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -127,7 +127,39 @@ int ep_get_layout_no_alloc(const int64_t* topk_idx, int64_t num_tokens, int num_
     return hip_status(ep::launch_layout(topk_idx, T, k, E, R, N, num_tokens_per_rank,
                                         num_tokens_per_node, num_tokens_per_expert,
                                         is_token_in_rank, rank_offset, expert_offset, token_slot,
-                                        expert_slot, node_slot, error_flag, ws,
+                                        expert_slot, node_slot, error_flag, ws, nullptr,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch_preprocess(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                           int num_experts, int num_ranks, int num_nodes,
+                           int32_t* num_tokens_per_rank, int32_t* num_tokens_per_node,
+                           int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                           int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
+                           int32_t* expert_slot, int32_t* node_slot, int32_t* error_flag,
+                           const float* prob, int prob_per_token, int64_t max_tokens_per_rank,
+                           float* prob_dest_major, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
+    const int k = num_topk, E = num_experts, R = num_ranks, N = num_nodes, P = prob_per_token;
+    const int st = check_layout_args(topk_idx, T, k, E, R, N, num_tokens_per_rank,
+                                     num_tokens_per_node, num_tokens_per_expert, rank_offset,
+                                     expert_offset, token_slot, expert_slot, node_slot,
+                                     error_flag);
+    if (st != EP_OK) return st;
+    if (P < 1 || static_cast<int64_t>(N) * P > (1 << 26)) return EP_ERR_ARG;
+    if (T > 0 && (!prob || !prob_dest_major)) return EP_ERR_ARG;
+    if (!aligned(prob, 4) || !aligned(prob_dest_major, 4) || !aligned(workspace, 16))
+        return EP_ERR_ALIGN;
+    if (Tmax < T) return EP_ERR_CAPACITY;
+    const size_t need = ep::layout_workspace_bytes(T, E, R, N);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return EP_ERR_CAPACITY;
+    const ep::LayoutWorkspace ws = ep::carve_layout_workspace(workspace, T, E, R, N);
+    const ep::RestripeTask rs = ep::plan_restripe(prob, T, N, P, Tmax, prob_dest_major);
+    return hip_status(ep::launch_layout(topk_idx, T, k, E, R, N, num_tokens_per_rank,
+                                        num_tokens_per_node, num_tokens_per_expert,
+                                        is_token_in_rank, rank_offset, expert_offset, token_slot,
+                                        expert_slot, node_slot, error_flag, ws, &rs,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -255,10 +287,11 @@ int ep_dispatch_send(const void* x, const int64_t* topk_idx, const float* topk_w
                      int64_t num_tokens, int hidden, int num_topk, int num_nodes,
                      const int32_t* node_slot, int64_t max_tokens_per_rank, void* stage_x,
                      int64_t* stage_topk_idx, float* stage_topk_weights, int32_t* stage_src,
-                     int32_t* error_flag, void* stream) {
+                     int32_t* error_flag, int num_workgroups, void* stream) {
     const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
     const int H = hidden, k = num_topk, N = num_nodes;
-    if (T < 0 || H < 1 || k < 1 || N < 1 || N > EP_MAX_RANKS || Tmax < 0 || Tmax > INT32_MAX)
+    if (T < 0 || H < 1 || k < 1 || N < 1 || N > EP_MAX_RANKS || Tmax < 0 || Tmax > INT32_MAX ||
+        num_workgroups < 0)
         return EP_ERR_ARG;
     if (H % 8 != 0) return EP_ERR_ALIGN;
     if (static_cast<int64_t>(H) / 8 * 64 > INT32_MAX) return EP_ERR_ARG;
@@ -274,7 +307,7 @@ int ep_dispatch_send(const void* x, const int64_t* topk_idx, const float* topk_w
         return EP_ERR_ALIGN;
     return hip_status(ep::launch_dispatch_send(x, topk_idx, topk_weights, T, H, k, N, node_slot,
                                                Tmax, stage_x, stage_topk_idx, stage_topk_weights,
-                                               stage_src, error_flag,
+                                               stage_src, error_flag, num_workgroups,
                                                static_cast<hipStream_t>(stream)));
 }
 
@@ -312,11 +345,12 @@ int ep_dispatch_recv(const void* stage_x, const int64_t* stage_topk_idx,
 int ep_combine_send(const void* partial, int64_t num_partial_rows, const int32_t* token_slot,
                     int64_t num_tokens, int hidden, int num_ranks, int num_nodes,
                     const int32_t* node_slot, int64_t max_tokens_per_rank, void* stage,
-                    int32_t* error_flag, void* stream) {
+                    int32_t* error_flag, int num_workgroups, void* stream) {
     const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
     const int H = hidden, R = num_ranks, N = num_nodes;
     if (T < 0 || H < 1 || R < 1 || R > EP_MAX_RANKS || N < 1 || R % N != 0 ||
-        num_partial_rows < 0 || num_partial_rows > INT32_MAX || Tmax < 0 || Tmax > INT32_MAX)
+        num_partial_rows < 0 || num_partial_rows > INT32_MAX || Tmax < 0 || Tmax > INT32_MAX ||
+        num_workgroups < 0)
         return EP_ERR_ARG;
     if (H % 8 != 0) return EP_ERR_ALIGN;
     if (static_cast<int64_t>(H) / 8 * 64 * N > INT32_MAX) return EP_ERR_ARG;
@@ -326,7 +360,7 @@ int ep_combine_send(const void* partial, int64_t num_partial_rows, const int32_t
         !aligned(node_slot, 4) || !aligned(error_flag, 4))
         return EP_ERR_ALIGN;
     return hip_status(ep::launch_combine_send(partial, num_partial_rows, token_slot, T, H, R, N,
-                                              node_slot, Tmax, stage, error_flag,
+                                              node_slot, Tmax, stage, error_flag, num_workgroups,
                                               static_cast<hipStream_t>(stream)));
 }
 
@@ -352,6 +386,15 @@ int ep_hbm_copy(const void* src, void* dst, size_t bytes, void* stream) {
     if (bytes > 0 && (!src || !dst)) return EP_ERR_ARG;
     if (bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16)) return EP_ERR_ALIGN;
     return hip_status(ep::launch_hbm_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+int ep_hbm_fan(const void* src, void* dst, size_t slab_bytes, int fan_in, int fan_out,
+               void* stream) {
+    if (fan_in < 1 || fan_out < 1 || fan_in > 64 || fan_out > 64) return EP_ERR_ARG;
+    if (slab_bytes > 0 && (!src || !dst)) return EP_ERR_ARG;
+    if (slab_bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16)) return EP_ERR_ALIGN;
+    return hip_status(ep::launch_hbm_fan(src, dst, slab_bytes, fan_in, fan_out,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

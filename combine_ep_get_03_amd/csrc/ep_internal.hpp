@@ -62,6 +62,69 @@ constexpr int32_t kErrTopkRange = 1;
 constexpr int32_t kErrRecvOverflow = 2;
 constexpr int32_t kErrSlotRange = 4;
 
+// ---------------------------------------------------------------- dense restripe
+// prob [T][N][P] -> [N][Tmax][P] in words W (128-bit when P % 4 == 0 and both pointers are
+// 16-byte aligned, else 32-bit): NV = N * VP words per token, VP per (token, node) slice.
+// A block of kRestripeThreads owns tokens [b tpb, b tpb + tpb) and walks their words in
+// source order, kRestripeU words in flight per lane; each slice lands as one contiguous
+// run of its node's block. The restripe's own kernel runs one block per run; the
+// layout's first launch can carry the same blocks after its own (ep_dispatch_preprocess).
+constexpr int kRestripeThreads = 256;
+constexpr int kRestripeU = 4;
+
+struct RestripeTask {
+    const void* in;
+    void* out;
+    int64_t T;
+    int64_t Tmax;
+    int NV, VP, tpb;
+    int vec;         // 128-bit words
+    int64_t blocks;  // blocks of kRestripeThreads covering the T tokens
+};
+
+template <typename W>
+__device__ __forceinline__ void restripe_run(const W* __restrict__ in, int64_t T, int NV, int VP,
+                                             int64_t Tmax, W* __restrict__ out, int tpb,
+                                             int64_t block) {
+    const int tid = threadIdx.x;
+    const int64_t t0 = block * tpb;
+    const int nt = static_cast<int>(min<int64_t>(tpb, T - t0));
+    const int total = nt * NV;
+    const W* src = in + t0 * NV;
+    for (int f0 = 0; f0 < total; f0 += kRestripeThreads * kRestripeU) {
+        W v[kRestripeU];
+#pragma unroll
+        for (int u = 0; u < kRestripeU; ++u) {
+            const int f = f0 + u * kRestripeThreads + tid;
+            if (f < total) v[u] = __builtin_nontemporal_load(src + f);
+        }
+#pragma unroll
+        for (int u = 0; u < kRestripeU; ++u) {
+            const int f = f0 + u * kRestripeThreads + tid;
+            if (f < total) {
+                const int tt = f / NV;
+                const int rem = f - tt * NV;
+                const int n = rem / VP;
+                const int vv = rem - n * VP;
+                __builtin_nontemporal_store(
+                    v[u], out + (static_cast<int64_t>(n) * Tmax + t0 + tt) * VP + vv);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void restripe_task_block(const RestripeTask& rs, int64_t block) {
+    if (rs.vec)
+        restripe_run<u32x4>(static_cast<const u32x4*>(rs.in), rs.T, rs.NV, rs.VP, rs.Tmax,
+                            static_cast<u32x4*>(rs.out), rs.tpb, block);
+    else
+        restripe_run<uint32_t>(static_cast<const uint32_t*>(rs.in), rs.T, rs.NV, rs.VP, rs.Tmax,
+                               static_cast<uint32_t*>(rs.out), rs.tpb, block);
+}
+
+// The blocks of a dense restripe (blocks == 0 when T == 0 or there is nothing to do).
+RestripeTask plan_restripe(const float* prob, int64_t T, int N, int P, int64_t Tmax, float* out);
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the error reported at launch. Arguments have been
 // validated by the C ABI layer.
@@ -94,11 +157,13 @@ constexpr size_t kLayoutScratchBytes = size_t{4} << 20;
 // The current device's address of that scratch array (looked up once per device).
 hipError_t layout_scratch_address(void** out);
 
+// `rs` (may be null): a dense restripe whose blocks ride along in the layout's first
+// launch, after the layout's own blocks.
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
                          int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                          int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
                          int32_t* expert_slot, int32_t* node_slot, int32_t* error_flag,
-                         const LayoutWorkspace& ws, hipStream_t stream);
+                         const LayoutWorkspace& ws, const RestripeTask* rs, hipStream_t stream);
 
 constexpr int kExpertSlotMaxK = 16;  // top-k limit of the expert-major slot output
 
@@ -120,7 +185,8 @@ hipError_t launch_dispatch_permute(const void* x, const float* topk_w, int64_t T
 hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const float* topk_w,
                                 int64_t T, int H, int k, int N, const int32_t* node_slot,
                                 int64_t Tmax, void* stage_x, int64_t* stage_idx, float* stage_w,
-                                int32_t* stage_src, int32_t* error_flag, hipStream_t stream);
+                                int32_t* stage_src, int32_t* error_flag, int max_blocks,
+                                hipStream_t stream);
 hipError_t launch_dispatch_recv(const void* stage_x, const int64_t* stage_idx,
                                 const float* stage_w, const int32_t* stage_src,
                                 const int32_t* count_n, int N, int64_t Tmax, int H, int k, int E,
@@ -141,7 +207,7 @@ hipError_t launch_combine(const void* partial, int64_t rows, const int32_t* toke
                           hipStream_t stream);
 hipError_t launch_combine_send(const void* partial, int64_t rows, const int32_t* token_slot,
                                int64_t T, int H, int R, int N, const int32_t* node_slot,
-                               int64_t Tmax, void* stage, int32_t* error_flag,
+                               int64_t Tmax, void* stage, int32_t* error_flag, int max_blocks,
                                hipStream_t stream);
 hipError_t launch_combine_recv(const void* stage, int N, int64_t Tmax, const int32_t* node_slot,
                                int64_t T, int H, void* out, int32_t* error_flag,
@@ -149,5 +215,7 @@ hipError_t launch_combine_recv(const void* stage, int N, int64_t Tmax, const int
 
 // hbm_copy.hip: the copy-bandwidth yardstick
 hipError_t launch_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_hbm_fan(const void* src, void* dst, size_t slab_bytes, int fan_in,
+                          int fan_out, hipStream_t stream);
 
 }  // namespace ep

@@ -39,6 +39,7 @@ static __device__ __align__(256) unsigned char scratch[kLayoutScratchBytes];
 namespace {
 
 constexpr int kBT = kLayoutBlockTokens;  // tokens (= threads) per block
+static_assert(kRestripeThreads == kBT, "restripe blocks ride along in layout launches");
 constexpr int kWavesBT = kBT / kWave;    // 4
 constexpr int kScanThreads = 1024;
 constexpr int kTileInts = 8192;          // 32 KiB LDS tile for the one-block column walks
@@ -273,11 +274,18 @@ __device__ __forceinline__ void write_wave_slots(const uint64_t* ball, const int
     }
 }
 
+// Blocks past the layout's own `nlb` blocks run the dense restripe that may ride along in
+// the layout's first launch (they return before any block barrier).
 template <int NW>
 __global__ __launch_bounds__(kBT) void layout_count_kernel(const int64_t* __restrict__ topk_idx,
                                                             int64_t T, int k, int E, int R, int N,
                                                             FastDiv er, FastDiv rpn,
-                                                            LayoutWorkspace ws) {
+                                                            LayoutWorkspace ws, int64_t nlb,
+                                                            RestripeTask rs) {
+    if (static_cast<int64_t>(blockIdx.x) >= nlb) {
+        restripe_task_block(rs, static_cast<int64_t>(blockIdx.x) - nlb);
+        return;
+    }
     extern __shared__ int32_t smem[];
     int32_t* s_hist = smem;                                      // [E]
     uint16_t* s_wr = reinterpret_cast<uint16_t*>(s_hist + E);    // [4][R] per-wave counts
@@ -502,7 +510,12 @@ __global__ __launch_bounds__(kBT) void layout_single_kernel(
     int32_t* __restrict__ count_e, int32_t* __restrict__ rank_offset,
     int32_t* __restrict__ expert_offset, int32_t* __restrict__ error_flag,
     int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank, int vec_out,
-    int32_t* __restrict__ exp_base, int32_t* __restrict__ node_slot, int vec_node) {
+    int32_t* __restrict__ exp_base, int32_t* __restrict__ node_slot, int vec_node,
+    RestripeTask rs) {
+    if (blockIdx.x >= 1) {  // a dense restripe riding along (see layout_count_kernel)
+        restripe_task_block(rs, static_cast<int64_t>(blockIdx.x) - 1);
+        return;
+    }
     extern __shared__ int32_t s_hist[];                        // [E]
     __shared__ uint64_t s_ball[kWavesBT * kFusedMaxRanks];     // [4][R]
     __shared__ uint64_t s_nball[kWavesBT * kFusedMaxRanks];    // [4][N]
@@ -813,22 +826,26 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
                        int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                        int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
                        int32_t* expert_slot, int32_t* node_slot, int32_t* error_flag,
-                       const LayoutWorkspace& ws, hipStream_t stream) {
+                       const LayoutWorkspace& ws, const RestripeTask* rs_in,
+                       hipStream_t stream) {
     const int want_base = expert_slot != nullptr ? 1 : 0;
     const int64_t nb = (T + kBT - 1) / kBT;
     const FastDiv er = FastDiv::make(E / R);
     const FastDiv rpn = FastDiv::make(R / N);
-    if (!grid_fits(nb, kBT)) return hipErrorInvalidConfiguration;
+    RestripeTask rs{};  // no restripe blocks unless one rides along
+    if (rs_in != nullptr) rs = *rs_in;
+    if (!grid_fits(nb + rs.blocks, kBT)) return hipErrorInvalidConfiguration;
     if constexpr (NW * kWave <= kFusedMaxRanks) {
         if (nb == 1) {
             const bool vec = R % 4 == 0 && reinterpret_cast<uintptr_t>(token_slot) % 16 == 0 &&
                              reinterpret_cast<uintptr_t>(in_rank) % 4 == 0;
             const bool vec_node = N % 4 == 0 && reinterpret_cast<uintptr_t>(node_slot) % 16 == 0;
-            hipLaunchKernelGGL(layout_single_kernel<NW>, dim3(1), dim3(kBT),
-                               sizeof(int32_t) * static_cast<size_t>(E), stream, topk_idx, T, k, E,
-                               R, N, er, rpn, count_r, count_n, count_e, rank_offset, expert_offset,
-                               error_flag, token_slot, in_rank, vec ? 1 : 0,
-                               want_base ? ws.blk_exp_base : nullptr, node_slot, vec_node ? 1 : 0);
+            hipLaunchKernelGGL(layout_single_kernel<NW>, dim3(static_cast<unsigned>(1 + rs.blocks)),
+                               dim3(kBT), sizeof(int32_t) * static_cast<size_t>(E), stream, topk_idx,
+                               T, k, E, R, N, er, rpn, count_r, count_n, count_e, rank_offset,
+                               expert_offset, error_flag, token_slot, in_rank, vec ? 1 : 0,
+                               want_base ? ws.blk_exp_base : nullptr, node_slot, vec_node ? 1 : 0,
+                               rs);
             EP_RETURN_IF_LAUNCH_FAILED();
             if (want_base) {
                 int nbits = 0;
@@ -844,8 +861,8 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
     if (nb > 0) {
         const size_t shm = sizeof(int32_t) * static_cast<size_t>(E) +
                            sizeof(uint16_t) * kWavesBT * (R + N);
-        hipLaunchKernelGGL(layout_count_kernel<NW>, dim3(static_cast<unsigned>(nb)), dim3(kBT),
-                           shm, stream, topk_idx, T, k, E, R, N, er, rpn, ws);
+        hipLaunchKernelGGL(layout_count_kernel<NW>, dim3(static_cast<unsigned>(nb + rs.blocks)),
+                           dim3(kBT), shm, stream, topk_idx, T, k, E, R, N, er, rpn, ws, nb, rs);
         EP_RETURN_IF_LAUNCH_FAILED();
     }
     bool fused = false;
@@ -944,11 +961,11 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R
                          int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                          int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
                          int32_t* expert_slot, int32_t* node_slot, int32_t* error_flag,
-                         const LayoutWorkspace& ws, hipStream_t stream) {
+                         const LayoutWorkspace& ws, const RestripeTask* rs, hipStream_t stream) {
 #define EP_LAYOUT_CASE(NW)                                                                     \
     return layout_impl<NW>(topk_idx, T, k, E, R, N, count_r, count_n, count_e, in_rank,        \
                            rank_offset, expert_offset, token_slot, expert_slot, node_slot,      \
-                           error_flag, ws, stream)
+                           error_flag, ws, rs, stream)
     if (R <= 64) EP_LAYOUT_CASE(1);
     if (R <= 128) EP_LAYOUT_CASE(2);
     if (R <= 256) EP_LAYOUT_CASE(4);

@@ -13,37 +13,14 @@
 namespace ep {
 namespace {
 
-constexpr int kRT = 256;
-constexpr int kRU = 4;
+constexpr int kRT = kRestripeThreads;
+constexpr int kRU = kRestripeU;
 
 template <typename W>
 __global__ __launch_bounds__(kRT) void restripe_kernel(const W* __restrict__ in, int64_t T,
                                                        int NV, int VP, int64_t Tmax,
                                                        W* __restrict__ out, int tpb) {
-    const int tid = threadIdx.x;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tpb;
-    const int nt = static_cast<int>(min<int64_t>(tpb, T - t0));
-    const int total = nt * NV;
-    const W* src = in + t0 * NV;
-    for (int f0 = 0; f0 < total; f0 += kRT * kRU) {
-        W v[kRU];
-#pragma unroll
-        for (int u = 0; u < kRU; ++u) {
-            const int f = f0 + u * kRT + tid;
-            if (f < total) v[u] = __builtin_nontemporal_load(src + f);
-        }
-#pragma unroll
-        for (int u = 0; u < kRU; ++u) {
-            const int f = f0 + u * kRT + tid;
-            if (f < total) {
-                const int tt = f / NV;
-                const int rem = f - tt * NV;
-                const int n = rem / VP;
-                const int vv = rem - n * VP;
-                __builtin_nontemporal_store(v[u], out + (static_cast<int64_t>(n) * Tmax + t0 + tt) * VP + vv);
-            }
-        }
-    }
+    restripe_run<W>(in, T, NV, VP, Tmax, out, tpb, blockIdx.x);
 }
 
 // Sparse path: only routed (token, node) slices move, to row node_slot[t][n] of the node's
@@ -97,24 +74,34 @@ __global__ __launch_bounds__(kRT) void restripe_sparse_kernel(
 
 }  // namespace
 
+RestripeTask plan_restripe(const float* prob, int64_t T, int N, int P, int64_t Tmax, float* out) {
+    RestripeTask rs{};
+    rs.in = prob;
+    rs.out = out;
+    rs.T = T;
+    rs.Tmax = Tmax;
+    rs.vec = (P % 4 == 0) && (reinterpret_cast<uintptr_t>(prob) % 16 == 0) &&
+             (reinterpret_cast<uintptr_t>(out) % 16 == 0);
+    rs.VP = rs.vec ? P / 4 : P;
+    rs.NV = N * rs.VP;
+    rs.tpb = std::max(1, (kRT * kRU) / rs.NV);
+    rs.blocks = T > 0 ? (T + rs.tpb - 1) / rs.tpb : 0;
+    return rs;
+}
+
 hipError_t launch_restripe(const float* prob, int64_t T, int N, int P, int64_t Tmax, float* out,
                            hipStream_t stream) {
     if (T == 0) return hipSuccess;
-    const bool vec = (P % 4 == 0) && (reinterpret_cast<uintptr_t>(prob) % 16 == 0) &&
-                     (reinterpret_cast<uintptr_t>(out) % 16 == 0);
-    const int VP = vec ? P / 4 : P;
-    const int NV = N * VP;
-    const int tpb = std::max(1, (kRT * kRU) / NV);
-    const int64_t grid = (T + tpb - 1) / tpb;
-    if (!grid_fits(grid, kRT)) return hipErrorInvalidConfiguration;
-    if (vec) {
-        hipLaunchKernelGGL(restripe_kernel<u32x4>, dim3(static_cast<unsigned>(grid)), dim3(kRT), 0,
-                           stream, reinterpret_cast<const u32x4*>(prob), T, NV, VP, Tmax,
-                           reinterpret_cast<u32x4*>(out), tpb);
+    const RestripeTask rs = plan_restripe(prob, T, N, P, Tmax, out);
+    if (!grid_fits(rs.blocks, kRT)) return hipErrorInvalidConfiguration;
+    if (rs.vec) {
+        hipLaunchKernelGGL(restripe_kernel<u32x4>, dim3(static_cast<unsigned>(rs.blocks)), dim3(kRT),
+                           0, stream, reinterpret_cast<const u32x4*>(prob), T, rs.NV, rs.VP, Tmax,
+                           reinterpret_cast<u32x4*>(out), rs.tpb);
     } else {
-        hipLaunchKernelGGL(restripe_kernel<uint32_t>, dim3(static_cast<unsigned>(grid)), dim3(kRT),
-                           0, stream, reinterpret_cast<const uint32_t*>(prob), T, NV, VP, Tmax,
-                           reinterpret_cast<uint32_t*>(out), tpb);
+        hipLaunchKernelGGL(restripe_kernel<uint32_t>, dim3(static_cast<unsigned>(rs.blocks)),
+                           dim3(kRT), 0, stream, reinterpret_cast<const uint32_t*>(prob), T, rs.NV,
+                           rs.VP, Tmax, reinterpret_cast<uint32_t*>(out), rs.tpb);
     }
     return hipGetLastError();
 }

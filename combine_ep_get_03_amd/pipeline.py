@@ -1,5 +1,5 @@
-"""One batch through the whole path on the GPU: layout -> dispatch -> restripe_prob ->
-combine, each step one call of the C ABI on the same stream; and the two-phase
+"""One batch through the whole path on the GPU: layout and restripe_prob (one call of the
+C ABI), dispatch, combine, on the same stream (or one call per step); and the two-phase
 ("hook") form of dispatch and combine, whose send phase returns a callable that enqueues
 the receive phase later.
 
@@ -78,7 +78,20 @@ class Path:
         B.ep_combine(partial, self.layout_buf.token_slot, out=self.out,
                      error_flag=self.error_flag, stream=stream)
 
+    def preprocess(self, b: DeviceBatch, stream=None) -> None:
+        """layout() and restripe() in one call: the restripe's blocks run in the layout's
+        first launch (ep_dispatch_preprocess)."""
+        self.layout_buf.compute_with_restripe(b.topk_idx, self.E, self.R, self.N, b.prob,
+                                              self.prob_dest_major, stream=stream)
+
     def step(self, b: DeviceBatch, stream=None) -> None:
+        """The whole path on one batch: layout and restripe (one call), dispatch, combine."""
+        self.preprocess(b, stream)
+        self.dispatch(b, stream)
+        self.combine(b, stream)
+
+    def step_separate(self, b: DeviceBatch, stream=None) -> None:
+        """The same outputs as step(), one call per step of the path."""
         self.layout(b, stream)
         self.dispatch(b, stream)
         self.restripe(b, stream)
@@ -95,14 +108,16 @@ class Path:
                              "node_slots=True and run layout() first")
         return self.stage
 
-    def dispatch_send(self, b: DeviceBatch, stream=None):
+    def dispatch_send(self, b: DeviceBatch, stream=None, num_workgroups: int = 0):
         """Enqueue the send phase; returns the receive hook, a callable(stream=None) that
-        enqueues the receive phase (on a stream ordered after this one)."""
+        enqueues the receive phase (on a stream ordered after this one). num_workgroups > 0
+        bounds the workgroups the send occupies (room for compute on another queue)."""
         st, lb = self._hook_buffers(), self.layout_buf
         B.ep_dispatch_send(b.x, b.topk_idx, b.topk_weights, lb.node_slot, stage_x=st.stage_x,
                            stage_topk_idx=st.stage_topk_idx,
                            stage_topk_weights=st.stage_topk_weights, stage_src=st.stage_src,
-                           error_flag=self.error_flag, stream=stream)
+                           error_flag=self.error_flag, num_workgroups=num_workgroups,
+                           stream=stream)
 
         self._dispatch_pending = True
 
@@ -117,7 +132,7 @@ class Path:
                                stream=stream)
         return recv_hook
 
-    def combine_send(self, b: DeviceBatch, stream=None):
+    def combine_send(self, b: DeviceBatch, stream=None, num_workgroups: int = 0):
         """Enqueue the combine's send phase (per-node sums); returns its receive hook.
         The sums reuse the dispatch's staging rows, so a pending dispatch receive hook
         must have been enqueued first."""
@@ -127,7 +142,8 @@ class Path:
         st, lb = self._hook_buffers(), self.layout_buf
         partial = self.recv.recv_x if b.partials is None else b.partials
         B.ep_combine_send(partial, lb.token_slot, lb.node_slot, stage=st.stage_x,
-                          error_flag=self.error_flag, stream=stream)
+                          error_flag=self.error_flag, num_workgroups=num_workgroups,
+                          stream=stream)
 
         def recv_hook(stream=None) -> None:
             B.ep_combine_recv(st.stage_x, lb.node_slot, out=self.out, error_flag=self.error_flag,

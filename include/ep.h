@@ -158,6 +158,25 @@ int ep_get_layout_no_alloc(const int64_t *topk_idx, int64_t num_tokens, int num_
                            int32_t *expert_slot, int32_t *node_slot, int32_t *error_flag,
                            void *stream);
 
+/* ep_dispatch_preprocess -- ep_get_layout and ep_restripe_prob of the same batch in one
+ * call: the preprocessing a dispatch needs before it moves rows ("[PR #634] Hybrid ep nixl
+ * restripe", section "Fix": the restripe is part of the dispatch's preprocessing, in place
+ * of the copy it replaces there). Outputs are exactly those of the two calls: the layout
+ * outputs as ep_get_layout with the same arguments, and prob_dest_major as
+ * ep_restripe_prob(prob, T, num_nodes, prob_per_token, max_tokens_per_rank). The
+ * restripe's blocks run inside the layout's first kernel launch, after the layout's own
+ * blocks, so the pair costs one launch less than the two calls.
+ * Sizes and errors: those of both calls (EP_ERR_CAPACITY also for Tmax < T). */
+int ep_dispatch_preprocess(const int64_t *topk_idx, int64_t num_tokens, int num_topk,
+                           int num_experts, int num_ranks, int num_nodes,
+                           int32_t *num_tokens_per_rank, int32_t *num_tokens_per_node,
+                           int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                           int32_t *rank_offset, int32_t *expert_offset, int32_t *token_slot,
+                           int32_t *expert_slot, int32_t *node_slot, int32_t *error_flag,
+                           const float *prob, int prob_per_token, int64_t max_tokens_per_rank,
+                           float *prob_dest_major, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 /* ep_dispatch -- pack every (token, rank) pair into its receive row.
  *
  * In:  x            bf16 [T][H] (any 16-bit payload; copied as bits)
@@ -285,6 +304,15 @@ int ep_combine(const void *partial, int64_t num_partial_rows, const int32_t *tok
  * send phase of combine are the intra-node hop (section 3.3.2). Staged row (n, s) is row
  * n * Tmax + s of every staging array.
  *
+ * The send phases take a workgroup budget, the counterpart of the page's point that hook
+ * mode frees SMs for compute while the data moves (section 2.2.2; "[PR #453] Higher
+ * Performance with Lower SM Occupancy through Zero-Copy and TMA Offloading" counts the SMs
+ * its kernels occupy). num_workgroups == 0 launches the full grid (the fastest send when
+ * it runs alone); num_workgroups > 0 launches at most that many workgroups, each looping
+ * over its share of the work, so a kernel on another queue (say a GEMM) keeps room on
+ * every CU. The results are the same either way. Overlap needs the two streams to feed
+ * different hardware queues.
+ *
  * ep_dispatch_send -- In: x bf16 [T][H]; topk_idx int64 [T][k]; topk_weights fp32 [T][k];
  *      node_slot int32 [T][N] from ep_get_layout.
  * Out: for every (t, n) with s = node_slot[t][n] >= 0, staged row (n, s):
@@ -295,13 +323,14 @@ int ep_combine(const void *partial, int64_t num_partial_rows, const int32_t *tok
  *      Other rows are not written. A slot >= Tmax is skipped and sets
  *      EP_DEVERR_RECV_OVERFLOW. topk_idx / topk_weights may be NULL when the matching
  *      staging array is NULL.
- * Sizes: H % 8 == 0; x and stage_x 16-byte aligned. Errors: EP_ERR_ARG, EP_ERR_ALIGN,
- *   EP_ERR_HIP. */
+ * num_workgroups: 0 (full grid) or the most 256-thread workgroups to occupy.
+ * Sizes: H % 8 == 0; x and stage_x 16-byte aligned. Errors: EP_ERR_ARG (also
+ *   num_workgroups < 0), EP_ERR_ALIGN, EP_ERR_HIP. */
 int ep_dispatch_send(const void *x, const int64_t *topk_idx, const float *topk_weights,
                      int64_t num_tokens, int hidden, int num_topk, int num_nodes,
                      const int32_t *node_slot, int64_t max_tokens_per_rank, void *stage_x,
                      int64_t *stage_topk_idx, float *stage_topk_weights, int32_t *stage_src,
-                     int32_t *error_flag, void *stream);
+                     int32_t *error_flag, int num_workgroups, void *stream);
 
 /* ep_dispatch_recv -- In: the staging arrays written by ep_dispatch_send; count_n int32 [N]
  *      (num_tokens_per_node from ep_get_layout: the staged rows of node n are 0..count_n[n]-1);
@@ -329,6 +358,8 @@ int ep_dispatch_recv(const void *stage_x, const int64_t *stage_topk_idx,
  *      d = token_slot[t][r] >= 0 of float(partial[d]) ), fp32 from +0.0f. Other rows are not
  *      written. A slot >= num_partial_rows sets EP_DEVERR_SLOT_RANGE, a node slot >= Tmax
  *      EP_DEVERR_RECV_OVERFLOW (both skipped).
+ *      num_workgroups: 0 (full grid) or the most 1024-thread workgroups to occupy
+ *      (EP_ERR_ARG if < 0).
  * ep_combine_recv -- In: stage from ep_combine_send; node_slot.
  * Out: out bf16 [T][H]; out[t] = bf16_rne( sum over nodes n ascending with
  *      s = node_slot[t][n] >= 0 of float(staged row (n, s)) ), fp32 from +0.0f; +0.0 for a
@@ -339,7 +370,7 @@ int ep_dispatch_recv(const void *stage_x, const int64_t *stage_topk_idx,
 int ep_combine_send(const void *partial, int64_t num_partial_rows, const int32_t *token_slot,
                     int64_t num_tokens, int hidden, int num_ranks, int num_nodes,
                     const int32_t *node_slot, int64_t max_tokens_per_rank, void *stage,
-                    int32_t *error_flag, void *stream);
+                    int32_t *error_flag, int num_workgroups, void *stream);
 int ep_combine_recv(const void *stage, int num_nodes, int64_t max_tokens_per_rank,
                     const int32_t *node_slot, int64_t num_tokens, int hidden, void *out,
                     int32_t *error_flag, void *stream);
@@ -349,6 +380,17 @@ int ep_combine_recv(const void *stage, int num_nodes, int64_t max_tokens_per_ran
  * copy-bandwidth yardstick and as the known-size reference for hardware byte counters.
  * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_HIP. */
 int ep_hbm_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* ep_hbm_fan -- measurement helper, not a step of the path: the yardstick for a mix of
+ * reads and writes. src holds fan_in slabs and dst fan_out slabs of slab_bytes each
+ * (contiguous, slab s at byte s * slab_bytes); every output slab becomes the bitwise XOR of
+ * the input slabs. fan_in F with fan_out 1 reads F bytes per byte written (the direction
+ * mix of ep_combine), fan_in 1 with fan_out F the reverse (that of ep_dispatch); all
+ * accesses are sequential 128-bit streams. slab_bytes a multiple of 16, both pointers
+ * 16-byte aligned, 1 <= fan_in, fan_out <= 64.
+ * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_HIP. */
+int ep_hbm_fan(const void *src, void *dst, size_t slab_bytes, int fan_in, int fan_out,
+               void *stream);
 
 #ifdef __cplusplus
 }

@@ -46,13 +46,28 @@ def oracle_all(cfg: W.Config, inp: W.Inputs, partial_rows=None) -> dict:
     return dict(lay=lay, d=d, rs=rs, cb=cb, M=int(lay["rank_offset"][-1]))
 
 
-def run_gpu(cfg: W.Config, inp: W.Inputs, device="cuda") -> Path:
+def run_gpu(cfg: W.Config, inp: W.Inputs, device="cuda", fused: bool = True) -> Path:
+    """One step of the path: layout and restripe in one call (ep_dispatch_preprocess), or
+    with fused=False one call per step (ep_get_layout ... ep_combine)."""
     b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials,
                               device=device)
     path = Path(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax, device=device)
     fill_sentinels(path)
-    path.step(b)
+    if fused:
+        path.step(b)
+    else:
+        path.step_separate(b)
     torch.cuda.synchronize()
+    return path
+
+
+def run_and_compare_both(cfg: W.Config, inp: W.Inputs, ref: dict, expect_flag: int = 0) -> Path:
+    """The step with the fused layout+restripe call and with one call per step: both must
+    match the oracle. Returns the last path."""
+    for fused in (False, True):
+        print(f"  {'fused layout+restripe' if fused else 'one call per step'}", flush=True)
+        path = run_gpu(cfg, inp, fused=fused)
+        compare_all(cfg, path, ref, expect_flag=expect_flag)
     return path
 
 

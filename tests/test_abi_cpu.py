@@ -37,8 +37,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) >= {"ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch",
-                          "ep_restripe_prob", "ep_combine",
+    assert set(names) >= {"ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch_preprocess",
+                          "ep_dispatch", "ep_restripe_prob", "ep_combine", "ep_hbm_fan",
                           "ep_layout_workspace_bytes", "ep_status_string", "ep_hbm_copy",
                           "ep_dispatch_fp8", "ep_dispatch_permute", "ep_restripe_prob_sparse",
                           "ep_dispatch_send", "ep_dispatch_recv", "ep_combine_send",
@@ -142,6 +142,24 @@ def test_layout_no_alloc_validation(lib):
     assert f(T=10**6, k=8, E=8192, R=64, N=8) == ep.EP_ERR_CAPACITY
 
 
+def test_dispatch_preprocess_validation(lib):
+    # the layout's checks plus the restripe's, all before anything is enqueued
+    def f(T=100, k=4, E=16, R=4, N=2, P=8, Tmax=100, prob=A16, out=A16, ws=A16, wsb=1 << 20,
+          slot=A16):
+        return lib.ep_dispatch_preprocess(A16, T, k, E, R, N, A16, A16, A16, A16, A16, A16, slot,
+                                          None, None, A16, prob, P, Tmax, out, ws, wsb, None)
+    assert f(E=15) == ep.EP_ERR_ARG
+    assert f(slot=None) == ep.EP_ERR_ARG
+    assert f(P=0) == ep.EP_ERR_ARG
+    assert f(N=2, P=1 << 26) == ep.EP_ERR_ARG
+    assert f(prob=None) == ep.EP_ERR_ARG
+    assert f(out=None) == ep.EP_ERR_ARG
+    assert f(prob=P(0x10002)) == ep.EP_ERR_ALIGN
+    assert f(ws=P(0x10008)) == ep.EP_ERR_ALIGN
+    assert f(Tmax=99) == ep.EP_ERR_CAPACITY
+    assert f(wsb=16) == ep.EP_ERR_CAPACITY
+
+
 def test_dispatch_permute_validation(lib):
     f = lib.ep_dispatch_permute
     assert f(A16, A16, 10, 60, 2, A16, A16, A16, A16, 20, A16, None) == ep.EP_ERR_ALIGN
@@ -207,8 +225,8 @@ def test_combine_validation(lib):
 
 def test_dispatch_send_recv_validation(lib):
     send = lib.ep_dispatch_send
-    a = lambda H=64, N=2, x=A16, idx=A16, ns=A16, sx=A16, sidx=A16, src=A16: (
-        x, idx, A16, 10, H, 2, N, ns, 10, sx, sidx, A16, src, A16, None)
+    a = lambda H=64, N=2, x=A16, idx=A16, ns=A16, sx=A16, sidx=A16, src=A16, wg=0: (
+        x, idx, A16, 10, H, 2, N, ns, 10, sx, sidx, A16, src, A16, wg, None)
     assert send(*a(H=60)) == ep.EP_ERR_ALIGN
     assert send(*a(x=MIS)) == ep.EP_ERR_ALIGN
     assert send(*a(sx=P(0x10008))) == ep.EP_ERR_ALIGN
@@ -216,6 +234,7 @@ def test_dispatch_send_recv_validation(lib):
     assert send(*a(ns=None)) == ep.EP_ERR_ARG
     assert send(*a(src=None)) == ep.EP_ERR_ARG
     assert send(*a(idx=None)) == ep.EP_ERR_ARG              # staged ids need topk_idx
+    assert send(*a(wg=-1)) == ep.EP_ERR_ARG                 # workgroup budget
     recv = lib.ep_dispatch_recv
     b = lambda H=64, N=2, R=4, cn=A16, sidx=A16, ridx=A16, rx=A16: (
         A16, sidx, A16, A16, cn, N, 10, H, 2, 8, R, A16, 10, rx, ridx, A16, A16, 40, A16, None)
@@ -228,13 +247,14 @@ def test_dispatch_send_recv_validation(lib):
 
 def test_combine_send_recv_validation(lib):
     send = lib.ep_combine_send
-    a = lambda H=64, R=4, N=2, st=A16, ns=A16, part=A16: (part, 10, A16, 10, H, R, N, ns, 10, st,
-                                                          A16, None)
+    a = lambda H=64, R=4, N=2, st=A16, ns=A16, part=A16, wg=0: (part, 10, A16, 10, H, R, N, ns,
+                                                                10, st, A16, wg, None)
     assert send(*a(N=3)) == ep.EP_ERR_ARG
     assert send(*a(ns=None)) == ep.EP_ERR_ARG
     assert send(*a(st=P(0x10008))) == ep.EP_ERR_ALIGN
     assert send(*a(H=20)) == ep.EP_ERR_ALIGN
     assert send(*a(part=MIS)) == ep.EP_ERR_ALIGN
+    assert send(*a(wg=-3)) == ep.EP_ERR_ARG
     recv = lib.ep_combine_recv
     assert recv(A16, 2, 2**31, A16, 10, 64, A16, None, None) == ep.EP_ERR_ARG   # N * Tmax
     assert recv(A16, 0, 10, A16, 10, 64, A16, None, None) == ep.EP_ERR_ARG
@@ -245,6 +265,11 @@ def test_combine_send_recv_validation(lib):
 def test_copy_validation(lib):
     assert lib.ep_hbm_copy(A16, A16, 24, None) == ep.EP_ERR_ALIGN
     assert lib.ep_hbm_copy(None, A16, 32, None) == ep.EP_ERR_ARG
+    assert lib.ep_hbm_fan(A16, A16, 24, 2, 1, None) == ep.EP_ERR_ALIGN
+    assert lib.ep_hbm_fan(A16, MIS, 32, 2, 1, None) == ep.EP_ERR_ALIGN
+    assert lib.ep_hbm_fan(None, A16, 32, 2, 1, None) == ep.EP_ERR_ARG
+    assert lib.ep_hbm_fan(A16, A16, 32, 0, 1, None) == ep.EP_ERR_ARG
+    assert lib.ep_hbm_fan(A16, A16, 32, 1, 65, None) == ep.EP_ERR_ARG
 
 
 def test_public_header_is_plain_c():

@@ -117,6 +117,26 @@ def test_hook_dispatch_and_combine(cfg):
     check_combine(cfg, inp, path, refs)
 
 
+@pytest.mark.parametrize("budget", [1, 3, 512])
+@pytest.mark.parametrize("name", ["tiny", "dsv3", "large", "h_ragged"])
+def test_send_phases_with_a_workgroup_budget(name, budget):
+    """A send phase capped to `budget` workgroups (each looping over its share) writes
+    exactly what the full grid writes."""
+    cfg = W.CONFIGS[name] if name in W.CONFIGS else next(c for c in EDGE if c.name == name)
+    print(f"\ncase: hook sends with {budget} workgroups {cfg}", flush=True)
+    inp, b, path = setup(cfg)
+    refs = oracle_refs(cfg, inp)
+    hook = path.dispatch_send(b, num_workgroups=budget)
+    hook()
+    torch.cuda.synchronize()
+    check_dispatch(cfg, inp, path, refs)
+    chook = path.combine_send(b, num_workgroups=budget)
+    chook()
+    torch.cuda.synchronize()
+    assert int(host(path.error_flag)[0]) == 0
+    check_combine(cfg, inp, path, refs)
+
+
 def test_recv_hook_on_another_stream_overlapping_a_gemm():
     cfg = W.CONFIGS["dsv3"]
     print(f"\ncase: hook overlap {cfg}", flush=True)

@@ -11,7 +11,7 @@ import combine_ep_get_03_amd as ep
 from combine_ep_get_03_amd.pipeline import DeviceBatch, Path
 
 from gpu_util import (SENT_U32, compare_all, fill_sentinels, host, oracle_all,
-                      run_gpu)
+                      run_and_compare_both, run_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,8 +27,7 @@ def test_config_full_path(name):
     cfg = W.CONFIGS[name]
     inp = _case(cfg)
     ref = oracle_all(cfg, inp)
-    path = run_gpu(cfg, inp)
-    compare_all(cfg, path, ref)
+    run_and_compare_both(cfg, inp, ref)
 
 
 EDGE = [
@@ -59,8 +58,7 @@ EDGE = [
 def test_edge_shapes(cfg):
     inp = _case(cfg)
     ref = oracle_all(cfg, inp)
-    path = run_gpu(cfg, inp)
-    compare_all(cfg, path, ref)
+    run_and_compare_both(cfg, inp, ref)
 
 
 def test_masked_and_out_of_range_ids():
@@ -76,8 +74,7 @@ def test_masked_and_out_of_range_ids():
     inp.topk_idx = idx
     ref = oracle_all(cfg, inp)
     assert ref["lay"]["error_flag"][0] == 1
-    path = run_gpu(cfg, inp)
-    compare_all(cfg, path, ref, expect_flag=ep.EP_DEVERR_TOPK_RANGE)
+    path = run_and_compare_both(cfg, inp, ref, expect_flag=ep.EP_DEVERR_TOPK_RANGE)
     assert np.all(host(path.out)[5] == 0)
 
 
