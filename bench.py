@@ -1,7 +1,9 @@
 """Benchmark of the single-GPU EP dispatch/combine path on one MI355X.
 
-One step = the whole path on one batch: ep_get_layout -> ep_dispatch -> ep_restripe_prob
--> ep_combine, enqueued on one stream. The K timed steps run as one HIP graph of K steps.
+One step = the whole path on one batch: ep_dispatch_preprocess (the layout and the
+restripe of prob in one call) -> ep_dispatch -> ep_combine, enqueued on one stream. The K
+timed steps run as one HIP graph of K steps. The same step as one call per step
+(ep_get_layout -> ep_dispatch -> ep_restripe_prob -> ep_combine) is timed beside it.
 Inputs are seeded synthetic data already resident in HBM when the timed region starts.
 Prints one JSON line.
 
@@ -55,24 +57,30 @@ def algorithmic_bytes(cfg, M: int) -> dict:
     }
 
 
-COUNTERS = os.path.join(ROOT, "profiles", "dsv3_hbm_counters.md")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {"dispatch": ["ep_internal.hpp", "dispatch.hip"],
                   "combine": ["ep_internal.hpp", "combine.hip"]}
 
 
+def counters_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"{workload}_hbm_counters.md")
+
+
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE,
-    calibrated on a copy kernel of known size), or None when the summary does not cover
-    this workload or the kernel's sources changed since the counters were taken."""
+    """HBM bytes per launch from the committed counter summary of this workload
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a copy kernel of known size), or None when no
+    summary covers the workload or the kernel's sources changed since the counters were
+    taken."""
     import hashlib
 
-    if workload != "dsv3" or not os.path.exists(COUNTERS):
+    path = counters_file(workload)
+    if not os.path.exists(path):
         return None
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "combine_ep_get_03_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    with open(COUNTERS) as fh:
+    with open(path) as fh:
         for line in fh:
             parts = line.split()
             if len(parts) == 4 and parts[0] == "traffic" and parts[1] == kernel:
@@ -257,11 +265,16 @@ def hook_section(torch, cfg, b, args, timed, M: int) -> dict:
            "combine_send": T * R * 4 + T * N * 4 + M * 2 * H + routed * 2 * H,
            "combine_recv": T * N * 4 + routed * 2 * H + T * 2 * H}
 
-    # overlap: the send phase on one stream, the GEMM on another, K times
+    # Overlap: K iterations of the send phase on one stream and the GEMM on another,
+    # against the two run back to back. The send's stream has a hardware queue of its own
+    # (HIP spreads plain streams over a few queues in turn, and two streams on one queue
+    # run their kernels one after the other). The send runs on the full grid and on a
+    # budget of SEND_BUDGET workgroups, which leaves room for the GEMM on every CU.
     a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
     w = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
     c = torch.empty(4096, 4096, device="cuda", dtype=torch.bfloat16)
-    comm, comp = torch.cuda.Stream(), torch.cuda.Stream()
+    comm, comm_handle = dedicated_queue_stream(torch)
+    comp = torch.cuda.Stream()
     main = torch.cuda.current_stream()
 
     def gemm():
@@ -271,7 +284,19 @@ def hook_section(torch, cfg, b, args, timed, M: int) -> dict:
         gemm()
     gemm_ms = timed(gemm, args.steps)
 
-    def overlapped(reps):
+    def send_alone(budget):
+        with torch.cuda.stream(comm):
+            hp.dispatch_send(b, stream=comm, num_workgroups=budget)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(comm)
+            for _ in range(args.steps):
+                hp.dispatch_send(b, stream=comm, num_workgroups=budget)
+            e1.record(comm)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    def overlapped(reps, budget):
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         s0.record(main)
@@ -279,7 +304,7 @@ def hook_section(torch, cfg, b, args, timed, M: int) -> dict:
         comp.wait_stream(main)
         for _ in range(reps):
             with torch.cuda.stream(comm):
-                hp.dispatch_send(b, stream=comm)
+                hp.dispatch_send(b, stream=comm, num_workgroups=budget)
             with torch.cuda.stream(comp):
                 gemm()
         main.wait_stream(comm)
@@ -288,19 +313,132 @@ def hook_section(torch, cfg, b, args, timed, M: int) -> dict:
         torch.cuda.synchronize()
         return s0.elapsed_time(s1) / reps
 
-    overlapped(3)
-    ov_ms = overlapped(args.steps)
+    ov = {"gemm_4096_bf16_us": round(gemm_ms * 1e3, 2), "send_stream": "own hardware queue"}
+    for tag, budget in (("full_grid", 0), (f"{SEND_BUDGET}_workgroups", SEND_BUDGET)):
+        send_ms = send_alone(budget)
+        overlapped(3, budget)
+        ov_ms = min(overlapped(args.steps, budget) for _ in range(3))
+        ov[tag] = {"send_us": round(send_ms * 1e3, 2),
+                   "serial_us": round((gemm_ms + send_ms) * 1e3, 2),
+                   "send_with_gemm_on_two_streams_us": round(ov_ms * 1e3, 2),
+                   "ratio_to_serial": round(ov_ms / (gemm_ms + send_ms), 4)}
+    if int(hp.error_flag.item()) != 0:
+        raise RuntimeError("device error flag in the overlapped send phases")
+    torch.cuda.synchronize()
+    destroy_stream(comm_handle)
     out = {n: {"avg_us": round(res[n] * 1e3, 2), "alg_bytes": alg[n],
                "hbm_gbps": round(alg[n] / (res[n] * 1e-3) / 1e9, 1)} for n in res}
     out["routed_token_node_pairs"] = routed
     out["dispatch_send_plus_recv_us"] = round((res["dispatch_send"] + res["dispatch_recv"]) * 1e3, 2)
     out["combine_send_plus_recv_us"] = round((res["combine_send"] + res["combine_recv"]) * 1e3, 2)
-    out["overlap"] = {"gemm_4096_bf16_us": round(gemm_ms * 1e3, 2),
-                      "send_us": round(res["dispatch_send"] * 1e3, 2),
-                      "serial_us": round((gemm_ms + res["dispatch_send"]) * 1e3, 2),
-                      "send_with_gemm_on_two_streams_us": round(ov_ms * 1e3, 2)}
+    out["overlap"] = ov
     del hp, a, w, c
     torch.cuda.empty_cache()
+    return out
+
+
+SEND_BUDGET = 512  # workgroups of the budgeted send phase: two per CU
+
+
+def _hip_runtime():
+    """The HIP runtime library torch has loaded (the library's calls go through the same)."""
+    import ctypes
+
+    with open("/proc/self/maps") as fh:
+        path = next(l.split()[-1] for l in fh if "libamdhip64" in l)
+    return ctypes.CDLL(path)
+
+
+def dedicated_queue_stream(torch):
+    """A stream with a hardware queue of its own: HIP gives each CU-masked stream its own
+    queue; the mask here enables every CU. Returns (torch stream, raw handle)."""
+    import ctypes
+
+    hip = _hip_runtime()
+    ncu = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    words = (ncu + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for i in range(ncu):
+        mask[i // 32] |= 1 << (i % 32)
+    h = ctypes.c_void_p()
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                 ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), words, mask)
+    if rc != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask returned {rc}")
+    return torch.cuda.ExternalStream(h.value), h.value
+
+
+def destroy_stream(handle) -> None:
+    import ctypes
+
+    hip = _hip_runtime()
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipStreamDestroy(ctypes.c_void_p(handle))
+
+
+def restripe_page_shape(torch, W, ep, steps: int, timed, flush_gib: float) -> dict:
+    """The restripe at the shape its page measures, prob [4096][8][128] -> [8][4096][128]:
+    the average of K back-to-back launches (warm: the 33.6 MB stay in the 256 MB Infinity
+    Cache between launches) and single launches after a spin (warm) and after a flush of
+    `flush_gib` GiB (cold)."""
+    c = W.CONFIGS["restripe"]
+    inp = W.make_inputs(c, with_x=False)
+    prob = torch.from_numpy(inp.prob).cuda()
+    out = torch.empty((c.N, c.Tmax, c.P), dtype=torch.float32, device="cuda")
+    fn = lambda: ep.ep_restripe_prob(prob, out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            fn()
+    g.replay()
+    ms = timed(g.replay, 1) / steps
+    del g
+    dist = launch_distribution(torch, ep, {"restripe": fn}, steps, flush_gib)
+    alg = 2 * c.T * c.N * c.P * 4
+    res = {"shape": f"[{c.T}][{c.N}][{c.P}] -> [{c.N}][{c.Tmax}][{c.P}]", "alg_bytes": alg,
+           "back_to_back_avg_us": round(ms * 1e3, 2),
+           "back_to_back_hbm_gbps": round(alg / (ms * 1e-3) / 1e9, 1),
+           "single_launch_warm_median_us": dist["warm"]["restripe"]["median_us"],
+           "single_launch_cold_median_us": dist["cold"]["restripe"]["median_us"],
+           "event_floor_us": dist["event_floor_us"]}
+    del prob, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def mix_yardstick(torch, ep, cfg, M: int, avg: dict, alg: dict, steps: int, timed) -> dict:
+    """What HBM sustains for the read/write mix of each big kernel, with every access a
+    sequential stream (ep_hbm_fan on slabs of T*H*2 bytes): F slabs reduced into one for the
+    combine (F = 7 and 8 around its M/T reads per write), one slab written F times for the
+    dispatch. The time at F = M/T is interpolated between the two."""
+    slab = cfg.T * cfg.H * 2
+    src = torch.empty(8 * slab, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(8 * slab, dtype=torch.uint8, device="cuda")
+    t = {}
+    for fi, fo in ((7, 1), (8, 1), (1, 7), (1, 8)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                ep.ep_hbm_fan(src, dst, slab, fi, fo)
+        g.replay()
+        t[(fi, fo)] = timed(g.replay, 1) / steps
+        del g
+    del src, dst
+    torch.cuda.empty_cache()
+    f = M / cfg.T
+    out = {"slab_bytes": slab, "reads_per_write": round(f, 4)}
+    for name, lo, hi in (("combine", (7, 1), (8, 1)), ("dispatch", (1, 7), (1, 8))):
+        ms = t[lo] + (f - 7) * (t[hi] - t[lo])
+        moved = (f + 1) * slab
+        out[name] = {"fan_7_us": round(t[lo] * 1e3, 2), "fan_8_us": round(t[hi] * 1e3, 2),
+                     "yardstick_us_at_mix": round(ms * 1e3, 2),
+                     "yardstick_gbps": round(moved / (ms * 1e-3) / 1e9, 1),
+                     "kernel_us": round(avg[name] * 1e3, 2),
+                     "kernel_hbm_gbps": round(alg[name] / (avg[name] * 1e-3) / 1e9, 1),
+                     "kernel_frac_of_yardstick": round((alg[name] / avg[name]) /
+                                                       (moved / ms), 4)}
     return out
 
 
@@ -427,6 +565,20 @@ def main():
     ms_step_replays = timed(g_step.replay, args.steps)
     ms_step_eager = timed(lambda: path.step(b), args.steps)
     del g_k
+    # the same K steps with one call per step of the path (no fused layout + restripe)
+    g_sep = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_sep):
+        for _ in range(args.steps):
+            path.step_separate(b)
+    for t in outputs:
+        t.view(torch.uint8).fill_(0xA5)
+    g_sep.replay()
+    torch.cuda.synchronize()
+    for t, r in zip(outputs, eager_ref):
+        if not torch.equal(t.view(torch.uint8), r.view(torch.uint8)):
+            raise RuntimeError("the one-call-per-step graph differs from the eager step")
+    ms_step_sep = timed(g_sep.replay, 1) / args.steps
+    del g_sep
 
     # Each call's average launch duration: one graph of K back-to-back launches of that
     # call alone, replayed between two events on the launch stream.
@@ -527,6 +679,9 @@ def main():
               "hbm_gbps": round(sb / (res["restripe_sparse"] * 1e-3) / 1e9, 1)}
     del sp_out, lbn
     hook = hook_section(torch, cfg, b, args, timed, M)
+    alg = algorithmic_bytes(cfg, M)
+    mix = mix_yardstick(torch, ep, cfg, M, avg, alg, args.steps, timed)
+    restripe_page = restripe_page_shape(torch, W, ep, args.steps, timed, args.flush_gib)
     small = (small_batches(torch, W, DeviceBatch, Path, cfg, args.steps, timed)
              if args.small_batches else None)
     dist_calls = {n: (lambda fn=fn: fn(b)) for n, fn in zip(names, calls)}
@@ -535,7 +690,6 @@ def main():
     if int(path.error_flag.item()) != 0:
         raise RuntimeError(f"device error flag {int(path.error_flag.item())}")
 
-    alg = algorithmic_bytes(cfg, M)
     payload = 2 * M * cfg.H * 2
     value = payload / (ms_step * 1e-3) / 1e9
     dom = max(("dispatch", "combine"), key=lambda n: avg[n])
@@ -556,6 +710,7 @@ def main():
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_one_graph_replay_each": round(ms_step_replays, 4),
         "ms_per_step_eager_launches": round(ms_step_eager, 4),
+        "ms_per_step_one_call_per_step": round(ms_step_sep, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -579,6 +734,8 @@ def main():
                      "traffic": measured_traffic(dom, cfg.name),
                      "alg_bytes_per_launch": alg[dom], "avg_launch_us": round(avg[dom] * 1e3, 2)},
         "copy_bandwidth_gbps": {k: round(v, 1) for k, v in copy_bw.items()},
+        "mix_yardstick": mix,
+        "restripe_page_shape": restripe_page,
         "dispatch_fp8": fp8,
         "dispatch_permute": permute,
         "restripe_sparse": sparse,
