@@ -54,6 +54,12 @@ def algorithmic_bytes(cfg, M: int) -> dict:
         "dispatch": T * H * 2 + T * k * 12 + T * R * 4 + M * (2 * H + 12 * k + 4),
         "restripe": 2 * T * N * P * 4,
         "combine": T * R * 4 + M * H * 2 + T * H * 2,
+        # the counts path: the counts and rank offsets with the restripe in one launch, then
+        # the dispatch that also writes the slot table, the bitmap and the node and expert
+        # counts and offsets
+        "layout_counts": T * k * 8 + (2 * R + 1) * 4 + 2 * T * N * P * 4,
+        "dispatch_layout": (T * H * 2 + T * k * 12 + M * (2 * H + 12 * k + 4) +
+                            T * R * (1 + 4) + (N + 2 * E + 1) * 4),
     }
 
 
@@ -515,9 +521,16 @@ def main():
 
     names = ["layout", "dispatch", "restripe", "combine"]
     calls = [path.layout, path.dispatch, path.restripe, path.combine]
+    if path.counts_path:
+        names += ["layout_counts", "dispatch_layout"]
+        calls += [path.layout_counts, path.dispatch_layout]
     # every element of these is written by each step (receive rows beyond M are not)
-    outputs = [path.layout_buf.token_slot, path.recv.recv_x[:M], path.recv.recv_topk_idx[:M],
-               path.recv.recv_src_idx[:M], path.prob_dest_major[:, :cfg.T], path.out]
+    lb = path.layout_buf
+    outputs = [lb.num_tokens_per_rank, lb.num_tokens_per_node, lb.num_tokens_per_expert,
+               lb.is_token_in_rank, lb.rank_offset, lb.expert_offset, lb.token_slot,
+               path.recv.recv_x[:M], path.recv.recv_topk_idx[:M],
+               path.recv.recv_topk_weights[:M], path.recv.recv_src_idx[:M],
+               path.prob_dest_major[:, :cfg.T], path.out]
     eager_ref = [t.clone() for t in outputs]
 
     def timed(fn, reps):
@@ -579,6 +592,23 @@ def main():
             raise RuntimeError("the one-call-per-step graph differs from the eager step")
     ms_step_sep = timed(g_sep.replay, 1) / args.steps
     del g_sep
+    # the same K steps on the preprocess path (layout and restripe in one call, then
+    # ep_dispatch), when the step itself is the counts path
+    ms_step_pre = None
+    if path.counts_path:
+        g_pre = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_pre):
+            for _ in range(args.steps):
+                path.step_preprocess(b)
+        for t in outputs:
+            t.view(torch.uint8).fill_(0xA5)
+        g_pre.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outputs, eager_ref):
+            if not torch.equal(t.view(torch.uint8), r.view(torch.uint8)):
+                raise RuntimeError("the preprocess-path graph differs from the eager step")
+        ms_step_pre = timed(g_pre.replay, 1) / args.steps
+        del g_pre
 
     # Each call's average launch duration: one graph of K back-to-back launches of that
     # call alone, replayed between two events on the launch stream.
@@ -711,6 +741,7 @@ def main():
         "ms_per_step_one_graph_replay_each": round(ms_step_replays, 4),
         "ms_per_step_eager_launches": round(ms_step_eager, 4),
         "ms_per_step_one_call_per_step": round(ms_step_sep, 4),
+        "ms_per_step_preprocess_path": None if ms_step_pre is None else round(ms_step_pre, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

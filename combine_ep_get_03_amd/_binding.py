@@ -17,8 +17,10 @@ LIB_PATH = os.path.join(_PKG, "libep.so")
 
 EP_OK, EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_CAPACITY, EP_ERR_HIP = 0, -1, -2, -3, -4
 EP_DEVERR_TOPK_RANGE, EP_DEVERR_RECV_OVERFLOW, EP_DEVERR_SLOT_RANGE = 1, 2, 4
+EP_DEVERR_WORKSPACE = 8
 EP_MAX_RANKS, EP_MAX_EXPERTS, EP_EXPERT_SLOT_MAX_K = 1024, 8192, 16
 EP_LAYOUT_SCRATCH_BYTES = 4 << 20
+EP_COUNTS_MAX_RANKS = 64
 
 _lib = None
 
@@ -46,6 +48,11 @@ def load() -> ctypes.CDLL:
                                 P]
     L.ep_get_layout_no_alloc.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
                                          P, P]
+    L.ep_layout_counts_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    L.ep_layout_counts_workspace_bytes.restype = sz
+    L.ep_layout_counts.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i32, i64, P, P, sz, P]
+    L.ep_dispatch_layout.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, P,
+                                     P, P, i64, P, P, sz, P]
     L.ep_dispatch_preprocess.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
                                          P, P, i32, i64, P, P, sz, P]
     L.ep_restripe_prob_sparse.argtypes = [P, i64, i32, i32, P, i64, P, P, P]
@@ -62,7 +69,8 @@ def load() -> ctypes.CDLL:
     L.ep_combine_recv.argtypes = [P, i32, i64, P, i64, i32, P, P, P]
     L.ep_hbm_copy.argtypes = [P, P, sz, P]
     L.ep_hbm_fan.argtypes = [P, P, sz, i32, i32, P]
-    for f in ("ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch_preprocess", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
+    for f in ("ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch_preprocess",
+              "ep_layout_counts", "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
               "ep_restripe_prob", "ep_restripe_prob_sparse", "ep_combine", "ep_dispatch_send",
               "ep_dispatch_recv", "ep_combine_send", "ep_combine_recv", "ep_hbm_copy",
               "ep_hbm_fan"):
@@ -212,6 +220,85 @@ def ep_dispatch_preprocess(topk_idx, num_experts: int, num_ranks: int, num_nodes
         _ptr(prob_dest_major, torch.float32, "prob_dest_major"),
         _ptr(workspace, torch.uint8, "workspace", True), ws_bytes, _stream(stream)),
         "ep_dispatch_preprocess")
+
+
+def ep_layout_counts_workspace_bytes(num_tokens: int, num_experts: int, num_ranks: int,
+                                     num_nodes: int) -> int:
+    return int(load().ep_layout_counts_workspace_bytes(num_tokens, num_experts, num_ranks,
+                                                       num_nodes))
+
+
+def ep_layout_counts(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
+                     num_tokens_per_rank, rank_offset, error_flag, workspace, prob=None,
+                     prob_dest_major=None, stream=None) -> None:
+    """The count launch of the counts path (num_ranks <= EP_COUNTS_MAX_RANKS): the rank
+    counts and offsets and the error flag, and with prob the restripe of prob. The first 4
+    bytes of `workspace` (uint8, ep_layout_counts_workspace_bytes) must be zero before its
+    first use; every call leaves them zero."""
+    T, k = topk_idx.shape
+    E, R, N = num_experts, num_ranks, num_nodes
+    _at_least(num_tokens_per_rank, R, "num_tokens_per_rank")
+    _at_least(rank_offset, R + 1, "rank_offset")
+    _at_least(error_flag, 1, "error_flag")
+    P, Tmax = 0, 0
+    if prob is not None:
+        if prob.dim() != 3 or prob_dest_major is None or prob_dest_major.dim() != 3:
+            raise ValueError("prob must be [T][N][P] and prob_dest_major [N][Tmax][P]")
+        Tp, Np, P = prob.shape
+        Nd, Tmax, Pd = prob_dest_major.shape
+        if Tp != T or Np != N or Nd != N or Pd != P:
+            raise ValueError("prob / prob_dest_major do not match the batch")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().ep_layout_counts(
+        _ptr(topk_idx, torch.int64, "topk_idx"), T, k, E, R, N,
+        _ptr(num_tokens_per_rank, torch.int32, "num_tokens_per_rank"),
+        _ptr(rank_offset, torch.int32, "rank_offset"),
+        _ptr(error_flag, torch.int32, "error_flag"),
+        _ptr(prob, torch.float32, "prob", True), P, Tmax,
+        _ptr(prob_dest_major, torch.float32, "prob_dest_major", True),
+        _ptr(workspace, torch.uint8, "workspace"), ws_bytes, _stream(stream)), "ep_layout_counts")
+
+
+def ep_dispatch_layout(x, topk_idx, topk_weights, num_experts: int, num_ranks: int,
+                       num_nodes: int, *, token_slot, recv_x, workspace, is_token_in_rank=None,
+                       num_tokens_per_node=None, num_tokens_per_expert=None, expert_offset=None,
+                       recv_topk_idx=None, recv_topk_weights=None, recv_src_idx=None,
+                       error_flag=None, stream=None) -> None:
+    """The dispatch of the counts path, after ep_layout_counts on the same batch and
+    workspace: ep_dispatch's outputs plus token_slot [T][R], is_token_in_rank [T][R] and the
+    node and expert counts and offsets."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    E, R, N = num_experts, num_ranks, num_nodes
+    cap = recv_x.shape[0]
+    _shape(topk_idx, (T, k), "topk_idx")
+    _shape(topk_weights, (T, k), "topk_weights")
+    _shape(token_slot, (T, R), "token_slot")
+    _shape(is_token_in_rank, (T, R), "is_token_in_rank")
+    _at_least(num_tokens_per_node, N, "num_tokens_per_node")
+    _at_least(num_tokens_per_expert, E, "num_tokens_per_expert")
+    _at_least(expert_offset, E + 1, "expert_offset")
+    _shape(recv_x, (cap, H), "recv_x")
+    _shape(recv_topk_idx, (cap, k), "recv_topk_idx")
+    _shape(recv_topk_weights, (cap, k), "recv_topk_weights")
+    _shape(recv_src_idx, (cap,), "recv_src_idx")
+    _at_least(error_flag, 1, "error_flag")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().ep_dispatch_layout(
+        _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int64, "topk_idx"),
+        _ptr(topk_weights, torch.float32, "topk_weights", True), T, H, k, E, R, N,
+        _ptr(num_tokens_per_node, torch.int32, "num_tokens_per_node", True),
+        _ptr(num_tokens_per_expert, torch.int32, "num_tokens_per_expert", True),
+        _ptr(expert_offset, torch.int32, "expert_offset", True),
+        _ptr(token_slot, torch.int32, "token_slot"),
+        _ptr(is_token_in_rank, torch.uint8, "is_token_in_rank", True),
+        _ptr(recv_x, torch.bfloat16, "recv_x"),
+        _ptr(recv_topk_idx, torch.int64, "recv_topk_idx", True),
+        _ptr(recv_topk_weights, torch.float32, "recv_topk_weights", True),
+        _ptr(recv_src_idx, torch.int32, "recv_src_idx", True), cap,
+        _ptr(error_flag, torch.int32, "error_flag", True),
+        _ptr(workspace, torch.uint8, "workspace"), ws_bytes, _stream(stream)),
+        "ep_dispatch_layout")
 
 
 def ep_dispatch(x, topk_idx, topk_weights, num_experts: int, num_ranks: int, token_slot, *,

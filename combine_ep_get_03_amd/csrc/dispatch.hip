@@ -244,6 +244,117 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
                                     recv_src, error_flag);
 }
 
+// The node and expert counts and offsets of the counts path, from the count launch's
+// per-block tables: head block h of ep_dispatch_layout's first launch takes expert columns
+// [256 h, 256 h + 256). A column sum of the blocks' inclusive expert prefixes is
+// expert_offset[e + 1]; the count is its difference with the column before, which each
+// thread sums as well (no LDS, no barrier: the dispatch kernel stays free of both). Head
+// block 0 also sums the node columns.
+__device__ __forceinline__ void counts_head_block(const CountsWorkspace& cw, int h, int nb,
+                                                  int E, int N, int32_t* __restrict__ count_n,
+                                                  int32_t* __restrict__ count_e,
+                                                  int32_t* __restrict__ expert_offset) {
+    constexpr int kB = 8;  // loads in flight per lane
+    const int tid = threadIdx.x;
+    const int e = h * kDestThreads + tid;
+    if ((count_e || expert_offset) && e < E) {
+        int sum = 0, before = 0;  // column e, and column e - 1 (0 for e = 0)
+        for (int b0 = 0; b0 < nb; b0 += kB) {
+            int v[kB], u0[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const int64_t row = static_cast<int64_t>(b0 + u) * E;
+                v[u] = b0 + u < nb ? cw.blk_exp[row + e] : 0;
+                u0[u] = (b0 + u < nb && e > 0) ? cw.blk_exp[row + e - 1] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                sum += v[u];
+                before += u0[u];
+            }
+        }
+        if (expert_offset) {
+            expert_offset[e + 1] = sum;
+            if (e == 0) expert_offset[0] = 0;
+        }
+        if (count_e) count_e[e] = sum - before;
+    }
+    if (h == 0 && count_n && tid < N) {
+        int sum = 0;
+        for (int bb = 0; bb < nb; ++bb) sum += cw.blk_node[static_cast<int64_t>(bb) * N + tid];
+        count_n[tid] = sum;
+    }
+}
+
+// Dispatch of the counts path (R <= 64): the same (token, destination) waves as
+// dispatch_kernel, but the receive rows come from the count launch's tables instead of a
+// token_slot row. Lane r < R holds, for rank r: the receive row of the token's block's
+// first token on r, the count of the block's earlier waves' tokens on r, and the ballot
+// of the token's wave for r; these loads, the token's rank mask (one word) and the row's
+// loads are all issued together. The token's row on rank r is then
+//     glob[b][r] + pfx[b][w][r] + popcount(ball[b][w][r] & (bits below the token)),
+// so a wave waits on one memory round trip before its stores, as dispatch_kernel does.
+// The token's first wave also writes the token's token_slot row and bitmap row. The first
+// `nhead` blocks are head blocks (counts_head_block) instead.
+template <int WPL, bool kMulti, int kThreads>
+__global__ __launch_bounds__(kThreads) void dispatch_layout_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int64_t t0, int64_t t_end, int V, int k, int R, int er,
+    CountsWorkspace cw, FastDiv D, int32_t* __restrict__ token_slot,
+    uint8_t* __restrict__ in_rank, u32x4* __restrict__ recv_x, int64_t* __restrict__ recv_idx,
+    float* __restrict__ recv_w, int32_t* __restrict__ recv_src, int64_t cap, int nhead, int nb,
+    int E, int N, int32_t* __restrict__ count_n, int32_t* __restrict__ count_e,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ error_flag) {
+    if (static_cast<int>(blockIdx.x) < nhead) {
+        counts_head_block(cw, blockIdx.x, nb, E, N, count_n, count_e, expert_offset);
+        return;
+    }
+    int64_t t;
+    int d;
+    if (!dest_wave_at(grid_wave<kThreads>() - nhead * (kThreads / kWave), t0, t_end, D, t, d))
+        return;
+    const int lane = lane_id();
+    constexpr int kBlk = kLayoutBlockTokens;
+    const int64_t b = t / kBlk;
+    const int w = static_cast<int>(t % kBlk) / kWave;
+    const int l = static_cast<int>(t % kWave);
+    const uint64_t m = cw.mask[t];
+    int32_t g = 0, pf = 0;
+    uint64_t bl = 0;
+    if (lane < R) {
+        const int64_t cell = (b * (kBlk / kWave) + w) * R + lane;
+        g = cw.glob[b * R + lane];
+        pf = cw.pfx[cell];
+        bl = cw.ball[cell];
+    }
+    const Routing rt(topk_idx ? topk_idx + t * k : nullptr, topk_w ? topk_w + t * k : nullptr, k,
+                     recv_idx || recv_w);
+    const u32x4* xr = x + t * V;
+    u32x4 v[WPL];
+    load_row_cached(v, xr, 0, V);  // first pass, issued with the tables' loads
+    const bool on = lane < R && ((m >> lane) & 1ull);
+    const int32_t slot = on ? g + pf + __popcll(bl & ((1ull << l) - 1ull)) : -1;
+    if (d == 0 && lane < R) {
+        token_slot[t * R + lane] = slot;
+        if (in_rank) in_rank[t * R + lane] = on ? 1 : 0;
+    }
+    uint64_t rest = m;  // the token's d-th destination rank, ascending
+    for (int i = 0; i < d && rest; ++i) rest &= rest - 1;
+    if (!rest) return;
+    const int rd = __builtin_ctzll(rest);
+    const int64_t sd = __builtin_amdgcn_readlane(slot, rd);
+    if (sd < 0 || sd >= cap) {  // (a negative row only comes from tables of a misused workspace)
+        if (lane == 0) raise_error(error_flag, kErrRecvOverflow);
+        return;
+    }
+    for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
+        if (v0 != 0) load_row_cached(v, xr, v0, V);
+        put_row<WPL, true>(v, v0, V, sd, rd, rt, er, static_cast<int32_t>(t), recv_x, recv_idx,
+                           recv_w, recv_src);
+        if constexpr (!kMulti) break;
+    }
+}
+
 // Two-phase dispatch ("[PR #347] Feature/sm free normal kernel", section 2.1), send
 // phase: each token's row, its k expert ids and weights and its id go once to every
 // node holding one of its experts, at row node_slot[t][n] of node n's block of Tmax rows
@@ -554,6 +665,38 @@ hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* 
                            static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, R,
                            E / R, token_slot, fd, P, static_cast<u32x4*>(recv_x), recv_idx, recv_w,
                            recv_src, cap, error_flag);
+    });
+}
+
+hipError_t launch_dispatch_layout(const void* x, const int64_t* topk_idx, const float* topk_w,
+                                  int64_t T, int H, int k, int E, int R, int N,
+                                  const CountsWorkspace& cw, int32_t* token_slot, uint8_t* in_rank,
+                                  void* recv_x, int64_t* recv_idx, float* recv_w,
+                                  int32_t* recv_src, int64_t cap, int32_t* count_n,
+                                  int32_t* count_e, int32_t* expert_offset, int32_t* error_flag,
+                                  hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int V = H / 8;
+    const int D = std::min(k, R);  // waves per token: ranks a token can reach
+    const FastDiv fd = FastDiv::make(D);
+    const int nb = static_cast<int>((T + kLayoutBlockTokens - 1) / kLayoutBlockTokens);
+    // head blocks of the first launch, a multiple of the 8 XCDs so that the dispatch's
+    // blocks keep the placement they have without them (a top-8 token's two blocks on
+    // neighbouring XCDs)
+    int head = 0;
+    if (count_e || expert_offset) head = (E + kDestThreads - 1) / kDestThreads;
+    else if (count_n) head = 1;
+    head = (head + 7) / 8 * 8;
+    return launch_by_token_range<14>(V, T, D, [&](auto wpl, auto multi, int64_t t0, int64_t t_end,
+                                                  unsigned grid) {
+        const int nhead = t0 == 0 ? head : 0;
+        hipLaunchKernelGGL((dispatch_layout_kernel<decltype(wpl)::value, decltype(multi)::value,
+                                                   kDestThreads>),
+                           dim3(grid + nhead), dim3(kDestThreads), 0, stream,
+                           static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, R,
+                           E / R, cw, fd, token_slot, in_rank, static_cast<u32x4*>(recv_x),
+                           recv_idx, recv_w, recv_src, cap, nhead, nb, E, N, count_n, count_e,
+                           expert_offset, error_flag);
     });
 }
 

@@ -163,6 +163,85 @@ int ep_dispatch_preprocess(const int64_t* topk_idx, int64_t num_tokens, int num_
                                         static_cast<hipStream_t>(stream)));
 }
 
+size_t ep_layout_counts_workspace_bytes(int64_t num_tokens, int num_experts, int num_ranks,
+                                        int num_nodes) {
+    if (num_tokens < 0 || num_experts < 1 || num_experts > EP_MAX_EXPERTS || num_ranks < 1 ||
+        num_ranks > EP_COUNTS_MAX_RANKS || num_nodes < 1 || num_experts % num_ranks != 0 ||
+        num_ranks % num_nodes != 0)
+        return 0;
+    return ep::counts_workspace_bytes(num_tokens, num_experts, num_ranks, num_nodes);
+}
+
+int ep_layout_counts(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                     int num_ranks, int num_nodes, int32_t* num_tokens_per_rank,
+                     int32_t* rank_offset, int32_t* error_flag, const float* prob,
+                     int prob_per_token, int64_t max_tokens_per_rank, float* prob_dest_major,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
+    const int k = num_topk, E = num_experts, R = num_ranks, N = num_nodes, P = prob_per_token;
+    if (!topology_ok(k, E, R, N) || R > EP_COUNTS_MAX_RANKS || !slots_fit_int32(T, k, R) ||
+        T > static_cast<int64_t>(INT32_MAX) / k)
+        return EP_ERR_ARG;
+    if (!num_tokens_per_rank || !rank_offset || !error_flag) return EP_ERR_ARG;
+    if (T > 0 && !topk_idx) return EP_ERR_ARG;
+    if (prob) {
+        if (P < 1 || static_cast<int64_t>(N) * P > (1 << 26)) return EP_ERR_ARG;
+        if (T > 0 && !prob_dest_major) return EP_ERR_ARG;
+    }
+    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) || !aligned(rank_offset, 4) ||
+        !aligned(error_flag, 4) || !aligned(prob, 4) || !aligned(prob_dest_major, 4) ||
+        !aligned(workspace, 16))
+        return EP_ERR_ALIGN;
+    if (prob && Tmax < T) return EP_ERR_CAPACITY;
+    const size_t need = ep::counts_workspace_bytes(T, E, R, N);
+    if (workspace_bytes < need || !workspace) return EP_ERR_CAPACITY;
+    const ep::CountsWorkspace cw = ep::carve_counts_workspace(workspace, T, E, R, N);
+    ep::RestripeTask rs{};
+    if (prob) rs = ep::plan_restripe(prob, T, N, P, Tmax, prob_dest_major);
+    return hip_status(ep::launch_layout_counts(topk_idx, T, k, E, R, N, num_tokens_per_rank,
+                                               rank_offset, error_flag, cw, &rs,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch_layout(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                       int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                       int num_ranks, int num_nodes, int32_t* num_tokens_per_node,
+                       int32_t* num_tokens_per_expert, int32_t* expert_offset,
+                       int32_t* token_slot, uint8_t* is_token_in_rank, void* recv_x,
+                       int64_t* recv_topk_idx, float* recv_topk_weights, int32_t* recv_src_idx,
+                       int64_t recv_capacity, int32_t* error_flag, const void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    const int64_t T = num_tokens;
+    const int H = hidden, k = num_topk, E = num_experts, R = num_ranks, N = num_nodes;
+    if (!topology_ok(k, E, R, N) || R > EP_COUNTS_MAX_RANKS || !slots_fit_int32(T, k, R) ||
+        T > static_cast<int64_t>(INT32_MAX) / k || H < 1 || recv_capacity < 0)
+        return EP_ERR_ARG;
+    if (H % 8 != 0) return EP_ERR_ALIGN;
+    if (static_cast<int64_t>(H) / 8 * 64 > INT32_MAX) return EP_ERR_ARG;
+    if (T > 0) {
+        if (!x || !token_slot || !recv_x || !topk_idx) return EP_ERR_ARG;
+        if (recv_topk_weights && !topk_weights) return EP_ERR_ARG;
+    }
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 8) ||
+        !aligned(topk_weights, 4) || !aligned(token_slot, 4) || !aligned(recv_topk_idx, 8) ||
+        !aligned(recv_topk_weights, 4) || !aligned(recv_src_idx, 4) || !aligned(error_flag, 4) ||
+        !aligned(num_tokens_per_node, 4) || !aligned(num_tokens_per_expert, 4) ||
+        !aligned(expert_offset, 4) || !aligned(workspace, 16))
+        return EP_ERR_ALIGN;
+    const size_t need = ep::counts_workspace_bytes(T, E, R, N);
+    if (workspace_bytes < need || !workspace) return EP_ERR_CAPACITY;
+    if (T == 0)  // an empty batch: zero counts and offsets, nothing to dispatch
+        return hip_status(ep::launch_zero_ints(num_tokens_per_node, N, num_tokens_per_expert, E,
+                                               expert_offset, E + 1,
+                                               static_cast<hipStream_t>(stream)));
+    const ep::CountsWorkspace cw =
+        ep::carve_counts_workspace(const_cast<void*>(workspace), T, E, R, N);
+    return hip_status(ep::launch_dispatch_layout(
+        x, topk_idx, topk_weights, T, H, k, E, R, N, cw, token_slot, is_token_in_rank, recv_x,
+        recv_topk_idx, recv_topk_weights, recv_src_idx, recv_capacity, num_tokens_per_node,
+        num_tokens_per_expert, expert_offset, error_flag, static_cast<hipStream_t>(stream)));
+}
+
 int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,
                 int64_t num_tokens, int hidden, int num_topk, int num_experts, int num_ranks,
                 const int32_t* token_slot, void* recv_x, int64_t* recv_topk_idx,

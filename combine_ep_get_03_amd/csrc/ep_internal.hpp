@@ -61,6 +61,7 @@ inline bool grid_fits(int64_t blocks, int threads) {
 constexpr int32_t kErrTopkRange = 1;
 constexpr int32_t kErrRecvOverflow = 2;
 constexpr int32_t kErrSlotRange = 4;
+constexpr int32_t kErrWorkspace = 8;
 
 // ---------------------------------------------------------------- dense restripe
 // prob [T][N][P] -> [N][Tmax][P] in words W (128-bit when P % 4 == 0 and both pointers are
@@ -167,6 +168,37 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R
 
 constexpr int kExpertSlotMaxK = 16;  // top-k limit of the expert-major slot output
 
+// Workspace of the counts path (ep_layout_counts, then ep_dispatch_layout; R <= 64). The
+// ticket counter comes first: it must be zero before the first call, and every call leaves
+// it zero again. The rest is rewritten by each call: per-256-token-block tables and one rank
+// mask per token.
+constexpr int kCountsMaxRanks = 64;
+struct CountsWorkspace {
+    int32_t* ticket;    // [1]     blocks of the count launch that have published
+    int32_t* blk_rank;  // [nb][R] tokens per rank in each block
+    int32_t* glob;      // [nb][R] receive row of each block's first token on each rank
+    int32_t* pfx;       // [nb][4][R] tokens on each rank in the block's earlier waves
+    uint64_t* ball;     // [nb][4][R] which of each wave's 64 tokens are on each rank
+    uint64_t* mask;     // [T] the ranks of each token
+    int32_t* blk_err;   // [nb] a bad expert id in the block
+    int32_t* blk_node;  // [nb][N] tokens per node in each block
+    int32_t* blk_exp;   // [nb][E] inclusive prefix over experts of each block's histogram
+};
+size_t counts_workspace_bytes(int64_t T, int E, int R, int N);
+CountsWorkspace carve_counts_workspace(void* base, int64_t T, int E, int R, int N);
+
+// Zero fill of up to three int32 arrays (NULL ones skipped) with a kernel, so that the
+// fill can be captured into a graph.
+hipError_t launch_zero_ints(int32_t* a, int na, int32_t* b, int nb, int32_t* c, int nc,
+                            hipStream_t stream);
+
+// The count launch of the counts path (the restripe's blocks may ride along): the rank
+// counts and offsets, the error flag, and the tables ep_dispatch_layout reads.
+hipError_t launch_layout_counts(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
+                                int32_t* count_r, int32_t* rank_offset, int32_t* error_flag,
+                                const CountsWorkspace& cw, const RestripeTask* rs,
+                                hipStream_t stream);
+
 // dispatch.hip: one-call dispatch, FP8 dispatch, expert-major permute, and the two
 // phases of the two-phase dispatch
 hipError_t launch_dispatch(const void* x, const int64_t* topk_idx, const float* topk_w,
@@ -187,6 +219,16 @@ hipError_t launch_dispatch_send(const void* x, const int64_t* topk_idx, const fl
                                 int64_t Tmax, void* stage_x, int64_t* stage_idx, float* stage_w,
                                 int32_t* stage_src, int32_t* error_flag, int max_blocks,
                                 hipStream_t stream);
+// The dispatch of the counts path: each wave computes its token's receive rows from the
+// count launch's tables; the token's first wave also writes its token_slot and bitmap rows.
+// A few leading blocks of the first launch write the node and expert counts and offsets.
+hipError_t launch_dispatch_layout(const void* x, const int64_t* topk_idx, const float* topk_w,
+                                  int64_t T, int H, int k, int E, int R, int N,
+                                  const CountsWorkspace& cw, int32_t* token_slot, uint8_t* in_rank,
+                                  void* recv_x, int64_t* recv_idx, float* recv_w,
+                                  int32_t* recv_src, int64_t cap, int32_t* count_n,
+                                  int32_t* count_e, int32_t* expert_offset, int32_t* error_flag,
+                                  hipStream_t stream);
 hipError_t launch_dispatch_recv(const void* stage_x, const int64_t* stage_idx,
                                 const float* stage_w, const int32_t* stage_src,
                                 const int32_t* count_n, int N, int64_t Tmax, int H, int k, int E,

@@ -906,7 +906,155 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
     return hipSuccess;
 }
 
+// ------------------------------------------------------------------- the counts path
+// Count launch of ep_layout_counts (R <= 64, one mask word per token). Each block counts
+// its 256 tokens as layout_count_kernel does and publishes, for ep_dispatch_layout: each
+// token's rank mask, each wave's rank ballots and the tokens of its earlier waves per
+// rank, the block's rank and node counts and the inclusive prefix of its expert
+// histogram. Every block then takes a ticket; the block that draws the last one (no block
+// waits for another) turns the blocks' rank counts into the rank totals and offsets and
+// the receive row of each block's first token on each rank, writes the error flag, and
+// zeroes the ticket for the next call. Blocks past `nlb` run the dense restripe riding
+// along in this launch.
+__global__ __launch_bounds__(kBT) void layout_counts_kernel(
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int N, FastDiv er,
+    FastDiv rpn, CountsWorkspace cw, int nlb, RestripeTask rs, int32_t* __restrict__ count_r,
+    int32_t* __restrict__ rank_offset, int32_t* __restrict__ error_flag) {
+    if (static_cast<int>(blockIdx.x) >= nlb) {
+        restripe_task_block(rs, static_cast<int64_t>(blockIdx.x) - nlb);
+        return;
+    }
+    extern __shared__ int32_t s_hist[];                      // [E]
+    __shared__ uint64_t s_ball[kWavesBT * kCountsMaxRanks];  // [4][R] rank ballots per wave
+    __shared__ uint16_t s_wn[kWavesBT * kCountsMaxRanks];    // [4][N] node counts per wave
+    __shared__ int32_t s_part[kBT];                          // last block: partial column sums
+    __shared__ int32_t s_ro[kCountsMaxRanks];                // last block: rank offsets
+    __shared__ int32_t s_scan[17];
+    __shared__ int32_t s_last;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int b = blockIdx.x;
+    const int64_t t = static_cast<int64_t>(b) * kBT + tid;
+
+    for (int e = tid; e < E; e += kBT) s_hist[e] = 0;
+    __syncthreads();
+    uint64_t rm[1] = {0}, nm[1] = {0};
+    int bad = 0;
+    if (t < T) {
+        token_masks<1, true, true>(topk_idx + t * k, k, E, er, rpn, rm, nm, s_hist, bad);
+        cw.mask[t] = rm[0];
+    }
+    wave_ballots<1, false>(rm, R, s_ball + wave * R);
+    wave_ballots<1, true>(nm, N, s_wn + wave * N);
+    __syncthreads();
+
+    for (int i = tid; i < kWavesBT * R; i += kBT) {
+        const int w = i / R, r = i - w * R;
+        int before = 0;
+        for (int v = 0; v < w; ++v) before += __popcll(s_ball[v * R + r]);
+        cw.ball[static_cast<int64_t>(b) * kWavesBT * R + i] = s_ball[i];
+        cw.pfx[static_cast<int64_t>(b) * kWavesBT * R + i] = before;
+        if (w == kWavesBT - 1) cw.blk_rank[static_cast<int64_t>(b) * R + r] = before + __popcll(s_ball[i]);
+    }
+    for (int n = tid; n < N; n += kBT) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesBT; ++w) c += s_wn[w * N + n];
+        cw.blk_node[static_cast<int64_t>(b) * N + n] = c;
+    }
+    int carry = 0;  // inclusive prefix of the block's expert histogram
+    for (int c0 = 0; c0 < E; c0 += kBT) {
+        const int e = c0 + tid;
+        const int h = e < E ? s_hist[e] : 0;
+        int chunk = 0;
+        const int ex = block_exclusive_scan(h, s_scan, chunk);
+        if (e < E) cw.blk_exp[static_cast<int64_t>(b) * E + e] = carry + ex + h;
+        carry += chunk;
+    }
+    const int any_bad = __syncthreads_or(bad);
+    if (tid == 0) cw.blk_err[b] = any_bad;
+
+    // publish (device-scope release by every thread), then draw a ticket
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const int drawn = atomicAdd(cw.ticket, 1);
+        s_last = drawn == nlb - 1;
+        // a ticket outside [0, nlb): the ticket was not zero on entry
+        if (drawn < 0 || drawn >= nlb) raise_error(error_flag, kErrWorkspace);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();  // acquire: the other blocks' tables
+
+    // rank columns of blk_rank [nb][R]: thread (c, r) sums rows [c q, c q + q) of column r
+    const int C = kBT / R;
+    const int q = (nlb + C - 1) / C;
+    const int r = tid % R, c = tid / R;
+    const bool col = c < C;
+    const int b0 = col ? min(nlb, c * q) : 0, b1 = col ? min(nlb, b0 + q) : 0;
+    int part = 0;
+    for (int bb = b0; bb < b1; bb += kBatch) {
+        int v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            v[u] = bb + u < b1 ? cw.blk_rank[static_cast<int64_t>(bb + u) * R + r] : 0;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) part += v[u];
+    }
+    int any = 0;
+    for (int bb = tid; bb < nlb; bb += kBT) any |= cw.blk_err[bb];
+    if (col) s_part[c * R + r] = part;
+    __syncthreads();
+    int tot = 0;
+    if (tid < R) {  // exclusive prefix of the parts over c, per rank
+        for (int cc = 0; cc < C; ++cc) {
+            const int p = s_part[cc * R + tid];
+            s_part[cc * R + tid] = tot;
+            tot += p;
+        }
+    }
+    int M = 0;
+    const int ro = block_exclusive_scan(tid < R ? tot : 0, s_scan, M);
+    if (tid < R) {
+        s_ro[tid] = ro;
+        count_r[tid] = tot;
+        rank_offset[tid] = ro;
+    }
+    if (tid == 0) rank_offset[R] = M;
+    __syncthreads();
+    if (col) {  // receive row of each block's first token on rank r
+        int run = s_ro[r] + s_part[c * R + r];
+        for (int bb = b0; bb < b1; ++bb) {
+            cw.glob[static_cast<int64_t>(bb) * R + r] = run;
+            run += cw.blk_rank[static_cast<int64_t>(bb) * R + r];
+        }
+    }
+    any = __syncthreads_or(any);
+    if (tid == 0) {
+        *error_flag = any ? kErrTopkRange : 0;
+        __hip_atomic_store(cw.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+__global__ __launch_bounds__(kBT) void zero_ints_kernel(int32_t* a, int na, int32_t* b, int nb,
+                                                        int32_t* c, int nc) {
+    for (int i = threadIdx.x; i < na; i += kBT) a[i] = 0;
+    for (int i = threadIdx.x; i < nb; i += kBT) b[i] = 0;
+    for (int i = threadIdx.x; i < nc; i += kBT) c[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero_ints(int32_t* a, int na, int32_t* b, int nb, int32_t* c, int nc,
+                            hipStream_t stream) {
+    if (!a) na = 0;
+    if (!b) nb = 0;
+    if (!c) nc = 0;
+    if (na + nb + nc == 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(kBT), 0, stream, a, na, b, nb, c, nc);
+    return hipGetLastError();
+}
 
 size_t layout_workspace_bytes(int64_t T, int E, int R, int N) {
     const size_t nb = static_cast<size_t>((T + kBT - 1) / kBT);
@@ -972,6 +1120,62 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R
     if (R <= 512) EP_LAYOUT_CASE(8);
     EP_LAYOUT_CASE(16);
 #undef EP_LAYOUT_CASE
+}
+
+size_t counts_workspace_bytes(int64_t T, int E, int R, int N) {
+    const size_t nb = static_cast<size_t>((T + kBT - 1) / kBT);
+    return align_up(4, 256) + 2 * align_up(nb * R * 4, 256) +
+           align_up(nb * kWavesBT * R * 4, 256) + align_up(nb * kWavesBT * R * 8, 256) +
+           align_up(static_cast<size_t>(T) * 8, 256) + align_up(nb * 4, 256) +
+           align_up(nb * N * 4, 256) + align_up(nb * E * 4, 256);
+}
+
+CountsWorkspace carve_counts_workspace(void* base, int64_t T, int E, int R, int N) {
+    const size_t nb = static_cast<size_t>((T + kBT - 1) / kBT);
+    char* p = static_cast<char*>(base);
+    CountsWorkspace cw;
+    cw.ticket = reinterpret_cast<int32_t*>(p);
+    p += align_up(4, 256);
+    cw.blk_rank = reinterpret_cast<int32_t*>(p);
+    p += align_up(nb * R * 4, 256);
+    cw.glob = reinterpret_cast<int32_t*>(p);
+    p += align_up(nb * R * 4, 256);
+    cw.pfx = reinterpret_cast<int32_t*>(p);
+    p += align_up(nb * kWavesBT * R * 4, 256);
+    cw.ball = reinterpret_cast<uint64_t*>(p);
+    p += align_up(nb * kWavesBT * R * 8, 256);
+    cw.mask = reinterpret_cast<uint64_t*>(p);
+    p += align_up(static_cast<size_t>(T) * 8, 256);
+    cw.blk_err = reinterpret_cast<int32_t*>(p);
+    p += align_up(nb * 4, 256);
+    cw.blk_node = reinterpret_cast<int32_t*>(p);
+    p += align_up(nb * N * 4, 256);
+    cw.blk_exp = reinterpret_cast<int32_t*>(p);
+    return cw;
+}
+
+hipError_t launch_layout_counts(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
+                                int32_t* count_r, int32_t* rank_offset, int32_t* error_flag,
+                                const CountsWorkspace& cw, const RestripeTask* rs_in,
+                                hipStream_t stream) {
+    RestripeTask rs{};
+    if (rs_in != nullptr) rs = *rs_in;
+    const int64_t nb = (T + kBT - 1) / kBT;
+    if (nb == 0) {
+        // an empty batch: the layout's own path writes the zero counts and offsets
+        const LayoutWorkspace none{};
+        return launch_layout(topk_idx, T, k, E, R, N, count_r, nullptr, nullptr, nullptr,
+                             rank_offset, nullptr, nullptr, nullptr, nullptr, error_flag, none,
+                             nullptr, stream);
+    }
+    if (nb > INT32_MAX || !grid_fits(nb + rs.blocks, kBT)) return hipErrorInvalidConfiguration;
+    const FastDiv er = FastDiv::make(E / R);
+    const FastDiv rpn = FastDiv::make(R / N);
+    hipLaunchKernelGGL(layout_counts_kernel, dim3(static_cast<unsigned>(nb + rs.blocks)),
+                       dim3(kBT), sizeof(int32_t) * static_cast<size_t>(E), stream, topk_idx, T,
+                       k, E, R, N, er, rpn, cw, static_cast<int>(nb), rs, count_r, rank_offset,
+                       error_flag);
+    return hipGetLastError();
 }
 
 }  // namespace ep

@@ -1,10 +1,17 @@
-"""One batch through the whole path on the GPU: layout and restripe_prob (one call of the
-C ABI), dispatch, combine, on the same stream (or one call per step); and the two-phase
-("hook") form of dispatch and combine, whose send phase returns a callable that enqueues
-the receive phase later.
+"""One batch through the whole path on the GPU, on one stream, in three forms with the same
+outputs:
+- the counts path (R <= EP_COUNTS_MAX_RANKS): ep_layout_counts (counts, offsets and the
+  restripe in one launch), ep_dispatch_layout (the dispatch computing the receive rows and
+  writing the slot table), ep_combine;
+- the preprocess path: ep_dispatch_preprocess (layout and restripe in one call),
+  ep_dispatch, ep_combine;
+- one call per step: ep_get_layout, ep_dispatch, ep_restripe_prob, ep_combine.
+`step()` takes the counts path where it applies. Also the two-phase ("hook") form of
+dispatch and combine, whose send phase returns a callable that enqueues the receive phase
+later.
 
-Device buffers are allocated once per shape (torch, memory plumbing only); `step()`
-enqueues the four calls and returns without synchronising.
+Device buffers are allocated once per shape (torch, memory plumbing only); the step
+functions enqueue their calls and return without synchronising.
 """
 from __future__ import annotations
 
@@ -55,6 +62,12 @@ class Path:
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
         self.stage: Optional[StageBuffers] = None
         self._dispatch_pending = False  # a dispatch send whose receive hook has not run
+        # The counts path writes no node slots, so a Path that keeps them for the two-phase
+        # calls steps on the preprocess path.
+        self.counts_path = R <= B.EP_COUNTS_MAX_RANKS and not node_slots
+        self.counts_ws: Optional[torch.Tensor] = None  # workspace of the counts path
+        if self.counts_path:
+            self._counts_workspace()
 
     @property
     def error_flag(self) -> torch.Tensor:
@@ -85,13 +98,60 @@ class Path:
                                               self.prob_dest_major, stream=stream)
 
     def step(self, b: DeviceBatch, stream=None) -> None:
-        """The whole path on one batch: layout and restripe (one call), dispatch, combine."""
+        """The whole path on one batch: step_counts() where R allows it and the Path keeps
+        no node slots, else step_preprocess()."""
+        if self.counts_path:
+            self.step_counts(b, stream)
+        else:
+            self.step_preprocess(b, stream)
+
+    def step_preprocess(self, b: DeviceBatch, stream=None) -> None:
+        """Layout and restripe (one call), dispatch, combine."""
         self.preprocess(b, stream)
         self.dispatch(b, stream)
         self.combine(b, stream)
 
+    def _counts_workspace(self) -> torch.Tensor:
+        if self.counts_ws is None:
+            if self.R > B.EP_COUNTS_MAX_RANKS:
+                raise ValueError(f"the counts path needs num_ranks <= {B.EP_COUNTS_MAX_RANKS}")
+            n = B.ep_layout_counts_workspace_bytes(self.T, self.E, self.R, self.N)
+            # zero-filled once: every call leaves the ticket at the start zero again
+            self.counts_ws = torch.zeros(max(16, n), dtype=torch.uint8, device=self.out.device)
+        return self.counts_ws
+
+    def step_counts(self, b: DeviceBatch, stream=None) -> None:
+        """The same outputs as step_preprocess() in one launch less: ep_layout_counts
+        (counts, and the restripe in the same launch), ep_dispatch_layout (the dispatch
+        computing every receive row itself, writing token_slot and the bitmap),
+        ep_combine. Needs R <= EP_COUNTS_MAX_RANKS."""
+        self.layout_counts(b, stream)
+        self.dispatch_layout(b, stream)
+        self.combine(b, stream)
+
+    def layout_counts(self, b: DeviceBatch, stream=None) -> None:
+        """The counts path's first call: rank counts and offsets, the per-block tables in the
+        workspace, and the restripe in the same launch."""
+        ws, lb = self._counts_workspace(), self.layout_buf
+        B.ep_layout_counts(b.topk_idx, self.E, self.R, self.N,
+                           num_tokens_per_rank=lb.num_tokens_per_rank,
+                           rank_offset=lb.rank_offset, error_flag=self.error_flag, workspace=ws,
+                           prob=b.prob, prob_dest_major=self.prob_dest_major, stream=stream)
+
+    def dispatch_layout(self, b: DeviceBatch, stream=None) -> None:
+        """The counts path's dispatch, after layout_counts() on the same batch."""
+        ws, lb, r = self._counts_workspace(), self.layout_buf, self.recv
+        B.ep_dispatch_layout(b.x, b.topk_idx, b.topk_weights, self.E, self.R, self.N,
+                             token_slot=lb.token_slot, is_token_in_rank=lb.is_token_in_rank,
+                             num_tokens_per_node=lb.num_tokens_per_node,
+                             num_tokens_per_expert=lb.num_tokens_per_expert,
+                             expert_offset=lb.expert_offset,
+                             recv_x=r.recv_x, recv_topk_idx=r.recv_topk_idx,
+                             recv_topk_weights=r.recv_topk_weights, recv_src_idx=r.recv_src_idx,
+                             error_flag=self.error_flag, workspace=ws, stream=stream)
+
     def step_separate(self, b: DeviceBatch, stream=None) -> None:
-        """The same outputs as step(), one call per step of the path."""
+        """The same outputs as step_preprocess(), one call per step of the path."""
         self.layout(b, stream)
         self.dispatch(b, stream)
         self.restripe(b, stream)

@@ -32,6 +32,11 @@ def fill_sentinels(path: Path) -> None:
     path.prob_dest_major.view(torch.int32).fill_(int(np.uint32(SENT_U32).view(np.int32)))
     path.out.view(torch.int16).fill_(np.int16(np.uint16(SENT_U16).view(np.int16)))
     path.layout_buf.token_slot.fill_(-99)
+    path.layout_buf.is_token_in_rank.fill_(0xCD)
+    for t in (path.layout_buf.num_tokens_per_rank, path.layout_buf.num_tokens_per_node,
+              path.layout_buf.num_tokens_per_expert, path.layout_buf.rank_offset,
+              path.layout_buf.expert_offset):
+        t.fill_(-55)
     path.layout_buf.error_flag.fill_(-1)
 
 
@@ -46,27 +51,34 @@ def oracle_all(cfg: W.Config, inp: W.Inputs, partial_rows=None) -> dict:
     return dict(lay=lay, d=d, rs=rs, cb=cb, M=int(lay["rank_offset"][-1]))
 
 
-def run_gpu(cfg: W.Config, inp: W.Inputs, device="cuda", fused: bool = True) -> Path:
-    """One step of the path: layout and restripe in one call (ep_dispatch_preprocess), or
-    with fused=False one call per step (ep_get_layout ... ep_combine)."""
+STEP_FORMS = {"separate": "one call per step", "preprocess": "layout+restripe in one call",
+              "counts": "counts path (two launches for layout and dispatch)",
+              "step": "Path.step (the counts path where R allows it)"}
+
+
+def run_gpu(cfg: W.Config, inp: W.Inputs, device="cuda", fused: bool = True,
+            form: str = None) -> Path:
+    """One step of the path: form "step" (Path.step; the default), "preprocess" (layout and
+    restripe in one call, ep_dispatch_preprocess), "separate" (one call per step), or
+    "counts" (ep_layout_counts + ep_dispatch_layout)."""
+    form = form or ("step" if fused else "separate")
     b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials,
                               device=device)
     path = Path(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax, device=device)
     fill_sentinels(path)
-    if fused:
-        path.step(b)
-    else:
-        path.step_separate(b)
+    {"step": path.step, "preprocess": path.step_preprocess, "separate": path.step_separate,
+     "counts": path.step_counts}[form](b)
     torch.cuda.synchronize()
     return path
 
 
 def run_and_compare_both(cfg: W.Config, inp: W.Inputs, ref: dict, expect_flag: int = 0) -> Path:
-    """The step with the fused layout+restripe call and with one call per step: both must
-    match the oracle. Returns the last path."""
-    for fused in (False, True):
-        print(f"  {'fused layout+restripe' if fused else 'one call per step'}", flush=True)
-        path = run_gpu(cfg, inp, fused=fused)
+    """The step in every form (the counts path where R allows it): each must match the
+    oracle. Returns the last path."""
+    forms = ["separate", "preprocess"] + (["counts"] if cfg.R <= 64 else [])
+    for form in forms:
+        print(f"  {STEP_FORMS[form]}", flush=True)
+        path = run_gpu(cfg, inp, form=form)
         compare_all(cfg, path, ref, expect_flag=expect_flag)
     return path
 

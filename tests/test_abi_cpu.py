@@ -38,7 +38,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch_preprocess",
-                          "ep_dispatch", "ep_restripe_prob", "ep_combine", "ep_hbm_fan",
+                          "ep_layout_counts", "ep_dispatch_layout",
+                          "ep_layout_counts_workspace_bytes", "ep_dispatch", "ep_restripe_prob", "ep_combine", "ep_hbm_fan",
                           "ep_layout_workspace_bytes", "ep_status_string", "ep_hbm_copy",
                           "ep_dispatch_fp8", "ep_dispatch_permute", "ep_restripe_prob_sparse",
                           "ep_dispatch_send", "ep_dispatch_recv", "ep_combine_send",
@@ -158,6 +159,46 @@ def test_dispatch_preprocess_validation(lib):
     assert f(ws=P(0x10008)) == ep.EP_ERR_ALIGN
     assert f(Tmax=99) == ep.EP_ERR_CAPACITY
     assert f(wsb=16) == ep.EP_ERR_CAPACITY
+
+
+def test_counts_path_validation(lib):
+    # both calls of the counts path check their arguments on the host; R <= 64
+    q = lib.ep_layout_counts_workspace_bytes
+    nb = 16
+    assert q(4096, 256, 32, 4) >= 4096 * 8 + nb * (2 * 32 * 4 + 4 * 32 * 12 + 4 + 4 * 4 + 256 * 4)
+    assert q(4096, 256, 128, 4) == 0                            # R > EP_COUNTS_MAX_RANKS
+    assert q(10, 15, 4, 2) == 0
+    assert ep.EP_COUNTS_MAX_RANKS == 64
+
+    def counts(T=100, k=4, E=16, R=4, N=2, prob=None, P=8, Tmax=100, out=None, ws=A16,
+               wsb=1 << 20, cr=A16):
+        return lib.ep_layout_counts(A16, T, k, E, R, N, cr, A16, A16, prob, P, Tmax, out, ws, wsb,
+                                    None)
+    assert counts(E=15) == ep.EP_ERR_ARG
+    assert counts(E=256, R=128, N=4) == ep.EP_ERR_ARG           # R > 64
+    assert counts(cr=None) == ep.EP_ERR_ARG
+    assert counts(T=300_000_000, k=8, E=16, R=4) == ep.EP_ERR_ARG
+    assert counts(prob=A16, out=None) == ep.EP_ERR_ARG
+    assert counts(prob=A16, out=A16, P=0) == ep.EP_ERR_ARG
+    assert counts(prob=A16, out=A16, Tmax=99) == ep.EP_ERR_CAPACITY
+    assert counts(prob=P(0x10002), out=A16) == ep.EP_ERR_ALIGN
+    assert counts(ws=P(0x10008)) == ep.EP_ERR_ALIGN
+    assert counts(wsb=16) == ep.EP_ERR_CAPACITY
+    assert counts(ws=None) == ep.EP_ERR_CAPACITY
+
+    def disp(T=10, H=64, k=2, E=8, R=4, N=2, x=A16, slot=A16, idx=A16, ws=A16, wsb=1 << 20,
+             rx=A16, ce=A16):
+        return lib.ep_dispatch_layout(x, idx, A16, T, H, k, E, R, N, A16, ce, A16, slot, A16, rx,
+                                      A16, A16, A16, 100, A16, ws, wsb, None)
+    assert disp(H=12) == ep.EP_ERR_ALIGN
+    assert disp(x=MIS) == ep.EP_ERR_ALIGN
+    assert disp(ce=P(0x10002)) == ep.EP_ERR_ALIGN
+    assert disp(slot=None) == ep.EP_ERR_ARG
+    assert disp(idx=None) == ep.EP_ERR_ARG
+    assert disp(E=256, R=128, N=4) == ep.EP_ERR_ARG
+    assert disp(N=3) == ep.EP_ERR_ARG
+    assert disp(wsb=16) == ep.EP_ERR_CAPACITY
+    assert disp(ws=P(0x10004)) == ep.EP_ERR_ALIGN
 
 
 def test_dispatch_permute_validation(lib):

@@ -40,3 +40,20 @@ def test_two_paths_on_two_streams():
     torch.cuda.synchronize()
     for c, p, r in zip(cfgs, paths, refs):
         compare_all(c, p, r)
+    # the counts path, interleaved the same way: each Path has its own workspace
+    for p in paths:
+        fill_sentinels(p)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for p, b, s in zip(paths, batches, streams):
+            with torch.cuda.stream(s):
+                p.layout_counts(b, stream=s)
+        for p, b, s in zip(paths, batches, streams):
+            with torch.cuda.stream(s):
+                p.dispatch_layout(b, stream=s)
+        for p, b, s in zip(paths, batches, streams):
+            with torch.cuda.stream(s):
+                p.combine(b, stream=s)
+    torch.cuda.synchronize()
+    for c, p, r in zip(cfgs, paths, refs):
+        compare_all(c, p, r)

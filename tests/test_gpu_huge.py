@@ -71,15 +71,18 @@ def _token_sample(rng) -> np.ndarray:
                     dtype=np.int64)
 
 
-def test_path_rows_past_2_31_words(big):
+@pytest.mark.parametrize("form", ["counts", "preprocess"])
+def test_path_rows_past_2_31_words(big, form):
+    """Both step forms: the counts path (ep_layout_counts + ep_dispatch_layout) and the
+    preprocess path (ep_dispatch_preprocess + ep_dispatch)."""
     lay, x, idx, w = big["lay"], big["x"], big["idx"], big["w"]
     M = int(lay["rank_offset"][-1])
     assert M * V > WORD_LIMIT
-    print(f"case: huge path M={M} ({M * V / WORD_LIMIT:.2f} x 2^31 words)", flush=True)
+    print(f"case: huge path ({form}) M={M} ({M * V / WORD_LIMIT:.2f} x 2^31 words)", flush=True)
     b = DeviceBatch.from_host(idx, w, x, big["prob"])
     path = Path(T, H, E, K, R, N, P, T)
     fill_sentinels(path)
-    path.step(b)
+    path.step_counts(b) if form == "counts" else path.step_preprocess(b)
     torch.cuda.synchronize()
     L = path.layout_buf
     assert int(host(L.error_flag)[0]) == 0
@@ -89,7 +92,9 @@ def test_path_rows_past_2_31_words(big):
                     ("token_slot", L.token_slot)):
         np.testing.assert_array_equal(host(t), lay[name], err_msg=name)
 
-    d = oracle.dispatch(big["xn"], idx, w, E, R, lay["token_slot"], M)
+    if "d" not in big:
+        big["d"] = oracle.dispatch(big["xn"], idx, w, E, R, lay["token_slot"], M)
+    d = big["d"]
     r = path.recv
     np.testing.assert_array_equal(_narrow(r.recv_x, M), d["recv_x"])
     np.testing.assert_array_equal(host(r.recv_topk_idx[:M]), d["recv_idx"])
@@ -165,7 +170,9 @@ def test_two_phase_rows_past_2_31_words(big):
     torch.cuda.synchronize()
     assert int(host(path.error_flag)[0]) == 0
     np.testing.assert_array_equal(host(path.layout_buf.node_slot), ns)
-    d = oracle.dispatch(big["xn"], idx, w, E, R, lay["token_slot"], M)
+    if "d" not in big:
+        big["d"] = oracle.dispatch(big["xn"], idx, w, E, R, lay["token_slot"], M)
+    d = big["d"]
     r = path.recv
     np.testing.assert_array_equal(_narrow(r.recv_x, M), d["recv_x"])
     np.testing.assert_array_equal(host(r.recv_topk_idx[:M]), d["recv_idx"])

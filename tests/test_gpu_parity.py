@@ -307,22 +307,24 @@ def test_launches_split_over_token_ranges():
     _check_permute_and_send(cfg, inp)
 
 
+@pytest.mark.parametrize("form", ["counts", "preprocess"])
 @pytest.mark.parametrize("name", ["tiny", "dsv3"])
-def test_graph_replay_matches_eager(name):
-    """The whole step captured in a HIP graph: every replay, with eager work and
-    synchronisation in between, reproduces the eager outputs bit for bit."""
+def test_graph_replay_matches_eager(name, form):
+    """The whole step captured in a HIP graph, in both step forms: every replay, with eager
+    work and synchronisation in between, reproduces the eager outputs bit for bit."""
     cfg = W.CONFIGS[name]
     inp = _case(cfg)
     ref = oracle_all(cfg, inp)
     b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials)
     path = Path(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax)
+    step = path.step_counts if form == "counts" else path.step_preprocess
     fill_sentinels(path)
-    path.step(b)
+    step(b)
     torch.cuda.synchronize()
     compare_all(cfg, path, ref)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        path.step(b)
+        step(b)
     for _ in range(3):
         fill_sentinels(path)
         torch.cuda.synchronize()
