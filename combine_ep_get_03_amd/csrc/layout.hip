@@ -974,10 +974,14 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     const int any_bad = __syncthreads_or(bad);
     if (tid == 0) cw.blk_err[b] = any_bad;
 
-    // publish (device-scope release by every thread), then draw a ticket
-    __threadfence();
+    // Publish, then draw a ticket. Each wave waits until its table stores have reached
+    // the L2; after the barrier, thread 0's device-scope release fence writes the XCD's
+    // L2 back once for the whole block (a fence per wave writes it back four times over,
+    // 3 us more at 64 blocks on MI355X).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
+        __threadfence();
         const int drawn = atomicAdd(cw.ticket, 1);
         s_last = drawn == nlb - 1;
         // a ticket outside [0, nlb): the ticket was not zero on entry
@@ -985,7 +989,10 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();  // acquire: the other blocks' tables
+    // acquire: the other blocks' tables (one fence, ordered before the block's loads by
+    // the barrier, as on the release side)
+    if (tid == 0) __threadfence();
+    __syncthreads();
 
     // rank columns of blk_rank [nb][R]: thread (c, r) sums rows [c q, c q + q) of column r
     const int C = kBT / R;
@@ -993,14 +1000,20 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     const int r = tid % R, c = tid / R;
     const bool col = c < C;
     const int b0 = col ? min(nlb, c * q) : 0, b1 = col ? min(nlb, b0 + q) : 0;
+    const int32_t* __restrict__ blk_rank = cw.blk_rank;
+    int32_t* __restrict__ glob = cw.glob;
     int part = 0;
+    int keep[kBatch];  // the first batch's rows, reused below when they are all of them
     for (int bb = b0; bb < b1; bb += kBatch) {
         int v[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
-            v[u] = bb + u < b1 ? cw.blk_rank[static_cast<int64_t>(bb + u) * R + r] : 0;
+            v[u] = bb + u < b1 ? blk_rank[static_cast<int64_t>(bb + u) * R + r] : 0;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) part += v[u];
+        for (int u = 0; u < kBatch; ++u) {
+            part += v[u];
+            if (bb == b0) keep[u] = v[u];
+        }
     }
     int any = 0;
     for (int bb = tid; bb < nlb; bb += kBT) any |= cw.blk_err[bb];
@@ -1025,9 +1038,18 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     __syncthreads();
     if (col) {  // receive row of each block's first token on rank r
         int run = s_ro[r] + s_part[c * R + r];
-        for (int bb = b0; bb < b1; ++bb) {
-            cw.glob[static_cast<int64_t>(bb) * R + r] = run;
-            run += cw.blk_rank[static_cast<int64_t>(bb) * R + r];
+        for (int bb = b0; bb < b1; bb += kBatch) {
+            int v[kBatch];  // a batch of rows in flight at once (L2 hits after the sums)
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                v[u] = b1 - b0 <= kBatch ? keep[u]
+                       : bb + u < b1     ? blk_rank[static_cast<int64_t>(bb + u) * R + r]
+                                         : 0;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (bb + u < b1) glob[static_cast<int64_t>(bb + u) * R + r] = run;
+                run += v[u];
+            }
         }
     }
     any = __syncthreads_or(any);
