@@ -936,6 +936,11 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     const int b = blockIdx.x;
     const int64_t t = static_cast<int64_t>(b) * kBT + tid;
 
+    // The flag is cleared by block 0 as it starts (the hardware starts blocks in index
+    // order, and a block raises a bit only after its counting pass, microseconds later) and
+    // is only ORed into afterwards, so the last block cannot erase a bit another block
+    // raised.
+    if (b == 0 && tid == 0) __hip_atomic_store(error_flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int e = tid; e < E; e += kBT) s_hist[e] = 0;
     __syncthreads();
     uint64_t rm[1] = {0}, nm[1] = {0};
@@ -1054,7 +1059,7 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     }
     any = __syncthreads_or(any);
     if (tid == 0) {
-        *error_flag = any ? kErrTopkRange : 0;
+        if (any) raise_error(error_flag, kErrTopkRange);
         __hip_atomic_store(cw.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }

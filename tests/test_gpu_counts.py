@@ -200,3 +200,20 @@ def test_dispatch_split_over_token_ranges():
     ref = oracle_all(cfg, inp)
     path = run_gpu(cfg, inp, form="counts")
     compare_all(cfg, path, ref)
+
+
+def test_workspace_with_a_nonzero_ticket_is_reported():
+    """A workspace whose ticket is not zero on entry (never zero-filled, or shared by calls
+    that overlap) sets EP_DEVERR_WORKSPACE; the outputs of that call are unspecified, but
+    every kernel ends and stays in bounds. Zeroing the ticket makes the next call exact."""
+    cfg = W.Config("c_ticket", T=4096, H=64, E=256, k=8, R=32, N=4, P=8, Tmax=4096)
+    print(f"\ncase: counts path {cfg} with the ticket set to 5", flush=True)
+    inp = W.make_inputs(cfg, with_partials=False)
+    ws = torch.zeros(ep.ep_layout_counts_workspace_bytes(cfg.T, cfg.E, cfg.R, cfg.N),
+                     dtype=torch.uint8, device="cuda")
+    ws[:4].view(torch.int32).fill_(5)
+    got = _counts_call(cfg, inp, ws)
+    assert int(got["flag"][0]) & ep.EP_DEVERR_WORKSPACE
+    ws[:4].view(torch.int32).zero_()
+    got = _counts_call(cfg, inp, ws)
+    _check(cfg, inp, got)
