@@ -1,6 +1,7 @@
 """The C ABI driven from plain C (tests/c_abi/ep_c_smoke.c): device buffers from the
-HIP runtime, the four calls on one stream, every output compared bit for bit with the
-oracle inside the program."""
+HIP runtime, the path on one stream as the four calls and as the counts path
+(ep_layout_counts, ep_dispatch_layout, ep_combine), every output compared bit for bit with
+the oracle inside the program."""
 import os
 import subprocess
 
@@ -20,4 +21,5 @@ def test_c_program_matches_the_oracle():
     print("\ncase: C ABI program (T=256, H=1024, E=16, top-4, R=4, N=2)", flush=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     print(r.stdout, r.stderr, flush=True)
-    assert r.returncode == 0 and "ok" in r.stdout
+    assert r.returncode == 0
+    assert "four calls ok" in r.stdout and "counts path ok" in r.stdout
