@@ -50,9 +50,9 @@ def load() -> ctypes.CDLL:
                                          P, P]
     L.ep_layout_counts_workspace_bytes.argtypes = [i64, i32, i32, i32]
     L.ep_layout_counts_workspace_bytes.restype = sz
-    L.ep_layout_counts.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i32, i64, P, P, sz, P]
+    L.ep_layout_counts.argtypes = [P, i64, i32, i32, i32, i32, P, P, i32, i64, P, P, sz, P]
     L.ep_dispatch_layout.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, P,
-                                     P, P, i64, P, P, sz, P]
+                                     P, P, P, P, i64, P, P, sz, P]
     L.ep_dispatch_preprocess.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
                                          P, P, i32, i64, P, P, sz, P]
     L.ep_restripe_prob_sparse.argtypes = [P, i64, i32, i32, P, i64, P, P, P]
@@ -229,16 +229,14 @@ def ep_layout_counts_workspace_bytes(num_tokens: int, num_experts: int, num_rank
 
 
 def ep_layout_counts(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
-                     num_tokens_per_rank, rank_offset, error_flag, workspace, prob=None,
-                     prob_dest_major=None, stream=None) -> None:
-    """The count launch of the counts path (num_ranks <= EP_COUNTS_MAX_RANKS): the rank
-    counts and offsets and the error flag, and with prob the restripe of prob. The first 4
-    bytes of `workspace` (uint8, ep_layout_counts_workspace_bytes) must be zero before its
-    first use; every call leaves them zero."""
+                     error_flag, workspace, prob=None, prob_dest_major=None,
+                     stream=None) -> None:
+    """The count launch of the counts path (num_ranks <= EP_COUNTS_MAX_RANKS): the
+    per-block tables in `workspace` and the error flag, and with prob the restripe of prob.
+    The first 4 bytes of `workspace` (uint8, ep_layout_counts_workspace_bytes) must be zero
+    before its first use; every call leaves them zero."""
     T, k = topk_idx.shape
     E, R, N = num_experts, num_ranks, num_nodes
-    _at_least(num_tokens_per_rank, R, "num_tokens_per_rank")
-    _at_least(rank_offset, R + 1, "rank_offset")
     _at_least(error_flag, 1, "error_flag")
     P, Tmax = 0, 0
     if prob is not None:
@@ -251,8 +249,6 @@ def ep_layout_counts(topk_idx, num_experts: int, num_ranks: int, num_nodes: int,
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load().ep_layout_counts(
         _ptr(topk_idx, torch.int64, "topk_idx"), T, k, E, R, N,
-        _ptr(num_tokens_per_rank, torch.int32, "num_tokens_per_rank"),
-        _ptr(rank_offset, torch.int32, "rank_offset"),
         _ptr(error_flag, torch.int32, "error_flag"),
         _ptr(prob, torch.float32, "prob", True), P, Tmax,
         _ptr(prob_dest_major, torch.float32, "prob_dest_major", True),
@@ -261,12 +257,13 @@ def ep_layout_counts(topk_idx, num_experts: int, num_ranks: int, num_nodes: int,
 
 def ep_dispatch_layout(x, topk_idx, topk_weights, num_experts: int, num_ranks: int,
                        num_nodes: int, *, token_slot, recv_x, workspace, is_token_in_rank=None,
-                       num_tokens_per_node=None, num_tokens_per_expert=None, expert_offset=None,
-                       recv_topk_idx=None, recv_topk_weights=None, recv_src_idx=None,
-                       error_flag=None, stream=None) -> None:
+                       num_tokens_per_rank=None, rank_offset=None, num_tokens_per_node=None,
+                       num_tokens_per_expert=None, expert_offset=None, recv_topk_idx=None,
+                       recv_topk_weights=None, recv_src_idx=None, error_flag=None,
+                       stream=None) -> None:
     """The dispatch of the counts path, after ep_layout_counts on the same batch and
     workspace: ep_dispatch's outputs plus token_slot [T][R], is_token_in_rank [T][R] and the
-    node and expert counts and offsets."""
+    rank, node and expert counts and offsets."""
     T, H = x.shape
     k = topk_idx.shape[1]
     E, R, N = num_experts, num_ranks, num_nodes
@@ -275,6 +272,8 @@ def ep_dispatch_layout(x, topk_idx, topk_weights, num_experts: int, num_ranks: i
     _shape(topk_weights, (T, k), "topk_weights")
     _shape(token_slot, (T, R), "token_slot")
     _shape(is_token_in_rank, (T, R), "is_token_in_rank")
+    _at_least(num_tokens_per_rank, R, "num_tokens_per_rank")
+    _at_least(rank_offset, R + 1, "rank_offset")
     _at_least(num_tokens_per_node, N, "num_tokens_per_node")
     _at_least(num_tokens_per_expert, E, "num_tokens_per_expert")
     _at_least(expert_offset, E + 1, "expert_offset")
@@ -287,6 +286,8 @@ def ep_dispatch_layout(x, topk_idx, topk_weights, num_experts: int, num_ranks: i
     _check(load().ep_dispatch_layout(
         _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int64, "topk_idx"),
         _ptr(topk_weights, torch.float32, "topk_weights", True), T, H, k, E, R, N,
+        _ptr(num_tokens_per_rank, torch.int32, "num_tokens_per_rank", True),
+        _ptr(rank_offset, torch.int32, "rank_offset", True),
         _ptr(num_tokens_per_node, torch.int32, "num_tokens_per_node", True),
         _ptr(num_tokens_per_expert, torch.int32, "num_tokens_per_expert", True),
         _ptr(expert_offset, torch.int32, "expert_offset", True),

@@ -166,6 +166,9 @@ __device__ __forceinline__ void dest_range(int d, int D, int P, int& lo, int& hi
     hi = d == D - 1 ? INT32_MAX : lo + P;
 }
 
+// Lanes past the row's end skip their loads; their words are zero, not undefined, so the
+// compiler keeps every load of the pass in flight at once rather than branching around
+// each one.
 template <int WPL>
 __device__ __forceinline__ void load_row_cached(u32x4 (&v)[WPL], const u32x4* __restrict__ xr,
                                                 int v0, int V) {
@@ -173,6 +176,7 @@ __device__ __forceinline__ void load_row_cached(u32x4 (&v)[WPL], const u32x4* __
 #pragma unroll
     for (int i = 0; i < WPL; ++i) {
         const int vi = v0 + i * kWave + lane;
+        v[i] = u32x4{0u, 0u, 0u, 0u};
         if (vi < V) v[i] = xr[vi];
     }
 }
@@ -244,18 +248,43 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
                                     recv_src, error_flag);
 }
 
-// The node and expert counts and offsets of the counts path, from the count launch's
-// per-block tables: head block h of ep_dispatch_layout's first launch takes expert columns
-// [256 h, 256 h + 256). A column sum of the blocks' inclusive expert prefixes is
+// The rank, node and expert counts and offsets of the counts path, from the count
+// launch's per-block tables: head block h of ep_dispatch_layout's first launch takes expert
+// columns [256 h, 256 h + 256). A column sum of the blocks' inclusive expert prefixes is
 // expert_offset[e + 1]; the count is its difference with the column before, which each
 // thread sums as well (no LDS, no barrier: the dispatch kernel stays free of both). Head
-// block 0 also sums the node columns.
+// block 0 also sums the node columns, and its first wave the rank columns (lane r), whose
+// scan across the wave gives the rank offsets.
 __device__ __forceinline__ void counts_head_block(const CountsWorkspace& cw, int h, int nb,
-                                                  int E, int N, int32_t* __restrict__ count_n,
+                                                  int E, int R, int N,
+                                                  int32_t* __restrict__ count_r,
+                                                  int32_t* __restrict__ rank_offset,
+                                                  int32_t* __restrict__ count_n,
                                                   int32_t* __restrict__ count_e,
                                                   int32_t* __restrict__ expert_offset) {
     constexpr int kB = 8;  // loads in flight per lane
     const int tid = threadIdx.x;
+    if (h == 0 && tid < kWave && (count_r || rank_offset)) {
+        int tot = 0;
+        for (int b0 = 0; b0 < nb; b0 += kB) {
+            int v[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+                v[u] = (b0 + u < nb && tid < R) ? cw.blk_rank[static_cast<int64_t>(b0 + u) * R + tid] : 0;
+#pragma unroll
+            for (int u = 0; u < kB; ++u) tot += v[u];
+        }
+        int x = tot;  // inclusive scan over the wave
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int y = __shfl_up(x, d, kWave);
+            if (tid >= d) x += y;
+        }
+        if (tid < R) {
+            if (count_r) count_r[tid] = tot;
+            if (rank_offset) rank_offset[tid] = x - tot;
+        }
+        if (tid == kWave - 1 && rank_offset) rank_offset[R] = x;
+    }
     const int e = h * kDestThreads + tid;
     if ((count_e || expert_offset) && e < E) {
         int sum = 0, before = 0;  // column e, and column e - 1 (0 for e = 0)
@@ -294,19 +323,25 @@ __device__ __forceinline__ void counts_head_block(const CountsWorkspace& cw, int
 // loads are all issued together. The token's row on rank r is then
 //     glob[b][r] + pfx[b][w][r] + popcount(ball[b][w][r] & (bits below the token)),
 // so a wave waits on one memory round trip before its stores, as dispatch_kernel does.
+// With kLocal (batches of at most kCountsLocalBlocks blocks, whose count launch has no
+// cross-block phase), lane r instead loads rank r's count in every block (at most 16
+// loads, issued with the rest) and forms glob[b][r] itself: the rank offset (a scan of the
+// totals across the wave) plus the counts of the blocks before b.
 // The token's first wave also writes the token's token_slot row and bitmap row. The first
 // `nhead` blocks are head blocks (counts_head_block) instead.
-template <int WPL, bool kMulti, int kThreads>
+template <int WPL, bool kMulti, bool kLocal, int kThreads>
 __global__ __launch_bounds__(kThreads) void dispatch_layout_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, int64_t t0, int64_t t_end, int V, int k, int R, int er,
     CountsWorkspace cw, FastDiv D, int32_t* __restrict__ token_slot,
     uint8_t* __restrict__ in_rank, u32x4* __restrict__ recv_x, int64_t* __restrict__ recv_idx,
     float* __restrict__ recv_w, int32_t* __restrict__ recv_src, int64_t cap, int nhead, int nb,
-    int E, int N, int32_t* __restrict__ count_n, int32_t* __restrict__ count_e,
+    int E, int N, int32_t* __restrict__ count_r, int32_t* __restrict__ rank_offset,
+    int32_t* __restrict__ count_n, int32_t* __restrict__ count_e,
     int32_t* __restrict__ expert_offset, int32_t* __restrict__ error_flag) {
     if (static_cast<int>(blockIdx.x) < nhead) {
-        counts_head_block(cw, blockIdx.x, nb, E, N, count_n, count_e, expert_offset);
+        counts_head_block(cw, blockIdx.x, nb, E, R, N, count_r, rank_offset, count_n, count_e,
+                          expert_offset);
         return;
     }
     int64_t t;
@@ -321,9 +356,16 @@ __global__ __launch_bounds__(kThreads) void dispatch_layout_kernel(
     const uint64_t m = cw.mask[t];
     int32_t g = 0, pf = 0;
     uint64_t bl = 0;
+    int cnt[kLocal ? kCountsLocalBlocks : 1];  // rank `lane`'s count in each block
+    if constexpr (kLocal) {
+#pragma unroll
+        for (int u = 0; u < kCountsLocalBlocks; ++u)
+            cnt[u] = (u < nb && lane < R) ? cw.blk_rank[u * R + lane] : 0;
+    } else if (lane < R) {
+        g = cw.glob[b * R + lane];
+    }
     if (lane < R) {
         const int64_t cell = (b * (kBlk / kWave) + w) * R + lane;
-        g = cw.glob[b * R + lane];
         pf = cw.pfx[cell];
         bl = cw.ball[cell];
     }
@@ -332,6 +374,20 @@ __global__ __launch_bounds__(kThreads) void dispatch_layout_kernel(
     const u32x4* xr = x + t * V;
     u32x4 v[WPL];
     load_row_cached(v, xr, 0, V);  // first pass, issued with the tables' loads
+    if constexpr (kLocal) {  // the counts arrive with the tables: glob[b][lane] from them
+        int tot = 0;
+#pragma unroll
+        for (int u = 0; u < kCountsLocalBlocks; ++u) {
+            tot += cnt[u];
+            if (u < b) g += cnt[u];
+        }
+        int x = tot;  // inclusive scan of the rank totals across the wave
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int y = __shfl_up(x, d, kWave);
+            if (lane >= d) x += y;
+        }
+        g += x - tot;
+    }
     const bool on = lane < R && ((m >> lane) & 1ull);
     const int32_t slot = on ? g + pf + __popcll(bl & ((1ull << l) - 1ull)) : -1;
     if (d == 0 && lane < R) {
@@ -672,9 +728,9 @@ hipError_t launch_dispatch_layout(const void* x, const int64_t* topk_idx, const 
                                   int64_t T, int H, int k, int E, int R, int N,
                                   const CountsWorkspace& cw, int32_t* token_slot, uint8_t* in_rank,
                                   void* recv_x, int64_t* recv_idx, float* recv_w,
-                                  int32_t* recv_src, int64_t cap, int32_t* count_n,
-                                  int32_t* count_e, int32_t* expert_offset, int32_t* error_flag,
-                                  hipStream_t stream) {
+                                  int32_t* recv_src, int64_t cap, int32_t* count_r,
+                                  int32_t* rank_offset, int32_t* count_n, int32_t* count_e,
+                                  int32_t* expert_offset, int32_t* error_flag, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
     const int D = std::min(k, R);  // waves per token: ranks a token can reach
@@ -685,18 +741,25 @@ hipError_t launch_dispatch_layout(const void* x, const int64_t* topk_idx, const 
     // neighbouring XCDs)
     int head = 0;
     if (count_e || expert_offset) head = (E + kDestThreads - 1) / kDestThreads;
-    else if (count_n) head = 1;
+    else if (count_n || count_r || rank_offset) head = 1;
     head = (head + 7) / 8 * 8;
+    const bool local = nb <= kCountsLocalBlocks;
     return launch_by_token_range<14>(V, T, D, [&](auto wpl, auto multi, int64_t t0, int64_t t_end,
                                                   unsigned grid) {
         const int nhead = t0 == 0 ? head : 0;
-        hipLaunchKernelGGL((dispatch_layout_kernel<decltype(wpl)::value, decltype(multi)::value,
-                                                   kDestThreads>),
-                           dim3(grid + nhead), dim3(kDestThreads), 0, stream,
-                           static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, R,
-                           E / R, cw, fd, token_slot, in_rank, static_cast<u32x4*>(recv_x),
-                           recv_idx, recv_w, recv_src, cap, nhead, nb, E, N, count_n, count_e,
-                           expert_offset, error_flag);
+        auto go = [&](auto loc) {
+            hipLaunchKernelGGL((dispatch_layout_kernel<decltype(wpl)::value, decltype(multi)::value,
+                                                       decltype(loc)::value, kDestThreads>),
+                               dim3(grid + nhead), dim3(kDestThreads), 0, stream,
+                               static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, R,
+                               E / R, cw, fd, token_slot, in_rank, static_cast<u32x4*>(recv_x),
+                               recv_idx, recv_w, recv_src, cap, nhead, nb, E, N, count_r,
+                               rank_offset, count_n, count_e, expert_offset, error_flag);
+        };
+        if (local)
+            go(std::true_type{});
+        else
+            go(std::false_type{});
     });
 }
 

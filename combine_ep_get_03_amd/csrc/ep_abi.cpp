@@ -173,8 +173,7 @@ size_t ep_layout_counts_workspace_bytes(int64_t num_tokens, int num_experts, int
 }
 
 int ep_layout_counts(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-                     int num_ranks, int num_nodes, int32_t* num_tokens_per_rank,
-                     int32_t* rank_offset, int32_t* error_flag, const float* prob,
+                     int num_ranks, int num_nodes, int32_t* error_flag, const float* prob,
                      int prob_per_token, int64_t max_tokens_per_rank, float* prob_dest_major,
                      void* workspace, size_t workspace_bytes, void* stream) {
     const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
@@ -182,15 +181,14 @@ int ep_layout_counts(const int64_t* topk_idx, int64_t num_tokens, int num_topk, 
     if (!topology_ok(k, E, R, N) || R > EP_COUNTS_MAX_RANKS || !slots_fit_int32(T, k, R) ||
         T > static_cast<int64_t>(INT32_MAX) / k)
         return EP_ERR_ARG;
-    if (!num_tokens_per_rank || !rank_offset || !error_flag) return EP_ERR_ARG;
+    if (!error_flag) return EP_ERR_ARG;
     if (T > 0 && !topk_idx) return EP_ERR_ARG;
     if (prob) {
         if (P < 1 || static_cast<int64_t>(N) * P > (1 << 26)) return EP_ERR_ARG;
         if (T > 0 && !prob_dest_major) return EP_ERR_ARG;
     }
-    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) || !aligned(rank_offset, 4) ||
-        !aligned(error_flag, 4) || !aligned(prob, 4) || !aligned(prob_dest_major, 4) ||
-        !aligned(workspace, 16))
+    if (!aligned(topk_idx, 8) || !aligned(error_flag, 4) || !aligned(prob, 4) ||
+        !aligned(prob_dest_major, 4) || !aligned(workspace, 16))
         return EP_ERR_ALIGN;
     if (prob && Tmax < T) return EP_ERR_CAPACITY;
     const size_t need = ep::counts_workspace_bytes(T, E, R, N);
@@ -198,14 +196,14 @@ int ep_layout_counts(const int64_t* topk_idx, int64_t num_tokens, int num_topk, 
     const ep::CountsWorkspace cw = ep::carve_counts_workspace(workspace, T, E, R, N);
     ep::RestripeTask rs{};
     if (prob) rs = ep::plan_restripe(prob, T, N, P, Tmax, prob_dest_major);
-    return hip_status(ep::launch_layout_counts(topk_idx, T, k, E, R, N, num_tokens_per_rank,
-                                               rank_offset, error_flag, cw, &rs,
+    return hip_status(ep::launch_layout_counts(topk_idx, T, k, E, R, N, error_flag, cw, &rs,
                                                static_cast<hipStream_t>(stream)));
 }
 
 int ep_dispatch_layout(const void* x, const int64_t* topk_idx, const float* topk_weights,
                        int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                       int num_ranks, int num_nodes, int32_t* num_tokens_per_node,
+                       int num_ranks, int num_nodes, int32_t* num_tokens_per_rank,
+                       int32_t* rank_offset, int32_t* num_tokens_per_node,
                        int32_t* num_tokens_per_expert, int32_t* expert_offset,
                        int32_t* token_slot, uint8_t* is_token_in_rank, void* recv_x,
                        int64_t* recv_topk_idx, float* recv_topk_weights, int32_t* recv_src_idx,
@@ -226,20 +224,24 @@ int ep_dispatch_layout(const void* x, const int64_t* topk_idx, const float* topk
         !aligned(topk_weights, 4) || !aligned(token_slot, 4) || !aligned(recv_topk_idx, 8) ||
         !aligned(recv_topk_weights, 4) || !aligned(recv_src_idx, 4) || !aligned(error_flag, 4) ||
         !aligned(num_tokens_per_node, 4) || !aligned(num_tokens_per_expert, 4) ||
-        !aligned(expert_offset, 4) || !aligned(workspace, 16))
+        !aligned(expert_offset, 4) || !aligned(num_tokens_per_rank, 4) ||
+        !aligned(rank_offset, 4) || !aligned(workspace, 16))
         return EP_ERR_ALIGN;
     const size_t need = ep::counts_workspace_bytes(T, E, R, N);
     if (workspace_bytes < need || !workspace) return EP_ERR_CAPACITY;
-    if (T == 0)  // an empty batch: zero counts and offsets, nothing to dispatch
-        return hip_status(ep::launch_zero_ints(num_tokens_per_node, N, num_tokens_per_expert, E,
-                                               expert_offset, E + 1,
-                                               static_cast<hipStream_t>(stream)));
+    if (T == 0) {  // an empty batch: zero counts and offsets, nothing to dispatch
+        const ep::ZeroInts z{{num_tokens_per_rank, rank_offset, num_tokens_per_node,
+                              num_tokens_per_expert, expert_offset},
+                             {R, R + 1, N, E, E + 1}};
+        return hip_status(ep::launch_zero_ints(z, static_cast<hipStream_t>(stream)));
+    }
     const ep::CountsWorkspace cw =
         ep::carve_counts_workspace(const_cast<void*>(workspace), T, E, R, N);
     return hip_status(ep::launch_dispatch_layout(
         x, topk_idx, topk_weights, T, H, k, E, R, N, cw, token_slot, is_token_in_rank, recv_x,
-        recv_topk_idx, recv_topk_weights, recv_src_idx, recv_capacity, num_tokens_per_node,
-        num_tokens_per_expert, expert_offset, error_flag, static_cast<hipStream_t>(stream)));
+        recv_topk_idx, recv_topk_weights, recv_src_idx, recv_capacity, num_tokens_per_rank,
+        rank_offset, num_tokens_per_node, num_tokens_per_expert, expert_offset, error_flag,
+        static_cast<hipStream_t>(stream)));
 }
 
 int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,

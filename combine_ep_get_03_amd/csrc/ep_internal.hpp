@@ -177,6 +177,7 @@ struct CountsWorkspace {
     int32_t* ticket;    // [1]     blocks of the count launch that have published
     int32_t* blk_rank;  // [nb][R] tokens per rank in each block
     int32_t* glob;      // [nb][R] receive row of each block's first token on each rank
+                        //         (written only for batches past kCountsLocalBlocks blocks)
     int32_t* pfx;       // [nb][4][R] tokens on each rank in the block's earlier waves
     uint64_t* ball;     // [nb][4][R] which of each wave's 64 tokens are on each rank
     uint64_t* mask;     // [T] the ranks of each token
@@ -187,17 +188,25 @@ struct CountsWorkspace {
 size_t counts_workspace_bytes(int64_t T, int E, int R, int N);
 CountsWorkspace carve_counts_workspace(void* base, int64_t T, int E, int R, int N);
 
-// Zero fill of up to three int32 arrays (NULL ones skipped) with a kernel, so that the
+// Zero fill of up to five int32 arrays (NULL ones skipped) with a kernel, so that the
 // fill can be captured into a graph.
-hipError_t launch_zero_ints(int32_t* a, int na, int32_t* b, int nb, int32_t* c, int nc,
-                            hipStream_t stream);
+struct ZeroInts {
+    int32_t* p[5];
+    int n[5];
+};
+hipError_t launch_zero_ints(const ZeroInts& z, hipStream_t stream);
 
-// The count launch of the counts path (the restripe's blocks may ride along): the rank
-// counts and offsets, the error flag, and the tables ep_dispatch_layout reads.
+// Batches of at most this many 256-token blocks take the counts path without a ticket:
+// each dispatch wave sums the per-block rank counts it needs itself (one load per block
+// per lane), so the count launch has no cross-block phase. Larger batches keep the
+// ticket, whose last block writes each block's first receive row per rank.
+constexpr int kCountsLocalBlocks = 16;
+
+// The count launch of the counts path (the restripe's blocks may ride along): the error
+// flag and the tables ep_dispatch_layout reads.
 hipError_t launch_layout_counts(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
-                                int32_t* count_r, int32_t* rank_offset, int32_t* error_flag,
-                                const CountsWorkspace& cw, const RestripeTask* rs,
-                                hipStream_t stream);
+                                int32_t* error_flag, const CountsWorkspace& cw,
+                                const RestripeTask* rs, hipStream_t stream);
 
 // dispatch.hip: one-call dispatch, FP8 dispatch, expert-major permute, and the two
 // phases of the two-phase dispatch
@@ -226,9 +235,9 @@ hipError_t launch_dispatch_layout(const void* x, const int64_t* topk_idx, const 
                                   int64_t T, int H, int k, int E, int R, int N,
                                   const CountsWorkspace& cw, int32_t* token_slot, uint8_t* in_rank,
                                   void* recv_x, int64_t* recv_idx, float* recv_w,
-                                  int32_t* recv_src, int64_t cap, int32_t* count_n,
-                                  int32_t* count_e, int32_t* expert_offset, int32_t* error_flag,
-                                  hipStream_t stream);
+                                  int32_t* recv_src, int64_t cap, int32_t* count_r,
+                                  int32_t* rank_offset, int32_t* count_n, int32_t* count_e,
+                                  int32_t* expert_offset, int32_t* error_flag, hipStream_t stream);
 hipError_t launch_dispatch_recv(const void* stage_x, const int64_t* stage_idx,
                                 const float* stage_w, const int32_t* stage_src,
                                 const int32_t* count_n, int N, int64_t Tmax, int H, int k, int E,

@@ -911,15 +911,15 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
 // its 256 tokens as layout_count_kernel does and publishes, for ep_dispatch_layout: each
 // token's rank mask, each wave's rank ballots and the tokens of its earlier waves per
 // rank, the block's rank and node counts and the inclusive prefix of its expert
-// histogram. Every block then takes a ticket; the block that draws the last one (no block
-// waits for another) turns the blocks' rank counts into the rank totals and offsets and
-// the receive row of each block's first token on each rank, writes the error flag, and
-// zeroes the ticket for the next call; a batch of one block takes its offsets from its
-// own counts instead. Blocks past `nlb` run the dense restripe riding along in this launch.
+// histogram. A batch of at most kCountsLocalBlocks blocks stops there: the dispatch's
+// waves sum the per-block rank counts themselves. In a larger batch every block then takes
+// a ticket; the block that draws the last one (no block waits for another) turns the
+// blocks' rank counts into the receive row of each block's first token on each rank and
+// zeroes the ticket for the next call. Blocks past `nlb` run the dense restripe riding
+// along in this launch.
 __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int N, FastDiv er,
-    FastDiv rpn, CountsWorkspace cw, int nlb, RestripeTask rs, int32_t* __restrict__ count_r,
-    int32_t* __restrict__ rank_offset, int32_t* __restrict__ error_flag) {
+    FastDiv rpn, CountsWorkspace cw, int nlb, RestripeTask rs, int32_t* __restrict__ error_flag) {
     if (static_cast<int>(blockIdx.x) >= nlb) {
         restripe_task_block(rs, static_cast<int64_t>(blockIdx.x) - nlb);
         return;
@@ -929,7 +929,6 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     __shared__ uint16_t s_wn[kWavesBT * kCountsMaxRanks];    // [4][N] node counts per wave
     __shared__ int32_t s_part[kBT];                          // last block: partial column sums
     __shared__ int32_t s_ro[kCountsMaxRanks];                // last block: rank offsets
-    __shared__ int32_t s_cnt[kCountsMaxRanks];               // this block's tokens per rank
     __shared__ int32_t s_scan[17];
     __shared__ int32_t s_last;
     const int tid = threadIdx.x;
@@ -960,11 +959,7 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
         for (int v = 0; v < w; ++v) before += __popcll(s_ball[v * R + r]);
         cw.ball[static_cast<int64_t>(b) * kWavesBT * R + i] = s_ball[i];
         cw.pfx[static_cast<int64_t>(b) * kWavesBT * R + i] = before;
-        if (w == kWavesBT - 1) {
-            const int cnt = before + __popcll(s_ball[i]);
-            cw.blk_rank[static_cast<int64_t>(b) * R + r] = cnt;
-            s_cnt[r] = cnt;
-        }
+        if (w == kWavesBT - 1) cw.blk_rank[static_cast<int64_t>(b) * R + r] = before + __popcll(s_ball[i]);
     }
     for (int n = tid; n < N; n += kBT) {
         int c = 0;
@@ -982,25 +977,8 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
         carry += chunk;
     }
     const int any_bad = __syncthreads_or(bad);
-    if (nlb == 1) {
-        // The block is the whole batch: the rank offsets come straight from its own counts,
-        // with no ticket and no second phase (3 us less at 256 tokens on MI355X).
-        if (wave == 0) {
-            const int lane = lane_id();
-            const int tot = lane < R ? s_cnt[lane] : 0;
-            int x = tot;
-            for (int d = 1; d < kWave; d <<= 1) {
-                const int y = __shfl_up(x, d, kWave);
-                if (lane >= d) x += y;
-            }
-            if (lane < R) {
-                count_r[lane] = tot;
-                rank_offset[lane] = x - tot;
-                cw.glob[lane] = x - tot;
-            }
-            if (lane == kWave - 1) rank_offset[R] = x;
-            if (lane == 0 && any_bad) raise_error(error_flag, kErrTopkRange);
-        }
+    if (nlb <= kCountsLocalBlocks) {  // no cross-block phase: the dispatch sums the counts
+        if (tid == 0 && any_bad) raise_error(error_flag, kErrTopkRange);
         return;
     }
     if (tid == 0) cw.blk_err[b] = any_bad;
@@ -1060,12 +1038,7 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     }
     int M = 0;
     const int ro = block_exclusive_scan(tid < R ? tot : 0, s_scan, M);
-    if (tid < R) {
-        s_ro[tid] = ro;
-        count_r[tid] = tot;
-        rank_offset[tid] = ro;
-    }
-    if (tid == 0) rank_offset[R] = M;
+    if (tid < R) s_ro[tid] = ro;
     __syncthreads();
     if (col) {  // receive row of each block's first token on rank r
         int run = s_ro[r] + s_part[c * R + r];
@@ -1090,22 +1063,23 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     }
 }
 
-__global__ __launch_bounds__(kBT) void zero_ints_kernel(int32_t* a, int na, int32_t* b, int nb,
-                                                        int32_t* c, int nc) {
-    for (int i = threadIdx.x; i < na; i += kBT) a[i] = 0;
-    for (int i = threadIdx.x; i < nb; i += kBT) b[i] = 0;
-    for (int i = threadIdx.x; i < nc; i += kBT) c[i] = 0;
+__global__ __launch_bounds__(kBT) void zero_ints_kernel(ZeroInts z) {
+#pragma unroll
+    for (int a = 0; a < 5; ++a)
+        for (int i = threadIdx.x; i < z.n[a]; i += kBT) z.p[a][i] = 0;
 }
 
 }  // namespace
 
-hipError_t launch_zero_ints(int32_t* a, int na, int32_t* b, int nb, int32_t* c, int nc,
-                            hipStream_t stream) {
-    if (!a) na = 0;
-    if (!b) nb = 0;
-    if (!c) nc = 0;
-    if (na + nb + nc == 0) return hipSuccess;
-    hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(kBT), 0, stream, a, na, b, nb, c, nc);
+hipError_t launch_zero_ints(const ZeroInts& z_in, hipStream_t stream) {
+    ZeroInts z = z_in;
+    int total = 0;
+    for (int a = 0; a < 5; ++a) {
+        if (!z.p[a]) z.n[a] = 0;
+        total += z.n[a];
+    }
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(kBT), 0, stream, z);
     return hipGetLastError();
 }
 
@@ -1208,26 +1182,23 @@ CountsWorkspace carve_counts_workspace(void* base, int64_t T, int E, int R, int 
 }
 
 hipError_t launch_layout_counts(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
-                                int32_t* count_r, int32_t* rank_offset, int32_t* error_flag,
-                                const CountsWorkspace& cw, const RestripeTask* rs_in,
-                                hipStream_t stream) {
+                                int32_t* error_flag, const CountsWorkspace& cw,
+                                const RestripeTask* rs_in, hipStream_t stream) {
     RestripeTask rs{};
     if (rs_in != nullptr) rs = *rs_in;
     const int64_t nb = (T + kBT - 1) / kBT;
-    if (nb == 0) {
-        // an empty batch: the layout's own path writes the zero counts and offsets
-        const LayoutWorkspace none{};
-        return launch_layout(topk_idx, T, k, E, R, N, count_r, nullptr, nullptr, nullptr,
-                             rank_offset, nullptr, nullptr, nullptr, nullptr, error_flag, none,
-                             nullptr, stream);
+    if (nb == 0) {  // an empty batch: no error, nothing to count or restripe
+        ZeroInts z{};
+        z.p[0] = error_flag;
+        z.n[0] = 1;
+        return launch_zero_ints(z, stream);
     }
     if (nb > INT32_MAX || !grid_fits(nb + rs.blocks, kBT)) return hipErrorInvalidConfiguration;
     const FastDiv er = FastDiv::make(E / R);
     const FastDiv rpn = FastDiv::make(R / N);
     hipLaunchKernelGGL(layout_counts_kernel, dim3(static_cast<unsigned>(nb + rs.blocks)),
                        dim3(kBT), sizeof(int32_t) * static_cast<size_t>(E), stream, topk_idx, T,
-                       k, E, R, N, er, rpn, cw, static_cast<int>(nb), rs, count_r, rank_offset,
-                       error_flag);
+                       k, E, R, N, er, rpn, cw, static_cast<int>(nb), rs, error_flag);
     return hipGetLastError();
 }
 

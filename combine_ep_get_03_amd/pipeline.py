@@ -130,19 +130,19 @@ class Path:
         self.combine(b, stream)
 
     def layout_counts(self, b: DeviceBatch, stream=None) -> None:
-        """The counts path's first call: rank counts and offsets, the per-block tables in the
-        workspace, and the restripe in the same launch."""
-        ws, lb = self._counts_workspace(), self.layout_buf
-        B.ep_layout_counts(b.topk_idx, self.E, self.R, self.N,
-                           num_tokens_per_rank=lb.num_tokens_per_rank,
-                           rank_offset=lb.rank_offset, error_flag=self.error_flag, workspace=ws,
-                           prob=b.prob, prob_dest_major=self.prob_dest_major, stream=stream)
+        """The counts path's first call: the per-block tables in the workspace, and the
+        restripe in the same launch."""
+        B.ep_layout_counts(b.topk_idx, self.E, self.R, self.N, error_flag=self.error_flag,
+                           workspace=self._counts_workspace(), prob=b.prob,
+                           prob_dest_major=self.prob_dest_major, stream=stream)
 
     def dispatch_layout(self, b: DeviceBatch, stream=None) -> None:
         """The counts path's dispatch, after layout_counts() on the same batch."""
         ws, lb, r = self._counts_workspace(), self.layout_buf, self.recv
         B.ep_dispatch_layout(b.x, b.topk_idx, b.topk_weights, self.E, self.R, self.N,
                              token_slot=lb.token_slot, is_token_in_rank=lb.is_token_in_rank,
+                             num_tokens_per_rank=lb.num_tokens_per_rank,
+                             rank_offset=lb.rank_offset,
                              num_tokens_per_node=lb.num_tokens_per_node,
                              num_tokens_per_expert=lb.num_tokens_per_expert,
                              expert_offset=lb.expert_offset,

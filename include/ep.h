@@ -185,50 +185,51 @@ int ep_dispatch_preprocess(const int64_t *topk_idx, int64_t num_tokens, int num_
  * num_ranks <= EP_COUNTS_MAX_RANKS. ep_get_layout needs a launch to count and one to turn
  * the counts into every (token, rank) receive row ("[PR #347] Feature/sm free normal kernel"
  * names get_dispatch_layout before the dispatch in its commit list). Here the second of
- * those launches is folded into the dispatch: ep_layout_counts counts (and may restripe
- * prob in the same launch, as ep_dispatch_preprocess does); ep_dispatch_layout computes
- * each token's receive rows inside the dispatch's waves from the tables the counts left in
- * the workspace, writing token_slot and the bitmap as it goes, and the node and expert
- * counts and offsets in a few blocks of its own. Together the two calls give every output
- * of ep_get_layout (without node_slot and expert_slot), ep_restripe_prob and ep_dispatch,
- * bit for bit; error_flag is overwritten by ep_layout_counts as by ep_get_layout.
+ * those launches is folded into the dispatch: ep_layout_counts counts per 256-token block
+ * into the workspace (and may restripe prob in the same launch, as ep_dispatch_preprocess
+ * does); ep_dispatch_layout computes each token's receive rows inside the dispatch's waves
+ * from those tables, writing token_slot and the bitmap as it goes, and the rank, node and
+ * expert counts and offsets in a few blocks of its own. Together the two calls give every
+ * output of ep_get_layout (without node_slot and expert_slot), ep_restripe_prob and
+ * ep_dispatch, bit for bit. error_flag is overwritten by ep_layout_counts (0, or
+ * EP_DEVERR_TOPK_RANGE) and only ORed into by ep_dispatch_layout.
  *
  * Workspace: `workspace` of at least ep_layout_counts_workspace_bytes(T, E, R, N) bytes,
  *   16-byte aligned. Its first 4 bytes are a ticket counter that must be ZERO before the
- *   first call (say hipMemset once after allocation) and that every call of
- *   ep_layout_counts leaves zero again (EP_DEVERR_WORKSPACE reports a non-zero one); the
- *   rest is rewritten by every call. Use it for nothing else, pass the same one (with the
- *   same T, E, R, N) to ep_dispatch_layout, and do not let calls on one workspace overlap
- *   in time.
+ *   first call (say hipMemset once after allocation); every call of ep_layout_counts leaves
+ *   it zero again (EP_DEVERR_WORKSPACE reports a non-zero one in a batch of more than 4096
+ *   tokens; smaller batches do not use it). The rest is rewritten by every call. Use it for
+ *   nothing else, pass the same one (with the same T, E, R, N) to ep_dispatch_layout, and
+ *   do not let calls on one workspace overlap in time.
  * Returns 0 for sizes ep_layout_counts rejects. */
 size_t ep_layout_counts_workspace_bytes(int64_t num_tokens, int num_experts, int num_ranks,
                                         int num_nodes);
 
-/* ep_layout_counts -- In: topk_idx int64 [T][k]. Out (as ep_get_layout):
- * num_tokens_per_rank [R], rank_offset [R+1], error_flag [1] (overwritten). With prob
- * non-NULL it also writes prob_dest_major exactly as
- * ep_restripe_prob(prob, T, num_nodes, prob_per_token, max_tokens_per_rank).
+/* ep_layout_counts -- In: topk_idx int64 [T][k]. Out: the per-block tables in `workspace`,
+ * error_flag [1] (overwritten). With prob non-NULL it also writes prob_dest_major exactly
+ * as ep_restripe_prob(prob, T, num_nodes, prob_per_token, max_tokens_per_rank).
  * Sizes: as ep_get_layout, num_ranks <= EP_COUNTS_MAX_RANKS and T * k <= INT32_MAX; with
  *   prob as ep_restripe_prob (EP_ERR_CAPACITY for Tmax < T).
  * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_CAPACITY (workspace too small or NULL),
  *   EP_ERR_HIP. */
 int ep_layout_counts(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-                     int num_ranks, int num_nodes, int32_t *num_tokens_per_rank,
-                     int32_t *rank_offset, int32_t *error_flag, const float *prob,
+                     int num_ranks, int num_nodes, int32_t *error_flag, const float *prob,
                      int prob_per_token, int64_t max_tokens_per_rank, float *prob_dest_major,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* ep_dispatch_layout -- after ep_layout_counts on the same batch and workspace, stream-
  * ordered: ep_dispatch's outputs (recv_x, recv_topk_idx, recv_topk_weights, recv_src_idx,
  * with the same meaning, capacity rule and error bits) and ep_get_layout's token_slot
- * [T][R], and, nullable, is_token_in_rank [T][R], num_tokens_per_node [N],
- * num_tokens_per_expert [E] and expert_offset [E+1]. topk_idx is required.
+ * [T][R], and, nullable, num_tokens_per_rank [R], rank_offset [R+1], is_token_in_rank
+ * [T][R], num_tokens_per_node [N], num_tokens_per_expert [E] and expert_offset [E+1], all
+ * as ep_get_layout defines them. topk_idx is required.
  * Sizes: as ep_dispatch, num_ranks <= EP_COUNTS_MAX_RANKS, num_nodes as given to
  *   ep_layout_counts. Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_CAPACITY (workspace),
  *   EP_ERR_HIP. */
 int ep_dispatch_layout(const void *x, const int64_t *topk_idx, const float *topk_weights,
                        int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                       int num_ranks, int num_nodes, int32_t *num_tokens_per_node,
+                       int num_ranks, int num_nodes, int32_t *num_tokens_per_rank,
+                       int32_t *rank_offset, int32_t *num_tokens_per_node,
                        int32_t *num_tokens_per_expert, int32_t *expert_offset,
                        int32_t *token_slot, uint8_t *is_token_in_rank, void *recv_x,
                        int64_t *recv_topk_idx, float *recv_topk_weights, int32_t *recv_src_idx,

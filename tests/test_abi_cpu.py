@@ -171,12 +171,12 @@ def test_counts_path_validation(lib):
     assert ep.EP_COUNTS_MAX_RANKS == 64
 
     def counts(T=100, k=4, E=16, R=4, N=2, prob=None, P=8, Tmax=100, out=None, ws=A16,
-               wsb=1 << 20, cr=A16):
-        return lib.ep_layout_counts(A16, T, k, E, R, N, cr, A16, A16, prob, P, Tmax, out, ws, wsb,
-                                    None)
+               wsb=1 << 20, flag=A16):
+        return lib.ep_layout_counts(A16, T, k, E, R, N, flag, prob, P, Tmax, out, ws, wsb, None)
     assert counts(E=15) == ep.EP_ERR_ARG
     assert counts(E=256, R=128, N=4) == ep.EP_ERR_ARG           # R > 64
-    assert counts(cr=None) == ep.EP_ERR_ARG
+    assert counts(flag=None) == ep.EP_ERR_ARG
+    assert counts(flag=P(0x10002)) == ep.EP_ERR_ALIGN
     assert counts(T=300_000_000, k=8, E=16, R=4) == ep.EP_ERR_ARG
     assert counts(prob=A16, out=None) == ep.EP_ERR_ARG
     assert counts(prob=A16, out=A16, P=0) == ep.EP_ERR_ARG
@@ -187,12 +187,14 @@ def test_counts_path_validation(lib):
     assert counts(ws=None) == ep.EP_ERR_CAPACITY
 
     def disp(T=10, H=64, k=2, E=8, R=4, N=2, x=A16, slot=A16, idx=A16, ws=A16, wsb=1 << 20,
-             rx=A16, ce=A16):
-        return lib.ep_dispatch_layout(x, idx, A16, T, H, k, E, R, N, A16, ce, A16, slot, A16, rx,
-                                      A16, A16, A16, 100, A16, ws, wsb, None)
+             rx=A16, ce=A16, cr=A16, ro=A16):
+        return lib.ep_dispatch_layout(x, idx, A16, T, H, k, E, R, N, cr, ro, A16, ce, A16, slot,
+                                      A16, rx, A16, A16, A16, 100, A16, ws, wsb, None)
     assert disp(H=12) == ep.EP_ERR_ALIGN
     assert disp(x=MIS) == ep.EP_ERR_ALIGN
     assert disp(ce=P(0x10002)) == ep.EP_ERR_ALIGN
+    assert disp(cr=P(0x10002)) == ep.EP_ERR_ALIGN
+    assert disp(ro=P(0x10001)) == ep.EP_ERR_ALIGN
     assert disp(slot=None) == ep.EP_ERR_ARG
     assert disp(idx=None) == ep.EP_ERR_ARG
     assert disp(E=256, R=128, N=4) == ep.EP_ERR_ARG

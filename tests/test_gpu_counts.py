@@ -37,11 +37,11 @@ def _counts_call(cfg, inp, ws, prob_out=None):
     rs = torch.full((cap,), -7, **i32)
     idx = torch.from_numpy(inp.topk_idx).to(dev)
     b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, None, device=dev)
-    ep.ep_layout_counts(idx, E, R, N, num_tokens_per_rank=o["count_r"],
-                        rank_offset=o["rank_offset"], error_flag=o["flag"], workspace=ws,
+    ep.ep_layout_counts(idx, E, R, N, error_flag=o["flag"], workspace=ws,
                         prob=b.prob if prob_out is not None else None, prob_dest_major=prob_out)
     ep.ep_dispatch_layout(b.x, idx, b.topk_weights, E, R, N, token_slot=o["token_slot"],
-                          is_token_in_rank=o["in_rank"], num_tokens_per_node=o["count_n"],
+                          is_token_in_rank=o["in_rank"], num_tokens_per_rank=o["count_r"],
+                          rank_offset=o["rank_offset"], num_tokens_per_node=o["count_n"],
                           num_tokens_per_expert=o["count_e"], expert_offset=o["expert_offset"],
                           recv_x=rx, recv_topk_idx=ri,
                           recv_topk_weights=rw, recv_src_idx=rs, error_flag=o["flag"],
@@ -80,6 +80,9 @@ SEQUENCE = [
     W.Config("c_ragged", T=1001, H=24, E=96, k=5, R=8, N=2, P=5, Tmax=1100),
     W.Config("c_dsv3_again", T=4096, H=64, E=256, k=8, R=32, N=4, P=8, Tmax=4096,
              routing="zipf"),
+    # the first size past 16 blocks, where the count launch takes the ticket again
+    W.Config("c_17_blocks", T=4097, H=16, E=256, k=8, R=64, N=8, P=4, Tmax=4100),
+    W.Config("c_16_blocks", T=4096, H=16, E=256, k=8, R=64, N=8, P=4, Tmax=4096),
 ]
 
 
@@ -133,10 +136,10 @@ def test_short_receive_buffer_sets_the_overflow_bit():
     cr, ro, flag = torch.empty(cfg.R, **i32), torch.empty(cfg.R + 1, **i32), torch.empty(1, **i32)
     slot = torch.empty((cfg.T, cfg.R), **i32)
     rx = torch.full((cap, cfg.H), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-    ep.ep_layout_counts(b.topk_idx, cfg.E, cfg.R, cfg.N, num_tokens_per_rank=cr, rank_offset=ro,
-                        error_flag=flag, workspace=ws)
+    ep.ep_layout_counts(b.topk_idx, cfg.E, cfg.R, cfg.N, error_flag=flag, workspace=ws)
     ep.ep_dispatch_layout(b.x, b.topk_idx, b.topk_weights, cfg.E, cfg.R, cfg.N, token_slot=slot,
-                          recv_x=rx, error_flag=flag, workspace=ws)
+                          num_tokens_per_rank=cr, rank_offset=ro, recv_x=rx, error_flag=flag,
+                          workspace=ws)
     torch.cuda.synchronize()
     assert int(flag.item()) == ep.EP_DEVERR_RECV_OVERFLOW
     d = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, cfg.E, cfg.R, lay["token_slot"], M)
@@ -204,9 +207,10 @@ def test_dispatch_split_over_token_ranges():
 
 def test_workspace_with_a_nonzero_ticket_is_reported():
     """A workspace whose ticket is not zero on entry (never zero-filled, or shared by calls
-    that overlap) sets EP_DEVERR_WORKSPACE; the outputs of that call are unspecified, but
-    every kernel ends and stays in bounds. Zeroing the ticket makes the next call exact."""
-    cfg = W.Config("c_ticket", T=4096, H=64, E=256, k=8, R=32, N=4, P=8, Tmax=4096)
+    that overlap) sets EP_DEVERR_WORKSPACE in a batch large enough to use the ticket (more
+    than 16 blocks of 256 tokens); the outputs of that call are unspecified, but every
+    kernel ends and stays in bounds. Zeroing the ticket makes the next call exact."""
+    cfg = W.Config("c_ticket", T=8192, H=64, E=256, k=8, R=32, N=4, P=8, Tmax=8192)
     print(f"\ncase: counts path {cfg} with the ticket set to 5", flush=True)
     inp = W.make_inputs(cfg, with_partials=False)
     ws = torch.zeros(ep.ep_layout_counts_workspace_bytes(cfg.T, cfg.E, cfg.R, cfg.N),
