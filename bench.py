@@ -54,12 +54,12 @@ def algorithmic_bytes(cfg, M: int) -> dict:
         "dispatch": T * H * 2 + T * k * 12 + T * R * 4 + M * (2 * H + 12 * k + 4),
         "restripe": 2 * T * N * P * 4,
         "combine": T * R * 4 + M * H * 2 + T * H * 2,
-        # the counts path: the counts and rank offsets with the restripe in one launch, then
-        # the dispatch that also writes the slot table, the bitmap and the node and expert
+        # the counts path: the counting pass with the restripe in one launch, then the
+        # dispatch that also writes the slot table, the bitmap and the rank, node and expert
         # counts and offsets
-        "layout_counts": T * k * 8 + (2 * R + 1) * 4 + 2 * T * N * P * 4,
+        "layout_counts": T * k * 8 + 2 * T * N * P * 4,
         "dispatch_layout": (T * H * 2 + T * k * 12 + M * (2 * H + 12 * k + 4) +
-                            T * R * (1 + 4) + (N + 2 * E + 1) * 4),
+                            T * R * (1 + 4) + (2 * R + 1 + N + 2 * E + 1) * 4),
     }
 
 
