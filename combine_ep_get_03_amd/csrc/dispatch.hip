@@ -166,18 +166,21 @@ __device__ __forceinline__ void dest_range(int d, int D, int P, int& lo, int& hi
     hi = d == D - 1 ? INT32_MAX : lo + P;
 }
 
-// Lanes past the row's end skip their loads; their words are zero, not undefined, so the
-// compiler keeps every load of the pass in flight at once rather than branching around
-// each one.
+// A pass inside the row (the whole row at 7168 channels) loads at fixed offsets; in a pass
+// that runs past the row's end, a lane past it loads the row's last word again instead of
+// skipping the load (its stores are skipped). Either way every load is unconditional, so
+// the compiler keeps them all in flight at once: with guarded loads it waited for each
+// before issuing the next at 7 words per lane.
 template <int WPL>
 __device__ __forceinline__ void load_row_cached(u32x4 (&v)[WPL], const u32x4* __restrict__ xr,
                                                 int v0, int V) {
     const int lane = lane_id();
+    if (v0 + WPL * kWave <= V) {
 #pragma unroll
-    for (int i = 0; i < WPL; ++i) {
-        const int vi = v0 + i * kWave + lane;
-        v[i] = u32x4{0u, 0u, 0u, 0u};
-        if (vi < V) v[i] = xr[vi];
+        for (int i = 0; i < WPL; ++i) v[i] = xr[v0 + i * kWave + lane];
+    } else {
+#pragma unroll
+        for (int i = 0; i < WPL; ++i) v[i] = xr[min(v0 + i * kWave + lane, V - 1)];
     }
 }
 
