@@ -662,8 +662,31 @@ def main():
         def permute_call():
             ep.ep_dispatch_permute(b.x, b.topk_weights, lbe.expert_slot, perm_x=px,
                                    perm_weights=pw, perm_src_idx=ps, error_flag=lbe.error_flag)
+        perm_calls = [("layout_with_expert_slots", layout_e), ("dispatch_permute", permute_call)]
+        # the counts path's form (R <= 64, T <= 16384): the count launch with each pair's
+        # in-block expert rank, then the permute forming the rows itself; checked bit-equal
+        counts_form = cfg.R <= ep.EP_COUNTS_MAX_RANKS and cfg.T <= 16384
+        if counts_form:
+            ws = torch.zeros(ep.ep_layout_counts_workspace_bytes(cfg.T, cfg.E, cfg.R, cfg.N),
+                             dtype=torch.uint8, device="cuda")
+            er = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+            es2 = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+            px2, pw2, ps2 = torch.empty_like(px), torch.empty_like(pw), torch.empty_like(ps)
+            flag2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+            def counts_e():
+                ep.ep_layout_counts(b.topk_idx, cfg.E, cfg.R, cfg.N, error_flag=flag2,
+                                    workspace=ws, expert_rank=er)
+
+            def permute_layout_call():
+                ep.ep_dispatch_permute_layout(b.x, b.topk_idx, b.topk_weights, cfg.E, cfg.R,
+                                              cfg.N, expert_rank=er, perm_x=px2, workspace=ws,
+                                              perm_weights=pw2, perm_src_idx=ps2,
+                                              expert_slot=es2, error_flag=flag2)
+            perm_calls += [("layout_counts_with_expert_ranks", counts_e),
+                           ("dispatch_permute_layout", permute_layout_call)]
         res = {}
-        for n, fn in (("layout_with_expert_slots", layout_e), ("dispatch_permute", permute_call)):
+        for n, fn in perm_calls:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for _ in range(args.steps):
@@ -679,6 +702,19 @@ def main():
                    "dispatch_permute_us": round(res["dispatch_permute"] * 1e3, 2),
                    "alg_bytes": pb,
                    "hbm_gbps": round(pb / (res["dispatch_permute"] * 1e-3) / 1e9, 1)}
+        if counts_form:
+            n_rows = int((lbe.expert_slot >= 0).sum().item())
+            if (int(flag2.item()) != 0 or not torch.equal(es2, lbe.expert_slot)
+                    or not torch.equal(px2[:n_rows], px[:n_rows])
+                    or not torch.equal(ps2[:n_rows], ps[:n_rows])):
+                raise RuntimeError("the counts path's permute differs from ep_dispatch_permute")
+            permute["counts_path"] = {
+                "layout_counts_with_expert_ranks_us":
+                    round(res["layout_counts_with_expert_ranks"] * 1e3, 2),
+                "dispatch_permute_layout_us": round(res["dispatch_permute_layout"] * 1e3, 2),
+                "both_us": round((res["layout_counts_with_expert_ranks"] +
+                                  res["dispatch_permute_layout"]) * 1e3, 2)}
+            del ws, er, es2, px2, pw2, ps2
         del px, pw, ps, lbe
     # Sparse restripe: layout with per-node slots, then only the routed (token, node)
     # slices packed per node (the dense restripe copies all T*N of them)

@@ -50,7 +50,9 @@ def load() -> ctypes.CDLL:
                                          P, P]
     L.ep_layout_counts_workspace_bytes.argtypes = [i64, i32, i32, i32]
     L.ep_layout_counts_workspace_bytes.restype = sz
-    L.ep_layout_counts.argtypes = [P, i64, i32, i32, i32, i32, P, P, i32, i64, P, P, sz, P]
+    L.ep_layout_counts.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, i32, i64, P, P, sz, P]
+    L.ep_dispatch_permute_layout.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P, P,
+                                             P, P, i64, P, P, sz, P]
     L.ep_dispatch_layout.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, P,
                                      P, P, P, P, i64, P, P, sz, P]
     L.ep_dispatch_preprocess.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
@@ -70,7 +72,7 @@ def load() -> ctypes.CDLL:
     L.ep_hbm_copy.argtypes = [P, P, sz, P]
     L.ep_hbm_fan.argtypes = [P, P, sz, i32, i32, P]
     for f in ("ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch_preprocess",
-              "ep_layout_counts", "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
+              "ep_layout_counts", "ep_dispatch_layout", "ep_dispatch_permute_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
               "ep_restripe_prob", "ep_restripe_prob_sparse", "ep_combine", "ep_dispatch_send",
               "ep_dispatch_recv", "ep_combine_send", "ep_combine_recv", "ep_hbm_copy",
               "ep_hbm_fan"):
@@ -229,15 +231,17 @@ def ep_layout_counts_workspace_bytes(num_tokens: int, num_experts: int, num_rank
 
 
 def ep_layout_counts(topk_idx, num_experts: int, num_ranks: int, num_nodes: int, *,
-                     error_flag, workspace, prob=None, prob_dest_major=None,
+                     error_flag, workspace, prob=None, prob_dest_major=None, expert_rank=None,
                      stream=None) -> None:
     """The count launch of the counts path (num_ranks <= EP_COUNTS_MAX_RANKS): the
-    per-block tables in `workspace` and the error flag, and with prob the restripe of prob.
-    The first 4 bytes of `workspace` (uint8, ep_layout_counts_workspace_bytes) must be zero
-    before its first use; every call leaves them zero."""
+    per-block tables in `workspace` and the error flag; with expert_rank (int32 [T][k]) each
+    pair's rank in its block among the pairs naming its expert; with prob the restripe of
+    prob. The first 4 bytes of `workspace` (uint8, ep_layout_counts_workspace_bytes) must
+    be zero before its first use; every call leaves them zero."""
     T, k = topk_idx.shape
     E, R, N = num_experts, num_ranks, num_nodes
     _at_least(error_flag, 1, "error_flag")
+    _shape(expert_rank, (T, k), "expert_rank")
     P, Tmax = 0, 0
     if prob is not None:
         if prob.dim() != 3 or prob_dest_major is None or prob_dest_major.dim() != 3:
@@ -250,6 +254,7 @@ def ep_layout_counts(topk_idx, num_experts: int, num_ranks: int, num_nodes: int,
     _check(load().ep_layout_counts(
         _ptr(topk_idx, torch.int64, "topk_idx"), T, k, E, R, N,
         _ptr(error_flag, torch.int32, "error_flag"),
+        _ptr(expert_rank, torch.int32, "expert_rank", True),
         _ptr(prob, torch.float32, "prob", True), P, Tmax,
         _ptr(prob_dest_major, torch.float32, "prob_dest_major", True),
         _ptr(workspace, torch.uint8, "workspace"), ws_bytes, _stream(stream)), "ep_layout_counts")
@@ -300,6 +305,45 @@ def ep_dispatch_layout(x, topk_idx, topk_weights, num_experts: int, num_ranks: i
         _ptr(error_flag, torch.int32, "error_flag", True),
         _ptr(workspace, torch.uint8, "workspace"), ws_bytes, _stream(stream)),
         "ep_dispatch_layout")
+
+
+def ep_dispatch_permute_layout(x, topk_idx, topk_weights, num_experts: int, num_ranks: int,
+                               num_nodes: int, *, expert_rank, perm_x, workspace,
+                               perm_weights=None, perm_src_idx=None, expert_slot=None,
+                               num_tokens_per_expert=None, expert_offset=None, error_flag=None,
+                               stream=None) -> None:
+    """The counts path's dispatch + permute, after ep_layout_counts on the same batch and
+    workspace with expert_rank: ep_dispatch_permute's outputs, the rows formed in the
+    permute's waves; optionally expert_slot [T][k] and the expert counts and offsets.
+    T <= 16384."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    E, R, N = num_experts, num_ranks, num_nodes
+    cap = perm_x.shape[0]
+    _shape(topk_idx, (T, k), "topk_idx")
+    _shape(topk_weights, (T, k), "topk_weights")
+    _shape(expert_rank, (T, k), "expert_rank")
+    _shape(expert_slot, (T, k), "expert_slot")
+    _at_least(num_tokens_per_expert, E, "num_tokens_per_expert")
+    _at_least(expert_offset, E + 1, "expert_offset")
+    _shape(perm_x, (cap, H), "perm_x")
+    _shape(perm_weights, (cap,), "perm_weights")
+    _shape(perm_src_idx, (cap,), "perm_src_idx")
+    _at_least(error_flag, 1, "error_flag")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().ep_dispatch_permute_layout(
+        _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int64, "topk_idx"),
+        _ptr(topk_weights, torch.float32, "topk_weights", True), T, H, k, E, R, N,
+        _ptr(expert_rank, torch.int32, "expert_rank"),
+        _ptr(num_tokens_per_expert, torch.int32, "num_tokens_per_expert", True),
+        _ptr(expert_offset, torch.int32, "expert_offset", True),
+        _ptr(expert_slot, torch.int32, "expert_slot", True),
+        _ptr(perm_x, torch.bfloat16, "perm_x"),
+        _ptr(perm_weights, torch.float32, "perm_weights", True),
+        _ptr(perm_src_idx, torch.int32, "perm_src_idx", True), cap,
+        _ptr(error_flag, torch.int32, "error_flag", True),
+        _ptr(workspace, torch.uint8, "workspace"), ws_bytes, _stream(stream)),
+        "ep_dispatch_permute_layout")
 
 
 def ep_dispatch(x, topk_idx, topk_weights, num_experts: int, num_ranks: int, token_slot, *,

@@ -414,6 +414,79 @@ __global__ __launch_bounds__(kThreads) void dispatch_layout_kernel(
     }
 }
 
+// Dispatch + permute of the counts path (at most kCountsPermuteBlocks 256-token blocks):
+// wave (t, j) forms pair (t, j)'s expert-major row itself, as expert_offset[e] + the pairs
+// naming e in the blocks before t's block + the pair's rank in its own block (the count
+// launch's expert_rank). Lane u < nb loads block u's inclusive expert prefix at e and at
+// e - 1: summed over every block, the prefix at e - 1 is expert_offset[e]; summed over the
+// blocks before t's, the difference is the second term. The pair's id and rank are loaded
+// with the row's first pass, the prefixes once the id has arrived. The first `nhead`
+// blocks are head blocks (the expert counts and offsets).
+template <int WPL, bool kMulti, int kThreads>
+__global__ __launch_bounds__(kThreads) void dispatch_permute_layout_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int64_t t0, int64_t t_end, int V, int k, int E, int N,
+    const int32_t* __restrict__ expert_rank, CountsWorkspace cw, int nb, FastDiv D,
+    u32x4* __restrict__ perm_x, float* __restrict__ perm_w, int32_t* __restrict__ perm_src,
+    int32_t* __restrict__ expert_slot, int64_t cap, int nhead, int32_t* __restrict__ count_e,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ error_flag) {
+    if (static_cast<int>(blockIdx.x) < nhead) {
+        counts_head_block(cw, blockIdx.x, nb, E, 0, N, nullptr, nullptr, nullptr, count_e,
+                          expert_offset);
+        return;
+    }
+    int64_t t;
+    int j;
+    if (!dest_wave_at(grid_wave<kThreads>() - nhead * (kThreads / kWave), t0, t_end, D, t, j))
+        return;
+    const int lane = lane_id();
+    const int64_t pair = t * k + j;
+    const int64_t e = topk_idx[pair];
+    const int rk = expert_rank[pair];
+    const float w = perm_w ? topk_w[pair] : 0.0f;
+    const u32x4* xr = x + t * V;
+    u32x4 v[WPL];
+    load_row_cached(v, xr, 0, V);  // first pass, issued with the pair's loads
+    if (e < 0 || e >= E) {         // masked (or bad: the count launch flagged it)
+        if (expert_slot && lane == 0) expert_slot[pair] = -1;
+        return;
+    }
+    const int ei = static_cast<int>(e);
+    const int64_t b = t / kLayoutBlockTokens;
+    int cur = 0, prev = 0;
+    if (lane < nb) {
+        cur = cw.blk_exp[static_cast<int64_t>(lane) * E + ei];
+        prev = ei > 0 ? cw.blk_exp[static_cast<int64_t>(lane) * E + ei - 1] : 0;
+    }
+    int before = lane < b ? cur - prev : 0;
+    int off = prev;
+#pragma unroll
+    for (int s = kWave / 2; s > 0; s >>= 1) {
+        before += __shfl_xor(before, s, kWave);
+        off += __shfl_xor(off, s, kWave);
+    }
+    const int64_t q = static_cast<int64_t>(off) + before + rk;
+    if (expert_slot && lane == 0) expert_slot[pair] = static_cast<int32_t>(q);
+    if (q >= cap) {
+        if (lane == 0) raise_error(error_flag, kErrRecvOverflow);
+        return;
+    }
+    u32x4* row = perm_x + q * V;
+    for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
+        if (v0 != 0) load_row_cached(v, xr, v0, V);
+#pragma unroll
+        for (int i = 0; i < WPL; ++i) {
+            const int vi = v0 + i * kWave + lane;
+            if (vi < V) store_row_word(row + vi, v[i]);
+        }
+        if constexpr (!kMulti) break;
+    }
+    if (lane == 0) {
+        if (perm_w) perm_w[q] = w;
+        if (perm_src) perm_src[q] = static_cast<int32_t>(t);
+    }
+}
+
 // Two-phase dispatch ("[PR #347] Feature/sm free normal kernel", section 2.1), send
 // phase: each token's row, its k expert ids and weights and its id go once to every
 // node holding one of its experts, at row node_slot[t][n] of node n's block of Tmax rows
@@ -800,6 +873,31 @@ hipError_t launch_dispatch_permute(const void* x, const float* topk_w, int64_t T
                            dim3(grid), dim3(kDestThreads), 0, stream,
                            static_cast<const u32x4*>(x), topk_w, t0, t_end, V, k, expert_slot,
                            fd, static_cast<u32x4*>(perm_x), perm_w, perm_src, cap, error_flag);
+    });
+}
+
+hipError_t launch_dispatch_permute_layout(const void* x, const int64_t* topk_idx,
+                                          const float* topk_w, int64_t T, int H, int k, int E,
+                                          int N, const int32_t* expert_rank,
+                                          const CountsWorkspace& cw, void* perm_x, float* perm_w,
+                                          int32_t* perm_src, int32_t* expert_slot, int64_t cap,
+                                          int32_t* count_e, int32_t* expert_offset,
+                                          int32_t* error_flag, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int V = H / 8;
+    const FastDiv fd = FastDiv::make(k);  // one wave per (token, slot)
+    const int nb = static_cast<int>((T + kLayoutBlockTokens - 1) / kLayoutBlockTokens);
+    int head = (count_e || expert_offset) ? (E + kDestThreads - 1) / kDestThreads : 0;
+    head = (head + 7) / 8 * 8;  // keeps the permute's blocks on their XCDs, as in the dispatch
+    return launch_by_token_range<14>(V, T, k, [&](auto wpl, auto multi, int64_t t0, int64_t t_end,
+                                                  unsigned grid) {
+        const int nhead = t0 == 0 ? head : 0;
+        hipLaunchKernelGGL((dispatch_permute_layout_kernel<decltype(wpl)::value,
+                                                           decltype(multi)::value, kDestThreads>),
+                           dim3(grid + nhead), dim3(kDestThreads), 0, stream,
+                           static_cast<const u32x4*>(x), topk_idx, topk_w, t0, t_end, V, k, E, N,
+                           expert_rank, cw, nb, fd, static_cast<u32x4*>(perm_x), perm_w, perm_src,
+                           expert_slot, cap, nhead, count_e, expert_offset, error_flag);
     });
 }
 

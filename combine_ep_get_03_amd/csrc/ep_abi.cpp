@@ -173,9 +173,10 @@ size_t ep_layout_counts_workspace_bytes(int64_t num_tokens, int num_experts, int
 }
 
 int ep_layout_counts(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-                     int num_ranks, int num_nodes, int32_t* error_flag, const float* prob,
-                     int prob_per_token, int64_t max_tokens_per_rank, float* prob_dest_major,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     int num_ranks, int num_nodes, int32_t* error_flag, int32_t* expert_rank,
+                     const float* prob, int prob_per_token, int64_t max_tokens_per_rank,
+                     float* prob_dest_major, void* workspace, size_t workspace_bytes,
+                     void* stream) {
     const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
     const int k = num_topk, E = num_experts, R = num_ranks, N = num_nodes, P = prob_per_token;
     if (!topology_ok(k, E, R, N) || R > EP_COUNTS_MAX_RANKS || !slots_fit_int32(T, k, R) ||
@@ -183,12 +184,13 @@ int ep_layout_counts(const int64_t* topk_idx, int64_t num_tokens, int num_topk, 
         return EP_ERR_ARG;
     if (!error_flag) return EP_ERR_ARG;
     if (T > 0 && !topk_idx) return EP_ERR_ARG;
+    if (expert_rank && k > EP_EXPERT_SLOT_MAX_K) return EP_ERR_ARG;
     if (prob) {
         if (P < 1 || static_cast<int64_t>(N) * P > (1 << 26)) return EP_ERR_ARG;
         if (T > 0 && !prob_dest_major) return EP_ERR_ARG;
     }
-    if (!aligned(topk_idx, 8) || !aligned(error_flag, 4) || !aligned(prob, 4) ||
-        !aligned(prob_dest_major, 4) || !aligned(workspace, 16))
+    if (!aligned(topk_idx, 8) || !aligned(error_flag, 4) || !aligned(expert_rank, 4) ||
+        !aligned(prob, 4) || !aligned(prob_dest_major, 4) || !aligned(workspace, 16))
         return EP_ERR_ALIGN;
     if (prob && Tmax < T) return EP_ERR_CAPACITY;
     const size_t need = ep::counts_workspace_bytes(T, E, R, N);
@@ -196,8 +198,8 @@ int ep_layout_counts(const int64_t* topk_idx, int64_t num_tokens, int num_topk, 
     const ep::CountsWorkspace cw = ep::carve_counts_workspace(workspace, T, E, R, N);
     ep::RestripeTask rs{};
     if (prob) rs = ep::plan_restripe(prob, T, N, P, Tmax, prob_dest_major);
-    return hip_status(ep::launch_layout_counts(topk_idx, T, k, E, R, N, error_flag, cw, &rs,
-                                               static_cast<hipStream_t>(stream)));
+    return hip_status(ep::launch_layout_counts(topk_idx, T, k, E, R, N, error_flag, expert_rank,
+                                               cw, &rs, static_cast<hipStream_t>(stream)));
 }
 
 int ep_dispatch_layout(const void* x, const int64_t* topk_idx, const float* topk_weights,
@@ -241,6 +243,46 @@ int ep_dispatch_layout(const void* x, const int64_t* topk_idx, const float* topk
         x, topk_idx, topk_weights, T, H, k, E, R, N, cw, token_slot, is_token_in_rank, recv_x,
         recv_topk_idx, recv_topk_weights, recv_src_idx, recv_capacity, num_tokens_per_rank,
         rank_offset, num_tokens_per_node, num_tokens_per_expert, expert_offset, error_flag,
+        static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch_permute_layout(const void* x, const int64_t* topk_idx,
+                               const float* topk_weights, int64_t num_tokens, int hidden,
+                               int num_topk, int num_experts, int num_ranks, int num_nodes,
+                               const int32_t* expert_rank, int32_t* num_tokens_per_expert,
+                               int32_t* expert_offset, int32_t* expert_slot, void* perm_x,
+                               float* perm_weights, int32_t* perm_src_idx, int64_t perm_capacity,
+                               int32_t* error_flag, const void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    const int64_t T = num_tokens;
+    const int H = hidden, k = num_topk, E = num_experts, R = num_ranks, N = num_nodes;
+    if (!topology_ok(k, E, R, N) || R > EP_COUNTS_MAX_RANKS || k > EP_EXPERT_SLOT_MAX_K ||
+        T > static_cast<int64_t>(ep::kCountsPermuteBlocks) * ep::kLayoutBlockTokens || H < 1 ||
+        perm_capacity < 0)
+        return EP_ERR_ARG;
+    if (H % 8 != 0) return EP_ERR_ALIGN;
+    if (T > 0) {
+        if (!x || !topk_idx || !expert_rank || !perm_x) return EP_ERR_ARG;
+        if (perm_weights && !topk_weights) return EP_ERR_ARG;
+    }
+    if (!aligned(x, 16) || !aligned(perm_x, 16) || !aligned(topk_idx, 8) ||
+        !aligned(topk_weights, 4) || !aligned(expert_rank, 4) || !aligned(expert_slot, 4) ||
+        !aligned(perm_weights, 4) || !aligned(perm_src_idx, 4) || !aligned(error_flag, 4) ||
+        !aligned(num_tokens_per_expert, 4) || !aligned(expert_offset, 4) ||
+        !aligned(workspace, 16))
+        return EP_ERR_ALIGN;
+    const size_t need = ep::counts_workspace_bytes(T, E, R, N);
+    if (workspace_bytes < need || !workspace) return EP_ERR_CAPACITY;
+    if (T == 0) {  // an empty batch: zero counts and offsets, nothing to move
+        const ep::ZeroInts z{{num_tokens_per_expert, expert_offset, nullptr, nullptr, nullptr},
+                             {E, E + 1, 0, 0, 0}};
+        return hip_status(ep::launch_zero_ints(z, static_cast<hipStream_t>(stream)));
+    }
+    const ep::CountsWorkspace cw =
+        ep::carve_counts_workspace(const_cast<void*>(workspace), T, E, R, N);
+    return hip_status(ep::launch_dispatch_permute_layout(
+        x, topk_idx, topk_weights, T, H, k, E, N, expert_rank, cw, perm_x, perm_weights,
+        perm_src_idx, expert_slot, perm_capacity, num_tokens_per_expert, expert_offset, error_flag,
         static_cast<hipStream_t>(stream)));
 }
 

@@ -201,12 +201,18 @@ hipError_t launch_zero_ints(const ZeroInts& z, hipStream_t stream);
 // per lane), so the count launch has no cross-block phase. Larger batches keep the
 // ticket, whose last block writes each block's first receive row per rank.
 constexpr int kCountsLocalBlocks = 16;
+// The counts path's permute forms each pair's expert-major row from every block's expert
+// prefix, one block per lane: at most this many 256-token blocks.
+constexpr int kCountsPermuteBlocks = 64;
 
 // The count launch of the counts path (the restripe's blocks may ride along): the error
-// flag and the tables ep_dispatch_layout reads.
+// flag and the tables ep_dispatch_layout reads; with expert_rank ([T][k], k <=
+// kExpertSlotMaxK), also each pair's rank among its 256-token block's pairs naming the same
+// expert, which ep_dispatch_permute_layout turns into expert-major rows.
 hipError_t launch_layout_counts(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
-                                int32_t* error_flag, const CountsWorkspace& cw,
-                                const RestripeTask* rs, hipStream_t stream);
+                                int32_t* error_flag, int32_t* expert_rank,
+                                const CountsWorkspace& cw, const RestripeTask* rs,
+                                hipStream_t stream);
 
 // dispatch.hip: one-call dispatch, FP8 dispatch, expert-major permute, and the two
 // phases of the two-phase dispatch
@@ -238,6 +244,13 @@ hipError_t launch_dispatch_layout(const void* x, const int64_t* topk_idx, const 
                                   int32_t* recv_src, int64_t cap, int32_t* count_r,
                                   int32_t* rank_offset, int32_t* count_n, int32_t* count_e,
                                   int32_t* expert_offset, int32_t* error_flag, hipStream_t stream);
+hipError_t launch_dispatch_permute_layout(const void* x, const int64_t* topk_idx,
+                                          const float* topk_w, int64_t T, int H, int k, int E,
+                                          int N, const int32_t* expert_rank,
+                                          const CountsWorkspace& cw, void* perm_x, float* perm_w,
+                                          int32_t* perm_src, int32_t* expert_slot, int64_t cap,
+                                          int32_t* count_e, int32_t* expert_offset,
+                                          int32_t* error_flag, hipStream_t stream);
 hipError_t launch_dispatch_recv(const void* stage_x, const int64_t* stage_idx,
                                 const float* stage_w, const int32_t* stage_src,
                                 const int32_t* count_n, int N, int64_t Tmax, int H, int k, int E,

@@ -750,34 +750,29 @@ __global__ __launch_bounds__(kBT) void layout_slot_kernel(
     }
 }
 
-// Expert-major row of every (token, slot) of one 256-token block: the block's base for
-// the expert (left in the workspace by the slot launch) plus the number of earlier pairs
-// of the block naming the same expert, in (token, slot) order. A stable ranking without
-// a sort: wave w owns the block's tokens [64w, 64w + 64), i.e. its 64k pairs in (token,
-// slot) order, and walks them in k rounds of 64 consecutive pairs, lane l holding pair
-// 64r + l, so rounds in order are the sort order. In a round, lanes naming the same
-// expert are matched with one ballot per id bit; a lane's rank is the count of its
-// matching lanes below it plus the wave's running count for the expert (LDS), which the
-// highest matching lane then advances. After a barrier the earlier waves' totals for the
-// expert are added.
-__global__ __launch_bounds__(kBT) void layout_expert_slot_kernel(
-    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int nbits,
-    const int32_t* __restrict__ blk_exp_base, int32_t* __restrict__ expert_slot) {
-    constexpr int kK = kExpertSlotMaxK;
-    extern __shared__ uint16_t s_run[];  // [kWavesBT][E], running count per wave and expert
-    const int tid = threadIdx.x;
-    const int lane = lane_id();
-    const int wave = tid / kWave;
-    const int64_t b = blockIdx.x;
-    for (int i = tid; i < kWavesBT * E; i += kBT) s_run[i] = 0;
-    __syncthreads();
+// Length of a wave's row of 16-bit expert counts in LDS: E rounded up to even, so that
+// every row starts 4-byte aligned.
+__host__ __device__ inline int run_row(int E) { return (E + 1) & ~1; }
+constexpr int kIdBits = 13;  // bits of an expert id below kMaxExperts
+static_assert((1 << kIdBits) == kMaxExperts, "the expert-rank ballots cover every id bit");
 
-    const int64_t t0 = b * kBT + static_cast<int64_t>(wave) * kWave;  // the wave's first token
-    const int64_t npairs = max<int64_t>(0, min<int64_t>(kWave, T - t0)) * k;
-    const int64_t* ids = topk_idx + t0 * k;
-    uint16_t* run = s_run + wave * E;
-    int key[kK];
-    int loc[kK];
+// In-block ranks of one wave's (token, slot) pairs among the pairs of its 256-token block
+// that name the same expert, in (token, slot) order. A stable ranking without a sort: wave
+// w owns the block's tokens [64w, 64w + 64), i.e. its 64k pairs in (token, slot) order, and
+// walks them in k rounds of 64 consecutive pairs, lane l holding pair 64r + l, so rounds in
+// order are the sort order. In a round, lanes naming the same expert are matched with one
+// ballot per id bit; a lane's rank is the count of its matching lanes below it plus the
+// wave's running count for the expert (`run`, this wave's row of an LDS table
+// [4][run_row(E)] of 16-bit counts; a wave counts at most 64 k <= 1024 pairs per expert),
+// which the highest matching lane then advances. key[r] is the expert of round r's pair
+// (-1 for a masked or bad id) and loc[r] its rank within the wave; after a barrier the
+// caller adds the earlier waves' totals for the expert (the rows above). Issuing the
+// rounds' LDS updates as atomics, all before any result is used, measured no faster.
+template <int kK>
+__device__ __forceinline__ void wave_expert_ranks(const int64_t* __restrict__ ids, int64_t npairs,
+                                                  int k, int E, int nbits, uint16_t* run,
+                                                  int (&key)[kK], int (&loc)[kK]) {
+    const int lane = lane_id();
     int64_t e_in[kK];
 #pragma unroll
     for (int r = 0; r < kK; ++r) {  // all loads first, in flight together
@@ -792,7 +787,11 @@ __global__ __launch_bounds__(kBT) void layout_expert_slot_kernel(
             const int64_t e = e_in[r];
             const int kr = (e >= 0 && e < E) ? static_cast<int>(e) : -1;
             uint64_t peers = wave_ballot(kr >= 0);
-            for (int bit = 0; bit < nbits; ++bit) {
+            // every id bit an expert can have (ids < EP_MAX_EXPERTS = 2^13): a bit above
+            // the highest id's is zero in every lane and leaves `peers` as it is, and the
+            // fixed trip count lets the rounds' ballots interleave
+#pragma unroll
+            for (int bit = 0; bit < kIdBits; ++bit) {
                 const bool on = kr >= 0 && ((kr >> bit) & 1);
                 const uint64_t m = wave_ballot(on);
                 peers &= on ? m : ~m;
@@ -806,6 +805,29 @@ __global__ __launch_bounds__(kBT) void layout_expert_slot_kernel(
             key[r] = kr;
         }
     }
+}
+
+// Expert-major row of every (token, slot) of one 256-token block: the block's base for
+// the expert (left in the workspace by the slot launch) plus the pair's in-block rank
+// (wave_expert_ranks).
+template <int kK>  // rounds: k <= kK
+__global__ __launch_bounds__(kBT) void layout_expert_slot_kernel(
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int nbits,
+    const int32_t* __restrict__ blk_exp_base, int32_t* __restrict__ expert_slot) {
+    extern __shared__ uint16_t s_run[];  // [kWavesBT][Ep], running count per wave and expert
+    const int Ep = run_row(E);
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+    const int64_t b = blockIdx.x;
+    for (int i = tid; i < kWavesBT * Ep; i += kBT) s_run[i] = 0;
+    __syncthreads();
+
+    const int64_t t0 = b * kBT + static_cast<int64_t>(wave) * kWave;  // the wave's first token
+    const int64_t npairs = max<int64_t>(0, min<int64_t>(kWave, T - t0)) * k;
+    int key[kK];
+    int loc[kK];
+    wave_expert_ranks<kK>(topk_idx + t0 * k, npairs, k, E, nbits, s_run + wave * Ep, key, loc);
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kK; ++r) {
@@ -814,11 +836,25 @@ __global__ __launch_bounds__(kBT) void layout_expert_slot_kernel(
             int slot = -1;
             if (key[r] >= 0) {
                 slot = blk_exp_base[b * E + key[r]] + loc[r];
-                for (int w = 0; w < wave; ++w) slot += s_run[w * E + key[r]];
+                for (int w = 0; w < wave; ++w) slot += s_run[w * Ep + key[r]];
             }
             expert_slot[t0 * k + p] = slot;
         }
     }
+}
+
+// The expert-slot launch over `blocks` blocks, with as many ranking rounds as k needs.
+void launch_expert_slots(const int64_t* topk_idx, int64_t T, int k, int E, int nbits,
+                         const int32_t* blk_exp_base, int32_t* expert_slot, int64_t blocks,
+                         hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(blocks));
+    const size_t lds = sizeof(uint16_t) * kWavesBT * run_row(E);
+    if (k <= 8)
+        hipLaunchKernelGGL(layout_expert_slot_kernel<8>, grid, dim3(kBT), lds, stream, topk_idx, T,
+                           k, E, nbits, blk_exp_base, expert_slot);
+    else
+        hipLaunchKernelGGL(layout_expert_slot_kernel<kExpertSlotMaxK>, grid, dim3(kBT), lds,
+                           stream, topk_idx, T, k, E, nbits, blk_exp_base, expert_slot);
 }
 
 template <int NW>
@@ -850,9 +886,8 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
             if (want_base) {
                 int nbits = 0;
                 while ((1 << nbits) < E) ++nbits;
-                hipLaunchKernelGGL(layout_expert_slot_kernel, dim3(1), dim3(kBT),
-                                   sizeof(uint16_t) * kWavesBT * E, stream, topk_idx, T, k, E,
-                                   nbits, ws.blk_exp_base, expert_slot);
+                launch_expert_slots(topk_idx, T, k, E, nbits, ws.blk_exp_base, expert_slot, 1,
+                                    stream);
                 EP_RETURN_IF_LAUNCH_FAILED();
             }
             return hipSuccess;
@@ -898,9 +933,7 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
     if (want_base && nb > 0) {
         int nbits = 0;
         while ((1 << nbits) < E) ++nbits;
-        hipLaunchKernelGGL(layout_expert_slot_kernel, dim3(static_cast<unsigned>(nb)), dim3(kBT),
-                           sizeof(uint16_t) * kWavesBT * E, stream, topk_idx, T, k, E, nbits,
-                           ws.blk_exp_base, expert_slot);
+        launch_expert_slots(topk_idx, T, k, E, nbits, ws.blk_exp_base, expert_slot, nb, stream);
         EP_RETURN_IF_LAUNCH_FAILED();
     }
     return hipSuccess;
@@ -917,14 +950,16 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
 // blocks' rank counts into the receive row of each block's first token on each rank and
 // zeroes the ticket for the next call. Blocks past `nlb` run the dense restripe riding
 // along in this launch.
+template <int kK>  // 0: no expert ranks; else their rounds, k <= kK
 __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int N, FastDiv er,
-    FastDiv rpn, CountsWorkspace cw, int nlb, RestripeTask rs, int32_t* __restrict__ error_flag) {
+    FastDiv rpn, CountsWorkspace cw, int nlb, RestripeTask rs, int32_t* __restrict__ error_flag,
+    int32_t* __restrict__ expert_rank, int nbits) {
     if (static_cast<int>(blockIdx.x) >= nlb) {
         restripe_task_block(rs, static_cast<int64_t>(blockIdx.x) - nlb);
         return;
     }
-    extern __shared__ int32_t s_hist[];                      // [E]
+    extern __shared__ int32_t s_hist[];                      // [E], then (expert_rank) [4][E] u16
     __shared__ uint64_t s_ball[kWavesBT * kCountsMaxRanks];  // [4][R] rank ballots per wave
     __shared__ uint16_t s_wn[kWavesBT * kCountsMaxRanks];    // [4][N] node counts per wave
     __shared__ int32_t s_part[kBT];                          // last block: partial column sums
@@ -941,7 +976,11 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     // is only ORed into afterwards, so the last block cannot erase a bit another block
     // raised.
     if (b == 0 && tid == 0) __hip_atomic_store(error_flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint16_t* s_run = reinterpret_cast<uint16_t*>(s_hist + E);
+    const int Ep = run_row(E);
     for (int e = tid; e < E; e += kBT) s_hist[e] = 0;
+    if constexpr (kK > 0)
+        for (int i = tid; i < kWavesBT * Ep; i += kBT) s_run[i] = 0;
     __syncthreads();
     uint64_t rm[1] = {0}, nm[1] = {0};
     int bad = 0;
@@ -977,6 +1016,27 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
         carry += chunk;
     }
     const int any_bad = __syncthreads_or(bad);
+    if constexpr (kK > 0) {  // each pair's rank among the block's pairs naming its expert
+        const int lane = lane_id();
+        const int64_t t0 = static_cast<int64_t>(b) * kBT + static_cast<int64_t>(wave) * kWave;
+        const int64_t npairs = max<int64_t>(0, min<int64_t>(kWave, T - t0)) * k;
+        int key[kK];
+        int loc[kK];
+        wave_expert_ranks<kK>(topk_idx + t0 * k, npairs, k, E, nbits, s_run + wave * Ep, key, loc);
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kK; ++r) {
+            const int p = r * kWave + lane;
+            if (r < k && p < npairs) {
+                int rank = -1;
+                if (key[r] >= 0) {
+                    rank = loc[r];
+                    for (int w = 0; w < wave; ++w) rank += s_run[w * Ep + key[r]];
+                }
+                expert_rank[t0 * k + p] = rank;
+            }
+        }
+    }
     if (nlb <= kCountsLocalBlocks) {  // no cross-block phase: the dispatch sums the counts
         if (tid == 0 && any_bad) raise_error(error_flag, kErrTopkRange);
         return;
@@ -1182,8 +1242,9 @@ CountsWorkspace carve_counts_workspace(void* base, int64_t T, int E, int R, int 
 }
 
 hipError_t launch_layout_counts(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
-                                int32_t* error_flag, const CountsWorkspace& cw,
-                                const RestripeTask* rs_in, hipStream_t stream) {
+                                int32_t* error_flag, int32_t* expert_rank,
+                                const CountsWorkspace& cw, const RestripeTask* rs_in,
+                                hipStream_t stream) {
     RestripeTask rs{};
     if (rs_in != nullptr) rs = *rs_in;
     const int64_t nb = (T + kBT - 1) / kBT;
@@ -1196,9 +1257,23 @@ hipError_t launch_layout_counts(const int64_t* topk_idx, int64_t T, int k, int E
     if (nb > INT32_MAX || !grid_fits(nb + rs.blocks, kBT)) return hipErrorInvalidConfiguration;
     const FastDiv er = FastDiv::make(E / R);
     const FastDiv rpn = FastDiv::make(R / N);
-    hipLaunchKernelGGL(layout_counts_kernel, dim3(static_cast<unsigned>(nb + rs.blocks)),
-                       dim3(kBT), sizeof(int32_t) * static_cast<size_t>(E), stream, topk_idx, T,
-                       k, E, R, N, er, rpn, cw, static_cast<int>(nb), rs, error_flag);
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const size_t run_bytes = sizeof(uint16_t) * kWavesBT * static_cast<size_t>(run_row(E));
+    const size_t lds = sizeof(int32_t) * static_cast<size_t>(E) + (expert_rank ? run_bytes : 0);
+    const dim3 grid(static_cast<unsigned>(nb + rs.blocks));
+    if (!expert_rank)
+        hipLaunchKernelGGL(layout_counts_kernel<0>, grid, dim3(kBT), lds, stream, topk_idx, T, k,
+                           E, R, N, er, rpn, cw, static_cast<int>(nb), rs, error_flag, expert_rank,
+                           nbits);
+    else if (k <= 8)
+        hipLaunchKernelGGL(layout_counts_kernel<8>, grid, dim3(kBT), lds, stream, topk_idx, T, k,
+                           E, R, N, er, rpn, cw, static_cast<int>(nb), rs, error_flag, expert_rank,
+                           nbits);
+    else
+        hipLaunchKernelGGL(layout_counts_kernel<kExpertSlotMaxK>, grid, dim3(kBT), lds, stream,
+                           topk_idx, T, k, E, R, N, er, rpn, cw, static_cast<int>(nb), rs,
+                           error_flag, expert_rank, nbits);
     return hipGetLastError();
 }
 

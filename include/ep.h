@@ -206,16 +206,20 @@ size_t ep_layout_counts_workspace_bytes(int64_t num_tokens, int num_experts, int
                                         int num_nodes);
 
 /* ep_layout_counts -- In: topk_idx int64 [T][k]. Out: the per-block tables in `workspace`,
- * error_flag [1] (overwritten). With prob non-NULL it also writes prob_dest_major exactly
+ * error_flag [1] (overwritten); with expert_rank non-NULL ([T][k] int32, k <=
+ * EP_EXPERT_SLOT_MAX_K), each pair's rank among the pairs of its block of 256 tokens that
+ * name the same expert, in (token, slot) order (-1 for a masked or bad id), for
+ * ep_dispatch_permute_layout. With prob non-NULL it also writes prob_dest_major exactly
  * as ep_restripe_prob(prob, T, num_nodes, prob_per_token, max_tokens_per_rank).
  * Sizes: as ep_get_layout, num_ranks <= EP_COUNTS_MAX_RANKS and T * k <= INT32_MAX; with
  *   prob as ep_restripe_prob (EP_ERR_CAPACITY for Tmax < T).
  * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_CAPACITY (workspace too small or NULL),
  *   EP_ERR_HIP. */
 int ep_layout_counts(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-                     int num_ranks, int num_nodes, int32_t *error_flag, const float *prob,
-                     int prob_per_token, int64_t max_tokens_per_rank, float *prob_dest_major,
-                     void *workspace, size_t workspace_bytes, void *stream);
+                     int num_ranks, int num_nodes, int32_t *error_flag, int32_t *expert_rank,
+                     const float *prob, int prob_per_token, int64_t max_tokens_per_rank,
+                     float *prob_dest_major, void *workspace, size_t workspace_bytes,
+                     void *stream);
 
 /* ep_dispatch_layout -- after ep_layout_counts on the same batch and workspace, stream-
  * ordered: ep_dispatch's outputs (recv_x, recv_topk_idx, recv_topk_weights, recv_src_idx,
@@ -235,6 +239,26 @@ int ep_dispatch_layout(const void *x, const int64_t *topk_idx, const float *topk
                        int64_t *recv_topk_idx, float *recv_topk_weights, int32_t *recv_src_idx,
                        int64_t recv_capacity, int32_t *error_flag, const void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* ep_dispatch_permute_layout -- the counts path's dispatch + permute ("[PR #634] Hybrid ep
+ * nixl restripe" measures "dispatch+permute"; its commit list names the scan over tokens
+ * per local expert): after ep_layout_counts on the same batch and workspace with
+ * expert_rank, stream-ordered, ep_dispatch_permute's outputs (perm_x, perm_weights,
+ * perm_src_idx, with the same meaning and capacity rule) for the expert-major rows that
+ * ep_get_layout's expert_slot defines, computed inside the permute's waves; and, nullable,
+ * expert_slot [T][k], num_tokens_per_expert [E] and expert_offset [E+1] as ep_get_layout
+ * defines them. topk_idx and expert_rank are required.
+ * Sizes: as ep_dispatch_permute, num_ranks <= EP_COUNTS_MAX_RANKS, and T <= 16384 (at most
+ *   64 blocks of 256 tokens: each wave reads one word per block). Errors: EP_ERR_ARG,
+ *   EP_ERR_ALIGN, EP_ERR_CAPACITY (workspace), EP_ERR_HIP. */
+int ep_dispatch_permute_layout(const void *x, const int64_t *topk_idx,
+                               const float *topk_weights, int64_t num_tokens, int hidden,
+                               int num_topk, int num_experts, int num_ranks, int num_nodes,
+                               const int32_t *expert_rank, int32_t *num_tokens_per_expert,
+                               int32_t *expert_offset, int32_t *expert_slot, void *perm_x,
+                               float *perm_weights, int32_t *perm_src_idx, int64_t perm_capacity,
+                               int32_t *error_flag, const void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 /* ep_dispatch -- pack every (token, rank) pair into its receive row.
  *

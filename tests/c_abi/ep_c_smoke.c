@@ -159,8 +159,8 @@ int main(void) {
                                cap, d_err, st));
             EP_OK_(ep_restripe_prob((const float *)d_prob, T, N, P, TMAX, (float *)d_prob_out, st));
         } else {
-            EP_OK_(ep_layout_counts(d_idx, T, K, E, R, N, d_err, (const float *)d_prob, P, TMAX,
-                                    (float *)d_prob_out, d_cws, cws_bytes, st));
+            EP_OK_(ep_layout_counts(d_idx, T, K, E, R, N, d_err, NULL, (const float *)d_prob, P,
+                                    TMAX, (float *)d_prob_out, d_cws, cws_bytes, st));
             EP_OK_(ep_dispatch_layout(d_x, d_idx, d_w, T, H, K, E, R, N, d_cr, d_ro, d_cn, d_ce, d_eo,
                                       d_slot, d_in, d_recv_x, d_ridx, d_rw, d_src, cap, d_err,
                                       d_cws, cws_bytes, st));

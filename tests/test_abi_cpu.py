@@ -38,8 +38,9 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch_preprocess",
-                          "ep_layout_counts", "ep_dispatch_layout",
-                          "ep_layout_counts_workspace_bytes", "ep_dispatch", "ep_restripe_prob", "ep_combine", "ep_hbm_fan",
+                          "ep_layout_counts", "ep_dispatch_layout", "ep_dispatch_permute_layout",
+                          "ep_layout_counts_workspace_bytes", "ep_dispatch", "ep_restripe_prob",
+                          "ep_combine", "ep_hbm_fan",
                           "ep_layout_workspace_bytes", "ep_status_string", "ep_hbm_copy",
                           "ep_dispatch_fp8", "ep_dispatch_permute", "ep_restripe_prob_sparse",
                           "ep_dispatch_send", "ep_dispatch_recv", "ep_combine_send",
@@ -171,8 +172,11 @@ def test_counts_path_validation(lib):
     assert ep.EP_COUNTS_MAX_RANKS == 64
 
     def counts(T=100, k=4, E=16, R=4, N=2, prob=None, P=8, Tmax=100, out=None, ws=A16,
-               wsb=1 << 20, flag=A16):
-        return lib.ep_layout_counts(A16, T, k, E, R, N, flag, prob, P, Tmax, out, ws, wsb, None)
+               wsb=1 << 20, flag=A16, erank=None):
+        return lib.ep_layout_counts(A16, T, k, E, R, N, flag, erank, prob, P, Tmax, out, ws, wsb,
+                                    None)
+    assert counts(k=17, E=32, erank=A16) == ep.EP_ERR_ARG      # k > EP_EXPERT_SLOT_MAX_K
+    assert counts(erank=P(0x10002)) == ep.EP_ERR_ALIGN
     assert counts(E=15) == ep.EP_ERR_ARG
     assert counts(E=256, R=128, N=4) == ep.EP_ERR_ARG           # R > 64
     assert counts(flag=None) == ep.EP_ERR_ARG
@@ -201,6 +205,21 @@ def test_counts_path_validation(lib):
     assert disp(N=3) == ep.EP_ERR_ARG
     assert disp(wsb=16) == ep.EP_ERR_CAPACITY
     assert disp(ws=P(0x10004)) == ep.EP_ERR_ALIGN
+
+    def perm(T=10, H=64, k=2, E=8, R=4, N=2, x=A16, idx=A16, er=A16, px=A16, ws=A16,
+             wsb=1 << 20, es=A16):
+        return lib.ep_dispatch_permute_layout(x, idx, A16, T, H, k, E, R, N, er, A16, A16, es, px,
+                                              A16, A16, 100, A16, ws, wsb, None)
+    assert perm(T=16385) == ep.EP_ERR_ARG                       # past 64 blocks of 256 tokens
+    assert perm(k=17, E=32) == ep.EP_ERR_ARG                    # k > EP_EXPERT_SLOT_MAX_K
+    assert perm(E=256, R=128, N=4) == ep.EP_ERR_ARG             # R > 64
+    assert perm(er=None) == ep.EP_ERR_ARG
+    assert perm(idx=None) == ep.EP_ERR_ARG
+    assert perm(px=None) == ep.EP_ERR_ARG
+    assert perm(H=12) == ep.EP_ERR_ALIGN
+    assert perm(x=MIS) == ep.EP_ERR_ALIGN
+    assert perm(es=P(0x10002)) == ep.EP_ERR_ALIGN
+    assert perm(wsb=16) == ep.EP_ERR_CAPACITY
 
 
 def test_dispatch_permute_validation(lib):
