@@ -770,7 +770,7 @@ static_assert((1 << kIdBits) == kMaxExperts, "the expert-rank ballots cover ever
 // rounds' LDS updates as atomics, all before any result is used, measured no faster.
 template <int kK>
 __device__ __forceinline__ void wave_expert_ranks(const int64_t* __restrict__ ids, int64_t npairs,
-                                                  int k, int E, int nbits, uint16_t* run,
+                                                  int k, int E, uint16_t* run,
                                                   int (&key)[kK], int (&loc)[kK]) {
     const int lane = lane_id();
     int64_t e_in[kK];
@@ -812,7 +812,7 @@ __device__ __forceinline__ void wave_expert_ranks(const int64_t* __restrict__ id
 // (wave_expert_ranks).
 template <int kK>  // rounds: k <= kK
 __global__ __launch_bounds__(kBT) void layout_expert_slot_kernel(
-    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int nbits,
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E,
     const int32_t* __restrict__ blk_exp_base, int32_t* __restrict__ expert_slot) {
     extern __shared__ uint16_t s_run[];  // [kWavesBT][Ep], running count per wave and expert
     const int Ep = run_row(E);
@@ -827,7 +827,7 @@ __global__ __launch_bounds__(kBT) void layout_expert_slot_kernel(
     const int64_t npairs = max<int64_t>(0, min<int64_t>(kWave, T - t0)) * k;
     int key[kK];
     int loc[kK];
-    wave_expert_ranks<kK>(topk_idx + t0 * k, npairs, k, E, nbits, s_run + wave * Ep, key, loc);
+    wave_expert_ranks<kK>(topk_idx + t0 * k, npairs, k, E, s_run + wave * Ep, key, loc);
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kK; ++r) {
@@ -844,17 +844,17 @@ __global__ __launch_bounds__(kBT) void layout_expert_slot_kernel(
 }
 
 // The expert-slot launch over `blocks` blocks, with as many ranking rounds as k needs.
-void launch_expert_slots(const int64_t* topk_idx, int64_t T, int k, int E, int nbits,
+void launch_expert_slots(const int64_t* topk_idx, int64_t T, int k, int E,
                          const int32_t* blk_exp_base, int32_t* expert_slot, int64_t blocks,
                          hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(blocks));
     const size_t lds = sizeof(uint16_t) * kWavesBT * run_row(E);
     if (k <= 8)
         hipLaunchKernelGGL(layout_expert_slot_kernel<8>, grid, dim3(kBT), lds, stream, topk_idx, T,
-                           k, E, nbits, blk_exp_base, expert_slot);
+                           k, E, blk_exp_base, expert_slot);
     else
         hipLaunchKernelGGL(layout_expert_slot_kernel<kExpertSlotMaxK>, grid, dim3(kBT), lds,
-                           stream, topk_idx, T, k, E, nbits, blk_exp_base, expert_slot);
+                           stream, topk_idx, T, k, E, blk_exp_base, expert_slot);
 }
 
 template <int NW>
@@ -884,9 +884,7 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
                                rs);
             EP_RETURN_IF_LAUNCH_FAILED();
             if (want_base) {
-                int nbits = 0;
-                while ((1 << nbits) < E) ++nbits;
-                launch_expert_slots(topk_idx, T, k, E, nbits, ws.blk_exp_base, expert_slot, 1,
+                launch_expert_slots(topk_idx, T, k, E, ws.blk_exp_base, expert_slot, 1,
                                     stream);
                 EP_RETURN_IF_LAUNCH_FAILED();
             }
@@ -931,9 +929,7 @@ hipError_t layout_impl(const int64_t* topk_idx, int64_t T, int k, int E, int R, 
         }
     }
     if (want_base && nb > 0) {
-        int nbits = 0;
-        while ((1 << nbits) < E) ++nbits;
-        launch_expert_slots(topk_idx, T, k, E, nbits, ws.blk_exp_base, expert_slot, nb, stream);
+        launch_expert_slots(topk_idx, T, k, E, ws.blk_exp_base, expert_slot, nb, stream);
         EP_RETURN_IF_LAUNCH_FAILED();
     }
     return hipSuccess;
@@ -954,7 +950,7 @@ template <int kK>  // 0: no expert ranks; else their rounds, k <= kK
 __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int N, FastDiv er,
     FastDiv rpn, CountsWorkspace cw, int nlb, RestripeTask rs, int32_t* __restrict__ error_flag,
-    int32_t* __restrict__ expert_rank, int nbits) {
+    int32_t* __restrict__ expert_rank) {
     if (static_cast<int>(blockIdx.x) >= nlb) {
         restripe_task_block(rs, static_cast<int64_t>(blockIdx.x) - nlb);
         return;
@@ -1022,7 +1018,7 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
         const int64_t npairs = max<int64_t>(0, min<int64_t>(kWave, T - t0)) * k;
         int key[kK];
         int loc[kK];
-        wave_expert_ranks<kK>(topk_idx + t0 * k, npairs, k, E, nbits, s_run + wave * Ep, key, loc);
+        wave_expert_ranks<kK>(topk_idx + t0 * k, npairs, k, E, s_run + wave * Ep, key, loc);
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < kK; ++r) {
@@ -1257,23 +1253,19 @@ hipError_t launch_layout_counts(const int64_t* topk_idx, int64_t T, int k, int E
     if (nb > INT32_MAX || !grid_fits(nb + rs.blocks, kBT)) return hipErrorInvalidConfiguration;
     const FastDiv er = FastDiv::make(E / R);
     const FastDiv rpn = FastDiv::make(R / N);
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
     const size_t run_bytes = sizeof(uint16_t) * kWavesBT * static_cast<size_t>(run_row(E));
     const size_t lds = sizeof(int32_t) * static_cast<size_t>(E) + (expert_rank ? run_bytes : 0);
     const dim3 grid(static_cast<unsigned>(nb + rs.blocks));
     if (!expert_rank)
         hipLaunchKernelGGL(layout_counts_kernel<0>, grid, dim3(kBT), lds, stream, topk_idx, T, k,
-                           E, R, N, er, rpn, cw, static_cast<int>(nb), rs, error_flag, expert_rank,
-                           nbits);
+                           E, R, N, er, rpn, cw, static_cast<int>(nb), rs, error_flag, expert_rank);
     else if (k <= 8)
         hipLaunchKernelGGL(layout_counts_kernel<8>, grid, dim3(kBT), lds, stream, topk_idx, T, k,
-                           E, R, N, er, rpn, cw, static_cast<int>(nb), rs, error_flag, expert_rank,
-                           nbits);
+                           E, R, N, er, rpn, cw, static_cast<int>(nb), rs, error_flag, expert_rank);
     else
         hipLaunchKernelGGL(layout_counts_kernel<kExpertSlotMaxK>, grid, dim3(kBT), lds, stream,
                            topk_idx, T, k, E, R, N, er, rpn, cw, static_cast<int>(nb), rs,
-                           error_flag, expert_rank, nbits);
+                           error_flag, expert_rank);
     return hipGetLastError();
 }
 
