@@ -1,5 +1,18 @@
-// hbm_copy.hip -- plain 128-bit device copy: the HBM copy-bandwidth yardstick and the
+// hbm_copy.hip -- 128-bit streams of a fixed read/write mix: the HBM copy-bandwidth
+// yardstick, the yardstick for the direction mixes of dispatch and combine, and the
 // known-size reference for hardware byte counters. Not a step of the dispatch path.
+//
+// Each stream takes the cache policy that measured fastest for its mix on MI355X, in
+// sequential streams of 512 MiB slabs (beyond the 256 MB Infinity Cache), best of three:
+// - one read per write (the copy): non-temporal loads, and stores at device scope (sc1),
+//   which write through the L2: 6.45 against 5.44 TB/s with non-temporal stores;
+// - reads that outnumber writes (the combine's mix): non-temporal loads and stores;
+//   device-scope stores were 1-5% slower from two reads per write up;
+// - one read per several writes (the dispatch's mix): cached loads and non-temporal
+//   stores; at the dispatch's own slab (58.7 MB, 1 to 7) they took 74.8 against 87.6 us
+//   with non-temporal loads, and device-scope stores were slower at every such mix.
+// Byte counters read the same with either store form (FETCH_SIZE 0.501 and WRITE_SIZE
+// 1.000 of the bytes moved, on the copy and on both mixes).
 #include "ep_internal.hpp"
 
 namespace ep {
@@ -11,24 +24,39 @@ namespace {
 
 constexpr int kCopyThreads = 256;
 constexpr int kCopyU = 4;
+// Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family targets; buffer ops
+// through it are bounds-checked against the resource's byte count: a load past it
+// returns zero and a store past it is dropped.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kLoadNonTemporal = 2;    // cache-policy bit nt of a buffer load
+constexpr int kStoreDeviceScope = 16;  // cache-policy bit sc1 of a buffer store
 
 __global__ __launch_bounds__(kCopyThreads) void hbm_copy_kernel(const u32x4* __restrict__ in,
                                                                 u32x4* __restrict__ out,
                                                                 int64_t n) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kCopyThreads * kCopyU;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyThreads * kCopyU + threadIdx.x;
-         base < n; base += stride) {
+    constexpr int64_t per_block = kCopyThreads * kCopyU;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * per_block;
+    for (int64_t b0 = static_cast<int64_t>(blockIdx.x) * per_block; b0 < n; b0 += stride) {
+        const int64_t left = n - b0;
+        const int bytes = static_cast<int>(left < per_block ? left : per_block) * 16;
+        // The block's words as two buffers of `bytes` bytes. Their bounds checks stand in
+        // for per-word guards: guarded stores each sit in a branch of their own, and the
+        // compiler then waits for all memory operations before every store, so the stores
+        // of a lane go out one at a time (measured 5.9 TB/s against 6.3 without the waits).
+        const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<u32x4*>(in + b0), 0, bytes, kRawBufferWord3);
+        const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<void*>(out + b0), 0, bytes, kRawBufferWord3);
         u32x4 v[kCopyU];
 #pragma unroll
-        for (int u = 0; u < kCopyU; ++u) {
-            const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
-            if (i < n) v[u] = load_stream(in + i);
-        }
+        for (int u = 0; u < kCopyU; ++u)
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                src, (u * kCopyThreads + static_cast<int>(threadIdx.x)) * 16, 0, kLoadNonTemporal);
 #pragma unroll
-        for (int u = 0; u < kCopyU; ++u) {
-            const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
-            if (i < n) store_stream(out + i, v[u]);
-        }
+        for (int u = 0; u < kCopyU; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v[u], dst, (u * kCopyThreads + static_cast<int>(threadIdx.x)) * 16, 0,
+                kStoreDeviceScope);
     }
 }
 
@@ -36,8 +64,9 @@ __global__ __launch_bounds__(kCopyThreads) void hbm_copy_kernel(const u32x4* __r
 // word i of the fan_in input slabs (slab = n words, contiguous). fan_in F, fan_out 1
 // moves F reads per write, the direction mix of the combine; fan_in 1, fan_out F one
 // read per F writes, the mix of the dispatch. Every access is a sequential stream, so
-// the time is what HBM sustains for that mix. One-shot threads of U words each.
-template <int U>
+// the time is what HBM sustains for that mix. One-shot threads of U words each; loads
+// are cached with kCached, else non-temporal.
+template <int U, bool kCached>
 __global__ __launch_bounds__(kCopyThreads) void hbm_fan_kernel(const u32x4* __restrict__ in,
                                                                u32x4* __restrict__ out,
                                                                int64_t n, int fan_in,
@@ -53,7 +82,8 @@ __global__ __launch_bounds__(kCopyThreads) void hbm_fan_kernel(const u32x4* __re
             const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
 #pragma unroll
             for (int q = 0; q < 8; ++q)
-                if (i < n && s + q < fan_in) v[u][q] = load_stream(in + (s + q) * n + i);
+                if (i < n && s + q < fan_in)
+                    v[u][q] = kCached ? in[(s + q) * n + i] : load_stream(in + (s + q) * n + i);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -81,15 +111,21 @@ hipError_t launch_hbm_fan(const void* src, void* dst, size_t slab_bytes, int fan
         constexpr int U = EP_FAN_U;
         const int64_t grid = (n + kCopyThreads * U - 1) / (kCopyThreads * U);
         if (!grid_fits(grid, kCopyThreads)) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(hbm_fan_kernel<U>, dim3(static_cast<unsigned>(grid)), dim3(kCopyThreads),
-                           0, stream, static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n,
-                           fan_in, fan_out);
+        hipLaunchKernelGGL((hbm_fan_kernel<U, false>), dim3(static_cast<unsigned>(grid)),
+                           dim3(kCopyThreads), 0, stream, static_cast<const u32x4*>(src),
+                           static_cast<u32x4*>(dst), n, fan_in, fan_out);
     } else {
         const int64_t grid = (n + kCopyThreads * kCopyU - 1) / (kCopyThreads * kCopyU);
         if (!grid_fits(grid, kCopyThreads)) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(hbm_fan_kernel<kCopyU>, dim3(static_cast<unsigned>(grid)),
-                           dim3(kCopyThreads), 0, stream, static_cast<const u32x4*>(src),
-                           static_cast<u32x4*>(dst), n, fan_in, fan_out);
+        // reads fewer than writes: cached loads (the dispatch's own row loads are cached)
+        if (fan_in < fan_out)
+            hipLaunchKernelGGL((hbm_fan_kernel<kCopyU, true>), dim3(static_cast<unsigned>(grid)),
+                               dim3(kCopyThreads), 0, stream, static_cast<const u32x4*>(src),
+                               static_cast<u32x4*>(dst), n, fan_in, fan_out);
+        else
+            hipLaunchKernelGGL((hbm_fan_kernel<kCopyU, false>), dim3(static_cast<unsigned>(grid)),
+                               dim3(kCopyThreads), 0, stream, static_cast<const u32x4*>(src),
+                               static_cast<u32x4*>(dst), n, fan_in, fan_out);
     }
     return hipGetLastError();
 }

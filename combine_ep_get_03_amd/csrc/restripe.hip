@@ -20,7 +20,7 @@ template <typename W>
 __global__ __launch_bounds__(kRT) void restripe_kernel(const W* __restrict__ in, int64_t T,
                                                        int NV, int VP, int64_t Tmax,
                                                        W* __restrict__ out, int tpb) {
-    restripe_run<W>(in, T, NV, VP, Tmax, out, tpb, blockIdx.x);
+    restripe_run<W, kRU>(in, T, NV, VP, Tmax, out, tpb, blockIdx.x);
 }
 
 // Sparse path: only routed (token, node) slices move, to row node_slot[t][n] of the node's
@@ -40,29 +40,28 @@ __global__ __launch_bounds__(kRT) void restripe_sparse_kernel(
     const W* src = in + t0 * NV;
     int32_t errbits = 0;
     for (int f0 = 0; f0 < total; f0 += kRT * kRU) {
+        // A lane past the end takes the last word, as in the dense walk: its loads need no
+        // guard, and its store, if any, repeats that word's.
         W v[kRU];
         int32_t s[kRU];
+        int f[kRU];
 #pragma unroll
         for (int u = 0; u < kRU; ++u) {
-            const int f = f0 + u * kRT + tid;
-            s[u] = -1;
-            if (f < total) {
-                const int tt = f / NV;
-                const int n = (f - tt * NV) / VP;
-                s[u] = node_slot[(t0 + tt) * N + n];
-                v[u] = __builtin_nontemporal_load(src + f);
-            }
+            f[u] = min(f0 + u * kRT + tid, total - 1);
+            const int tt = f[u] / NV;
+            const int n = (f[u] - tt * NV) / VP;
+            s[u] = node_slot[(t0 + tt) * N + n];
+            v[u] = __builtin_nontemporal_load(src + f[u]);
         }
 #pragma unroll
         for (int u = 0; u < kRU; ++u) {
-            const int f = f0 + u * kRT + tid;
-            if (f < total && s[u] >= 0) {
+            if (s[u] >= 0) {
                 if (s[u] >= Tmax) {
                     errbits |= kErrRecvOverflow;
                     continue;
                 }
-                const int tt = f / NV;
-                const int rem = f - tt * NV;
+                const int tt = f[u] / NV;
+                const int rem = f[u] - tt * NV;
                 const int n = rem / VP;
                 const int vv = rem - n * VP;
                 __builtin_nontemporal_store(v[u], out + (static_cast<int64_t>(n) * Tmax + s[u]) * VP + vv);
