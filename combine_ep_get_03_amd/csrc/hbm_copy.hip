@@ -106,26 +106,32 @@ hipError_t launch_hbm_fan(const void* src, void* dst, size_t slab_bytes, int fan
                           int fan_out, hipStream_t stream) {
     const int64_t n = static_cast<int64_t>(slab_bytes / 16);
     if (n == 0) return hipSuccess;
-    // a lane keeps about eight loads in flight: U words of fan_in slabs each
+    // a lane keeps about eight loads in flight: U words of fan_in slabs each; reads fewer
+    // than writes take cached loads (the dispatch's own row loads are cached)
+    const auto in = static_cast<const u32x4*>(src);
+    const auto out = static_cast<u32x4*>(dst);
+    const bool cached = fan_in < fan_out;
     if (fan_in >= 4) {
         constexpr int U = EP_FAN_U;
         const int64_t grid = (n + kCopyThreads * U - 1) / (kCopyThreads * U);
         if (!grid_fits(grid, kCopyThreads)) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((hbm_fan_kernel<U, false>), dim3(static_cast<unsigned>(grid)),
-                           dim3(kCopyThreads), 0, stream, static_cast<const u32x4*>(src),
-                           static_cast<u32x4*>(dst), n, fan_in, fan_out);
+        const dim3 g(static_cast<unsigned>(grid));
+        if (cached)
+            hipLaunchKernelGGL((hbm_fan_kernel<U, true>), g, dim3(kCopyThreads), 0, stream, in, out,
+                               n, fan_in, fan_out);
+        else
+            hipLaunchKernelGGL((hbm_fan_kernel<U, false>), g, dim3(kCopyThreads), 0, stream, in, out,
+                               n, fan_in, fan_out);
     } else {
         const int64_t grid = (n + kCopyThreads * kCopyU - 1) / (kCopyThreads * kCopyU);
         if (!grid_fits(grid, kCopyThreads)) return hipErrorInvalidConfiguration;
-        // reads fewer than writes: cached loads (the dispatch's own row loads are cached)
-        if (fan_in < fan_out)
-            hipLaunchKernelGGL((hbm_fan_kernel<kCopyU, true>), dim3(static_cast<unsigned>(grid)),
-                               dim3(kCopyThreads), 0, stream, static_cast<const u32x4*>(src),
-                               static_cast<u32x4*>(dst), n, fan_in, fan_out);
+        const dim3 g(static_cast<unsigned>(grid));
+        if (cached)
+            hipLaunchKernelGGL((hbm_fan_kernel<kCopyU, true>), g, dim3(kCopyThreads), 0, stream, in,
+                               out, n, fan_in, fan_out);
         else
-            hipLaunchKernelGGL((hbm_fan_kernel<kCopyU, false>), dim3(static_cast<unsigned>(grid)),
-                               dim3(kCopyThreads), 0, stream, static_cast<const u32x4*>(src),
-                               static_cast<u32x4*>(dst), n, fan_in, fan_out);
+            hipLaunchKernelGGL((hbm_fan_kernel<kCopyU, false>), g, dim3(kCopyThreads), 0, stream, in,
+                               out, n, fan_in, fan_out);
     }
     return hipGetLastError();
 }

@@ -40,7 +40,7 @@ def test_copy_of_zero_bytes_writes_nothing():
 
 
 @pytest.mark.parametrize("fan_in,fan_out", [(7, 1), (8, 1), (1, 7), (1, 8), (2, 1), (1, 2),
-                                            (1, 1), (4, 3)])
+                                            (1, 1), (4, 3), (4, 8)])
 @pytest.mark.parametrize("slab", [16 * 3001, 16 * 1024 * 3])
 def test_fan_writes_the_xor_of_its_slabs(fan_in, fan_out, slab):
     print(f"\ncase: ep_hbm_fan {fan_in}:{fan_out} slab {slab}", flush=True)
