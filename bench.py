@@ -64,7 +64,7 @@ def algorithmic_bytes(cfg, M: int) -> dict:
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {"dispatch": ["ep_internal.hpp", "dispatch.hip"],
+KERNEL_SOURCES = {"dispatch": ["ep_internal.hpp", "dispatch_rows.hpp", "dispatch.hip"],
                   "combine": ["ep_internal.hpp", "combine.hip"]}
 
 
@@ -449,10 +449,22 @@ def mix_yardstick(torch, ep, cfg, M: int, avg: dict, alg: dict, steps: int, time
 
 
 def small_batches(torch, W, DeviceBatch, Path, cfg, steps: int, timed) -> dict:
-    """The whole step at decode-sized batches of the same shape (256 and 1024 tokens), timed
-    like the headline step (one graph of K steps); seeded inputs of their own."""
+    """The whole step at decode-sized batches of the same shape (64, 256 and 1024 tokens),
+    timed like the headline step (one graph of K steps); seeded inputs of their own. Up to
+    256 tokens Path.step is ep_layout_dispatch + ep_combine; the counts path's step (three
+    launches) is timed beside it there, and its outputs checked equal."""
+    def graph_ms(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                fn()
+        g.replay()
+        ms = timed(g.replay, 1) / steps
+        del g
+        return ms
+
     out = {}
-    for T in (256, 1024):
+    for T in (64, 256, 1024):
         c = cfg.with_(T=T, Tmax=T, name=f"{cfg.name}_T{T}")
         inp = W.make_inputs(c)
         b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials)
@@ -460,18 +472,23 @@ def small_batches(torch, W, DeviceBatch, Path, cfg, steps: int, timed) -> dict:
         p.step(b)
         torch.cuda.synchronize()
         M = int(p.layout_buf.rank_offset[-1].item())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(steps):
-                p.step(b)
-        g.replay()
-        ms = timed(g.replay, 1) / steps
-        del g
+        ms = graph_ms(lambda: p.step(b))
         if int(p.error_flag.item()) != 0:
             raise RuntimeError(f"device error flag at T={T}")
-        out[f"T{T}"] = {"step_us": round(ms * 1e3, 2), "M_token_rank_pairs": M,
-                        "algorithm_gbps": round(2 * M * c.H * 2 / (ms * 1e-3) / 1e9, 1),
-                        "tokens_per_s": round(T / (ms * 1e-3), 1)}
+        one = p.counts_path and T <= 256
+        r = {"step_us": round(ms * 1e3, 2),
+             "step": "ep_layout_dispatch + ep_combine" if one else "the counts path",
+             "M_token_rank_pairs": M,
+             "algorithm_gbps": round(2 * M * c.H * 2 / (ms * 1e-3) / 1e9, 1),
+             "tokens_per_s": round(T / (ms * 1e-3), 1)}
+        if one:
+            ref = (p.out.clone(), p.recv.recv_x[:M].clone(), p.prob_dest_major[:, :T].clone())
+            r["counts_path_step_us"] = round(graph_ms(lambda: p.step_counts(b)) * 1e3, 2)
+            torch.cuda.synchronize()
+            if not (torch.equal(ref[0], p.out) and torch.equal(ref[1], p.recv.recv_x[:M]) and
+                    torch.equal(ref[2], p.prob_dest_major[:, :T])):
+                raise RuntimeError(f"the counts path's step differs at T={T}")
+        out[f"T{T}"] = r
         del p, b
     torch.cuda.empty_cache()
     return out

@@ -21,6 +21,7 @@ EP_DEVERR_WORKSPACE = 8
 EP_MAX_RANKS, EP_MAX_EXPERTS, EP_EXPERT_SLOT_MAX_K = 1024, 8192, 16
 EP_LAYOUT_SCRATCH_BYTES = 4 << 20
 EP_COUNTS_MAX_RANKS = 64
+EP_LAYOUT_DISPATCH_MAX_TOKENS = 256
 
 _lib = None
 
@@ -53,6 +54,8 @@ def load() -> ctypes.CDLL:
     L.ep_layout_counts.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, i32, i64, P, P, sz, P]
     L.ep_dispatch_permute_layout.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P, P,
                                              P, P, i64, P, P, sz, P]
+    L.ep_layout_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, P,
+                                     P, P, P, P, i64, P, i32, i64, P, P, P]
     L.ep_dispatch_layout.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, P,
                                      P, P, P, P, i64, P, P, sz, P]
     L.ep_dispatch_preprocess.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
@@ -305,6 +308,60 @@ def ep_dispatch_layout(x, topk_idx, topk_weights, num_experts: int, num_ranks: i
         _ptr(error_flag, torch.int32, "error_flag", True),
         _ptr(workspace, torch.uint8, "workspace"), ws_bytes, _stream(stream)),
         "ep_dispatch_layout")
+
+
+def ep_layout_dispatch(x, topk_idx, topk_weights, num_experts: int, num_ranks: int,
+                       num_nodes: int, *, token_slot, recv_x, num_tokens_per_rank, rank_offset,
+                       error_flag, is_token_in_rank=None, num_tokens_per_node=None,
+                       num_tokens_per_expert=None, expert_offset=None, recv_topk_idx=None,
+                       recv_topk_weights=None, recv_src_idx=None, prob=None,
+                       prob_dest_major=None, stream=None) -> None:
+    """The layout, the dispatch and (with prob) the restripe of a batch of at most
+    EP_LAYOUT_DISPATCH_MAX_TOKENS tokens in one launch: ep_get_layout's counts, offsets,
+    token_slot and bitmap, ep_dispatch's outputs and prob_dest_major, and the error flag."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    E, R, N = num_experts, num_ranks, num_nodes
+    cap = recv_x.shape[0]
+    _shape(topk_idx, (T, k), "topk_idx")
+    _shape(topk_weights, (T, k), "topk_weights")
+    _shape(token_slot, (T, R), "token_slot")
+    _shape(is_token_in_rank, (T, R), "is_token_in_rank")
+    _at_least(num_tokens_per_rank, R, "num_tokens_per_rank")
+    _at_least(rank_offset, R + 1, "rank_offset")
+    _at_least(num_tokens_per_node, N, "num_tokens_per_node")
+    _at_least(num_tokens_per_expert, E, "num_tokens_per_expert")
+    _at_least(expert_offset, E + 1, "expert_offset")
+    _shape(recv_x, (cap, H), "recv_x")
+    _shape(recv_topk_idx, (cap, k), "recv_topk_idx")
+    _shape(recv_topk_weights, (cap, k), "recv_topk_weights")
+    _shape(recv_src_idx, (cap,), "recv_src_idx")
+    _at_least(error_flag, 1, "error_flag")
+    P, Tmax = 0, 0
+    if prob is not None:
+        if prob.dim() != 3 or prob_dest_major is None or prob_dest_major.dim() != 3:
+            raise ValueError("prob must be [T][N][P] and prob_dest_major [N][Tmax][P]")
+        Tp, Np, P = prob.shape
+        Nd, Tmax, Pd = prob_dest_major.shape
+        if Tp != T or Np != N or Nd != N or Pd != P:
+            raise ValueError("prob / prob_dest_major do not match the batch")
+    _check(load().ep_layout_dispatch(
+        _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int64, "topk_idx"),
+        _ptr(topk_weights, torch.float32, "topk_weights", True), T, H, k, E, R, N,
+        _ptr(num_tokens_per_rank, torch.int32, "num_tokens_per_rank"),
+        _ptr(rank_offset, torch.int32, "rank_offset"),
+        _ptr(num_tokens_per_node, torch.int32, "num_tokens_per_node", True),
+        _ptr(num_tokens_per_expert, torch.int32, "num_tokens_per_expert", True),
+        _ptr(expert_offset, torch.int32, "expert_offset", True),
+        _ptr(token_slot, torch.int32, "token_slot"),
+        _ptr(is_token_in_rank, torch.uint8, "is_token_in_rank", True),
+        _ptr(recv_x, torch.bfloat16, "recv_x"),
+        _ptr(recv_topk_idx, torch.int64, "recv_topk_idx", True),
+        _ptr(recv_topk_weights, torch.float32, "recv_topk_weights", True),
+        _ptr(recv_src_idx, torch.int32, "recv_src_idx", True), cap,
+        _ptr(prob, torch.float32, "prob", True), P, Tmax,
+        _ptr(prob_dest_major, torch.float32, "prob_dest_major", True),
+        _ptr(error_flag, torch.int32, "error_flag"), _stream(stream)), "ep_layout_dispatch")
 
 
 def ep_dispatch_permute_layout(x, topk_idx, topk_weights, num_experts: int, num_ranks: int,

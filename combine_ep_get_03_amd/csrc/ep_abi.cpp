@@ -14,6 +14,10 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
 
 // Topology sizes shared by layout and dispatch.
+static_assert(EP_LAYOUT_DISPATCH_MAX_TOKENS == ep::kLayoutBlockTokens,
+              "ep_layout_dispatch covers one block of the layout");
+static_assert(EP_COUNTS_MAX_RANKS == ep::kCountsMaxRanks, "one rank mask word per token");
+
 bool topology_ok(int k, int E, int R, int N) {
     if (E < 1 || E > EP_MAX_EXPERTS || R < 1 || R > EP_MAX_RANKS || N < 1) return false;
     if (E % R != 0 || R % N != 0) return false;
@@ -243,6 +247,50 @@ int ep_dispatch_layout(const void* x, const int64_t* topk_idx, const float* topk
         x, topk_idx, topk_weights, T, H, k, E, R, N, cw, token_slot, is_token_in_rank, recv_x,
         recv_topk_idx, recv_topk_weights, recv_src_idx, recv_capacity, num_tokens_per_rank,
         rank_offset, num_tokens_per_node, num_tokens_per_expert, expert_offset, error_flag,
+        static_cast<hipStream_t>(stream)));
+}
+
+int ep_layout_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                       int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                       int num_ranks, int num_nodes, int32_t* num_tokens_per_rank,
+                       int32_t* rank_offset, int32_t* num_tokens_per_node,
+                       int32_t* num_tokens_per_expert, int32_t* expert_offset,
+                       int32_t* token_slot, uint8_t* is_token_in_rank, void* recv_x,
+                       int64_t* recv_topk_idx, float* recv_topk_weights, int32_t* recv_src_idx,
+                       int64_t recv_capacity, const float* prob, int prob_per_token,
+                       int64_t max_tokens_per_rank, float* prob_dest_major, int32_t* error_flag,
+                       void* stream) {
+    const int64_t T = num_tokens, Tmax = max_tokens_per_rank;
+    const int H = hidden, k = num_topk, E = num_experts, R = num_ranks, N = num_nodes;
+    const int P = prob_per_token;
+    if (!topology_ok(k, E, R, N) || R > EP_COUNTS_MAX_RANKS || T < 0 ||
+        T > EP_LAYOUT_DISPATCH_MAX_TOKENS || H < 1 || recv_capacity < 0)
+        return EP_ERR_ARG;
+    if (H % 8 != 0) return EP_ERR_ALIGN;
+    if (!error_flag) return EP_ERR_ARG;
+    if (T > 0) {
+        if (!x || !topk_idx || !token_slot || !recv_x || !num_tokens_per_rank || !rank_offset)
+            return EP_ERR_ARG;
+        if (recv_topk_weights && !topk_weights) return EP_ERR_ARG;
+    }
+    if (prob) {
+        if (P < 1 || static_cast<int64_t>(N) * P > (1 << 26)) return EP_ERR_ARG;
+        if (T > 0 && !prob_dest_major) return EP_ERR_ARG;
+    }
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 8) ||
+        !aligned(topk_weights, 4) || !aligned(token_slot, 4) || !aligned(recv_topk_idx, 8) ||
+        !aligned(recv_topk_weights, 4) || !aligned(recv_src_idx, 4) || !aligned(error_flag, 4) ||
+        !aligned(num_tokens_per_node, 4) || !aligned(num_tokens_per_expert, 4) ||
+        !aligned(expert_offset, 4) || !aligned(num_tokens_per_rank, 4) ||
+        !aligned(rank_offset, 4) || !aligned(prob, 4) || !aligned(prob_dest_major, 4))
+        return EP_ERR_ALIGN;
+    if (prob && Tmax < T) return EP_ERR_CAPACITY;
+    ep::RestripeTask rs{};
+    if (prob && T > 0) rs = ep::plan_restripe(prob, T, N, P, Tmax, prob_dest_major);
+    return hip_status(ep::launch_layout_dispatch(
+        x, topk_idx, topk_weights, T, H, k, E, R, N, &rs, num_tokens_per_rank, rank_offset,
+        num_tokens_per_node, num_tokens_per_expert, expert_offset, token_slot, is_token_in_rank,
+        recv_x, recv_topk_idx, recv_topk_weights, recv_src_idx, recv_capacity, error_flag,
         static_cast<hipStream_t>(stream)));
 }
 

@@ -198,13 +198,24 @@ struct CountsWorkspace {
 size_t counts_workspace_bytes(int64_t T, int E, int R, int N);
 CountsWorkspace carve_counts_workspace(void* base, int64_t T, int E, int R, int N);
 
-// Zero fill of up to five int32 arrays (NULL ones skipped) with a kernel, so that the
+// Zero fill of up to six int32 arrays (NULL ones skipped) with a kernel, so that the
 // fill can be captured into a graph.
+constexpr int kZeroArrays = 6;
 struct ZeroInts {
-    int32_t* p[5];
-    int n[5];
+    int32_t* p[kZeroArrays];
+    int n[kZeroArrays];
 };
 hipError_t launch_zero_ints(const ZeroInts& z, hipStream_t stream);
+
+// layout.hip: the layout, the dispatch and (with rs) the restripe of a batch of at most
+// one 256-token group (R <= kCountsMaxRanks) in one launch.
+hipError_t launch_layout_dispatch(const void* x, const int64_t* topk_idx, const float* topk_w,
+                                  int64_t T, int H, int k, int E, int R, int N,
+                                  const RestripeTask* rs, int32_t* count_r, int32_t* rank_offset,
+                                  int32_t* count_n, int32_t* count_e, int32_t* expert_offset,
+                                  int32_t* token_slot, uint8_t* in_rank, void* recv_x,
+                                  int64_t* recv_idx, float* recv_w, int32_t* recv_src,
+                                  int64_t cap, int32_t* error_flag, hipStream_t stream);
 
 // Batches of at most this many 256-token blocks take the counts path without a ticket:
 // each dispatch wave sums the per-block rank counts it needs itself (one load per block

@@ -26,6 +26,7 @@
 #include <atomic>
 #include <mutex>
 
+#include "dispatch_rows.hpp"
 #include "ep_internal.hpp"
 
 namespace ep {
@@ -499,23 +500,23 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
 }
 
 // The whole layout of a batch of at most one 256-token group (up to 256 tokens, R <= 256)
-// in one block and one launch: the counts, offsets and slots need no cross-block
-// exchange, so the count and slot kernels collapse into one, with block barriers only.
-// Same outputs as the two-launch path; the expert-major slots (when asked for) still take
-// the expert-slot launch, whose per-block base is then the expert offset itself.
+// in one block: the counts, offsets and slots need no cross-block exchange, so the count
+// and slot kernels collapse into one, with block barriers only. Same outputs as the
+// two-launch path; the expert-major slots (when asked for) still take the expert-slot
+// launch, whose per-block base is then the expert offset itself. With flag_first the
+// block clears the error flag as it starts and ORs its bit in at the end (other blocks of
+// the launch may raise bits meanwhile); else it stores the flag once at the end.
 template <int NW>
-__global__ __launch_bounds__(kBT) void layout_single_kernel(
+__device__ __forceinline__ void layout_single_block(
     const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int N, FastDiv er,
     FastDiv rpn, int32_t* __restrict__ count_r, int32_t* __restrict__ count_n,
     int32_t* __restrict__ count_e, int32_t* __restrict__ rank_offset,
     int32_t* __restrict__ expert_offset, int32_t* __restrict__ error_flag,
     int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank, int vec_out,
     int32_t* __restrict__ exp_base, int32_t* __restrict__ node_slot, int vec_node,
-    RestripeTask rs) {
-    if (blockIdx.x >= 1) {  // a dense restripe riding along (see layout_count_kernel)
-        restripe_task_block(rs, static_cast<int64_t>(blockIdx.x) - 1);
-        return;
-    }
+    bool flag_first) {
+    if (flag_first && threadIdx.x == 0)
+        __hip_atomic_store(error_flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     extern __shared__ int32_t s_hist[];                        // [E]
     __shared__ uint64_t s_ball[kWavesBT * kFusedMaxRanks];     // [4][R]
     __shared__ uint64_t s_nball[kWavesBT * kFusedMaxRanks];    // [4][N]
@@ -580,7 +581,12 @@ __global__ __launch_bounds__(kBT) void layout_single_kernel(
     }
     if (tid == 0 && expert_offset) expert_offset[E] = carry;
     const int any_bad = __syncthreads_or(bad);  // also orders the slot bases before the reads
-    if (tid == 0) *error_flag = any_bad ? kErrTopkRange : 0;
+    if (tid == 0) {
+        if (!flag_first)
+            *error_flag = any_bad ? kErrTopkRange : 0;
+        else if (any_bad)
+            raise_error(error_flag, kErrTopkRange);
+    }
 
 #pragma unroll
     for (int q = 0; q < kWavesBT; ++q) {
@@ -590,6 +596,24 @@ __global__ __launch_bounds__(kBT) void layout_single_kernel(
             write_wave_slots(s_nball + q * N, s_nbase + q * N, T, q * kWave, N, vec_node != 0,
                              node_slot, nullptr);
     }
+}
+
+template <int NW>
+__global__ __launch_bounds__(kBT) void layout_single_kernel(
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int N, FastDiv er,
+    FastDiv rpn, int32_t* __restrict__ count_r, int32_t* __restrict__ count_n,
+    int32_t* __restrict__ count_e, int32_t* __restrict__ rank_offset,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ error_flag,
+    int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank, int vec_out,
+    int32_t* __restrict__ exp_base, int32_t* __restrict__ node_slot, int vec_node,
+    RestripeTask rs) {
+    if (blockIdx.x >= 1) {  // a dense restripe riding along (see layout_count_kernel)
+        restripe_task_block(rs, static_cast<int64_t>(blockIdx.x) - 1);
+        return;
+    }
+    layout_single_block<NW>(topk_idx, T, k, E, R, N, er, rpn, count_r, count_n, count_e,
+                            rank_offset, expert_offset, error_flag, token_slot, in_rank, vec_out,
+                            exp_base, node_slot, vec_node, false);
 }
 
 // Columns [c0, c0+width) of a [rows][cols] int32 matrix, one column per thread
@@ -1119,9 +1143,120 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
     }
 }
 
+// ------------------------------------------------------- layout + dispatch in one launch
+// ep_layout_dispatch: the layout, the dispatch and the restripe of a batch of at most one
+// 256-token group in one launch, no block waiting for another.
+// - Block 0 is the single-group layout (layout_single_block): counts, offsets, token_slot
+//   and the bitmap. It clears the error flag as it starts.
+// - Blocks 1 .. ndisp each hold four (token, destination) waves of the dispatch, as
+//   dispatch_layout_kernel's. A block recomputes the group's rank masks and each wave's
+//   rank ballots in LDS while its rows' loads are in flight (the ids are 16 KiB at top-8
+//   and are L2 hits after the first blocks), and forms its receive rows from them: rank r's offset is
+//   the scan of the group's rank totals across the wave, and a token's row on r adds the
+//   group's tokens before it on r, the same rows the layout block writes to token_slot.
+// - The blocks after those run the dense restripe.
+// This replaces the counts path's count launch for such a batch: its fixed cost is the
+// largest part of a decode-sized step.
+template <int WPL, bool kMulti>
+__global__ __launch_bounds__(kBT) void layout_dispatch_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int64_t T, int V, int k, int E, int R, int N, FastDiv er,
+    FastDiv rpn, FastDiv D, int ndisp, RestripeTask rs, int32_t* __restrict__ count_r,
+    int32_t* __restrict__ count_n, int32_t* __restrict__ count_e,
+    int32_t* __restrict__ rank_offset, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank, int vec_out,
+    u32x4* __restrict__ recv_x, int64_t* __restrict__ recv_idx, float* __restrict__ recv_w,
+    int32_t* __restrict__ recv_src, int64_t cap, int32_t* __restrict__ error_flag) {
+    const int b = blockIdx.x;
+    if (b == 0) {
+        layout_single_block<1>(topk_idx, T, k, E, R, N, er, rpn, count_r, count_n, count_e,
+                               rank_offset, expert_offset, error_flag, token_slot, in_rank,
+                               vec_out, nullptr, nullptr, 0, true);
+        return;
+    }
+    if (b > ndisp) {
+        restripe_task_block(rs, static_cast<int64_t>(b - 1 - ndisp));
+        return;
+    }
+    __shared__ uint64_t s_mask[kBT];                          // each token's rank mask
+    __shared__ uint64_t s_wball[kWavesBT * kCountsMaxRanks];  // [4][R] rank ballots per wave
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = lane_id();
+    int64_t t;
+    int d;
+    // a wave past the batch still computes its share of the masks and meets the barrier
+    const bool live = dest_wave_at((b - 1) * kWavesBT + wave, 0, T, D, t, d);
+    if (!live) t = 0;
+    // Thread i forms token i's rank mask. Its first kBatch ids are loaded before the row's
+    // first pass, unconditionally at clamped indices (out-of-range ones are ignored below),
+    // so the mask is formed while the row is still in flight.
+    const int ti = min(tid, static_cast<int>(T) - 1);
+    const int64_t* ids = topk_idx + static_cast<int64_t>(ti) * k;
+    int64_t ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) ev[u] = ids[min(u, k - 1)];
+    const Routing rt(topk_idx + t * k, topk_w ? topk_w + t * k : nullptr, k, recv_idx || recv_w);
+    const u32x4* xr = x + t * V;
+    u32x4 v[WPL];
+    load_row_cached(v, xr, 0, V);  // first pass
+    uint64_t rm[1] = {0};
+    const bool own = tid < T;
+    auto add_id = [&](int64_t e, bool use) {
+        if (use && e >= 0 && e < E) rm[0] |= 1ull << er.div(static_cast<int>(e));
+    };
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) add_id(ev[u], own && u < k);
+    for (int j0 = kBatch; j0 < k; j0 += kBatch) {  // top-k beyond kBatch: the rest in turn
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) ev[u] = ids[min(j0 + u, k - 1)];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) add_id(ev[u], own && j0 + u < k);
+    }
+    s_mask[tid] = rm[0];
+    wave_ballots<1, false>(rm, R, s_wball + wave * R);
+    __syncthreads();
+    if (!live) return;
+    const int wt = static_cast<int>(t) / kWave, lt = static_cast<int>(t) % kWave;
+    int tot = 0, before = 0;  // lane r: the group's tokens on r, and those before t
+    if (lane < R) {
+#pragma unroll
+        for (int w = 0; w < kWavesBT; ++w) {
+            const uint64_t bl = s_wball[w * R + lane];
+            const int c = __popcll(bl);
+            tot += c;
+            if (w < wt) before += c;
+            else if (w == wt) before += __popcll(bl & ((1ull << lt) - 1ull));
+        }
+    }
+    int xs = tot;  // inclusive scan of the totals across the wave
+    for (int s = 1; s < kWave; s <<= 1) {
+        const int y = __shfl_up(xs, s, kWave);
+        if (lane >= s) xs += y;
+    }
+    const uint64_t m = s_mask[t];
+    const bool on = lane < R && ((m >> lane) & 1ull);
+    const int32_t slot = on ? xs - tot + before : -1;
+    uint64_t rest = m;  // the token's d-th destination rank, ascending
+    for (int i = 0; i < d && rest; ++i) rest &= rest - 1;
+    if (!rest) return;
+    const int rd = __builtin_ctzll(rest);
+    const int64_t sd = __builtin_amdgcn_readlane(slot, rd);
+    if (sd >= cap) {
+        if (lane == 0) raise_error(error_flag, kErrRecvOverflow);
+        return;
+    }
+    for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
+        if (v0 != 0) load_row_cached(v, xr, v0, V);
+        put_row<WPL, true>(v, v0, V, sd, rd, rt, er.d, static_cast<int32_t>(t), recv_x, recv_idx,
+                           recv_w, recv_src);
+        if constexpr (!kMulti) break;
+    }
+}
+
 __global__ __launch_bounds__(kBT) void zero_ints_kernel(ZeroInts z) {
 #pragma unroll
-    for (int a = 0; a < 5; ++a)
+    for (int a = 0; a < kZeroArrays; ++a)
         for (int i = threadIdx.x; i < z.n[a]; i += kBT) z.p[a][i] = 0;
 }
 
@@ -1130,7 +1265,7 @@ __global__ __launch_bounds__(kBT) void zero_ints_kernel(ZeroInts z) {
 hipError_t launch_zero_ints(const ZeroInts& z_in, hipStream_t stream) {
     ZeroInts z = z_in;
     int total = 0;
-    for (int a = 0; a < 5; ++a) {
+    for (int a = 0; a < kZeroArrays; ++a) {
         if (!z.p[a]) z.n[a] = 0;
         total += z.n[a];
     }
@@ -1267,6 +1402,42 @@ hipError_t launch_layout_counts(const int64_t* topk_idx, int64_t T, int k, int E
                            topk_idx, T, k, E, R, N, er, rpn, cw, static_cast<int>(nb), rs,
                            error_flag, expert_rank);
     return hipGetLastError();
+}
+
+
+hipError_t launch_layout_dispatch(const void* x, const int64_t* topk_idx, const float* topk_w,
+                                  int64_t T, int H, int k, int E, int R, int N,
+                                  const RestripeTask* rs_in, int32_t* count_r,
+                                  int32_t* rank_offset, int32_t* count_n, int32_t* count_e,
+                                  int32_t* expert_offset, int32_t* token_slot, uint8_t* in_rank,
+                                  void* recv_x, int64_t* recv_idx, float* recv_w,
+                                  int32_t* recv_src, int64_t cap, int32_t* error_flag,
+                                  hipStream_t stream) {
+    if (T == 0) {  // an empty batch: no error, zero counts and offsets, nothing to move
+        const ZeroInts z{{error_flag, count_r, rank_offset, count_n, count_e, expert_offset},
+                         {1, R, R + 1, N, E, E + 1}};
+        return launch_zero_ints(z, stream);
+    }
+    if (T > kBT || R > kCountsMaxRanks) return hipErrorInvalidValue;
+    RestripeTask rs{};
+    if (rs_in != nullptr) rs = *rs_in;
+    const int V = H / 8;
+    const int D = std::min(k, R);  // waves per token
+    const int ndisp = static_cast<int>((T * D + kWavesBT - 1) / kWavesBT);
+    if (!grid_fits(1 + ndisp + rs.blocks, kBT)) return hipErrorInvalidConfiguration;
+    const bool vec = R % 4 == 0 && reinterpret_cast<uintptr_t>(token_slot) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(in_rank) % 4 == 0;
+    const FastDiv er = FastDiv::make(E / R), rpn = FastDiv::make(R / N), fd = FastDiv::make(D);
+    const dim3 grid(static_cast<unsigned>(1 + ndisp + rs.blocks));
+    const size_t shm = sizeof(int32_t) * static_cast<size_t>(E);
+    return with_row_width<14, false>(V, [&](auto wpl, auto multi) {
+        hipLaunchKernelGGL((layout_dispatch_kernel<decltype(wpl)::value, decltype(multi)::value>),
+                           grid, dim3(kBT), shm, stream, static_cast<const u32x4*>(x), topk_idx,
+                           topk_w, T, V, k, E, R, N, er, rpn, fd, ndisp, rs, count_r, count_n,
+                           count_e, rank_offset, expert_offset, token_slot, in_rank, vec ? 1 : 0,
+                           static_cast<u32x4*>(recv_x), recv_idx, recv_w, recv_src, cap,
+                           error_flag);
+    });
 }
 
 }  // namespace ep

@@ -2,11 +2,12 @@
 outputs:
 - the counts path (R <= EP_COUNTS_MAX_RANKS): ep_layout_counts (counts, offsets and the
   restripe in one launch), ep_dispatch_layout (the dispatch computing the receive rows and
-  writing the slot table), ep_combine;
+  writing the slot table), ep_combine; for a batch of at most
+  EP_LAYOUT_DISPATCH_MAX_TOKENS tokens the first two are one call, ep_layout_dispatch;
 - the preprocess path: ep_dispatch_preprocess (layout and restripe in one call),
   ep_dispatch, ep_combine;
 - one call per step: ep_get_layout, ep_dispatch, ep_restripe_prob, ep_combine.
-`step()` takes the counts path where it applies. Also the two-phase ("hook") form of
+`step()` takes the one-call layout + dispatch or the counts path where they apply. Also the two-phase ("hook") form of
 dispatch and combine, whose send phase returns a callable that enqueues the receive phase
 later.
 
@@ -98,12 +99,38 @@ class Path:
                                               self.prob_dest_major, stream=stream)
 
     def step(self, b: DeviceBatch, stream=None) -> None:
-        """The whole path on one batch: step_counts() where R allows it and the Path keeps
-        no node slots, else step_preprocess()."""
-        if self.counts_path:
+        """The whole path on one batch: where R allows it and the Path keeps no node slots,
+        step_small() for a batch of at most EP_LAYOUT_DISPATCH_MAX_TOKENS tokens and
+        step_counts() for a larger one; else step_preprocess()."""
+        if self.counts_path and 0 < self.T <= B.EP_LAYOUT_DISPATCH_MAX_TOKENS:
+            self.step_small(b, stream)
+        elif self.counts_path:
             self.step_counts(b, stream)
         else:
             self.step_preprocess(b, stream)
+
+    def step_small(self, b: DeviceBatch, stream=None) -> None:
+        """The same outputs as step_counts() in two launches: ep_layout_dispatch (layout,
+        dispatch and restripe), ep_combine. Needs T <= EP_LAYOUT_DISPATCH_MAX_TOKENS and
+        R <= EP_COUNTS_MAX_RANKS."""
+        self.layout_dispatch(b, stream)
+        self.combine(b, stream)
+
+    def layout_dispatch(self, b: DeviceBatch, stream=None) -> None:
+        """Layout, dispatch and restripe of a batch of at most EP_LAYOUT_DISPATCH_MAX_TOKENS
+        tokens in one launch."""
+        lb, r = self.layout_buf, self.recv
+        B.ep_layout_dispatch(b.x, b.topk_idx, b.topk_weights, self.E, self.R, self.N,
+                             token_slot=lb.token_slot, recv_x=r.recv_x,
+                             num_tokens_per_rank=lb.num_tokens_per_rank,
+                             rank_offset=lb.rank_offset, error_flag=self.error_flag,
+                             is_token_in_rank=lb.is_token_in_rank,
+                             num_tokens_per_node=lb.num_tokens_per_node,
+                             num_tokens_per_expert=lb.num_tokens_per_expert,
+                             expert_offset=lb.expert_offset, recv_topk_idx=r.recv_topk_idx,
+                             recv_topk_weights=r.recv_topk_weights,
+                             recv_src_idx=r.recv_src_idx, prob=b.prob,
+                             prob_dest_major=self.prob_dest_major, stream=stream)
 
     def step_preprocess(self, b: DeviceBatch, stream=None) -> None:
         """Layout and restripe (one call), dispatch, combine."""

@@ -82,6 +82,7 @@ enum {
 #define EP_EXPERT_SLOT_MAX_K 16  /* largest top-k for which ep_get_layout fills expert_slot */
 #define EP_LAYOUT_SCRATCH_BYTES 4194304  /* device scratch of ep_get_layout_no_alloc (4 MiB) */
 #define EP_COUNTS_MAX_RANKS 64  /* largest num_ranks of ep_layout_counts / ep_dispatch_layout */
+#define EP_LAYOUT_DISPATCH_MAX_TOKENS 256  /* largest batch of ep_layout_dispatch */
 
 /* Static string for a status code; never NULL. */
 const char *ep_status_string(int status);
@@ -239,6 +240,35 @@ int ep_dispatch_layout(const void *x, const int64_t *topk_idx, const float *topk
                        int64_t *recv_topk_idx, float *recv_topk_weights, int32_t *recv_src_idx,
                        int64_t recv_capacity, int32_t *error_flag, const void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* ep_layout_dispatch -- the layout, the dispatch and (with prob) the restripe of a batch of
+ * at most EP_LAYOUT_DISPATCH_MAX_TOKENS tokens in one kernel launch, so that a decode-sized
+ * step is this call and ep_combine. It computes get_dispatch_layout and then the dispatch
+ * ("[PR #347] Feature/sm free normal kernel": commit list, and section 3.2.1 for the
+ * dispatch's payload) and the restripe that replaces dispatch_preprocess's copy ("[PR #634]
+ * Hybrid ep nixl restripe", section "Fix"). Outputs, bit for bit those of ep_get_layout +
+ * ep_dispatch (+ ep_restripe_prob) with the same meanings: num_tokens_per_rank [R],
+ * rank_offset [R+1], token_slot [T][R] and recv_x (all required when T > 0);
+ * is_token_in_rank [T][R], num_tokens_per_node [N], num_tokens_per_expert [E],
+ * expert_offset [E+1], recv_topk_idx, recv_topk_weights, recv_src_idx (nullable); with
+ * prob non-NULL, prob_dest_major as ep_restripe_prob(prob, T, num_nodes, prob_per_token,
+ * max_tokens_per_rank). error_flag [1] is overwritten: 0, or EP_DEVERR_TOPK_RANGE and
+ * EP_DEVERR_RECV_OVERFLOW as ep_get_layout and ep_dispatch set them (rows past
+ * recv_capacity are skipped). Each block of the launch recomputes the batch's rank masks
+ * from topk_idx, so no block waits for another.
+ * Sizes: 0 <= T <= EP_LAYOUT_DISPATCH_MAX_TOKENS, num_ranks <= EP_COUNTS_MAX_RANKS, the
+ *   rest as ep_get_layout and ep_dispatch; with prob as ep_restripe_prob (EP_ERR_CAPACITY
+ *   for Tmax < T). Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_CAPACITY, EP_ERR_HIP. */
+int ep_layout_dispatch(const void *x, const int64_t *topk_idx, const float *topk_weights,
+                       int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                       int num_ranks, int num_nodes, int32_t *num_tokens_per_rank,
+                       int32_t *rank_offset, int32_t *num_tokens_per_node,
+                       int32_t *num_tokens_per_expert, int32_t *expert_offset,
+                       int32_t *token_slot, uint8_t *is_token_in_rank, void *recv_x,
+                       int64_t *recv_topk_idx, float *recv_topk_weights, int32_t *recv_src_idx,
+                       int64_t recv_capacity, const float *prob, int prob_per_token,
+                       int64_t max_tokens_per_rank, float *prob_dest_major, int32_t *error_flag,
+                       void *stream);
 
 /* ep_dispatch_permute_layout -- the counts path's dispatch + permute ("[PR #634] Hybrid ep
  * nixl restripe" measures "dispatch+permute"; its commit list names the scan over tokens

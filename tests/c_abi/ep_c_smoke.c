@@ -1,8 +1,10 @@
 /* ep_c_smoke.c -- a plain C consumer of the C ABI in include/ep.h (no Python, no torch):
- * device buffers from the HIP runtime, one batch through the path on one stream in two
+ * device buffers from the HIP runtime, one batch through the path on one stream in three
  * forms -- ep_get_layout, ep_dispatch, ep_restripe_prob, ep_combine; then the counts path,
- * ep_layout_counts (with the restripe), ep_dispatch_layout, ep_combine -- each time with the
- * outputs pre-filled with a sentinel, copied back and compared bit for bit with the CPU
+ * ep_layout_counts (with the restripe), ep_dispatch_layout, ep_combine; then
+ * ep_layout_dispatch (layout, dispatch and restripe in one launch), ep_combine -- each
+ * time with the outputs pre-filled with a sentinel, copied back and compared bit for bit
+ * with the CPU
  * oracle (TEST INFRASTRUCTURE, linked only into this test program).
  *
  * Inputs: T = 256 tokens, hidden 1024, 16 experts, top-4 distinct experts per token,
@@ -133,7 +135,7 @@ int main(void) {
     static float rw[T * K * K];
     static uint32_t prob_out[N * TMAX * P];
     int ok = 1;
-    for (int form = 0; form < 2; ++form) {
+    for (int form = 0; form < 3; ++form) {
         /* outputs pre-filled with a sentinel, so an element left unwritten shows */
         HIP_OK(hipMemset(d_cr, 0xAB, sizeof(int32_t) * R));
         HIP_OK(hipMemset(d_cn, 0xAB, sizeof(int32_t) * N));
@@ -158,12 +160,17 @@ int main(void) {
             EP_OK_(ep_dispatch(d_x, d_idx, d_w, T, H, K, E, R, d_slot, d_recv_x, d_ridx, d_rw, d_src,
                                cap, d_err, st));
             EP_OK_(ep_restripe_prob((const float *)d_prob, T, N, P, TMAX, (float *)d_prob_out, st));
-        } else {
+        } else if (form == 1) {
             EP_OK_(ep_layout_counts(d_idx, T, K, E, R, N, d_err, NULL, (const float *)d_prob, P,
                                     TMAX, (float *)d_prob_out, d_cws, cws_bytes, st));
             EP_OK_(ep_dispatch_layout(d_x, d_idx, d_w, T, H, K, E, R, N, d_cr, d_ro, d_cn, d_ce, d_eo,
                                       d_slot, d_in, d_recv_x, d_ridx, d_rw, d_src, cap, d_err,
                                       d_cws, cws_bytes, st));
+        } else {
+            EP_OK_(ep_layout_dispatch(d_x, d_idx, d_w, T, H, K, E, R, N, d_cr, d_ro, d_cn, d_ce, d_eo,
+                                      d_slot, d_in, d_recv_x, d_ridx, d_rw, d_src, cap,
+                                      (const float *)d_prob, P, TMAX, (float *)d_prob_out, d_err,
+                                      st));
         }
         EP_OK_(ep_combine(d_partial, cap, d_slot, T, H, R, d_out, d_err, st));
         HIP_OK(hipStreamSynchronize(st));
@@ -184,7 +191,7 @@ int main(void) {
         HIP_OK(hipMemcpy(prob_out, d_prob_out, sizeof prob_out, hipMemcpyDeviceToHost));
         HIP_OK(hipMemcpy(out, d_out, sizeof out, hipMemcpyDeviceToHost));
 
-        const char *name = form == 0 ? "four calls" : "counts path";
+        const char *name = form == 0 ? "four calls" : form == 1 ? "counts path" : "one launch";
         int f_ok = 1;
         f_ok &= err == 0 && o_err == 0;
         f_ok &= same("num_tokens_per_rank", cr, o_cr, sizeof cr);

@@ -53,29 +53,31 @@ def oracle_all(cfg: W.Config, inp: W.Inputs, partial_rows=None) -> dict:
 
 STEP_FORMS = {"separate": "one call per step", "preprocess": "layout+restripe in one call",
               "counts": "counts path (two launches for layout and dispatch)",
+              "small": "layout, dispatch and restripe in one launch (T <= 256)",
               "step": "Path.step (the counts path where R allows it)"}
 
 
 def run_gpu(cfg: W.Config, inp: W.Inputs, device="cuda", fused: bool = True,
             form: str = None) -> Path:
     """One step of the path: form "step" (Path.step; the default), "preprocess" (layout and
-    restripe in one call, ep_dispatch_preprocess), "separate" (one call per step), or
-    "counts" (ep_layout_counts + ep_dispatch_layout)."""
+    restripe in one call, ep_dispatch_preprocess), "separate" (one call per step), "counts"
+    (ep_layout_counts + ep_dispatch_layout) or "small" (ep_layout_dispatch)."""
     form = form or ("step" if fused else "separate")
     b = DeviceBatch.from_host(inp.topk_idx, inp.topk_weights, inp.x, inp.prob, inp.partials,
                               device=device)
     path = Path(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.N, cfg.P, cfg.Tmax, device=device)
     fill_sentinels(path)
     {"step": path.step, "preprocess": path.step_preprocess, "separate": path.step_separate,
-     "counts": path.step_counts}[form](b)
+     "counts": path.step_counts, "small": path.step_small}[form](b)
     torch.cuda.synchronize()
     return path
 
 
 def run_and_compare_both(cfg: W.Config, inp: W.Inputs, ref: dict, expect_flag: int = 0) -> Path:
-    """The step in every form (the counts path where R allows it): each must match the
-    oracle. Returns the last path."""
+    """The step in every form (the counts path where R allows it, and the one-launch layout
+    and dispatch where T does too): each must match the oracle. Returns the last path."""
     forms = ["separate", "preprocess"] + (["counts"] if cfg.R <= 64 else [])
+    forms += ["small"] if cfg.R <= 64 and 0 < cfg.T <= 256 else []
     for form in forms:
         print(f"  {STEP_FORMS[form]}", flush=True)
         path = run_gpu(cfg, inp, form=form)

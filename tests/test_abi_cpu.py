@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "ep_layout_workspace_bytes", "ep_status_string", "ep_hbm_copy",
                           "ep_dispatch_fp8", "ep_dispatch_permute", "ep_restripe_prob_sparse",
                           "ep_dispatch_send", "ep_dispatch_recv", "ep_combine_send",
-                          "ep_combine_recv"}
+                          "ep_combine_recv", "ep_layout_dispatch"}
     out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (ep_\w+)", out))
@@ -220,6 +220,43 @@ def test_counts_path_validation(lib):
     assert perm(x=MIS) == ep.EP_ERR_ALIGN
     assert perm(es=P(0x10002)) == ep.EP_ERR_ALIGN
     assert perm(wsb=16) == ep.EP_ERR_CAPACITY
+
+
+def test_layout_dispatch_validation(lib):
+    # the one-launch layout + dispatch: at most 256 tokens, R <= 64; counts and offsets required
+    assert ep.EP_LAYOUT_DISPATCH_MAX_TOKENS == 256
+
+    def ld(T=10, H=64, k=2, E=8, R=4, N=2, x=A16, idx=A16, w=A16, cr=A16, ro=A16, slot=A16,
+           rx=A16, rw=A16, cap=100, prob=None, P=8, Tmax=10, out=None, flag=A16):
+        return lib.ep_layout_dispatch(x, idx, w, T, H, k, E, R, N, cr, ro, A16, A16, A16, slot,
+                                      A16, rx, A16, rw, A16, cap, prob, P, Tmax, out, flag, None)
+    assert ld(T=257) == ep.EP_ERR_ARG                           # past one 256-token group
+    assert ld(T=-1) == ep.EP_ERR_ARG
+    assert ld(E=256, R=128, N=4) == ep.EP_ERR_ARG               # R > 64
+    assert ld(E=15) == ep.EP_ERR_ARG
+    assert ld(N=3) == ep.EP_ERR_ARG
+    assert ld(k=0) == ep.EP_ERR_ARG
+    assert ld(cap=-1) == ep.EP_ERR_ARG
+    assert ld(flag=None) == ep.EP_ERR_ARG
+    assert ld(cr=None) == ep.EP_ERR_ARG
+    assert ld(ro=None) == ep.EP_ERR_ARG
+    assert ld(slot=None) == ep.EP_ERR_ARG
+    assert ld(rx=None) == ep.EP_ERR_ARG
+    assert ld(idx=None) == ep.EP_ERR_ARG
+    assert ld(x=None) == ep.EP_ERR_ARG
+    assert ld(w=None) == ep.EP_ERR_ARG                          # weights asked for, none given
+    assert ld(H=12) == ep.EP_ERR_ALIGN
+    assert ld(x=MIS) == ep.EP_ERR_ALIGN
+    assert ld(rx=MIS) == ep.EP_ERR_ALIGN
+    assert ld(ro=P(0x10002)) == ep.EP_ERR_ALIGN
+    assert ld(flag=P(0x10002)) == ep.EP_ERR_ALIGN
+    assert ld(prob=A16, out=None) == ep.EP_ERR_ARG
+    assert ld(prob=A16, out=A16, P=0) == ep.EP_ERR_ARG
+    assert ld(prob=A16, out=A16, Tmax=9) == ep.EP_ERR_CAPACITY
+    assert ld(prob=P(0x10002), out=A16) == ep.EP_ERR_ALIGN
+    # an empty batch needs no buffers but the flag (its counts are zeroed on the device)
+    assert ld(T=0, x=None, idx=None, w=None, cr=None, ro=None, slot=None, rx=None,
+              rw=None, flag=None) == ep.EP_ERR_ARG
 
 
 def test_dispatch_permute_validation(lib):

@@ -23,3 +23,4 @@ def test_c_program_matches_the_oracle():
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0
     assert "four calls ok" in r.stdout and "counts path ok" in r.stdout
+    assert "one launch ok" in r.stdout
