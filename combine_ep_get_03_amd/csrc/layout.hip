@@ -505,7 +505,8 @@ __global__ __launch_bounds__(kBT) void layout_slot_fused_kernel(
 // two-launch path; the expert-major slots (when asked for) still take the expert-slot
 // launch, whose per-block base is then the expert offset itself. With flag_first the
 // block clears the error flag as it starts and ORs its bit in at the end (other blocks of
-// the launch may raise bits meanwhile); else it stores the flag once at the end.
+// the launch may raise bits meanwhile); else it stores the flag once at the end. With
+// token_slot NULL it writes no slots (nor the bitmap).
 template <int NW>
 __device__ __forceinline__ void layout_single_block(
     const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int N, FastDiv er,
@@ -590,8 +591,9 @@ __device__ __forceinline__ void layout_single_block(
 
 #pragma unroll
     for (int q = 0; q < kWavesBT; ++q) {
-        write_wave_slots(s_ball + q * R, s_base + q * R, T, q * kWave, R, vec_out != 0, token_slot,
-                         in_rank);
+        if (token_slot)
+            write_wave_slots(s_ball + q * R, s_base + q * R, T, q * kWave, R, vec_out != 0,
+                             token_slot, in_rank);
         if (node_slot)
             write_wave_slots(s_nball + q * N, s_nbase + q * N, T, q * kWave, N, vec_node != 0,
                              node_slot, nullptr);
@@ -1146,14 +1148,15 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
 // ------------------------------------------------------- layout + dispatch in one launch
 // ep_layout_dispatch: the layout, the dispatch and the restripe of a batch of at most one
 // 256-token group in one launch, no block waiting for another.
-// - Block 0 is the single-group layout (layout_single_block): counts, offsets, token_slot
-//   and the bitmap. It clears the error flag as it starts.
+// - Block 0 is the single-group layout (layout_single_block) without the slots: counts and
+//   offsets. It clears the error flag as it starts.
 // - Blocks 1 .. ndisp each hold four (token, destination) waves of the dispatch, as
 //   dispatch_layout_kernel's. A block recomputes the group's rank masks and each wave's
 //   rank ballots in LDS while its rows' loads are in flight (the ids are 16 KiB at top-8
 //   and are L2 hits after the first blocks), and forms its receive rows from them: rank r's offset is
 //   the scan of the group's rank totals across the wave, and a token's row on r adds the
-//   group's tokens before it on r, the same rows the layout block writes to token_slot.
+//   group's tokens before it on r. A token's first wave also writes its token_slot and
+//   bitmap rows, which keeps those writes off the layout block, the longest one.
 // - The blocks after those run the dense restripe.
 // This replaces the counts path's count launch for such a batch: its fixed cost is the
 // largest part of a decode-sized step.
@@ -1164,14 +1167,14 @@ __global__ __launch_bounds__(kBT) void layout_dispatch_kernel(
     FastDiv rpn, FastDiv D, int ndisp, RestripeTask rs, int32_t* __restrict__ count_r,
     int32_t* __restrict__ count_n, int32_t* __restrict__ count_e,
     int32_t* __restrict__ rank_offset, int32_t* __restrict__ expert_offset,
-    int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank, int vec_out,
+    int32_t* __restrict__ token_slot, uint8_t* __restrict__ in_rank,
     u32x4* __restrict__ recv_x, int64_t* __restrict__ recv_idx, float* __restrict__ recv_w,
     int32_t* __restrict__ recv_src, int64_t cap, int32_t* __restrict__ error_flag) {
     const int b = blockIdx.x;
-    if (b == 0) {
+    if (b == 0) {  // counts and offsets; the dispatch waves write the slots
         layout_single_block<1>(topk_idx, T, k, E, R, N, er, rpn, count_r, count_n, count_e,
-                               rank_offset, expert_offset, error_flag, token_slot, in_rank,
-                               vec_out, nullptr, nullptr, 0, true);
+                               rank_offset, expert_offset, error_flag, nullptr, nullptr, 0,
+                               nullptr, nullptr, 0, true);
         return;
     }
     if (b > ndisp) {
@@ -1237,6 +1240,10 @@ __global__ __launch_bounds__(kBT) void layout_dispatch_kernel(
     const uint64_t m = s_mask[t];
     const bool on = lane < R && ((m >> lane) & 1ull);
     const int32_t slot = on ? xs - tot + before : -1;
+    if (d == 0 && lane < R) {  // the token's first wave writes its slot row and bitmap row
+        token_slot[t * R + lane] = slot;
+        if (in_rank) in_rank[t * R + lane] = on ? 1 : 0;
+    }
     uint64_t rest = m;  // the token's d-th destination rank, ascending
     for (int i = 0; i < d && rest; ++i) rest &= rest - 1;
     if (!rest) return;
@@ -1425,8 +1432,6 @@ hipError_t launch_layout_dispatch(const void* x, const int64_t* topk_idx, const 
     const int D = std::min(k, R);  // waves per token
     const int ndisp = static_cast<int>((T * D + kWavesBT - 1) / kWavesBT);
     if (!grid_fits(1 + ndisp + rs.blocks, kBT)) return hipErrorInvalidConfiguration;
-    const bool vec = R % 4 == 0 && reinterpret_cast<uintptr_t>(token_slot) % 16 == 0 &&
-                     reinterpret_cast<uintptr_t>(in_rank) % 4 == 0;
     const FastDiv er = FastDiv::make(E / R), rpn = FastDiv::make(R / N), fd = FastDiv::make(D);
     const dim3 grid(static_cast<unsigned>(1 + ndisp + rs.blocks));
     const size_t shm = sizeof(int32_t) * static_cast<size_t>(E);
@@ -1434,7 +1439,7 @@ hipError_t launch_layout_dispatch(const void* x, const int64_t* topk_idx, const 
         hipLaunchKernelGGL((layout_dispatch_kernel<decltype(wpl)::value, decltype(multi)::value>),
                            grid, dim3(kBT), shm, stream, static_cast<const u32x4*>(x), topk_idx,
                            topk_w, T, V, k, E, R, N, er, rpn, fd, ndisp, rs, count_r, count_n,
-                           count_e, rank_offset, expert_offset, token_slot, in_rank, vec ? 1 : 0,
+                           count_e, rank_offset, expert_offset, token_slot, in_rank,
                            static_cast<u32x4*>(recv_x), recv_idx, recv_w, recv_src, cap,
                            error_flag);
     });
