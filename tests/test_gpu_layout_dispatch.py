@@ -204,3 +204,36 @@ def test_graph_replays_match_the_eager_call():
         assert torch.equal(p.layout_buf.token_slot, ref[1])
         assert torch.equal(p.prob_dest_major, ref[2])
         assert int(p.error_flag.item()) == 0
+
+
+def _random_shapes(n=16, seed=4711):
+    """Seeded topologies up to 256 tokens and 64 ranks: ranks off powers of two, odd top-k,
+    ragged T, hidden sizes of one and several passes, uniform or Zipf routing."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.choice([1, 2, 3, 4, 8]))
+        rpn = int(rng.choice([1, 2, 3, 5, 8]))
+        R = N * rpn
+        er = int(rng.choice([1, 2, 3, 4, 8]))
+        E = R * er
+        k = int(rng.integers(1, min(E, 12) + 1))
+        T = int(rng.integers(1, 257))
+        H = int(rng.choice([8, 64, 200, 1024, 7168, 9000]))
+        P = int(rng.integers(1, 40))
+        routing = "zipf" if rng.random() < 0.3 else "uniform"
+        out.append(W.Config(f"ldr{i}_T{T}_H{H}_E{E}_k{k}_R{R}_N{N}", T=T, H=H, E=E, k=k, R=R,
+                            N=N, P=P, Tmax=T + int(rng.integers(0, 20)), routing=routing,
+                            seed=2000 + i))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_shapes(), ids=lambda c: c.name)
+def test_random_shapes(cfg):
+    print(f"\ncase: ep_layout_dispatch random shape {cfg}", flush=True)
+    inp = W.make_inputs(cfg, with_partials=False)
+    prob_out = torch.full((cfg.N, cfg.Tmax, cfg.P), -3.0, dtype=torch.float32, device="cuda")
+    got = _call(cfg, inp, prob_out=prob_out)
+    _check(cfg, inp, got)
+    np.testing.assert_array_equal(host(prob_out).view(np.uint32),
+                                  _restripe_ref(cfg, inp).view(np.uint32))
