@@ -202,6 +202,25 @@ __device__ __forceinline__ void counts_head_block(const CountsWorkspace& cw, int
     }
 }
 
+// glob[b][lane] for a batch of at most kCountsLocalBlocks blocks: the receive row of
+// block b's first token on rank `lane`, from that rank's count in every block (cnt[u],
+// loaded by the caller): the rank's offset (a scan of the rank totals across the wave)
+// plus its counts in the blocks before b.
+__device__ __forceinline__ int32_t local_glob(const int (&cnt)[kCountsLocalBlocks], int64_t b) {
+    int tot = 0, g = 0;
+#pragma unroll
+    for (int u = 0; u < kCountsLocalBlocks; ++u) {
+        tot += cnt[u];
+        if (u < b) g += cnt[u];
+    }
+    int x = tot;  // inclusive scan of the rank totals across the wave
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d, kWave);
+        if (lane_id() >= d) x += y;
+    }
+    return g + x - tot;
+}
+
 // Dispatch of the counts path (R <= 64): the same (token, destination) waves as
 // dispatch_kernel, but the receive rows come from the count launch's tables instead of a
 // token_slot row. Lane r < R holds, for rank r: the receive row of the token's block's
@@ -261,20 +280,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_layout_kernel(
     const u32x4* xr = x + t * V;
     u32x4 v[WPL];
     load_row_cached(v, xr, 0, V);  // first pass, issued with the tables' loads
-    if constexpr (kLocal) {  // the counts arrive with the tables: glob[b][lane] from them
-        int tot = 0;
-#pragma unroll
-        for (int u = 0; u < kCountsLocalBlocks; ++u) {
-            tot += cnt[u];
-            if (u < b) g += cnt[u];
-        }
-        int x = tot;  // inclusive scan of the rank totals across the wave
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int y = __shfl_up(x, d, kWave);
-            if (lane >= d) x += y;
-        }
-        g += x - tot;
-    }
+    if constexpr (kLocal) g = local_glob(cnt, b);  // the counts arrive with the tables
     const bool on = lane < R && ((m >> lane) & 1ull);
     const int32_t slot = on ? g + pf + __popcll(bl & ((1ull << l) - 1ull)) : -1;
     if (d == 0 && lane < R) {
@@ -295,6 +301,50 @@ __global__ __launch_bounds__(kThreads) void dispatch_layout_kernel(
         put_row<WPL, true>(v, v0, V, sd, rd, rt, er, static_cast<int32_t>(t), recv_x, recv_idx,
                            recv_w, recv_src);
         if constexpr (!kMulti) break;
+    }
+}
+
+// ep_get_layout's second launch for a batch of 2 to kCountsLocalBlocks blocks (R <= 64, no
+// node or expert slots), after the counts path's count launch: one wave per token writes
+// its token_slot and bitmap rows from the count launch's tables, each row formed as the
+// counts path's dispatch forms it; the first `nhead` blocks are head blocks
+// (counts_head_block: the counts and offsets).
+template <int kThreads>
+__global__ __launch_bounds__(kThreads) void counts_slots_kernel(
+    int64_t T, int R, CountsWorkspace cw, int32_t* __restrict__ token_slot,
+    uint8_t* __restrict__ in_rank, int nhead, int nb, int E, int N,
+    int32_t* __restrict__ count_r, int32_t* __restrict__ rank_offset,
+    int32_t* __restrict__ count_n, int32_t* __restrict__ count_e,
+    int32_t* __restrict__ expert_offset) {
+    if (static_cast<int>(blockIdx.x) < nhead) {
+        counts_head_block(cw, blockIdx.x, nb, E, R, N, count_r, rank_offset, count_n, count_e,
+                          expert_offset);
+        return;
+    }
+    const int64_t t = grid_wave<kThreads>() - nhead * (kThreads / kWave);
+    if (t >= T) return;
+    const int lane = lane_id();
+    constexpr int kBlk = kLayoutBlockTokens;
+    const int64_t b = t / kBlk;
+    const int w = static_cast<int>(t % kBlk) / kWave;
+    const int l = static_cast<int>(t % kWave);
+    const uint64_t m = cw.mask[t];
+    int cnt[kCountsLocalBlocks];  // rank `lane`'s count in each block
+#pragma unroll
+    for (int u = 0; u < kCountsLocalBlocks; ++u)
+        cnt[u] = (u < nb && lane < R) ? cw.blk_rank[u * R + lane] : 0;
+    int32_t pf = 0;
+    uint64_t bl = 0;
+    if (lane < R) {
+        const int64_t cell = (b * (kBlk / kWave) + w) * R + lane;
+        pf = cw.pfx[cell];
+        bl = cw.ball[cell];
+    }
+    const int32_t g = local_glob(cnt, b);
+    const bool on = lane < R && ((m >> lane) & 1ull);
+    if (lane < R) {
+        token_slot[t * R + lane] = on ? g + pf + __popcll(bl & ((1ull << l) - 1ull)) : -1;
+        if (in_rank) in_rank[t * R + lane] = on ? 1 : 0;
     }
 }
 
@@ -706,6 +756,21 @@ hipError_t launch_dispatch_layout(const void* x, const int64_t* topk_idx, const 
         else
             go(std::false_type{});
     });
+}
+
+hipError_t launch_counts_slots(int64_t T, int E, int R, int N, const CountsWorkspace& cw,
+                               int32_t* token_slot, uint8_t* in_rank, int32_t* count_r,
+                               int32_t* rank_offset, int32_t* count_n, int32_t* count_e,
+                               int32_t* expert_offset, hipStream_t stream) {
+    const int nb = static_cast<int>((T + kLayoutBlockTokens - 1) / kLayoutBlockTokens);
+    if (T == 0 || nb > kCountsLocalBlocks || R > kCountsMaxRanks) return hipErrorInvalidValue;
+    constexpr int kWpb = kDestThreads / kWave;
+    const int nhead = (count_e || expert_offset) ? (E + kDestThreads - 1) / kDestThreads : 1;
+    const unsigned grid = static_cast<unsigned>(nhead + (T + kWpb - 1) / kWpb);
+    hipLaunchKernelGGL(counts_slots_kernel<kDestThreads>, dim3(grid), dim3(kDestThreads), 0,
+                       stream, T, R, cw, token_slot, in_rank, nhead, nb, E, N, count_r,
+                       rank_offset, count_n, count_e, expert_offset);
+    return hipGetLastError();
 }
 
 hipError_t launch_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_w,

@@ -92,11 +92,10 @@ int ep_get_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int
     if (!aligned(workspace, 16)) return EP_ERR_ALIGN;
     const size_t need = ep::layout_workspace_bytes(T, E, R, N);
     if (workspace_bytes < need || (need > 0 && !workspace)) return EP_ERR_CAPACITY;
-    const ep::LayoutWorkspace ws = ep::carve_layout_workspace(workspace, T, E, R, N);
     return hip_status(ep::launch_layout(topk_idx, T, k, E, R, N, num_tokens_per_rank,
                                         num_tokens_per_node, num_tokens_per_expert,
                                         is_token_in_rank, rank_offset, expert_offset, token_slot,
-                                        expert_slot, node_slot, error_flag, ws, nullptr,
+                                        expert_slot, node_slot, error_flag, workspace, nullptr,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -127,11 +126,10 @@ int ep_get_layout_no_alloc(const int64_t* topk_idx, int64_t num_tokens, int num_
     }
     void* scratch = nullptr;
     if (ep::layout_scratch_address(&scratch) != hipSuccess) return EP_ERR_HIP;
-    const ep::LayoutWorkspace ws = ep::carve_layout_workspace(scratch, T, E, R, N);
     return hip_status(ep::launch_layout(topk_idx, T, k, E, R, N, num_tokens_per_rank,
                                         num_tokens_per_node, num_tokens_per_expert,
                                         is_token_in_rank, rank_offset, expert_offset, token_slot,
-                                        expert_slot, node_slot, error_flag, ws, nullptr,
+                                        expert_slot, node_slot, error_flag, scratch, nullptr,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -158,12 +156,11 @@ int ep_dispatch_preprocess(const int64_t* topk_idx, int64_t num_tokens, int num_
     if (Tmax < T) return EP_ERR_CAPACITY;
     const size_t need = ep::layout_workspace_bytes(T, E, R, N);
     if (workspace_bytes < need || (need > 0 && !workspace)) return EP_ERR_CAPACITY;
-    const ep::LayoutWorkspace ws = ep::carve_layout_workspace(workspace, T, E, R, N);
     const ep::RestripeTask rs = ep::plan_restripe(prob, T, N, P, Tmax, prob_dest_major);
     return hip_status(ep::launch_layout(topk_idx, T, k, E, R, N, num_tokens_per_rank,
                                         num_tokens_per_node, num_tokens_per_expert,
                                         is_token_in_rank, rank_offset, expert_offset, token_slot,
-                                        expert_slot, node_slot, error_flag, ws, &rs,
+                                        expert_slot, node_slot, error_flag, workspace, &rs,
                                         static_cast<hipStream_t>(stream)));
 }
 

@@ -170,11 +170,12 @@ hipError_t layout_scratch_address(void** out);
 
 // `rs` (may be null): a dense restripe whose blocks ride along in the layout's first
 // launch, after the layout's own blocks.
+// ws_base: a workspace of layout_workspace_bytes(T, E, R, N) bytes, 16-byte aligned.
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R, int N,
                          int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                          int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
                          int32_t* expert_slot, int32_t* node_slot, int32_t* error_flag,
-                         const LayoutWorkspace& ws, const RestripeTask* rs, hipStream_t stream);
+                         void* ws_base, const RestripeTask* rs, hipStream_t stream);
 
 constexpr int kExpertSlotMaxK = 16;  // top-k limit of the expert-major slot output
 
@@ -206,6 +207,13 @@ struct ZeroInts {
     int n[kZeroArrays];
 };
 hipError_t launch_zero_ints(const ZeroInts& z, hipStream_t stream);
+
+// dispatch.hip: ep_get_layout's slot launch from the counts path's tables (2 to
+// kCountsLocalBlocks blocks, R <= kCountsMaxRanks).
+hipError_t launch_counts_slots(int64_t T, int E, int R, int N, const CountsWorkspace& cw,
+                               int32_t* token_slot, uint8_t* in_rank, int32_t* count_r,
+                               int32_t* rank_offset, int32_t* count_n, int32_t* count_e,
+                               int32_t* expert_offset, hipStream_t stream);
 
 // layout.hip: the layout, the dispatch and (with rs) the restripe of a batch of at most
 // one 256-token group (R <= kCountsMaxRanks) in one launch.

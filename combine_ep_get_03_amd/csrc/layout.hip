@@ -1281,10 +1281,23 @@ hipError_t launch_zero_ints(const ZeroInts& z_in, hipStream_t stream) {
     return hipGetLastError();
 }
 
+namespace {
+// Batches that ep_get_layout counts with the counts path's count launch and turns into
+// slots from its tables (counts_slots_kernel), when no node or expert slots are asked for:
+// more than one 256-token block (one block takes the one-block kernel) and at most
+// kCountsLocalBlocks, whose rows need no cross-block phase; one rank-mask word per token.
+bool counts_layout_shape(int64_t T, int R) {
+    const int64_t nb = (T + kBT - 1) / kBT;
+    return R <= kCountsMaxRanks && nb > 1 && nb <= kCountsLocalBlocks;
+}
+}  // namespace
+
 size_t layout_workspace_bytes(int64_t T, int E, int R, int N) {
     const size_t nb = static_cast<size_t>((T + kBT - 1) / kBT);
-    return align_up(nb * R * 4, 256) + align_up(nb * N * 4, 256) + 2 * align_up(nb * E * 4, 256) +
-           align_up(nb * 4, 256);
+    const size_t own = align_up(nb * R * 4, 256) + align_up(nb * N * 4, 256) +
+                       2 * align_up(nb * E * 4, 256) + align_up(nb * 4, 256);
+    // batches that take the counts path's tables need room for those instead
+    return counts_layout_shape(T, R) ? std::max(own, counts_workspace_bytes(T, E, R, N)) : own;
 }
 
 LayoutWorkspace carve_layout_workspace(void* base, int64_t T, int E, int R, int N) {
@@ -1334,7 +1347,16 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R
                          int32_t* count_r, int32_t* count_n, int32_t* count_e, uint8_t* in_rank,
                          int32_t* rank_offset, int32_t* expert_offset, int32_t* token_slot,
                          int32_t* expert_slot, int32_t* node_slot, int32_t* error_flag,
-                         const LayoutWorkspace& ws, const RestripeTask* rs, hipStream_t stream) {
+                         void* ws_base, const RestripeTask* rs, hipStream_t stream) {
+    if (counts_layout_shape(T, R) && !expert_slot && !node_slot) {
+        const CountsWorkspace cw = carve_counts_workspace(ws_base, T, E, R, N);
+        const hipError_t e =
+            launch_layout_counts(topk_idx, T, k, E, R, N, error_flag, nullptr, cw, rs, stream);
+        if (e != hipSuccess) return e;
+        return launch_counts_slots(T, E, R, N, cw, token_slot, in_rank, count_r, rank_offset,
+                                   count_n, count_e, expert_offset, stream);
+    }
+    const LayoutWorkspace ws = carve_layout_workspace(ws_base, T, E, R, N);
 #define EP_LAYOUT_CASE(NW)                                                                     \
     return layout_impl<NW>(topk_idx, T, k, E, R, N, count_r, count_n, count_e, in_rank,        \
                            rank_offset, expert_offset, token_slot, expert_slot, node_slot,      \
