@@ -91,9 +91,11 @@ const char *ep_status_string(int status);
  * makes before allocating ("[PR #347] Feature/sm free normal kernel", section 2.2.2, a
  * utility that estimates the minimum buffer size before the call). The workspace holds
  * per-256-token-block count tables: rank counts [nb][R], node counts [nb][N], two expert
- * tables [nb][E] and error bits [nb], nb = ceil(T / 256), each 256-byte aligned. Returns 0
- * when num_tokens == 0 (no workspace needed; NULL is then accepted) and also when the
- * sizes are ones ep_get_layout rejects. */
+ * tables [nb][E] and error bits [nb], nb = ceil(T / 256), each 256-byte aligned; for 2 to
+ * 16 blocks at num_ranks <= EP_COUNTS_MAX_RANKS, at least ep_layout_counts_workspace_bytes
+ * (such a batch, when no node or expert slots are asked for, is counted as the counts path
+ * counts it). Returns 0 when num_tokens == 0 (no workspace needed; NULL is then accepted)
+ * and also when the sizes are ones ep_get_layout rejects. */
 size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_experts, int num_ranks,
                                  int num_nodes);
 
