@@ -483,6 +483,12 @@ def small_batches(torch, W, DeviceBatch, Path, cfg, steps: int, timed) -> dict:
              "tokens_per_s": round(T / (ms * 1e-3), 1)}
         if one:
             ref = (p.out.clone(), p.recv.recv_x[:M].clone(), p.prob_dest_major[:, :T].clone())
+            # per call, each a graph of K launches of that call alone
+            r["layout_dispatch_us"] = round(graph_ms(lambda: p.layout_dispatch(b)) * 1e3, 2)
+            r["combine_us"] = round(graph_ms(lambda: p.combine(b)) * 1e3, 2)
+            r["counts_path_layout_counts_us"] = round(graph_ms(lambda: p.layout_counts(b)) * 1e3, 2)
+            r["counts_path_dispatch_layout_us"] = round(
+                graph_ms(lambda: p.dispatch_layout(b)) * 1e3, 2)
             r["counts_path_step_us"] = round(graph_ms(lambda: p.step_counts(b)) * 1e3, 2)
             torch.cuda.synchronize()
             if not (torch.equal(ref[0], p.out) and torch.equal(ref[1], p.recv.recv_x[:M]) and
