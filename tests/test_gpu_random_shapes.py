@@ -52,8 +52,22 @@ def test_random_shape_every_call(cfg):
     torch.cuda.synchronize()
     compare_all(cfg, path, ref)
 
-    # node slots, sparse restripe and the two-phase calls
+    # the layout alone, without node or expert slots (for 2 to 16 blocks at R <= 64 it is
+    # formed from the counts path's tables)
+    lb = LayoutBuffers.alloc(cfg.T, cfg.E, cfg.R, cfg.N)
+    lb.token_slot.fill_(-77)
+    lb.is_token_in_rank.fill_(0xCD)
+    lb.compute(b.topk_idx, cfg.E, cfg.R, cfg.N)
+    torch.cuda.synchronize()
     lay = ref["lay"]
+    for name, want in (("token_slot", "token_slot"), ("is_token_in_rank", "in_rank"),
+                       ("num_tokens_per_rank", "count_r"), ("rank_offset", "rank_offset"),
+                       ("num_tokens_per_node", "count_n"), ("num_tokens_per_expert", "count_e"),
+                       ("expert_offset", "expert_offset")):
+        np.testing.assert_array_equal(host(getattr(lb, name)), lay[want], err_msg=name)
+    assert int(host(lb.error_flag)[0]) == 0
+
+    # node slots, sparse restripe and the two-phase calls
     ns = oracle.node_slots(inp.topk_idx, cfg.E, cfg.R, cfg.N)
     np.testing.assert_array_equal(host(path.layout_buf.node_slot), ns)
     sp = torch.full((cfg.N, cfg.Tmax, cfg.P), -1.0, dtype=torch.float32, device="cuda")
