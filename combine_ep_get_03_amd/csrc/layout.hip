@@ -1149,7 +1149,9 @@ __global__ __launch_bounds__(kBT) void layout_counts_kernel(
 // ep_layout_dispatch: the layout, the dispatch and the restripe of a batch of at most one
 // 256-token group in one launch, no block waiting for another.
 // - Block 0 is the single-group layout (layout_single_block) without the slots: counts and
-//   offsets. It clears the error flag as it starts.
+//   offsets. It clears the error flag as it starts and ORs its bit in at its end. Another
+//   block raises a bit (a receive row past the capacity) only after its ids' round trip
+//   and a block barrier, microseconds after block 0, which the hardware starts first.
 // - Blocks 1 .. ndisp each hold four (token, destination) waves of the dispatch, as
 //   dispatch_layout_kernel's. A block recomputes the group's rank masks and each wave's
 //   rank ballots in LDS while its rows' loads are in flight (the ids are 16 KiB at top-8
