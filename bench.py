@@ -418,19 +418,31 @@ def mix_yardstick(torch, ep, cfg, M: int, avg: dict, alg: dict, steps: int, time
     """What HBM sustains for the read/write mix of each big kernel, with every access a
     sequential stream (ep_hbm_fan on slabs of T*H*2 bytes): F slabs reduced into one for the
     combine (F = 7 and 8 around its M/T reads per write), one slab written F times for the
-    dispatch. The time at F = M/T is interpolated between the two."""
+    dispatch. The time at F = M/T is interpolated between the two. For the combine the
+    same fan-in is also timed with its reads spread over R sequential streams, one per
+    rank's block of the receive buffer (ep_hbm_spread, when T*H*2 splits into whole
+    chunks over the R regions)."""
     slab = cfg.T * cfg.H * 2
     src = torch.empty(8 * slab, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty(8 * slab, dtype=torch.uint8, device="cuda")
     t = {}
-    for fi, fo in ((7, 1), (8, 1), (1, 7), (1, 8)):
+
+    def graph_of(fn):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(steps):
-                ep.ep_hbm_fan(src, dst, slab, fi, fo)
+                fn()
         g.replay()
-        t[(fi, fo)] = timed(g.replay, 1) / steps
+        ms = timed(g.replay, 1) / steps
         del g
+        return ms
+    for fi, fo in ((7, 1), (8, 1), (1, 7), (1, 8)):
+        t[(fi, fo)] = graph_of(lambda: ep.ep_hbm_fan(src, dst, slab, fi, fo))
+    chunk = ep.EP_HBM_SPREAD_CHUNK_BYTES
+    spread_ok = slab % chunk == 0 and all((F * (slab // chunk)) % cfg.R == 0 for F in (7, 8))
+    if spread_ok:
+        for F in (7, 8):
+            t[("spread", F)] = graph_of(lambda: ep.ep_hbm_spread(src, dst, slab, F, cfg.R))
     del src, dst
     torch.cuda.empty_cache()
     f = M / cfg.T
@@ -445,6 +457,18 @@ def mix_yardstick(torch, ep, cfg, M: int, avg: dict, alg: dict, steps: int, time
                      "kernel_hbm_gbps": round(alg[name] / (avg[name] * 1e-3) / 1e9, 1),
                      "kernel_frac_of_yardstick": round((alg[name] / avg[name]) /
                                                        (moved / ms), 4)}
+    if spread_ok:
+        lo, hi = t[("spread", 7)], t[("spread", 8)]
+        ms = lo + (f - 7) * (hi - lo)
+        moved = (f + 1) * slab
+        out["combine"]["spread_over_ranks"] = {
+            "regions": cfg.R, "chunk_bytes": chunk,
+            "fan_7_us": round(lo * 1e3, 2), "fan_8_us": round(hi * 1e3, 2),
+            "yardstick_us_at_mix": round(ms * 1e3, 2),
+            "yardstick_gbps": round(moved / (ms * 1e-3) / 1e9, 1),
+            "kernel_frac_of_yardstick": round((alg["combine"] / avg["combine"]) / (moved / ms), 4)}
+    else:
+        out["combine"]["spread_over_ranks"] = None
     return out
 
 

@@ -22,6 +22,7 @@ EP_MAX_RANKS, EP_MAX_EXPERTS, EP_EXPERT_SLOT_MAX_K = 1024, 8192, 16
 EP_LAYOUT_SCRATCH_BYTES = 4 << 20
 EP_COUNTS_MAX_RANKS = 64
 EP_LAYOUT_DISPATCH_MAX_TOKENS = 256
+EP_HBM_SPREAD_CHUNK_BYTES = 4096
 
 _lib = None
 
@@ -74,11 +75,12 @@ def load() -> ctypes.CDLL:
     L.ep_combine_recv.argtypes = [P, i32, i64, P, i64, i32, P, P, P]
     L.ep_hbm_copy.argtypes = [P, P, sz, P]
     L.ep_hbm_fan.argtypes = [P, P, sz, i32, i32, P]
+    L.ep_hbm_spread.argtypes = [P, P, sz, i32, i32, P]
     for f in ("ep_get_layout", "ep_get_layout_no_alloc", "ep_dispatch_preprocess",
               "ep_layout_counts", "ep_dispatch_layout", "ep_dispatch_permute_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_permute",
               "ep_restripe_prob", "ep_restripe_prob_sparse", "ep_combine", "ep_dispatch_send",
               "ep_dispatch_recv", "ep_combine_send", "ep_combine_recv", "ep_hbm_copy",
-              "ep_hbm_fan"):
+              "ep_hbm_fan", "ep_hbm_spread"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -647,3 +649,20 @@ def ep_hbm_fan(src, dst, slab_bytes: int, fan_in: int, fan_out: int, stream=None
         raise ValueError("fan_in / fan_out slabs exceed a buffer")
     _check(load().ep_hbm_fan(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
                              slab_bytes, fan_in, fan_out, _stream(stream)), "ep_hbm_fan")
+
+
+
+def ep_hbm_spread(src, dst, out_bytes: int, fan_in: int, regions: int, stream=None) -> None:
+    """Measurement helper: output chunk b of dst (chunks of EP_HBM_SPREAD_CHUNK_BYTES)
+    becomes the XOR of the input chunks fan_in*b .. fan_in*b + fan_in - 1 of src, input
+    chunk j being chunk j // regions of region j % regions (src = fan_in * out_bytes bytes
+    in `regions` equal regions)."""
+    if not (src.is_cuda and dst.is_cuda):
+        raise ValueError("src and dst must be device tensors")
+    _on_current_device(src, "src")
+    _on_current_device(dst, "dst")
+    if (fan_in * out_bytes > src.numel() * src.element_size() or
+            out_bytes > dst.numel() * dst.element_size()):
+        raise ValueError("fan_in * out_bytes or out_bytes exceeds a buffer")
+    _check(load().ep_hbm_spread(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                out_bytes, fan_in, regions, _stream(stream)), "ep_hbm_spread")

@@ -565,4 +565,16 @@ int ep_hbm_fan(const void* src, void* dst, size_t slab_bytes, int fan_in, int fa
                                          static_cast<hipStream_t>(stream)));
 }
 
+int ep_hbm_spread(const void* src, void* dst, size_t out_bytes, int fan_in, int regions,
+                  void* stream) {
+    if (fan_in < 1 || fan_in > 8 || regions < 1 || regions > EP_MAX_RANKS) return EP_ERR_ARG;
+    if (out_bytes % EP_HBM_SPREAD_CHUNK_BYTES != 0) return EP_ERR_ARG;
+    const uint64_t chunks = static_cast<uint64_t>(fan_in) * (out_bytes / EP_HBM_SPREAD_CHUNK_BYTES);
+    if (chunks % static_cast<uint64_t>(regions) != 0) return EP_ERR_ARG;
+    if (out_bytes > 0 && (!src || !dst)) return EP_ERR_ARG;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return EP_ERR_ALIGN;
+    return hip_status(ep::launch_hbm_spread(src, dst, out_bytes, fan_in, regions,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -310,5 +310,7 @@ hipError_t launch_combine_recv(const void* stage, int N, int64_t Tmax, const int
 hipError_t launch_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_hbm_fan(const void* src, void* dst, size_t slab_bytes, int fan_in,
                           int fan_out, hipStream_t stream);
+hipError_t launch_hbm_spread(const void* src, void* dst, size_t out_bytes, int fan_in,
+                             int regions, hipStream_t stream);
 
 }  // namespace ep

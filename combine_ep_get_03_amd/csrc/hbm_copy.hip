@@ -1,6 +1,7 @@
 // hbm_copy.hip -- 128-bit streams of a fixed read/write mix: the HBM copy-bandwidth
 // yardstick, the yardstick for the direction mixes of dispatch and combine, and the
-// known-size reference for hardware byte counters. Not a step of the dispatch path.
+// known-size reference for hardware byte counters, and the combine's fan-in spread over
+// one sequential stream per rank. Not a step of the dispatch path.
 //
 // Each stream takes the cache policy that measured fastest for its mix on MI355X, in
 // sequential streams of 512 MiB slabs (beyond the 256 MB Infinity Cache), best of three:
@@ -13,6 +14,7 @@
 //   with non-temporal loads, and device-scope stores were slower at every such mix.
 // Byte counters read the same with either store form (FETCH_SIZE 0.501 and WRITE_SIZE
 // 1.000 of the bytes moved, on the copy and on both mixes).
+#include "ep.h"
 #include "ep_internal.hpp"
 
 namespace ep {
@@ -117,6 +119,35 @@ __global__ __launch_bounds__(kCopyThreads) void hbm_fan_kernel(const u32x4* __re
     }
 }
 
+// Fan-in yardstick with the reads spread over S sequential streams, the way the combine's
+// source rows lie in one block of the receive buffer per rank. Block b XORs the input
+// chunks j = F b + q (q < F) of kSpreadWords words into output chunk b; chunk j is chunk
+// j / S of region j % S (regions of region_words words, back to back), so every region
+// is read from its start in order while the grid walks the output. Eight loads per lane,
+// unconditionally, as in the fan's form for seven or more slabs: q past F loads chunk
+// F b + F - 1 again.
+constexpr int kSpreadWords = EP_HBM_SPREAD_CHUNK_BYTES / 16;  // one word per lane
+static_assert(kSpreadWords == kCopyThreads, "a spread block is one chunk");
+
+__global__ __launch_bounds__(kCopyThreads) void hbm_spread_kernel(const u32x4* __restrict__ in,
+                                                                  u32x4* __restrict__ out,
+                                                                  int fan_in, int regions,
+                                                                  int64_t region_words) {
+    const int64_t b = blockIdx.x;
+    const int tid = threadIdx.x;
+    u32x4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int64_t j = fan_in * b + min(q, fan_in - 1);
+        v[q] = load_stream(in + (j % regions) * region_words + (j / regions) * kSpreadWords + tid);
+    }
+    u32x4 acc = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        if (q < fan_in) acc ^= v[q];
+    store_stream(out + b * kSpreadWords + tid, acc);
+}
+
 }  // namespace
 
 hipError_t launch_hbm_fan(const void* src, void* dst, size_t slab_bytes, int fan_in,
@@ -150,6 +181,19 @@ hipError_t launch_hbm_fan(const void* src, void* dst, size_t slab_bytes, int fan
             hipLaunchKernelGGL((hbm_fan_kernel<kCopyU, false, false>), g, dim3(kCopyThreads), 0,
                                stream, in, out, n, fan_in, fan_out);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_hbm_spread(const void* src, void* dst, size_t out_bytes, int fan_in,
+                             int regions, hipStream_t stream) {
+    const int64_t nb = static_cast<int64_t>(out_bytes / (16 * kSpreadWords));
+    if (nb == 0) return hipSuccess;
+    // the caller guarantees (fan_in * nb) % regions == 0: src is exactly fan_in * nb chunks
+    const int64_t region_words = fan_in * nb / regions * kSpreadWords;
+    if (!grid_fits(nb, kCopyThreads)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(hbm_spread_kernel, dim3(static_cast<unsigned>(nb)), dim3(kCopyThreads), 0,
+                       stream, static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), fan_in,
+                       regions, region_words);
     return hipGetLastError();
 }
 

@@ -510,6 +510,21 @@ int ep_hbm_copy(const void *src, void *dst, size_t bytes, void *stream);
 int ep_hbm_fan(const void *src, void *dst, size_t slab_bytes, int fan_in, int fan_out,
                void *stream);
 
+/* ep_hbm_spread -- measurement helper, not a step of the path: the fan-in yardstick with
+ * its reads spread over `regions` sequential streams, as the combine's source rows lie in
+ * one block of the receive buffer per rank. dst is cut into chunks of
+ * EP_HBM_SPREAD_CHUNK_BYTES; src holds fan_in * out_bytes bytes cut into `regions` equal
+ * regions, back to back. Output chunk b becomes the bitwise XOR of the input chunks
+ * j = fan_in * b + q (0 <= q < fan_in), chunk j being chunk j / regions of region
+ * j % regions, so each region is read from its start in order. Loads and stores are
+ * non-temporal. out_bytes a multiple of EP_HBM_SPREAD_CHUNK_BYTES, 1 <= fan_in <= 8,
+ * 1 <= regions <= EP_MAX_RANKS, (fan_in * out_bytes / EP_HBM_SPREAD_CHUNK_BYTES) % regions
+ * == 0 (else EP_ERR_ARG); both pointers 16-byte aligned.
+ * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_HIP. */
+#define EP_HBM_SPREAD_CHUNK_BYTES 4096
+int ep_hbm_spread(const void *src, void *dst, size_t out_bytes, int fan_in, int regions,
+                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "ep_layout_workspace_bytes", "ep_status_string", "ep_hbm_copy",
                           "ep_dispatch_fp8", "ep_dispatch_permute", "ep_restripe_prob_sparse",
                           "ep_dispatch_send", "ep_dispatch_recv", "ep_combine_send",
-                          "ep_combine_recv", "ep_layout_dispatch"}
+                          "ep_combine_recv", "ep_layout_dispatch", "ep_hbm_spread"}
     out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (ep_\w+)", out))
@@ -369,6 +369,17 @@ def test_copy_validation(lib):
     assert lib.ep_hbm_fan(None, A16, 32, 2, 1, None) == ep.EP_ERR_ARG
     assert lib.ep_hbm_fan(A16, A16, 32, 0, 1, None) == ep.EP_ERR_ARG
     assert lib.ep_hbm_fan(A16, A16, 32, 1, 65, None) == ep.EP_ERR_ARG
+    C = ep.EP_HBM_SPREAD_CHUNK_BYTES
+    sp = lib.ep_hbm_spread
+    assert sp(A16, A16, C + 16, 7, 7, None) == ep.EP_ERR_ARG     # not whole chunks
+    assert sp(A16, A16, 32 * C, 0, 32, None) == ep.EP_ERR_ARG    # fan_in < 1
+    assert sp(A16, A16, 32 * C, 9, 32, None) == ep.EP_ERR_ARG    # fan_in > 8
+    assert sp(A16, A16, 32 * C, 7, 0, None) == ep.EP_ERR_ARG     # no region
+    assert sp(A16, A16, 32 * C, 7, ep.EP_MAX_RANKS + 1, None) == ep.EP_ERR_ARG
+    assert sp(A16, A16, 3 * C, 7, 32, None) == ep.EP_ERR_ARG     # 21 chunks over 32 regions
+    assert sp(None, A16, 32 * C, 7, 32, None) == ep.EP_ERR_ARG
+    assert sp(A16, MIS, 32 * C, 7, 32, None) == ep.EP_ERR_ALIGN
+    assert sp(None, None, 0, 7, 32, None) == ep.EP_OK           # nothing to move
 
 
 def test_public_header_is_plain_c():

@@ -1,7 +1,9 @@
 """The measurement helpers behind the bench's yardsticks move exactly the bytes they
-claim: the copy writes dst[:n] = src[:n] and nothing past it, and the fan writes the
-XOR of its input slabs into every output slab and nothing past them. Both are checked
-at sizes that end inside a block's share and in a whole number of blocks."""
+claim: the copy writes dst[:n] = src[:n] and nothing past it, the fan writes the XOR of
+its input slabs into every output slab and nothing past them, and the spread writes into
+each output chunk the XOR of its input chunks under the region mapping. The copy and the
+fan are checked at sizes that end inside a block's share and in a whole number of
+blocks."""
 import numpy as np
 import pytest
 import torch
@@ -40,7 +42,7 @@ def test_copy_of_zero_bytes_writes_nothing():
 
 
 @pytest.mark.parametrize("fan_in,fan_out", [(7, 1), (8, 1), (1, 7), (1, 8), (2, 1), (1, 2),
-                                            (1, 1), (4, 3), (4, 8)])
+                                            (1, 1), (4, 3), (4, 8), (12, 1), (9, 2), (16, 1)])
 @pytest.mark.parametrize("slab", [16 * 3001, 16 * 1024 * 3])
 def test_fan_writes_the_xor_of_its_slabs(fan_in, fan_out, slab):
     print(f"\ncase: ep_hbm_fan {fan_in}:{fan_out} slab {slab}", flush=True)
@@ -54,3 +56,26 @@ def test_fan_writes_the_xor_of_its_slabs(fan_in, fan_out, slab):
     for j in range(fan_out):
         np.testing.assert_array_equal(d[j * slab:(j + 1) * slab], want, err_msg=f"slab {j}")
     assert bool((d[fan_out * slab:] == SENT).all())
+
+
+@pytest.mark.parametrize("fan_in,regions,nchunks", [(7, 32, 64), (8, 32, 64), (7, 7, 48),
+                                                    (8, 8, 48), (1, 1, 5), (3, 1, 7),
+                                                    (5, 64, 64), (7, 28, 4)])
+def test_spread_writes_the_xor_of_its_chunks(fan_in, regions, nchunks):
+    print(f"\ncase: ep_hbm_spread fan_in {fan_in} regions {regions} chunks {nchunks}", flush=True)
+    C = ep.EP_HBM_SPREAD_CHUNK_BYTES
+    out_bytes = nchunks * C
+    src = _rand_bytes(fan_in * out_bytes, fan_in * 131 + regions + nchunks)
+    dst = torch.full((out_bytes + 4096,), SENT, dtype=torch.uint8, device="cuda")
+    ep.ep_hbm_spread(src, dst, out_bytes, fan_in, regions)
+    torch.cuda.synchronize()
+    # input chunk j is chunk j // regions of region j % regions
+    s = src.cpu().numpy().reshape(regions, fan_in * nchunks // regions, C)
+    want = np.zeros((nchunks, C), dtype=np.uint8)
+    for b in range(nchunks):
+        for q in range(fan_in):
+            j = fan_in * b + q
+            want[b] ^= s[j % regions, j // regions]
+    d = dst.cpu().numpy()
+    np.testing.assert_array_equal(d[:out_bytes].reshape(nchunks, C), want)
+    assert bool((d[out_bytes:] == SENT).all())
