@@ -387,8 +387,8 @@ def destroy_stream(handle) -> None:
 def restripe_page_shape(torch, W, ep, steps: int, timed, flush_gib: float) -> dict:
     """The restripe at the shape its page measures, prob [4096][8][128] -> [8][4096][128]:
     the average of K back-to-back launches (warm: the 33.6 MB stay in the 256 MB Infinity
-    Cache between launches) and single launches after a spin (warm) and after a flush of
-    `flush_gib` GiB (cold)."""
+    Cache between launches), right after the yardsticks and again after 200 ms of idle,
+    and single launches after a spin (warm) and after a flush of `flush_gib` GiB (cold)."""
     c = W.CONFIGS["restripe"]
     inp = W.make_inputs(c, with_x=False)
     prob = torch.from_numpy(inp.prob).cuda()
@@ -400,12 +400,18 @@ def restripe_page_shape(torch, W, ep, steps: int, timed, flush_gib: float) -> di
             fn()
     g.replay()
     ms = timed(g.replay, 1) / steps
+    # The same graph after the GPU has idled: for some 30-100 ms after sustained HBM
+    # traffic (the bench's yardsticks run just before) short launches run slower.
+    torch.cuda.synchronize()
+    time.sleep(0.2)
+    ms_idle = timed(g.replay, 1) / steps
     del g
     dist = launch_distribution(torch, ep, {"restripe": fn}, steps, flush_gib)
     alg = 2 * c.T * c.N * c.P * 4
     res = {"shape": f"[{c.T}][{c.N}][{c.P}] -> [{c.N}][{c.Tmax}][{c.P}]", "alg_bytes": alg,
            "back_to_back_avg_us": round(ms * 1e3, 2),
            "back_to_back_hbm_gbps": round(alg / (ms * 1e-3) / 1e9, 1),
+           "back_to_back_after_200ms_idle_avg_us": round(ms_idle * 1e3, 2),
            "single_launch_warm_median_us": dist["warm"]["restripe"]["median_us"],
            "single_launch_cold_median_us": dist["cold"]["restripe"]["median_us"],
            "event_floor_us": dist["event_floor_us"]}
