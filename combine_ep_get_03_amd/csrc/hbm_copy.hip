@@ -135,11 +135,19 @@ __global__ __launch_bounds__(kCopyThreads) void hbm_spread_kernel(const u32x4* _
                                                                   int64_t region_words) {
     const int64_t b = blockIdx.x;
     const int tid = threadIdx.x;
+    // chunk j0 = fan_in * b < 2^27 (fan_in <= 8, at most 2^24 blocks); one 32-bit division
+    // per wave, then each next chunk is one region further on
+    const uint32_t j0 = static_cast<uint32_t>(fan_in) * static_cast<uint32_t>(blockIdx.x);
+    uint32_t r = j0 % static_cast<uint32_t>(regions);
+    uint32_t c = j0 / static_cast<uint32_t>(regions);
     u32x4 v[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        const int64_t j = fan_in * b + min(q, fan_in - 1);
-        v[q] = load_stream(in + (j % regions) * region_words + (j / regions) * kSpreadWords + tid);
+        if (q > 0 && q < fan_in && ++r == static_cast<uint32_t>(regions)) {
+            r = 0;
+            ++c;
+        }
+        v[q] = load_stream(in + r * region_words + static_cast<int64_t>(c) * kSpreadWords + tid);
     }
     u32x4 acc = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
