@@ -408,11 +408,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_permute_layout_kernel(
     u32x4* row = perm_x + q * V;
     for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
         if (v0 != 0) load_row_cached(v, xr, v0, V);
-#pragma unroll
-        for (int i = 0; i < WPL; ++i) {
-            const int vi = v0 + i * kWave + lane;
-            if (vi < V) store_row_word(row + vi, v[i]);
-        }
+        store_row_pass(row, V, v0, v);
         if constexpr (!kMulti) break;
     }
     if (lane == 0) {
@@ -472,11 +468,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_permute_kernel(
     u32x4* row = perm_x + q * V;
     for (int v0 = 0; v0 < V; v0 += kWave * WPL) {
         if (v0 != 0) load_row_cached(v, xr, v0, V);
-#pragma unroll
-        for (int i = 0; i < WPL; ++i) {
-            const int vi = v0 + i * kWave + lane;
-            if (vi < V) store_row_word(row + vi, v[i]);
-        }
+        store_row_pass(row, V, v0, v);
         if constexpr (!kMulti) break;
     }
     if (lane == 0) {
@@ -607,15 +599,12 @@ __device__ __forceinline__ void put_fp8_row(const u32x4 (&code)[WPP], const floa
                                             float* __restrict__ recv_w,
                                             int32_t* __restrict__ recv_src) {
     const int lane = lane_id();
-    u32x4* row = recv_codes + sd * P2;
     float* srow_out = recv_scales + sd * G;
+    store_row_pass(recv_codes + sd * P2, P2, p0, code);
 #pragma unroll
     for (int i = 0; i < WPP; ++i) {
         const int pi = p0 + i * kWave + lane;
-        if (pi < P2) {
-            store_stream(row + pi, code[i]);
-            if ((lane & 7) == 0) srow_out[pi / 8] = scale[i];
-        }
+        if (pi < P2 && (lane & 7) == 0) srow_out[pi / 8] = scale[i];
     }
     if (p0 != 0) return;
     if (recv_idx || recv_w) rt.write<true>(sd, rd, er, recv_idx, recv_w);

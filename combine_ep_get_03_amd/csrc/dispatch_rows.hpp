@@ -11,16 +11,38 @@
 namespace ep {
 namespace {
 
-#ifndef EP_DISPATCH_NT_STORE
-#define EP_DISPATCH_NT_STORE 1
+#ifndef EP_ROW_STORE_POLICY
+#define EP_ROW_STORE_POLICY (kPolicyNt | kPolicySc1)
 #endif
 
-__device__ __forceinline__ void store_row_word(u32x4* p, u32x4 v) {
-#if EP_DISPATCH_NT_STORE
-    store_stream(p, v);
-#else
-    *p = v;
-#endif
+// One pass of a destination row: words v0 + 64 i + lane (i < WPL) of a row of V words
+// (the same row for every lane of the wave). The row is addressed through a buffer
+// resource of V words, whose bounds check drops the words at V and beyond, so no store
+// waits behind a per-word guard. The stores are non-temporal at device scope (nt sc1).
+// Measured on MI355X against guarded non-temporal stores, same box, identical outputs:
+// the dispatch 81.3 against 82.6 us at 4096 tokens (top-8 over 32 ranks, 7168 channels)
+// and 333.8 against 341.4 us at 16384 tokens over 64 ranks, the dispatch with its slots
+// 82.0 against 83.6 and 334.7 against 340.4 us. Unguarded stores that were non-temporal
+// only ran as the guarded ones, and device-scope stores that were not non-temporal ran
+// 12-15% slower. The same policy on the combine's output rows was slower at 4096 tokens.
+template <int WPL>
+__device__ __forceinline__ void store_row_pass(u32x4* row, int V, int v0,
+                                               const u32x4 (&v)[WPL]) {
+    // readfirstlane returns a signed int: each half goes through uint32_t, so the low half
+    // is not sign-extended into the high one
+    const uint64_t a = reinterpret_cast<uint64_t>(row);
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32))));
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a))));
+    const uint64_t ua = (static_cast<uint64_t>(hi) << 32) | lo;
+    const __amdgpu_buffer_rsrc_t rr =
+        raw_buffer(reinterpret_cast<const void*>(ua), static_cast<uint32_t>(V) * 16u);
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < WPL; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(v[i], rr, (v0 + i * kWave + lane) * 16, 0,
+                                               EP_ROW_STORE_POLICY);
 }
 
 // A token's k-slot routing as it travels with its row. Lane j < 64 holds slot j (loaded
@@ -76,12 +98,7 @@ __device__ __forceinline__ void put_row(const u32x4 (&v)[WPL], int v0, int V, in
                                         u32x4* __restrict__ dst_x, int64_t* __restrict__ dst_idx,
                                         float* __restrict__ dst_w, int32_t* __restrict__ dst_src) {
     const int lane = lane_id();
-    u32x4* row = dst_x + sd * V;
-#pragma unroll
-    for (int i = 0; i < WPL; ++i) {
-        const int vi = v0 + i * kWave + lane;
-        if (vi < V) store_row_word(row + vi, v[i]);
-    }
+    store_row_pass(dst_x + sd * V, V, v0, v);
     if (v0 != 0) return;
     if (dst_idx || dst_w) rt.write<kRankView>(sd, rank, er, dst_idx, dst_w);
     if (dst_src && lane == 0) dst_src[sd] = src;

@@ -48,6 +48,19 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
+// Raw buffer resources (untyped, stride 0): word 3 of such a resource on gfx9-family
+// targets, and the cache-policy bits of a buffer access's aux operand. Buffer ops through
+// the resource are bounds-checked against its byte count: a load past it returns zero
+// and a store past it is dropped.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kPolicySc0 = 1;
+constexpr int kPolicyNt = 2;
+constexpr int kPolicySc1 = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRawBufferWord3);
+}
+
 // Sticky device error word: bits are only ever added.
 __device__ __forceinline__ void raise_error(int32_t* flag, int32_t bits) {
     if (flag) atomicOr(flag, bits);

@@ -26,12 +26,6 @@ namespace {
 
 constexpr int kCopyThreads = 256;
 constexpr int kCopyU = 4;
-// Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family targets; buffer ops
-// through it are bounds-checked against the resource's byte count: a load past it
-// returns zero and a store past it is dropped.
-constexpr int kRawBufferWord3 = 0x00020000;
-constexpr int kLoadNonTemporal = 2;    // cache-policy bit nt of a buffer load
-constexpr int kStoreDeviceScope = 16;  // cache-policy bit sc1 of a buffer store
 
 __global__ __launch_bounds__(kCopyThreads) void hbm_copy_kernel(const u32x4* __restrict__ in,
                                                                 u32x4* __restrict__ out,
@@ -45,20 +39,18 @@ __global__ __launch_bounds__(kCopyThreads) void hbm_copy_kernel(const u32x4* __r
         // for per-word guards: guarded stores each sit in a branch of their own, and the
         // compiler then waits for all memory operations before every store, so the stores
         // of a lane go out one at a time (measured 5.9 TB/s against 6.3 without the waits).
-        const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<u32x4*>(in + b0), 0, bytes, kRawBufferWord3);
-        const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
-            static_cast<void*>(out + b0), 0, bytes, kRawBufferWord3);
+        const __amdgpu_buffer_rsrc_t src = raw_buffer(in + b0, bytes);
+        const __amdgpu_buffer_rsrc_t dst = raw_buffer(out + b0, bytes);
         u32x4 v[kCopyU];
 #pragma unroll
         for (int u = 0; u < kCopyU; ++u)
             v[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                src, (u * kCopyThreads + static_cast<int>(threadIdx.x)) * 16, 0, kLoadNonTemporal);
+                src, (u * kCopyThreads + static_cast<int>(threadIdx.x)) * 16, 0, kPolicyNt);
 #pragma unroll
         for (int u = 0; u < kCopyU; ++u)
             __builtin_amdgcn_raw_buffer_store_b128(
                 v[u], dst, (u * kCopyThreads + static_cast<int>(threadIdx.x)) * 16, 0,
-                kStoreDeviceScope);
+                kPolicySc1);
     }
 }
 
