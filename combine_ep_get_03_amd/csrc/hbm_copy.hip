@@ -9,9 +9,10 @@
 //   which write through the L2: 6.45 against 5.44 TB/s with non-temporal stores;
 // - reads that outnumber writes (the combine's mix): non-temporal loads and stores;
 //   device-scope stores were 1-5% slower from two reads per write up;
-// - one read per several writes (the dispatch's mix): cached loads and non-temporal
-//   stores; at the dispatch's own slab (58.7 MB, 1 to 7) they took 74.8 against 87.6 us
-//   with non-temporal loads, and device-scope stores were slower at every such mix.
+// - one read per several writes (the dispatch's mix): cached loads, and stores that are
+//   non-temporal and at device scope (nt sc1); at the dispatch's own slab (58.7 MB, 1 to
+//   7) cached loads took 74.8 against 87.6 us with non-temporal ones, and nt sc1 stores
+//   74.9 against 75.5-76.3 us with nt stores (device-scope stores without nt: 84-85 us).
 // Byte counters read the same with either store form (FETCH_SIZE 0.501 and WRITE_SIZE
 // 1.000 of the bytes moved, on the copy and on both mixes).
 #include "ep.h"
@@ -102,11 +103,27 @@ __global__ __launch_bounds__(kCopyThreads) void hbm_fan_kernel(const u32x4* __re
             for (int q = 0; q < 8; ++q)
                 if (s + q < fan_in) acc[u] ^= v[u][q];
     }
-    for (int j = 0; j < fan_out; ++j) {
+    if constexpr (kCached) {
+        // reads fewer than writes: unguarded stores, non-temporal at device scope, through
+        // a buffer of the block's words of each output slab (its bounds check drops the
+        // words past n), as the dispatch stores its rows
+        const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kCopyThreads * U;
+        const uint32_t bytes = static_cast<uint32_t>(min<int64_t>(n - b0, kCopyThreads * U)) * 16u;
+        for (int j = 0; j < fan_out; ++j) {
+            const __amdgpu_buffer_rsrc_t dst = raw_buffer(out + j * n + b0, bytes);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
-            if (i < n) store_stream(out + j * n + i, acc[u]);
+            for (int u = 0; u < U; ++u)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    acc[u], dst, (u * kCopyThreads + static_cast<int>(threadIdx.x)) * 16, 0,
+                    kPolicyNt | kPolicySc1);
+        }
+    } else {
+        for (int j = 0; j < fan_out; ++j) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
+                if (i < n) store_stream(out + j * n + i, acc[u]);
+            }
         }
     }
 }

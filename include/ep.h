@@ -503,8 +503,9 @@ int ep_hbm_copy(const void *src, void *dst, size_t bytes, void *stream);
  * (contiguous, slab s at byte s * slab_bytes); every output slab becomes the bitwise XOR of
  * the input slabs. fan_in F with fan_out 1 reads F bytes per byte written (the direction
  * mix of ep_combine), fan_in 1 with fan_out F the reverse (that of ep_dispatch); all
- * accesses are sequential 128-bit streams, with cached loads when fan_in < fan_out (as the
- * dispatch's row loads) and non-temporal loads otherwise. slab_bytes a multiple of 16,
+ * accesses are sequential 128-bit streams, with cached loads and stores that are
+ * non-temporal at device scope when fan_in < fan_out (as the dispatch's rows), and
+ * non-temporal loads and stores otherwise. slab_bytes a multiple of 16,
  * both pointers 16-byte aligned, 1 <= fan_in, fan_out <= 64.
  * Errors: EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_HIP. */
 int ep_hbm_fan(const void *src, void *dst, size_t slab_bytes, int fan_in, int fan_out,
