@@ -20,7 +20,7 @@ template <typename W>
 __global__ __launch_bounds__(kRT) void restripe_kernel(const W* __restrict__ in, int64_t T,
                                                        int NV, int VP, int64_t Tmax,
                                                        W* __restrict__ out, int tpb) {
-    restripe_run<W, kRU>(in, T, NV, VP, Tmax, out, tpb, blockIdx.x);
+    restripe_run<W, kRU, true>(in, T, NV, VP, Tmax, out, tpb, blockIdx.x);
 }
 
 // Sparse path: only routed (token, node) slices move, to row node_slot[t][n] of the node's
