@@ -114,9 +114,11 @@ __device__ __forceinline__ void restripe_run(const W* __restrict__ in, int64_t T
     // The block's stores land in N runs, from its tokens' row of node 0 to that of node
     // N - 1. With kSc1, where that span is below 2 GiB, they go through one buffer resource
     // over it as device-scope stores (sc1), the fastest form for a copy's one write per
-    // read. Measured on MI355X against non-temporal stores (the restripe's own launch,
-    // graphs of 50 launches, identical outputs): 4.3 against 4.8 us at [4096][8][128],
-    // 2.4 against 2.6 us at [4096][4][64], 4.4 against 5.4 us at [16384][8][32].
+    // read alone. Measured on MI355X against non-temporal stores (the restripe's own
+    // launch, graphs of 50 launches, identical outputs): 4.3 against 4.8 us at
+    // [4096][8][128], 2.4 against 2.6 us at [4096][4][64], 4.4 against 5.4 us at
+    // [16384][8][32]. Both of its callers keep kSc1 off: in a step the kernels after it ran
+    // slower by more than it saves.
     const int N = NV / VP;
     const int64_t span = ((static_cast<int64_t>(N) - 1) * Tmax * VP + static_cast<int64_t>(nt) * VP) *
                          static_cast<int64_t>(sizeof(W));
