@@ -102,7 +102,13 @@ struct RestripeTask {
     int64_t blocks;  // blocks of kRestripeThreads covering the T tokens
 };
 
-template <typename W, int kU, bool kSc1>
+// Device-scope stores (one buffer resource over a block's output span, sc1) made the
+// restripe faster alone (4.3 against 4.8 us at [4096][8][128], 4.4 against 5.4 us at
+// [16384][8][32], 2.4 against 2.6 us at [4096][4][64] on MI355X) but the kernels after
+// it slower: at 16384 tokens (top-8 over 64 ranks) the counts-path step took 698.3
+// against 688.0 us with them inside the count launch, and one call per step 714.8
+// against 700.2 us with them in the restripe's own launch. Both keep non-temporal stores.
+template <typename W, int kU>
 __device__ __forceinline__ void restripe_run(const W* __restrict__ in, int64_t T, int NV, int VP,
                                              int64_t Tmax, W* __restrict__ out, int tpb,
                                              int64_t block) {
@@ -111,43 +117,6 @@ __device__ __forceinline__ void restripe_run(const W* __restrict__ in, int64_t T
     const int nt = static_cast<int>(min<int64_t>(tpb, T - t0));
     const int total = nt * NV;
     const W* src = in + t0 * NV;
-    // The block's stores land in N runs, from its tokens' row of node 0 to that of node
-    // N - 1. With kSc1, where that span is below 2 GiB, they go through one buffer resource
-    // over it as device-scope stores (sc1), the fastest form for a copy's one write per
-    // read alone. Measured on MI355X against non-temporal stores (the restripe's own
-    // launch, graphs of 50 launches, identical outputs): 4.3 against 4.8 us at
-    // [4096][8][128], 2.4 against 2.6 us at [4096][4][64], 4.4 against 5.4 us at
-    // [16384][8][32]. Both of its callers keep kSc1 off: in a step the kernels after it ran
-    // slower by more than it saves.
-    const int N = NV / VP;
-    const int64_t span = ((static_cast<int64_t>(N) - 1) * Tmax * VP + static_cast<int64_t>(nt) * VP) *
-                         static_cast<int64_t>(sizeof(W));
-    if (kSc1 && span <= INT32_MAX) {
-        const __amdgpu_buffer_rsrc_t ro = raw_buffer(out + t0 * VP, static_cast<uint32_t>(span));
-        for (int f0 = 0; f0 < total; f0 += kRestripeThreads * kU) {
-            W v[kU];
-            int f[kU];
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                f[u] = min(f0 + u * kRestripeThreads + tid, total - 1);
-                v[u] = __builtin_nontemporal_load(src + f[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const int tt = f[u] / NV;
-                const int rem = f[u] - tt * NV;
-                const int n = rem / VP;
-                const int vv = rem - n * VP;
-                const int off = static_cast<int>(((static_cast<int64_t>(n) * Tmax + tt) * VP + vv) *
-                                                 static_cast<int64_t>(sizeof(W)));
-                if constexpr (sizeof(W) == 16)
-                    __builtin_amdgcn_raw_buffer_store_b128(v[u], ro, off, 0, kPolicySc1);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b32(v[u], ro, off, 0, kPolicySc1);
-            }
-        }
-        return;
-    }
     for (int f0 = 0; f0 < total; f0 += kRestripeThreads * kU) {
         // A lane past the end takes the last word: it loads it and stores it again, the
         // same value to the same place, so no access needs a guard. A guarded access sits
@@ -173,25 +142,14 @@ __device__ __forceinline__ void restripe_run(const W* __restrict__ in, int64_t T
     }
 }
 
-// Inside a layout launch the restripe keeps non-temporal stores: with device-scope ones
-// the count launch itself ran shorter, but the whole step at 16384 tokens (top-8 over 64
-// ranks, 8 x 32 floats per token) took 698.3 against 688.0 us (same box, identical
-// outputs), and at 4096 tokens it was unchanged.
-#ifndef EP_RESTRIPE_TASK_SC1
-#define EP_RESTRIPE_TASK_SC1 0
-#endif
-
 // One restripe block inside a layout launch: one word in flight per lane.
 __device__ __forceinline__ void restripe_task_block(const RestripeTask& rs, int64_t block) {
     if (rs.vec)
-        restripe_run<u32x4, 1, EP_RESTRIPE_TASK_SC1>(static_cast<const u32x4*>(rs.in), rs.T, rs.NV,
-                                                     rs.VP, rs.Tmax, static_cast<u32x4*>(rs.out),
-                                                     rs.tpb, block);
+        restripe_run<u32x4, 1>(static_cast<const u32x4*>(rs.in), rs.T, rs.NV, rs.VP, rs.Tmax,
+                               static_cast<u32x4*>(rs.out), rs.tpb, block);
     else
-        restripe_run<uint32_t, 1, EP_RESTRIPE_TASK_SC1>(static_cast<const uint32_t*>(rs.in), rs.T,
-                                                        rs.NV, rs.VP, rs.Tmax,
-                                                        static_cast<uint32_t*>(rs.out), rs.tpb,
-                                                        block);
+        restripe_run<uint32_t, 1>(static_cast<const uint32_t*>(rs.in), rs.T, rs.NV, rs.VP,
+                                  rs.Tmax, static_cast<uint32_t*>(rs.out), rs.tpb, block);
 }
 
 // The blocks of a dense restripe (blocks == 0 when T == 0 or there is nothing to do).

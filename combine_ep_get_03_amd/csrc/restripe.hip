@@ -13,14 +13,6 @@
 namespace ep {
 namespace {
 
-// The restripe's own launch stores non-temporally too. Device-scope stores made it faster
-// alone (4.4 against 6.7 us at 16384 tokens, 8 x 32 floats each) but the next kernels
-// slower: one call per step (layout, dispatch, restripe, combine) took 714.8 against
-// 700.2 us there, same box, identical outputs; at 4096 tokens both forms were equal.
-#ifndef EP_RESTRIPE_OWN_SC1
-#define EP_RESTRIPE_OWN_SC1 0
-#endif
-
 constexpr int kRT = kRestripeThreads;
 constexpr int kRU = kRestripeU;
 
@@ -28,7 +20,7 @@ template <typename W>
 __global__ __launch_bounds__(kRT) void restripe_kernel(const W* __restrict__ in, int64_t T,
                                                        int NV, int VP, int64_t Tmax,
                                                        W* __restrict__ out, int tpb) {
-    restripe_run<W, kRU, EP_RESTRIPE_OWN_SC1>(in, T, NV, VP, Tmax, out, tpb, blockIdx.x);
+    restripe_run<W, kRU>(in, T, NV, VP, Tmax, out, tpb, blockIdx.x);
 }
 
 // Sparse path: only routed (token, node) slices move, to row node_slot[t][n] of the node's
